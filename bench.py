@@ -1,0 +1,245 @@
+"""Benchmark of the DLRM hot path on one MI355X.
+
+Default workload ("forward"): batch 32768, 13 log-normal dense features,
+bottom MLP 13-512-256-128, 26 fp32 tables of d = 128 with log-uniform
+cardinalities in [100, 4e7] (about 2e8 rows, about 100 GB in HBM), one
+Zipf(1.1) index per bag, 351-pair interaction, top MLP
+479-1024-1024-512-256-1, bf16 MLPs with fp32 accumulation.  A step is one
+full forward pass over one batch (bottom MLP, pooled lookups, interaction,
+top MLP with sigmoid); inputs are resident in HBM before timing starts.
+
+Prints one JSON line: samples/s, the roofline of the dominant kernel (the
+embedding gather: algorithmic bytes per launch over its average launch time,
+measured with HIP events on its stream), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "DLRM fwd samples/s at 1 GPU; EmbeddingBag HBM GB/s as % of peak"
+
+
+def gather_bytes(K, B, d, nnz):
+    """Algorithmic bytes of one pooled-lookup launch: every looked-up row,
+    the int64 indices and offsets, and the pooled output."""
+    return 4 * d * nnz + 8 * nnz + 8 * (K * B + 1) + 4 * K * B * d
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="forward", choices=["forward", "embbag", "interaction", "train", "tiny"])
+    p.add_argument("--batches", type=int, default=2, help="distinct input batches rotated over the steps")
+    p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-samples", type=int, default=0, help="oracle sample size (0: automatic)")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events recorded on the stream that runs the kernel."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self, stream):
+        import torch
+
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        return e0
+
+    def stop(self, e0, stream):
+        import torch
+
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(stream)
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+def cpu_baseline(w, batches, bottom, top, n_samples):
+    """The oracle (as it stands) on the first n_samples of batch 0: forward
+    for forward-type workloads, pooled lookups for the gather microbench,
+    the sparse update for the training step.  Row regeneration and input
+    slicing are excluded from the timed region."""
+    import oracle
+    from synth import workloads as W
+
+    dense, idx, off = batches[0][:3]
+    S = min(n_samples, w.B)
+    samples = np.arange(S)
+    sidx, soff = W.sub_bags(idx, off, w.K, w.B, samples)
+    ws = w.scaled(B=S)
+    tabs, local, _ = W.compact_rows(ws, sidx, soff)
+    quant = w.mlp_dtype == "bf16"
+    t0 = time.perf_counter()
+    E = oracle.embbag_fwd(tabs, local, soff, S)
+    if w.name not in ("embbag",):
+        x0, _, _ = oracle.mlp_fwd(dense[:S], [p[0] for p in bottom], [p[2] for p in bottom], quant, True)
+        X = np.concatenate([x0, E], axis=1).reshape(S, w.n, w.d)
+        top_in = oracle.interact_fwd(X)
+        oracle.mlp_fwd(top_in, [p[0] for p in top], [p[2] for p in top], quant, False)
+        if w.train:
+            G = batches[0][3].reshape(w.B, -1)[:S]
+            oracle.embbag_bwd_sgd(tabs, local, soff, S, G, w.d, w.lr)
+    dt = time.perf_counter() - t0
+    return S, dt, oracle.num_threads()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): this build has no multi-GPU path; the "
+              "sharding design is documented but not built.", file=sys.stderr)
+        sys.exit(1)
+    import torch
+
+    import deep_learning_recommendation_amd as D
+    from deep_learning_recommendation_amd import pipeline as PL
+    from synth import device as SD
+    from synth import workloads as W
+    import dataclasses
+
+    w = W.get(args.workload)
+    if args.uniform:
+        w = dataclasses.replace(w, index_dist="uniform")
+    t_setup = time.perf_counter()
+    dev = "cuda"
+    tables = SD.make_tables(w)
+    bf16 = w.mlp_dtype == "bf16"
+    bottom = W.mlp_params(w, "bottom") if w.bottom else None
+    top = W.mlp_params(w, "top") if w.top else None
+    batches = []
+    for bi in range(args.batches):
+        idx, off = W.indices_offsets(w, bi)
+        dense = W.dense(w, bi) if w.dense_dim else None
+        G = W.upstream_grad(w, bi) if w.train else None
+        y = W.labels(w, bi) if w.train else None
+        batches.append((dense, idx, off, G, y))
+    dbatches = []
+    for (dense, idx, off, G, y) in batches:
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        dbatches.append((t(dense), t(idx), t(off), t(G), t(y), int(off[-1])))
+    model = None
+    if w.bottom:
+        bp = PL.make_mlp(w.bottom, [p[0] for p in bottom], [p[2] for p in bottom], bf16)
+        tp = PL.make_mlp(w.top, [p[0] for p in top], [p[2] for p in top], bf16)
+        model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=w.train)
+        if w.train:
+            model.sparse_workspace(max(b[5] for b in dbatches))
+    else:
+        ptrs = D.device_pointer_array(tables)
+        out = torch.empty((w.B, w.K * w.d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream()
+    gather_t = Timer()
+    call_t = {}
+
+    def step(i, timed):
+        dense, idx, off, G, y, nnz = dbatches[i % len(dbatches)]
+        if model is None:
+            e0 = gather_t.start(stream) if timed else None
+            D.dlrm_embbag_fwd(ptrs, w.K, w.d, idx, off, w.B, out, w.K * w.d, 0)
+            if timed:
+                gather_t.stop(e0, stream)
+            return
+        n, d = model.n, model.d
+        ev = {}
+
+        def mark(name):
+            if timed:
+                ev[name] = gather_t.start(stream)
+
+        mark("bottom_mlp")
+        D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
+                       model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.X, n * d, None,
+                       model.ws_bot, w.train)
+        mark("embbag")
+        D.dlrm_embbag_fwd(model.table_ptrs, w.K, d, idx, off, w.B, model.X, n * d, d)
+        mark("interact")
+        D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
+        mark("top_mlp")
+        D.dlrm_mlp_fwd(model.top_in, model.top_ld, w.B, model.top.dims, model.top.Ws, model.top.w_ld,
+                       model.top.biases, model.top.w_dtype, D.DLRM_ACT_NONE, model.logit, 1, model.prob,
+                       model.ws_top, w.train)
+        if w.train:
+            mark("dense_bwd")
+            D.dlrm_bce_grad(model.logit, 1, y, w.B, model.dlogit)
+            D.dlrm_mlp_bwd(w.B, model.top.dims, model.top.Ws, model.top.w_ld, D.DLRM_ACT_NONE, model.ws_top,
+                           model.logit, 1, model.dlogit, 1, model.dW_top, model.db_top, None, 0, model.ws_top_bwd)
+            D.dlrm_mlp_bwd(w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld, D.DLRM_ACT_RELU,
+                           model.ws_bot, model.X, n * d, G, n * d, model.dW_bot, model.db_bot, None, 0,
+                           model.ws_bot_bwd)
+            mark("sparse_bwd_sgd")
+            D.dlrm_embbag_bwd_sgd(model.table_ptrs, w.K, d, w.rows, idx, off, w.B, nnz, G, n * d, d, w.lr,
+                                  model.ws_sparse)
+        mark("end")
+        if timed:
+            names = list(ev)
+            for a, b in zip(names[:-1], names[1:]):
+                call_t.setdefault(a, []).append((ev[a], ev[b]))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = w.B * args.steps / elapsed
+    breakdown = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in call_t.items()}
+    nnz_mean = float(np.mean([b[5] for b in dbatches]))
+    gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean)
+    g_ms = breakdown.get("embbag", gather_t.mean_ms())
+    achieved = gbytes / (g_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "embbag_fwd_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": int(gbytes), "avg_launch_ms": round(g_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        ns = args.cpu_samples or {"forward": 16384, "embbag": 16384, "interaction": 512, "train": 1024,
+                                  "tiny": 128}[w.name]
+        S, dt, thr = cpu_baseline(w, batches, bottom, top, ns)
+        what = {"forward": "forward pass", "embbag": "pooled lookups", "interaction": "forward pass",
+                "train": "forward pass and sparse SGD update", "tiny": "forward pass"}[w.name]
+        cpu = {"value": round(S / dt, 2), "unit": "samples/s", "cores": thr, "kind": "oracle",
+               "sample": f"{what} of the first {S} samples of batch 0 ({dt:.1f} s; tables regenerated for the "
+                         f"touched rows only, outside the timed region)"}
+
+    cfg = {"workload": w.name, "batch": w.B, "tables": w.K, "d": w.d, "rows_total": int(sum(w.rows)),
+           "bag": f"{w.bag}:{w.bag_len}", "index": f"{w.index_dist}" + (f"({w.alpha})" if w.index_dist == "zipf" else ""),
+           "bottom_mlp": "-".join(map(str, w.bottom)), "top_mlp": "-".join(map(str, w.top)),
+           "mlp_dtype": w.mlp_dtype, "table_dtype": "f32", "batches_rotated": args.batches}
+    res = {"metric": METRIC, "value": round(value, 1), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32+bf16" if w.mlp_dtype == "bf16" else "f32", "data": "synthetic",
+           "config": cfg, "roofline": roofline, "cpu_baseline": cpu,
+           "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()}, "setup_s": round(t_setup, 1)}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,403 @@
+// GEMM family for the bottom and top MLPs ("Deep Learning Recommendation
+// Model (DLRM)" explainer, Key Method Details: Bottom MLP, Top MLP;
+// briansu.co DLRM, Key equations, Output).
+//
+// gemm_bf16: C = act(A W^T + b) with A [M][K] and W [N][K] both K-contiguous,
+// the natural layout of a fully connected layer y = x W^T.  gfx950 bf16 MFMA
+// v_mfma_f32_32x32x16_bf16: each lane feeds 8 consecutive k of one row of A
+// (row l % 32, k (l / 32) * 8) and of W, so both operands are read from LDS
+// with one 16-byte ds_read per fragment.  Block tile BM x BN x 32 with four
+// waves in a 2 x 2 grid, LDS rows padded to 80 bytes (conflict-free 16-byte
+// reads), double-buffered LDS with global loads for the next k-tile in flight
+// during the MFMAs.  Tiles are walked N-fastest and block ids are regrouped
+// so that the tiles sharing an A panel land on one XCD (one L2).
+#include "gemm.hpp"
+
+namespace dlrm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 32;
+constexpr int LDS_STRIDE = BK + 8;  // bf16 per LDS row: 80 bytes
+
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+__device__ __forceinline__ float relu_f(float v) { return v > 0.f ? v : 0.f; }
+
+// 8 consecutive bf16 (row, k..k+7); zero outside rows x [0, kend).
+template <bool VEC>
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, int64_t ld, int row, int rows, int k,
+                                            int kend) {
+  if (row >= rows || k >= kend) return make_uint4(0u, 0u, 0u, 0u);
+  const uint16_t* p = base + (int64_t)row * ld + k;
+  if (VEC && k + 8 <= kend) return *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (k + 2 * i < kend) ? (uint32_t)p[2 * i] : 0u;
+    const uint32_t hi = (k + 2 * i + 1 < kend) ? (uint32_t)p[2 * i + 1] : 0u;
+    w[i] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int BM, int BN, bool VEC, typename OutT, bool PARTIAL>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                        const uint16_t* __restrict__ W, int64_t ldw,
+                                                        const float* __restrict__ bias, OutT* __restrict__ C,
+                                                        int64_t ldc, int M, int N, int K, int relu, int tiles_n,
+                                                        int k_per_split) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int AP = BM / 64, BP = BN / 64;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int bid = blockIdx.x;
+  const int total = gridDim.x;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int tile_m = bid / tiles_n, tile_n = bid - tile_m * tiles_n;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int kbeg = (int)blockIdx.z * k_per_split;
+  const int kend = min(K, kbeg + k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  uint4 ga[AP], gb[BP];
+  auto gload = [&](int kt) {
+    const int k = kbeg + kt * BK + lc;
+#pragma unroll
+    for (int i = 0; i < AP; ++i) ga[i] = load_chunk<VEC>(A, lda, m0 + i * 64 + lr, M, k, kend);
+#pragma unroll
+    for (int i = 0; i < BP; ++i) gb[i] = load_chunk<VEC>(W, ldw, n0 + i * 64 + lr, N, k, kend);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i) *reinterpret_cast<uint4*>(&As[buf][(i * 64 + lr) * LDS_STRIDE + lc]) = ga[i];
+#pragma unroll
+    for (int i = 0; i < BP; ++i) *reinterpret_cast<uint4*>(&Bs[buf][(i * 64 + lr) * LDS_STRIDE + lc]) = gb[i];
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kof = ks * 16 + (lane >> 5) * 8;
+      bf16x8 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * WM + i * 32 + (lane & 31)) * LDS_STRIDE + kof]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * WN + j * 32 + (lane & 31)) * LDS_STRIDE + kof]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // D layout of a 32x32 block: lane l holds column l % 32 and rows
+  // 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int j = n0 + wn * WN + tn * 32 + (lane & 31);
+    const float bj = (!PARTIAL && bias != nullptr && j < N) ? bias[j] : 0.f;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = m0 + wm * WM + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (i < M && j < N) {
+          float val = acc[tm][tn][v];
+          if (PARTIAL) {
+            C[((int64_t)blockIdx.z * M + i) * ldc + j] = val;
+          } else {
+            val = val + bj;
+            if (relu) val = relu_f(val);
+            store_out(&C[(int64_t)i * ldc + j], val);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, bool VEC, typename OutT, bool PARTIAL>
+void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
+                 int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, VEC, OutT, PARTIAL>), dim3(tm * tn, 1, splits), dim3(256), 0, s, A,
+                     lda, W, ldw, bias, C, ldc, M, N, K, relu, tn, k_per_split);
+}
+
+template <bool VEC, typename OutT, bool PARTIAL>
+void pick_tile(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
+               int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
+  const int64_t big = ceil_div(M, 256) * ceil_div(N, 128) * splits;
+  if (big >= 512)
+    launch_gemm<256, 128, VEC, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split, s);
+  else
+    launch_gemm<128, 128, VEC, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split, s);
+}
+
+// ---------------------------------------------------------------- small K
+
+template <typename InT>
+__device__ __forceinline__ float in_as_bf16(const InT* p);
+template <>
+__device__ __forceinline__ float in_as_bf16<float>(const float* p) {
+  return bf16_to_f32(f32_to_bf16(*p));
+}
+template <>
+__device__ __forceinline__ float in_as_bf16<uint16_t>(const uint16_t* p) {
+  return bf16_to_f32(*p);
+}
+
+// one thread per (row, 8 consecutive outputs); products of two bf16 values
+// are exact in fp32, sums fp32 in k order
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(256) void smallk_kernel(const InT* __restrict__ in, int64_t ld_in,
+                                                     const uint16_t* __restrict__ W, int64_t ldw,
+                                                     const float* __restrict__ bias, OutT* __restrict__ C,
+                                                     int64_t ldc, int M, int N, int K, int relu) {
+  const int n8 = (N + 7) / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)M * n8) return;
+  const int m = (int)(t / n8);
+  const int nb = (int)(t - (int64_t)m * n8) * 8;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  const InT* row = in + (int64_t)m * ld_in;
+  for (int k = 0; k < K; ++k) {
+    const float x = in_as_bf16<InT>(row + k);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (nb + j < N) acc[j] = __builtin_fmaf(x, bf16_to_f32(W[(int64_t)(nb + j) * ldw + k]), acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (nb + j < N) {
+      float v = acc[j] + bias[nb + j];
+      if (relu) v = relu_f(v);
+      store_out(&C[(int64_t)m * ldc + nb + j], v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- GEMV (N == 1)
+
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                        const uint16_t* __restrict__ w,
+                                                        const float* __restrict__ bias, float* __restrict__ out,
+                                                        int64_t ldo, float* __restrict__ prob, int M, int K,
+                                                        int relu, int vec) {
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < M) {
+    const uint16_t* a = A + (int64_t)row * lda;
+    for (int k = sub * 8; k < K; k += 128) {
+      if (vec && k + 8 <= K) {
+        const uint4 av = *reinterpret_cast<const uint4*>(a + k);
+        const uint4 wv = *reinterpret_cast<const uint4*>(w + k);
+        const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = __builtin_fmaf(bf16_to_f32((uint16_t)(aw[i] & 0xffffu)), bf16_to_f32((uint16_t)(ww[i] & 0xffffu)), acc);
+          acc = __builtin_fmaf(bf16_to_f32((uint16_t)(aw[i] >> 16)), bf16_to_f32((uint16_t)(ww[i] >> 16)), acc);
+        }
+      } else {
+        for (int i = 0; i < 8 && k + i < K; ++i) acc = __builtin_fmaf(bf16_to_f32(a[k + i]), bf16_to_f32(w[k + i]), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 16);
+  if (sub == 0 && row < M) {
+    float v = acc + bias[0];
+    if (relu) v = relu_f(v);
+    out[(int64_t)row * ldo] = v;
+    if (prob) prob[row] = 1.f / (1.f + expf(-v));
+  }
+}
+
+// ---------------------------------------------------------------- fp32 network
+
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
+                                                       const float* __restrict__ W, int64_t ldw,
+                                                       const float* __restrict__ bias, float* __restrict__ C,
+                                                       int64_t ldc, float* __restrict__ prob, int M, int N, int K,
+                                                       int relu) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)M * N) return;
+  const int m = (int)(t / N), n = (int)(t - (int64_t)(t / N) * N);
+  const float* a = A + (int64_t)m * lda;
+  const float* w = W + (int64_t)n * ldw;
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(a[k], w[k], acc);
+  float v = acc + bias[n];
+  if (relu) v = relu_f(v);
+  C[(int64_t)m * ldc + n] = v;
+  if (prob && N == 1) prob[m] = 1.f / (1.f + expf(-v));
+}
+
+// ---------------------------------------------------------------- helpers
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ldi,
+                                                             uint16_t* __restrict__ out, int64_t ldo, int R,
+                                                             int C) {
+  __shared__ uint16_t tile[64][66];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? in[(int64_t)r * ldi + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) out[(int64_t)c * ldo + r] = tile[tx][i];
+  }
+}
+
+__global__ __launch_bounds__(256) void convert_bf16_kernel(const float* __restrict__ in, int64_t ldi,
+                                                           uint16_t* __restrict__ out, int64_t ldo, int R, int C,
+                                                           int Cpad) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)R * Cpad) return;
+  const int r = (int)(t / Cpad), c = (int)(t - (int64_t)r * Cpad);
+  out[(int64_t)r * ldo + c] = c < C ? f32_to_bf16(in[(int64_t)r * ldi + c]) : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                            const float* __restrict__ bias, float* __restrict__ C,
+                                                            int64_t ldc, int relu) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t MN = (int64_t)M * N;
+  if (t >= MN) return;
+  const int i = (int)(t / N), j = (int)(t - (int64_t)i * N);
+  float v = 0.f;
+  for (int z = 0; z < splits; ++z) v = v + part[z * MN + t];
+  if (bias) v = v + bias[j];
+  if (relu) v = relu_f(v);
+  C[(int64_t)i * ldc + j] = v;
+}
+
+}  // namespace
+
+int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, void* C,
+              int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s) {
+  if (M <= 0 || N <= 0) return DLRM_OK;
+  const bool vec = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0;
+  const int kps = (int)round_up(K, BK);
+  if (out_bf16) {
+    auto* c = static_cast<uint16_t*>(C);
+    if (vec) pick_tile<true, uint16_t, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+    else pick_tile<false, uint16_t, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+  } else {
+    auto* c = static_cast<float*>(C);
+    if (vec) pick_tile<true, float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+    else pick_tile<false, float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+  }
+  return launch_status();
+}
+
+int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M, int N,
+                     int K, int splits, hipStream_t s) {
+  if (M <= 0 || N <= 0) return DLRM_OK;
+  const bool vec = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0;
+  const int kps = (int)round_up(ceil_div(K, splits), BK);
+  if (vec) pick_tile<true, float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
+  else pick_tile<false, float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
+  return launch_status();
+}
+
+int reduce_splits(const float* part, int splits, int M, int N, const float* bias, float* C, int64_t ldc, bool relu,
+                  hipStream_t s) {
+  const int64_t MN = (int64_t)M * N;
+  if (MN <= 0) return DLRM_OK;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)ceil_div(MN, 256)), dim3(256), 0, s, part, splits, M, N,
+                     bias, C, ldc, (int)relu);
+  return launch_status();
+}
+
+int gemm_smallk(const void* in, bool in_bf16, int64_t ld_in, const uint16_t* W, int64_t ldw, const float* bias,
+                void* C, int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s) {
+  const int64_t threads = (int64_t)M * ceil_div(N, 8);
+  if (threads <= 0) return DLRM_OK;
+  const dim3 grid((unsigned)ceil_div(threads, 256)), block(256);
+  if (in_bf16) {
+    if (out_bf16)
+      hipLaunchKernelGGL((smallk_kernel<uint16_t, uint16_t>), grid, block, 0, s, static_cast<const uint16_t*>(in),
+                         ld_in, W, ldw, bias, static_cast<uint16_t*>(C), ldc, M, N, K, (int)relu);
+    else
+      hipLaunchKernelGGL((smallk_kernel<uint16_t, float>), grid, block, 0, s, static_cast<const uint16_t*>(in), ld_in,
+                         W, ldw, bias, static_cast<float*>(C), ldc, M, N, K, (int)relu);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((smallk_kernel<float, uint16_t>), grid, block, 0, s, static_cast<const float*>(in), ld_in, W,
+                         ldw, bias, static_cast<uint16_t*>(C), ldc, M, N, K, (int)relu);
+    else
+      hipLaunchKernelGGL((smallk_kernel<float, float>), grid, block, 0, s, static_cast<const float*>(in), ld_in, W,
+                         ldw, bias, static_cast<float*>(C), ldc, M, N, K, (int)relu);
+  }
+  return launch_status();
+}
+
+int gemv_bf16(const uint16_t* A, int64_t lda, const uint16_t* w, const float* bias, float* out, int64_t ldo,
+              float* prob, int M, int K, bool relu, hipStream_t s) {
+  if (M <= 0) return DLRM_OK;
+  const int vec = aligned16(A) && aligned16(w) && (lda % 8) == 0;
+  hipLaunchKernelGGL(gemv_bf16_kernel, dim3((unsigned)ceil_div(M, 16)), dim3(256), 0, s, A, lda, w, bias, out, ldo,
+                     prob, M, K, (int)relu, vec);
+  return launch_status();
+}
+
+int gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const float* bias, float* C, int64_t ldc,
+             float* prob, int M, int N, int K, bool relu, hipStream_t s) {
+  const int64_t total = (int64_t)M * N;
+  if (total <= 0) return DLRM_OK;
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, A, lda, W, ldw, bias, C,
+                     ldc, prob, M, N, K, (int)relu);
+  return launch_status();
+}
+
+int transpose_bf16(const uint16_t* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int R, int C, hipStream_t s) {
+  if (R <= 0 || C <= 0) return DLRM_OK;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)ceil_div(C, 64), (unsigned)ceil_div(R, 64)), dim3(256), 0,
+                     s, in, ld_in, out, ld_out, R, C);
+  return launch_status();
+}
+
+int convert_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int R, int C, hipStream_t s) {
+  const int Cpad = (int)(round_up(C, 8) < ld_out ? round_up(C, 8) : ld_out);
+  const int64_t total = (int64_t)R * Cpad;
+  if (total <= 0) return DLRM_OK;
+  hipLaunchKernelGGL(convert_bf16_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, in, ld_in, out, ld_out,
+                     R, C, Cpad);
+  return launch_status();
+}
+
+}  // namespace dlrm

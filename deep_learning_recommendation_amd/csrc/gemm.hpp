@@ -1,0 +1,38 @@
+// Internal GEMM-family launchers used by the MLP forward and backward.
+#pragma once
+
+#include "common.hpp"
+
+namespace dlrm {
+
+// C[M][N] = act(A[M][K] * W[N][K]^T + bias[N]) on bf16 operands with fp32
+// accumulation (MFMA).  A, W: bf16 bits; C: fp32 or bf16 (out_bf16).
+// With splits > 1, each of `splits` K-slices writes fp32 partials to
+// part[z][M][N] (no bias or activation) and reduce_splits() finishes.
+int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, void* C,
+              int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s);
+int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M, int N,
+                     int K, int splits, hipStream_t s);
+int reduce_splits(const float* part, int splits, int M, int N, const float* bias, float* C, int64_t ldc,
+                  bool relu, hipStream_t s);
+
+// First layer with fp32 or bf16 input and small K: inputs rounded to bf16,
+// fp32 sums over k ascending.  Output bf16 or fp32.
+int gemm_smallk(const void* in, bool in_bf16, int64_t ld_in, const uint16_t* W, int64_t ldw, const float* bias,
+                void* C, int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s);
+
+// N == 1 layer: out[m] = sum_k A[m][k] w[k] + bias; prob = sigmoid(out).
+int gemv_bf16(const uint16_t* A, int64_t lda, const uint16_t* w, const float* bias, float* out, int64_t ldo,
+              float* prob, int M, int K, bool relu, hipStream_t s);
+
+// fp32 network: C = act(A W^T + bias), A fp32, W fp32.
+int gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const float* bias, float* C, int64_t ldc,
+             float* prob, int M, int N, int K, bool relu, hipStream_t s);
+
+// out[c][r] = in[r][c] (bf16 bits).
+int transpose_bf16(const uint16_t* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int R, int C, hipStream_t s);
+
+// out[r][c] = bf16(in[r][c]) for c < C, zero for C <= c < ld_pad_to.
+int convert_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int R, int C, hipStream_t s);
+
+}  // namespace dlrm

@@ -1,0 +1,363 @@
+// Multilayer perceptrons of the model: the bottom MLP (dense features -> d)
+// and the top MLP (interaction row -> logit -> sigmoid), "Deep Learning
+// Recommendation Model (DLRM)" explainer, Key Method Details (Bottom MLP, Top
+// MLP, Loss); briansu.co DLRM, Key equations (Output).
+//
+// Forward: one launch per layer.  bf16 networks keep hidden activations as
+// bf16 rows padded to a multiple of 8 elements so every MFMA operand load is
+// 16 bytes; the first layer of a narrow input (K <= 32, e.g. 13 dense
+// features) uses a VALU kernel, N == 1 output layers a GEMV with the sigmoid
+// fused, everything else the bf16 MFMA GEMM with bias + ReLU + convert fused
+// in its epilogue.
+//
+// Backward (bf16 networks): per layer, delta = g * 1[y > 0] (bf16 for the
+// MFMA operands), db by a deterministic two-stage column sum, dW = delta^T x
+// as a split-K MFMA GEMM over the batch (partials summed in a fixed order),
+// and g_prev = delta W.  Transposed copies make every GEMM the K-contiguous
+// form the MFMA kernel reads.
+#include "gemm.hpp"
+
+namespace dlrm {
+namespace {
+
+struct FwdLayout {
+  size_t bytes = 0;
+  size_t act_off[65];  // act_off[l]: layer l's input buffer (l = 0 .. L-1); ~0 if none
+  int64_t act_ld[65];
+  bool act_bf16 = true;
+};
+
+// Shared by forward and backward: where layer inputs live in the forward workspace.
+bool fwd_layout(int64_t B, int32_t L, const int32_t* dims, int32_t w_dtype, int32_t save_acts, FwdLayout* lay) {
+  if (L < 1 || L > 64 || B < 1) return false;
+  for (int l = 0; l <= L; ++l)
+    if (dims[l] < 1) return false;
+  Carver cv(nullptr);
+  const bool bf = (w_dtype == DLRM_BF16);
+  lay->act_bf16 = bf;
+  const size_t esz = bf ? 2 : 4;
+  for (int l = 0; l <= L; ++l) {
+    lay->act_off[l] = ~(size_t)0;
+    lay->act_ld[l] = bf ? round_up(dims[l], 8) : dims[l];
+  }
+  // layer 0's input: a bf16 copy of the caller's input (always for bf16 nets:
+  // fp32 inputs are rounded once here; kept for the backward pass)
+  if (bf) {
+    cv.take<char>(esz * (size_t)(B * lay->act_ld[0]));
+    lay->act_off[0] = 0;
+  }
+  if (save_acts) {
+    for (int l = 1; l < L; ++l) {
+      cv.used = (size_t)round_up((int64_t)cv.used, 256);
+      lay->act_off[l] = cv.used;
+      cv.used += esz * (size_t)(B * lay->act_ld[l]);
+    }
+  } else {
+    int64_t wmax = 0;
+    for (int l = 1; l < L; ++l) wmax = lay->act_ld[l] > wmax ? lay->act_ld[l] : wmax;
+    size_t ping = 0, pong = 0;
+    if (L > 1) {
+      cv.used = (size_t)round_up((int64_t)cv.used, 256);
+      ping = cv.used;
+      cv.used += esz * (size_t)(B * wmax);
+      cv.used = (size_t)round_up((int64_t)cv.used, 256);
+      pong = cv.used;
+      cv.used += esz * (size_t)(B * wmax);
+    }
+    for (int l = 1; l < L; ++l) lay->act_off[l] = (l & 1) ? ping : pong;
+  }
+  lay->bytes = cv.bytes();
+  return true;
+}
+
+__global__ __launch_bounds__(256) void copy_bf16_kernel(const uint16_t* __restrict__ in, int64_t ldi,
+                                                        uint16_t* __restrict__ out, int64_t ldo, int R, int C,
+                                                        int Cpad) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)R * Cpad) return;
+  const int r = (int)(t / Cpad), c = (int)(t - (int64_t)r * Cpad);
+  out[(int64_t)r * ldo + c] = c < C ? in[(int64_t)r * ldi + c] : (uint16_t)0;
+}
+
+template <typename YT>
+__device__ __forceinline__ bool positive(const YT* p);
+template <>
+__device__ __forceinline__ bool positive<float>(const float* p) {
+  return *p > 0.f;
+}
+template <>
+__device__ __forceinline__ bool positive<uint16_t>(const uint16_t* p) {
+  return bf16_to_f32(*p) > 0.f;
+}
+
+// delta = g * 1[y > 0] (or g), stored as bf16 [B][ldd]
+template <typename YT>
+__global__ __launch_bounds__(256) void delta_kernel(const float* __restrict__ g, int64_t ldg,
+                                                    const YT* __restrict__ y, int64_t ldy, int relu,
+                                                    uint16_t* __restrict__ dlt, int64_t ldd, int B, int N) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)B * N) return;
+  const int b = (int)(t / N), o = (int)(t - (int64_t)b * N);
+  float v = g[(int64_t)b * ldg + o];
+  if (relu && !positive<YT>(y + (int64_t)b * ldy + o)) v = 0.f;
+  dlt[(int64_t)b * ldd + o] = f32_to_bf16(v);
+}
+
+// db partials: part[chunk][o] = sum over rows of the chunk of masked g (fp32, row order)
+template <typename YT>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const float* __restrict__ g, int64_t ldg,
+                                                             const YT* __restrict__ y, int64_t ldy, int relu,
+                                                             float* __restrict__ part, int B, int N, int rows_per) {
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= N) return;
+  const int r0 = blockIdx.y * rows_per, r1 = min(B, r0 + rows_per);
+  float s = 0.f;
+  for (int b = r0; b < r1; ++b) {
+    float v = g[(int64_t)b * ldg + o];
+    if (relu && !positive<YT>(y + (int64_t)b * ldy + o)) v = 0.f;
+    s = s + v;
+  }
+  part[(int64_t)blockIdx.y * N + o] = s;
+}
+
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int chunks, int N,
+                                                           float* __restrict__ db) {
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= N) return;
+  float s = 0.f;
+  for (int c = 0; c < chunks; ++c) s = s + part[(int64_t)c * N + o];
+  db[o] = s;
+}
+
+__global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__ logit, int64_t ld,
+                                                       const float* __restrict__ y, int64_t B, float* __restrict__ dY) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const float s = 1.f / (1.f + expf(-logit[b * ld]));
+  dY[b] = (s - y[b]) / (float)B;
+}
+
+struct BwdLayout {
+  size_t g[2], dlt, dltT, xT, wT, part, dbp, bytes;
+  int64_t ld_dlt, ld_B, splits_max;
+};
+
+constexpr int kColChunks = 32;
+constexpr int kMaxSplits = 16;
+
+bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
+  if (L < 1 || L > 64 || B < 1) return false;
+  int64_t wmax = 0, wfo = 0, prod = 0;
+  for (int l = 0; l <= L; ++l) {
+    if (dims[l] < 1) return false;
+    wmax = dims[l] > wmax ? dims[l] : wmax;
+  }
+  for (int l = 0; l < L; ++l) {
+    wfo = dims[l + 1] > wfo ? dims[l + 1] : wfo;
+    const int64_t p = (int64_t)dims[l] * dims[l + 1];
+    prod = p > prod ? p : prod;
+  }
+  Carver cv(nullptr);
+  lay->ld_dlt = round_up(wfo, 8);
+  lay->ld_B = round_up(B, 8);
+  lay->splits_max = kMaxSplits;
+  auto take = [&](size_t bytes) {
+    cv.used = (size_t)round_up((int64_t)cv.used, 256);
+    const size_t at = cv.used;
+    cv.used += bytes;
+    return at;
+  };
+  lay->g[0] = take(4 * (size_t)(B * wmax));
+  lay->g[1] = take(4 * (size_t)(B * wmax));
+  lay->dlt = take(2 * (size_t)(B * lay->ld_dlt));
+  lay->dltT = take(2 * (size_t)(wfo * lay->ld_B));
+  lay->xT = take(2 * (size_t)(wmax * lay->ld_B));
+  lay->wT = take(2 * (size_t)(wmax * lay->ld_dlt));
+  lay->part = take(4 * (size_t)(kMaxSplits * prod));
+  lay->dbp = take(4 * (size_t)(kColChunks * wfo));
+  lay->bytes = cv.bytes();
+  return true;
+}
+
+}  // namespace
+}  // namespace dlrm
+
+using namespace dlrm;
+
+extern "C" size_t dlrm_mlp_workspace_size(int64_t B, int32_t L, const int32_t* dims, int32_t w_dtype,
+                                          int32_t save_acts) {
+  if (!dims) return 0;
+  FwdLayout lay;
+  if (!fwd_layout(B, L, dims, w_dtype, save_acts, &lay)) return 0;
+  return lay.bytes ? lay.bytes : 256;
+}
+
+extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int64_t B, int32_t L,
+                            const int32_t* dims, const void* const* W, const int32_t* w_ld, const float* const* bias,
+                            int32_t w_dtype, int32_t last_act, float* out, int64_t out_ld, float* prob, void* ws,
+                            size_t ws_bytes, int32_t save_acts, hipStream_t stream) {
+  if (!in || !dims || !W || !bias || !out) return DLRM_E_INVALID;
+  if (w_dtype != DLRM_F32 && w_dtype != DLRM_BF16) return DLRM_E_INVALID;
+  if (in_dtype != DLRM_F32 && in_dtype != DLRM_BF16) return DLRM_E_INVALID;
+  if (w_dtype == DLRM_F32 && in_dtype != DLRM_F32) return DLRM_E_INVALID;
+  if (last_act != DLRM_ACT_NONE && last_act != DLRM_ACT_RELU) return DLRM_E_INVALID;
+  if (B < 1 || B > 0x7fffffffLL) return DLRM_E_INVALID;
+  FwdLayout lay;
+  if (!fwd_layout(B, L, dims, w_dtype, save_acts, &lay)) return DLRM_E_INVALID;
+  if (in_ld < dims[0] || out_ld < dims[L]) return DLRM_E_INVALID;
+  for (int l = 0; l < L; ++l) {
+    if (!W[l] || !bias[l]) return DLRM_E_INVALID;
+    if (w_ld && w_ld[l] < dims[l]) return DLRM_E_INVALID;
+  }
+  if (prob && dims[L] != 1) return DLRM_E_INVALID;
+  if (lay.bytes > 0 && (!ws || ws_bytes < lay.bytes)) return DLRM_E_WORKSPACE;
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u)) return DLRM_E_INVALID;
+  char* wsb = static_cast<char*>(ws);
+  const int M = (int)B;
+  int rc = DLRM_OK;
+
+  if (w_dtype == DLRM_F32) {
+    const float* src = static_cast<const float*>(in);
+    int64_t ld_src = in_ld;
+    for (int l = 0; l < L && rc == DLRM_OK; ++l) {
+      const int fi = dims[l], fo = dims[l + 1];
+      const bool last = (l == L - 1);
+      const bool relu = !last || last_act == DLRM_ACT_RELU;
+      float* dst = last ? out : reinterpret_cast<float*>(wsb + lay.act_off[l + 1]);
+      const int64_t ld_dst = last ? out_ld : lay.act_ld[l + 1];
+      const int64_t wl = w_ld ? w_ld[l] : fi;
+      rc = gemm_f32(src, ld_src, static_cast<const float*>(W[l]), wl, bias[l], dst, ld_dst, last ? prob : nullptr, M,
+                    fo, fi, relu, stream);
+      src = dst;
+      ld_src = ld_dst;
+    }
+    return rc;
+  }
+
+  // bf16 network: layer 0's input rounded once into the workspace
+  uint16_t* act0 = reinterpret_cast<uint16_t*>(wsb + lay.act_off[0]);
+  if (in_dtype == DLRM_F32) {
+    rc = convert_to_bf16(static_cast<const float*>(in), in_ld, act0, lay.act_ld[0], M, dims[0], stream);
+  } else {
+    const int Cpad = (int)lay.act_ld[0];
+    const int64_t total = (int64_t)M * Cpad;
+    hipLaunchKernelGGL(copy_bf16_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(in), in_ld, act0, lay.act_ld[0], M, dims[0], Cpad);
+    rc = launch_status();
+  }
+  for (int l = 0; l < L && rc == DLRM_OK; ++l) {
+    const int fi = dims[l], fo = dims[l + 1];
+    const bool last = (l == L - 1);
+    const bool relu = !last || last_act == DLRM_ACT_RELU;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(wsb + lay.act_off[l]);
+    const int64_t ld_src = lay.act_ld[l];
+    const uint16_t* w = static_cast<const uint16_t*>(W[l]);
+    const int64_t wl = w_ld ? w_ld[l] : fi;
+    void* dst = last ? static_cast<void*>(out) : static_cast<void*>(wsb + lay.act_off[l + 1]);
+    const int64_t ld_dst = last ? out_ld : lay.act_ld[l + 1];
+    if (last && fo == 1)
+      rc = gemv_bf16(src, ld_src, w, bias[l], out, out_ld, prob, M, fi, relu, stream);
+    else if (fi <= 32)
+      rc = gemm_smallk(src, true, ld_src, w, wl, bias[l], dst, ld_dst, !last, M, fo, fi, relu, stream);
+    else
+      rc = gemm_bf16(src, ld_src, w, wl, bias[l], dst, ld_dst, !last, M, fo, fi, relu, stream);
+  }
+  return rc;
+}
+
+extern "C" size_t dlrm_mlp_bwd_workspace_size(int64_t B, int32_t L, const int32_t* dims) {
+  if (!dims) return 0;
+  BwdLayout lay;
+  if (!bwd_layout(B, L, dims, &lay)) return 0;
+  return lay.bytes;
+}
+
+extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const void* const* W, const int32_t* w_ld,
+                            int32_t last_act, const void* fwd_ws, const float* out, int64_t out_ld, const float* dY,
+                            int64_t dy_ld, float* const* dW, float* const* db, float* dX, int64_t dx_ld, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (!dims || !W || !fwd_ws || !dY || !dW || !db) return DLRM_E_INVALID;
+  if (last_act != DLRM_ACT_NONE && last_act != DLRM_ACT_RELU) return DLRM_E_INVALID;
+  if (last_act == DLRM_ACT_RELU && !out) return DLRM_E_INVALID;
+  if (B < 1 || B > 0x7fffffffLL) return DLRM_E_INVALID;
+  FwdLayout fl;
+  BwdLayout bl;
+  if (!fwd_layout(B, L, dims, DLRM_BF16, 1, &fl) || !bwd_layout(B, L, dims, &bl)) return DLRM_E_INVALID;
+  if (dy_ld < dims[L] || (out && out_ld < dims[L]) || (dX && dx_ld < dims[0])) return DLRM_E_INVALID;
+  for (int l = 0; l < L; ++l) {
+    if (!W[l] || !dW[l] || !db[l]) return DLRM_E_INVALID;
+    if (w_ld && w_ld[l] < dims[l]) return DLRM_E_INVALID;
+  }
+  if (!ws || ws_bytes < bl.bytes) return DLRM_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) || (reinterpret_cast<uintptr_t>(fwd_ws) & 255u)) return DLRM_E_INVALID;
+
+  const char* fws = static_cast<const char*>(fwd_ws);
+  char* w = static_cast<char*>(ws);
+  float* gbuf[2] = {reinterpret_cast<float*>(w + bl.g[0]), reinterpret_cast<float*>(w + bl.g[1])};
+  uint16_t* dlt = reinterpret_cast<uint16_t*>(w + bl.dlt);
+  uint16_t* dltT = reinterpret_cast<uint16_t*>(w + bl.dltT);
+  uint16_t* xT = reinterpret_cast<uint16_t*>(w + bl.xT);
+  uint16_t* wT = reinterpret_cast<uint16_t*>(w + bl.wT);
+  float* part = reinterpret_cast<float*>(w + bl.part);
+  float* dbp = reinterpret_cast<float*>(w + bl.dbp);
+  const int M = (int)B;
+  const int rows_per = (int)ceil_div(B, kColChunks);
+  const int chunks = (int)ceil_div(B, rows_per);
+
+  const float* g = dY;
+  int64_t ldg = dy_ld;
+  int rc = DLRM_OK;
+  for (int l = L - 1; l >= 0 && rc == DLRM_OK; --l) {
+    const int fi = dims[l], fo = dims[l + 1];
+    const bool relu = (l < L - 1) || last_act == DLRM_ACT_RELU;
+    const int64_t total = (int64_t)M * fo;
+    const dim3 g1((unsigned)ceil_div(total, 256)), b1(256);
+    const dim3 gc((unsigned)ceil_div(fo, 256), (unsigned)chunks);
+    // 1. delta (bf16) and db
+    if (l == L - 1) {
+      const float* y = relu ? out : g;  // mask source unused when relu == 0
+      const int64_t ldy = relu ? out_ld : ldg;
+      hipLaunchKernelGGL((delta_kernel<float>), g1, b1, 0, stream, g, ldg, y, ldy, (int)relu, dlt, bl.ld_dlt, M, fo);
+      hipLaunchKernelGGL((colsum_partial_kernel<float>), gc, b1, 0, stream, g, ldg, y, ldy, (int)relu, dbp, M, fo,
+                         rows_per);
+    } else {
+      const uint16_t* y = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l + 1]);
+      hipLaunchKernelGGL((delta_kernel<uint16_t>), g1, b1, 0, stream, g, ldg, y, fl.act_ld[l + 1], (int)relu, dlt,
+                         bl.ld_dlt, M, fo);
+      hipLaunchKernelGGL((colsum_partial_kernel<uint16_t>), gc, b1, 0, stream, g, ldg, y, fl.act_ld[l + 1], (int)relu,
+                         dbp, M, fo, rows_per);
+    }
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 256)), b1, 0, stream, dbp, chunks, fo, db[l]);
+    if ((rc = launch_status()) != DLRM_OK) break;
+    // 2. dW = delta^T x  (M = fo, N = fi, K = B), split over the batch
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l]);
+    if ((rc = transpose_bf16(dlt, bl.ld_dlt, dltT, bl.ld_B, M, fo, stream)) != DLRM_OK) break;
+    if ((rc = transpose_bf16(x, fl.act_ld[l], xT, bl.ld_B, M, fi, stream)) != DLRM_OK) break;
+    const int64_t tiles = ceil_div(fo, 128) * ceil_div(fi, 128);
+    int splits = (int)ceil_div(512, tiles);
+    if (splits > kMaxSplits) splits = kMaxSplits;
+    if (splits > (int)ceil_div(M, 256)) splits = (int)ceil_div(M, 256);
+    if (splits < 1) splits = 1;
+    if ((rc = gemm_bf16_splitk(dltT, bl.ld_B, xT, bl.ld_B, part, fo, fi, M, splits, stream)) != DLRM_OK) break;
+    if ((rc = reduce_splits(part, splits, fo, fi, nullptr, dW[l], fi, false, stream)) != DLRM_OK) break;
+    // 3. g_prev = delta W  (M = B, N = fi, K = fo)
+    if (l > 0 || dX) {
+      const int64_t wl = w_ld ? w_ld[l] : fi;
+      if ((rc = transpose_bf16(static_cast<const uint16_t*>(W[l]), wl, wT, bl.ld_dlt, fo, fi, stream)) != DLRM_OK) break;
+      float* gp = (l == 0) ? dX : gbuf[l & 1];
+      const int64_t ldp = (l == 0) ? dx_ld : fi;
+      rc = gemm_bf16(dlt, bl.ld_dlt, wT, bl.ld_dlt, nullptr, gp, ldp, false, M, fi, fo, false, stream);
+      g = gp;
+      ldg = ldp;
+    }
+  }
+  return rc;
+}
+
+extern "C" int dlrm_bce_grad(const float* logit, int64_t logit_ld, const float* y, int64_t B, float* dY,
+                             hipStream_t stream) {
+  if (!logit || !y || !dY || B < 1 || logit_ld < 1) return DLRM_E_INVALID;
+  hipLaunchKernelGGL(bce_grad_kernel, dim3((unsigned)ceil_div(B, 256)), dim3(256), 0, stream, logit, logit_ld, y, B,
+                     dY);
+  return launch_status();
+}

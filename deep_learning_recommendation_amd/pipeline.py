@@ -1,0 +1,124 @@
+"""The DLRM forward pass and training step as a sequence of libdlrm calls.
+
+Holds device buffers (torch tensors: memory only) and orders the C-ABI
+calls on one stream; it performs no arithmetic itself.
+
+Forward ([SU] "briansu.co DLRM", How it works and Key equations):
+  1. dlrm_mlp_fwd(bottom)   dense [B][13] -> X[:, 0, :]          (fp32)
+  2. dlrm_embbag_fwd        bags of K tables -> X[:, 1..K, :]     (fp32)
+  3. dlrm_interact_fwd      X -> [x_dense, tril(X X^T)]           (bf16 row)
+  4. dlrm_mlp_fwd(top)      -> logit, sigmoid(logit)
+Training step (sum-pooled tables, row-wise SGD):
+  forward with saved activations, dlrm_bce_grad, dlrm_mlp_bwd(top),
+  dlrm_mlp_bwd(bottom) seeded by the X row-0 gradient, and
+  dlrm_embbag_bwd_sgd with the X rows 1..K gradient.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as C
+
+
+def _round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+@dataclass
+class MLPParams:
+    dims: tuple
+    Ws: list        # device tensors [out][w_ld] (bf16 or fp32)
+    w_ld: list
+    biases: list    # device fp32 [out]
+    w_dtype: int
+
+
+def make_mlp(dims, weights, biases, bf16: bool, device="cuda") -> MLPParams:
+    """Device copies of host weights, rows padded to a multiple of 8 elements
+    (bf16) so the MFMA GEMM reads every operand with 16-byte loads."""
+    Ws, lds, bs = [], [], []
+    for W, b in zip(weights, biases):
+        out_f, in_f = W.shape
+        if bf16:
+            ld = _round_up(in_f, 8)
+            Wd = torch.zeros((out_f, ld), dtype=torch.bfloat16, device=device)
+            Wd[:, :in_f] = torch.as_tensor(W).to(device=device, dtype=torch.bfloat16)
+        else:
+            ld = in_f
+            Wd = torch.as_tensor(W, dtype=torch.float32).to(device).contiguous()
+        Ws.append(Wd)
+        lds.append(ld)
+        bs.append(torch.as_tensor(b, dtype=torch.float32).to(device).contiguous())
+    return MLPParams(tuple(int(x) for x in dims), Ws, lds, bs, C.DLRM_BF16 if bf16 else C.DLRM_F32)
+
+
+class DLRM:
+    """Device state and call sequence for one batch size."""
+
+    def __init__(self, B: int, K: int, d: int, rows, tables, bottom: MLPParams, top: MLPParams, train: bool = False,
+                 device="cuda"):
+        self.B, self.K, self.d, self.n = B, K, d, K + 1
+        self.rows = [int(r) for r in rows]
+        self.tables = tables
+        self.table_ptrs = C.device_pointer_array(tables)
+        self.bottom, self.top = bottom, top
+        self.train = train
+        n, dev = self.n, device
+        self.P = n * (n - 1) // 2
+        self.top_w = d + self.P
+        self.X = torch.empty((B, n, d), dtype=torch.float32, device=dev)
+        top_dtype = torch.bfloat16 if top.w_dtype == C.DLRM_BF16 else torch.float32
+        self.top_ld = _round_up(self.top_w, 8) if top_dtype == torch.bfloat16 else _round_up(self.top_w, 4)
+        self.top_in = torch.empty((B, self.top_ld), dtype=top_dtype, device=dev)
+        self.logit = torch.empty((B, 1), dtype=torch.float32, device=dev)
+        self.prob = torch.empty((B,), dtype=torch.float32, device=dev)
+        save = bool(train)
+        self.ws_bot = self._ws(C.dlrm_mlp_workspace_size(B, bottom.dims, bottom.w_dtype, save))
+        self.ws_top = self._ws(C.dlrm_mlp_workspace_size(B, top.dims, top.w_dtype, save))
+        if train:
+            self.ws_bot_bwd = self._ws(C.dlrm_mlp_bwd_workspace_size(B, bottom.dims))
+            self.ws_top_bwd = self._ws(C.dlrm_mlp_bwd_workspace_size(B, top.dims))
+            self.dW_bot = [torch.empty((o, i), dtype=torch.float32, device=dev)
+                           for i, o in zip(bottom.dims[:-1], bottom.dims[1:])]
+            self.db_bot = [torch.empty((o,), dtype=torch.float32, device=dev) for o in bottom.dims[1:]]
+            self.dW_top = [torch.empty((o, i), dtype=torch.float32, device=dev)
+                           for i, o in zip(top.dims[:-1], top.dims[1:])]
+            self.db_top = [torch.empty((o,), dtype=torch.float32, device=dev) for o in top.dims[1:]]
+            self.dlogit = torch.empty((B,), dtype=torch.float32, device=dev)
+            self.ws_sparse = None
+
+    @staticmethod
+    def _ws(nbytes: int):
+        return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device="cuda")
+
+    def forward(self, dense, indices, offsets, stream=None):
+        B, n, d = self.B, self.n, self.d
+        save = self.train
+        C.dlrm_mlp_fwd(dense, dense.shape[1], B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld,
+                       self.bottom.biases, self.bottom.w_dtype, C.DLRM_ACT_RELU, self.X, n * d, None, self.ws_bot,
+                       save, stream)
+        C.dlrm_embbag_fwd(self.table_ptrs, self.K, d, indices, offsets, B, self.X, n * d, d, stream)
+        C.dlrm_interact_fwd(self.X, B, n, d, n * d, self.top_in, self.top_ld, stream)
+        C.dlrm_mlp_fwd(self.top_in, self.top_ld, B, self.top.dims, self.top.Ws, self.top.w_ld, self.top.biases,
+                       self.top.w_dtype, C.DLRM_ACT_NONE, self.logit, 1, self.prob, self.ws_top, save, stream)
+        return self.logit, self.prob
+
+    def sparse_workspace(self, nnz: int):
+        need = C.dlrm_embbag_bwd_sgd_workspace_size(self.K, self.B, nnz, self.d)
+        if self.ws_sparse is None or self.ws_sparse.numel() < need:
+            self.ws_sparse = self._ws(need)
+        return self.ws_sparse
+
+    def backward(self, labels, G, indices, offsets, nnz: int, lr: float, stream=None):
+        """Dense gradients (top: from the BCE loss; bottom: from G[:, 0, :]) and
+        the sparse SGD update of the tables from G[:, 1..K, :]."""
+        B, n, d = self.B, self.n, self.d
+        C.dlrm_bce_grad(self.logit, 1, labels, B, self.dlogit, stream)
+        C.dlrm_mlp_bwd(B, self.top.dims, self.top.Ws, self.top.w_ld, C.DLRM_ACT_NONE, self.ws_top, self.logit, 1,
+                       self.dlogit, 1, self.dW_top, self.db_top, None, 0, self.ws_top_bwd, stream)
+        C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.X,
+                       n * d, G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
+        C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, G, n * d, d, lr,
+                              self.sparse_workspace(nnz), stream)

@@ -1,0 +1,210 @@
+/*
+ * dlrm.h -- C ABI of libdlrm.so, the DLRM hot path on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The model (cited by web page and section):
+ *   [EXPL] "Deep Learning Recommendation Model (DLRM)" explainer
+ *          (nadeemcite.github.io): Core Idea; Key Method Details
+ *          (Embedding tables, Bottom MLP, Interaction layer, Top MLP, Loss).
+ *   [SU]   "DLRM - Deep Learning Recommendation Model" (briansu.co/recsys/dlrm):
+ *          How it works; Key equations (Interaction, Output);
+ *          Limitations & trade-offs (memory-bound, one shared d).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless the comment says "host".
+ *   - The caller owns all memory.  The library never allocates, frees or
+ *     synchronises; scratch space is passed in as a workspace whose size a
+ *     *_workspace_size query returns.
+ *   - Every call enqueues work on `stream` and returns an int status:
+ *       DLRM_OK (0), DLRM_E_INVALID (null pointer, size or alignment out of
+ *       range), DLRM_E_WORKSPACE (workspace too small), DLRM_E_HIP (a launch
+ *       failed; dlrm_last_hip_error() returns the hipError_t),
+ *       DLRM_E_UNSUPPORTED (valid but not implemented, e.g. key width).
+ *     Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is enqueued.
+ *   - Index values are a precondition (0 <= idx < rows of its table,
+ *     offsets non-decreasing); they are not checked on the hot path.
+ *     dlrm_check_indices() validates them on the device.
+ *   - Results are bitwise deterministic run to run.  Calls on different
+ *     streams are safe when their outputs do not overlap.
+ *   - Row-major everywhere.  "ld" arguments are leading dimensions in
+ *     elements of the array's own type.
+ */
+#ifndef DLRM_H_
+#define DLRM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLRM_ABI_VERSION 1
+
+enum {
+  DLRM_OK = 0,
+  DLRM_E_INVALID = -1,
+  DLRM_E_WORKSPACE = -2,
+  DLRM_E_HIP = -3,
+  DLRM_E_UNSUPPORTED = -4
+};
+
+/* element types */
+enum { DLRM_F32 = 0, DLRM_BF16 = 1 };
+
+/* activation after a layer */
+enum { DLRM_ACT_NONE = 0, DLRM_ACT_RELU = 1 };
+
+int dlrm_abi_version(void);
+const char* dlrm_strerror(int status);
+/* hipError_t of the last failed launch on this thread (0 if none). */
+int dlrm_last_hip_error(void);
+
+/*
+ * Embedding lookup with sum pooling (forward).
+ * [EXPL] Key Method Details, "Embedding tables"; [SU] How it works: each
+ * categorical feature k has its own table T_k of m_k rows of width d and
+ * looks up rows by integer id.  Several ids in one bag are summed; a bag of
+ * one id is exactly the row lookup.
+ *
+ *   tables   device array of K device pointers; T_k is fp32 [m_k][d],
+ *            16-byte aligned.
+ *   indices  int64 [nnz], table-major.
+ *   offsets  int64 [K*B + 1], non-decreasing, offsets[0] = 0: bag (k, b)
+ *            owns indices[offsets[k*B+b] .. offsets[k*B+b+1]).
+ *   out      fp32; bag (k, b) is written to
+ *            out[b*out_ld + out_col0 + k*d + c], c < d (out_ld >= out_col0
+ *            + K*d; out and out_ld*4, out_col0*4 must keep 16-byte alignment).
+ *   Result:  out = sum over the bag's ids in ascending position of the rows,
+ *            accumulated in fp32 from +0.0 (empty bag: +0.0).  Bit-exact.
+ *   Limits:  d % 4 == 0, 4 <= d <= 1024, K >= 1, B >= 1.
+ */
+int dlrm_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const int64_t* indices,
+                    const int64_t* offsets, int64_t B, float* out, int64_t out_ld, int64_t out_col0,
+                    hipStream_t stream);
+
+/*
+ * Pairwise dot-product interaction, packed strict lower triangle, concat.
+ * [SU] Key equations, Interaction: Z = tril(X X^T), X = [x_dense; e_1..e_K]
+ * of shape n x d, n = K + 1.  [EXPL] Key Method Details, "Interaction
+ * layer": only pairs of distinct vectors, n(n-1)/2 values.  [SU] Key
+ * equations, Output: the top MLP input is [x_dense, vec(Z)].
+ *
+ *   X        fp32, sample b's matrix at X + b*x_ld, rows of d floats
+ *            (x_ld >= n*d, x_ld % 4 == 0, 16-byte aligned).
+ *   out      DLRM_F32 or DLRM_BF16 (out_dtype), sample b's row at
+ *            out + b*out_ld: out[c] = X_b[0][c] for c < d, then
+ *            out[d + i(i-1)/2 + j] = sum_c X_b[i][c] X_b[j][c] for j < i < n.
+ *            out_ld >= d + n(n-1)/2.  Columns beyond that (up to out_ld) are
+ *            written with zeros up to the next multiple of 8.
+ *   Accuracy: fp32 products, fp32 accumulation (|err| <= d u sum|x_i x_j|).
+ *   Limits:  2 <= n <= 128, d % 4 == 0, 4 <= d <= 256.
+ */
+int dlrm_interact_fwd(const float* X, int64_t B, int32_t n, int32_t d, int64_t x_ld, void* out,
+                      int32_t out_dtype, int64_t out_ld, hipStream_t stream);
+
+/*
+ * Multilayer perceptron, forward.
+ * [EXPL] Key Method Details, "Bottom MLP" (FC layers with ReLU, output
+ * width d) and "Top MLP" (FC layers with ReLU ending in a sigmoid); [SU] Key
+ * equations, Output: y = sigma(MLP_top(...)).
+ *
+ * Layer l (0 <= l < L) maps width dims[l] to dims[l+1]:
+ *     y = act(x W_l^T + b_l),  act = ReLU for l < L-1, last_act for l = L-1.
+ *   in       [B][in_ld] of in_dtype (DLRM_F32 or DLRM_BF16), 16-byte aligned
+ *            when bf16 with in_ld % 8 == 0 (other layouts take a slower path).
+ *   dims     host [L+1].
+ *   W        host array of L device pointers, W_l is w_dtype [dims[l+1]][w_ld[l]].
+ *   w_ld     host [L] or NULL (then w_ld[l] = dims[l]).
+ *   bias     host array of L device pointers, fp32 [dims[l+1]].
+ *   w_dtype  DLRM_BF16: inputs of every layer are rounded to bf16 (nearest
+ *            even), products are exact, sums fp32 (MFMA); hidden activations
+ *            are stored as bf16.  DLRM_F32: everything fp32.
+ *   out      fp32 [B][out_ld], the last layer's output (the logit when
+ *            dims[L] == 1 and last_act == DLRM_ACT_NONE).
+ *   prob     nullable fp32 [B]; when dims[L] == 1 receives 1/(1+exp(-out)).
+ *   ws       workspace of dlrm_mlp_workspace_size() bytes (256-byte aligned).
+ *   save_acts != 0 keeps every layer's input in ws for dlrm_mlp_bwd.
+ */
+size_t dlrm_mlp_workspace_size(int64_t B, int32_t L, const int32_t* dims, int32_t w_dtype, int32_t save_acts);
+int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int64_t B, int32_t L, const int32_t* dims,
+                 const void* const* W, const int32_t* w_ld, const float* const* bias, int32_t w_dtype,
+                 int32_t last_act, float* out, int64_t out_ld, float* prob, void* ws, size_t ws_bytes,
+                 int32_t save_acts, hipStream_t stream);
+
+/*
+ * Multilayer perceptron, backward (bf16 networks).
+ * Training minimises binary cross-entropy ([EXPL] Key Method Details,
+ * "Loss"); the caller passes dY = dLoss/d(out) (for BCE on the logit,
+ * (sigma(logit) - y) / B).
+ *
+ *   fwd_ws   the workspace of a dlrm_mlp_fwd call with save_acts != 0 and the
+ *            same B, L, dims; out/out_ld that call's output (used for the
+ *            last layer's ReLU mask when last_act == DLRM_ACT_RELU).
+ *   dY       fp32 [B][dy_ld].
+ *   dW       host array of L device pointers, fp32 [dims[l+1]][dims[l]]:
+ *            dW_l = delta_l^T x_l (overwritten).
+ *   db       host array of L device pointers, fp32 [dims[l+1]] (overwritten).
+ *   dX       nullable fp32 [B][dx_ld], gradient w.r.t. the MLP input.
+ *   delta_l = g_l * 1[y_l > 0] on ReLU layers; g_{l-1} = delta_l W_l.  The
+ *   GEMMs take bf16 operands (delta rounded to bf16) with fp32 sums.
+ *   ws       dlrm_mlp_bwd_workspace_size() bytes.
+ */
+size_t dlrm_mlp_bwd_workspace_size(int64_t B, int32_t L, const int32_t* dims);
+int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const void* const* W, const int32_t* w_ld,
+                 int32_t last_act, const void* fwd_ws, const float* out, int64_t out_ld, const float* dY,
+                 int64_t dy_ld, float* const* dW, float* const* db, float* dX, int64_t dx_ld, void* ws,
+                 size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradient of the mean binary cross-entropy w.r.t. the logit.
+ * [EXPL] Key Method Details, "Loss": binary cross-entropy on the click
+ * probability sigma(logit) ([SU] Key equations, Output).  For
+ *   loss = -(1/B) sum_b [y_b log s_b + (1 - y_b) log(1 - s_b)],  s_b = sigma(logit_b)
+ * the derivative is dY[b] = (s_b - y_b) / B.
+ *   logit    fp32 [B] with stride logit_ld; y fp32 [B] (0 or 1); dY fp32 [B].
+ */
+int dlrm_bce_grad(const float* logit, int64_t logit_ld, const float* y, int64_t B, float* dY, hipStream_t stream);
+
+/*
+ * Sparse embedding backward with row-wise SGD, in place.
+ * Sum pooling passes each bag's gradient unchanged to every row it looked
+ * up, once per occurrence.  For every row r of table k that the batch
+ * touches:
+ *     g = sum over r's occurrences p in table k's bags, ascending p, of
+ *         G[b(p)*g_ld + g_col0 + k*d + c]          (fp32, from +0.0)
+ *     T_k[r][c] <- T_k[r][c] - (lr * g[c])         (two fp32 roundings)
+ * computed by a stable radix sort of (table, row) keys, a run-length
+ * segmentation and one serial fp32 sum per (row, column).  Untouched rows
+ * are not written.  Bit-exact and deterministic.
+ *
+ *   tables   device array of K device pointers, fp32 [m_k][d], updated.
+ *   rows     host [K], m_k (bounds the key width: K * max m_k < 2^32).
+ *   indices, offsets, B as for dlrm_embbag_fwd; nnz = offsets[K*B] (host).
+ *   G        fp32 [B][g_ld]; bag (k, b)'s gradient at G[b*g_ld + g_col0 + k*d].
+ *            B * g_ld * 4 < 2^31.
+ *   ws       dlrm_embbag_bwd_sgd_workspace_size() bytes (256-byte aligned).
+ *   Limits:  d % 4 == 0, 4 <= d <= 1024, nnz < 2^31.
+ */
+size_t dlrm_embbag_bwd_sgd_workspace_size(int32_t K, int64_t B, int64_t nnz, int32_t d);
+int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_t* rows, const int64_t* indices,
+                        const int64_t* offsets, int64_t B, int64_t nnz, const float* G, int64_t g_ld,
+                        int64_t g_col0, float lr, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Validate indices and offsets on the device.  rows_dev: device int64 [K].
+ * Adds to *bad_count (device int64, caller zeroes it) the number of indices
+ * outside [0, rows[k]) plus the number of decreasing offset steps, plus one
+ * if offsets[0] != 0.
+ */
+int dlrm_check_indices(const int64_t* indices, const int64_t* offsets, int32_t K, int64_t B,
+                       const int64_t* rows_dev, int64_t* bad_count, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLRM_H_ */

@@ -126,7 +126,7 @@ def zipf_cdf(m: int, alpha: float) -> np.ndarray:
         np.power(w, -alpha, out=w)
         np.cumsum(w, out=w)
         w /= w[-1]
-        if len(_ZIPF_CDF_CACHE) > 4:
+        if sum(c.size for c in _ZIPF_CDF_CACHE.values()) + m > 3e8:
             _ZIPF_CDF_CACHE.clear()
         _ZIPF_CDF_CACHE[key] = cdf = w
     return cdf

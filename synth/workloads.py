@@ -225,3 +225,20 @@ def compact_rows(w: Workload, idx: np.ndarray, offsets: np.ndarray, seed_tables:
         row_ids.append(u)
         tables.append(R.table_rows(seed, k, w.rows[k], u, w.d))
     return tables, local, row_ids
+
+
+def sub_bags(idx: np.ndarray, offsets: np.ndarray, K: int, B: int, samples) -> tuple:
+    """Indices and offsets of the listed samples' bags only (same order)."""
+    samples = np.asarray(samples)
+    S = len(samples)
+    lens = np.empty(K * S, dtype=np.int64)
+    parts = []
+    for k in range(K):
+        a = offsets[k * B + samples]
+        e = offsets[k * B + samples + 1]
+        lens[k * S:(k + 1) * S] = e - a
+        parts.extend(idx[x:y] for x, y in zip(a, e))
+    new_off = np.zeros(K * S + 1, dtype=np.int64)
+    np.cumsum(lens, out=new_off[1:])
+    new_idx = np.concatenate(parts) if parts else np.zeros(0, np.int64)
+    return new_idx, new_off

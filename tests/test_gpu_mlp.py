@@ -1,0 +1,143 @@
+"""MLP forward/backward on the GPU against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dlrm_cases import DEV, banner, to_dev
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _mlp_dev(dims, params, bf16):
+    from deep_learning_recommendation_amd import pipeline as PL
+
+    return PL.make_mlp(dims, [p[0] for p in params], [p[2] for p in params], bf16)
+
+
+def _fwd(mp, x, last_relu, save=False, in_bf16=False):
+    import deep_learning_recommendation_amd as D
+
+    B = x.shape[0]
+    xin = to_dev(x)
+    if in_bf16:
+        ld = ((x.shape[1] + 7) // 8) * 8
+        xb = torch.zeros((B, ld), dtype=torch.bfloat16, device=DEV)
+        xb[:, :x.shape[1]] = xin.to(torch.bfloat16)
+        xin = xb
+    out_w = mp.dims[-1]
+    out = torch.empty((B, out_w), dtype=torch.float32, device=DEV)
+    prob = torch.empty((B,), dtype=torch.float32, device=DEV) if out_w == 1 else None
+    ws = torch.empty((max(256, D.dlrm_mlp_workspace_size(B, mp.dims, mp.w_dtype, save)),), dtype=torch.uint8,
+                     device=DEV)
+    D.dlrm_mlp_fwd(xin, xin.shape[1], B, mp.dims, mp.Ws, mp.w_ld, mp.biases, mp.w_dtype,
+                   D.DLRM_ACT_RELU if last_relu else D.DLRM_ACT_NONE, out, out_w, prob, ws, save)
+    torch.cuda.synchronize()
+    return out, prob, ws
+
+
+@pytest.mark.parametrize("name,which", [("forward", "bottom"), ("forward", "top"), ("interaction", "bottom"),
+                                        ("interaction", "top"), ("train", "top")])
+def test_mlp_bf16_forward(name, which):
+    w = W.get(name)
+    dims = w.bottom if which == "bottom" else w.top
+    B = 1000  # ragged against every tile size
+    banner(f"mlp bf16 {name}/{which} dims={dims} B={B}")
+    params = W.mlp_params(w, which)
+    g = np.random.default_rng(11)
+    if which == "bottom":
+        x = (g.lognormal(0, 1, (B, dims[0])) if w.dense_dist == "lognormal" else g.standard_normal((B, dims[0])))
+    else:
+        x = g.standard_normal((B, dims[0])) * 0.5
+    x = x.astype(np.float32)
+    mp = _mlp_dev(dims, params, True)
+    out, prob, _ = _fwd(mp, x, which == "bottom", in_bf16=(which == "top"))
+    ref, ref_p, _ = oracle.mlp_fwd(x, [p[0] for p in params], [p[2] for p in params], True, which == "bottom")
+    got = out.cpu().numpy()
+    if which == "top":
+        # logits: 2e-2 absolute (bf16 MLP against the bf16-emulating oracle)
+        assert np.max(np.abs(got - ref)) <= 2e-2
+        assert np.max(np.abs(prob.cpu().numpy() - ref_p)) <= 2e-2 / 4  # sigma is 1/4-Lipschitz
+    else:
+        err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err <= 1e-2, err
+        assert np.max(np.abs(got - ref)) <= 2e-2 * max(1.0, np.abs(ref).max())
+
+
+def test_mlp_f32_tiny_network():
+    w = W.get("tiny")
+    for which in ("bottom", "top"):
+        dims = w.bottom if which == "bottom" else w.top
+        banner(f"mlp fp32 tiny/{which}")
+        params = W.mlp_params(w, which)
+        x = np.random.default_rng(3).standard_normal((w.B, dims[0])).astype(np.float32)
+        mp = _mlp_dev(dims, params, False)
+        out, prob, _ = _fwd(mp, x, which == "bottom")
+        ref, ref_p, _ = oracle.mlp_fwd(x, [p[0] for p in params], [p[2] for p in params], False, which == "bottom")
+        # fp32 FMA chains over K <= 64 per layer: relative error far below 1e-4
+        assert np.all(np.abs(out.cpu().numpy() - ref) <= 1e-4 * np.maximum(1.0, np.abs(ref)))
+        if prob is not None:
+            assert np.max(np.abs(prob.cpu().numpy() - ref_p)) <= 1e-6
+
+
+def test_mlp_identity_layers_exact():
+    # W = I, b = 0 on bf16-representable inputs: every output is exact
+    import deep_learning_recommendation_amd as D  # noqa: F401
+
+    banner("mlp identity")
+    d = 64
+    I = np.eye(d, dtype=np.float32)
+    z = np.zeros(d, np.float32)
+    params = [(I, None, z), (I, None, z)]
+    x = torch.randn(333, d).to(torch.bfloat16).float().numpy()
+    mp = _mlp_dev((d, d, d), params, True)
+    out, _, _ = _fwd(mp, x, True)
+    assert np.array_equal(out.cpu().numpy(), np.maximum(x, 0))
+
+
+@pytest.mark.parametrize("which", ["bottom", "top"])
+def test_mlp_bf16_backward(which):
+    import deep_learning_recommendation_amd as D
+
+    w = W.get("train")
+    dims = w.bottom if which == "bottom" else w.top
+    B = 520
+    banner(f"mlp backward train/{which} B={B}")
+    params = W.mlp_params(w, which)
+    g = np.random.default_rng(21)
+    x = (g.lognormal(0, 1, (B, dims[0])) if which == "bottom" else g.standard_normal((B, dims[0])) * 0.5)
+    x = x.astype(np.float32)
+    mp = _mlp_dev(dims, params, True)
+    last_relu = which == "bottom"
+    out, prob, ws = _fwd(mp, x, last_relu, save=True, in_bf16=(which == "top"))
+    if which == "top":
+        y = (g.random(B) < 0.5).astype(np.float32)
+        dY_dev = torch.empty((B,), dtype=torch.float32, device=DEV)
+        D.dlrm_bce_grad(out, 1, to_dev(y), B, dY_dev)
+        torch.cuda.synchronize()
+        dY = dY_dev.cpu().numpy().reshape(B, 1)
+        # BCE seed (sigma(logit) - y) / B against the oracle's own forward
+        ref_logit, ref_p, _ = oracle.mlp_fwd(x, [p[0] for p in params], [p[2] for p in params], True, False)
+        assert np.max(np.abs(dY[:, 0] - (ref_p - y) / B)) <= 2e-2 / 4 / B + 1e-9
+    else:
+        dY = (g.standard_normal((B, dims[-1])) * 0.01).astype(np.float32)
+        dY_dev = to_dev(dY)
+    dWs = [torch.empty((o, i), dtype=torch.float32, device=DEV) for i, o in zip(dims[:-1], dims[1:])]
+    dbs = [torch.empty((o,), dtype=torch.float32, device=DEV) for o in dims[1:]]
+    dX = torch.empty((B, dims[0]), dtype=torch.float32, device=DEV)
+    wsb = torch.empty((D.dlrm_mlp_bwd_workspace_size(B, dims),), dtype=torch.uint8, device=DEV)
+    D.dlrm_mlp_bwd(B, dims, mp.Ws, mp.w_ld, D.DLRM_ACT_RELU if last_relu else D.DLRM_ACT_NONE, ws, out, dims[-1],
+                   dY_dev, dims[-1], dWs, dbs, dX, dims[0], wsb)
+    torch.cuda.synchronize()
+    # oracle backward from its own saved activations (same bf16 rounding points)
+    _, _, acts = oracle.mlp_fwd(x, [p[0] for p in params], [p[2] for p in params], True, last_relu, save_acts=True)
+    rW, rb, rX = oracle.mlp_bwd([p[0] for p in params], acts, dY, last_relu, want_dx=True)
+
+    def rel(a, b):
+        return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30)
+
+    for l in range(len(dims) - 1):
+        assert rel(dWs[l].cpu().numpy(), rW[l]) <= 2e-2, (l, rel(dWs[l].cpu().numpy(), rW[l]))
+        assert rel(dbs[l].cpu().numpy(), rb[l]) <= 2e-2, (l, rel(dbs[l].cpu().numpy(), rb[l]))
+    assert rel(dX.cpu().numpy(), rX) <= 2e-2
