@@ -6,11 +6,12 @@
 // the natural layout of a fully connected layer y = x W^T.  gfx950 bf16 MFMA
 // v_mfma_f32_32x32x16_bf16: each lane feeds 8 consecutive k of one row of A
 // (row l % 32, k (l / 32) * 8) and of W, so both operands are read from LDS
-// with one 16-byte ds_read per fragment.  Block tile BM x BN x 32 with four
-// waves in a 2 x 2 grid, LDS rows padded to 80 bytes (conflict-free 16-byte
-// reads), double-buffered LDS with global loads for the next k-tile in flight
-// during the MFMAs.  Tiles are walked N-fastest and block ids are regrouped
-// so that the tiles sharing an A panel land on one XCD (one L2).
+// with one 16-byte ds_read per fragment.  Block tile BM x BN x 64 with four
+// waves in a 2 x 2 grid (wave tiles up to 128 x 128, accumulators in AGPRs),
+// LDS rows padded by 16 bytes (conflict-free 16-byte reads), double-buffered
+// LDS with the next k-tile's global loads in flight during the MFMAs.  Tiles
+// are walked N-fastest and block ids are regrouped so that the tiles sharing
+// an A panel land on one XCD (one L2).
 #include "gemm.hpp"
 
 namespace dlrm {
@@ -43,8 +44,223 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Fast path: 16-byte aligned operands with lda, ldw multiples of 8.
+//
+// Tiles move from global memory straight into LDS with global_load_lds_dwordx4
+// (no register staging): each wave instruction fills one contiguous 1 KB
+// block of LDS, i.e. 8 rows of a 64-wide bf16 k-slice.  Inside a row the
+// eight 16-byte chunks are XOR-swizzled (physical chunk = chunk ^ ((row >> 1)
+// & 7)) so that the 16 lanes that one LDS cycle serves read 16 distinct bank
+// groups.  Two LDS stages: the loads of k-tile kt+1 run during the MFMAs of
+// k-tile kt; one barrier per k-tile.  Rows past M or N re-read the last row
+// (their results are never stored); columns past K in the last k-tile are
+// zeroed in LDS before use.  The bf16 epilogue goes through LDS so that every
+// global store is a full 16-byte chunk.
+template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
+    const float* __restrict__ bias, OutT* __restrict__ C, int64_t ldc, int M, int N, int K, int relu, int tiles_n,
+    int k_per_split) {
+  constexpr int BK = 64;
+  constexpr int RB = BK * 2;                      // bytes per tile row
+  constexpr int WAVES_N = BN / WN, NWAVES = (BM / WM) * WAVES_N;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_INS = BM * RB / 1024 / NWAVES, B_INS = BN * RB / 1024 / NWAVES;
+  constexpr int STAGE = (BM + BN) * RB;
+  constexpr int EPI_LS = WN * 2 + 16;             // epilogue LDS row stride (bytes)
+  constexpr int EPI = BM * (BN / WN) * EPI_LS;
+  constexpr int SMEM = (2 * STAGE > EPI) ? 2 * STAGE : EPI;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave - (wave / WAVES_N) * WAVES_N;
+  int bid = blockIdx.x;
+  const int total = gridDim.x;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int tile_m = bid / tiles_n, tile_n = bid - tile_m * tiles_n;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int kbeg = (int)blockIdx.z * k_per_split;
+  const int kend = min(K, kbeg + k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int kpad = (kend + 7) & ~7;
+
+  // this lane's DMA rows: instruction j of wave w fills rows (w*INS + j)*8 + lane/8
+  const int lrow = lane >> 3, lpc = lane & 7;
+  const uint16_t* a_row[A_INS];
+  const uint16_t* b_row[B_INS];
+  int a_c[A_INS], b_c[B_INS];
+#pragma unroll
+  for (int j = 0; j < A_INS; ++j) {
+    const int row = (wave * A_INS + j) * 8 + lrow;
+    a_row[j] = A + (int64_t)min(m0 + row, M - 1) * lda;
+    a_c[j] = (lpc ^ ((row >> 1) & 7)) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j) {
+    const int row = (wave * B_INS + j) * 8 + lrow;
+    b_row[j] = W + (int64_t)min(n0 + row, N - 1) * ldw;
+    b_c[j] = (lpc ^ ((row >> 1) & 7)) * 8;
+  }
+  auto issue = [&](int kt) {
+    char* st = smem + (kt & 1) * STAGE;
+    const int k0 = kbeg + kt * BK;
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(a_row[j] + min(k0 + a_c[j], kpad - 8)),
+                                       (void __attribute__((address_space(3)))*)(st + (wave * A_INS + j) * 1024), 16,
+                                       0, 0);
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(b_row[j] + min(k0 + b_c[j], kpad - 8)),
+                                       (void __attribute__((address_space(3)))*)(st + BM * RB +
+                                                                                 (wave * B_INS + j) * 1024),
+                                       16, 0, 0);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int r32 = lane & 31, half = lane >> 5;
+  if (nk > 0) issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const char* st = smem + (kt & 1) * STAGE;
+    if (kt + 1 < nk) issue(kt + 1);
+    const int valid = kend - (kbeg + kt * BK);
+    if (valid < BK) {
+      // last k-tile is partial: zero columns [valid, BK) of every A and W row
+      char* wst = smem + (kt & 1) * STAGE;
+      for (int e = tid; e < (BM + BN) * 8; e += NWAVES * 64) {
+        const int row = e >> 3, c = e & 7;
+        if (c * 8 + 8 > valid) {
+          uint16_t* p = reinterpret_cast<uint16_t*>(wst + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            if (c * 8 + x >= valid) p[x] = 0;
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = 2 * ks + half;
+      bf16x8 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WM + i * 32 + r32;
+        a[i] = *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WN + j * 32 + r32;
+        b[j] = *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // D layout of a 32x32 block: lane l holds column l % 32 and rows
+  // 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
+  constexpr bool kBf16Out = sizeof(OutT) == 2 && !PARTIAL;
+  const bool staged = kBf16Out && m0 + BM <= M && n0 + BN <= N && (ldc % 8) == 0 &&
+                      (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+  if (staged) {
+    __syncthreads();  // all waves are done reading the k-tiles
+    char* ep = smem + (wm * WM * (BN / WN) + wn * WM) * EPI_LS;  // this wave's WM x WN region
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const float bj = bias != nullptr ? bias[n0 + wn * WN + tn * 32 + r32] : 0.f;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = tm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          float val = acc[tm][tn][v] + bj;
+          if (relu) val = relu_f(val);
+          *reinterpret_cast<uint16_t*>(ep + i * EPI_LS + (tn * 32 + r32) * 2) = f32_to_bf16(val);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (region is wave-private)
+    constexpr int CH = WN / 8;            // 16-byte chunks per row
+#pragma unroll
+    for (int it = 0; it < WM * CH / 64; ++it) {
+      const int e = it * 64 + lane;
+      const int row = e / CH, ch = e - (e / CH) * CH;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + row * EPI_LS + ch * 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(C) + (int64_t)(m0 + wm * WM + row) * ldc + n0 + wn * WN +
+                                ch * 8) = v;
+    }
+    return;
+  }
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int j = n0 + wn * WN + tn * 32 + r32;
+    const float bj = (!PARTIAL && bias != nullptr && j < N) ? bias[j] : 0.f;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = m0 + wm * WM + tm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (i < M && j < N) {
+          float val = acc[tm][tn][v];
+          if (PARTIAL) {
+            C[((int64_t)blockIdx.z * M + i) * ldc + j] = val;
+          } else {
+            val = val + bj;
+            if (relu) val = relu_f(val);
+            store_out(&C[(int64_t)i * ldc + j], val);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL>
+void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
+                 int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  constexpr int threads = (BM / WM) * (BN / WN) * 64;
+  hipLaunchKernelGGL((gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL>), dim3(tm * tn, 1, splits),
+                     dim3(threads), 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu, tn, k_per_split);
+}
+
+// Tile choice: the largest block tile that still gives every CU a tile.
+template <typename OutT, bool PARTIAL>
+void pick_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
+               int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
+  const int64_t t256x256 = ceil_div(M, 256) * ceil_div(N, 256) * splits;
+  const int64_t t256x128 = ceil_div(M, 256) * ceil_div(N, 128) * splits;
+  // fp32 stores with bias would exceed 256 registers in the 256 x 256 tile
+  constexpr bool kWide = sizeof(OutT) == 2 || PARTIAL;
+  if (kWide && t256x256 >= 256)
+    launch_fast<256, 256, 128, 64, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split,
+                                                  s);
+  else if (t256x128 >= 256)
+    launch_fast<256, 128, 64, 64, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split,
+                                                 s);
+  else
+    launch_fast<128, 128, 64, 64, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split,
+                                                 s);
+}
+
 template <int BM, int BN, bool VEC, typename OutT, bool PARTIAL>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                         const uint16_t* __restrict__ W, int64_t ldw,
                                                         const float* __restrict__ bias, OutT* __restrict__ C,
                                                         int64_t ldc, int M, int N, int K, int relu, int tiles_n,
@@ -143,67 +359,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   }
 }
 
-template <int BM, int BN, bool VEC, typename OutT, bool PARTIAL>
-void launch_gemm(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
-                 int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
-  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, VEC, OutT, PARTIAL>), dim3(tm * tn, 1, splits), dim3(256), 0, s, A,
-                     lda, W, ldw, bias, C, ldc, M, N, K, relu, tn, k_per_split);
-}
 
-template <bool VEC, typename OutT, bool PARTIAL>
-void pick_tile(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
-               int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
-  const int64_t big = ceil_div(M, 256) * ceil_div(N, 128) * splits;
-  if (big >= 512)
-    launch_gemm<256, 128, VEC, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split, s);
-  else
-    launch_gemm<128, 128, VEC, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split, s);
-}
-
-// ---------------------------------------------------------------- small K
-
-template <typename InT>
-__device__ __forceinline__ float in_as_bf16(const InT* p);
-template <>
-__device__ __forceinline__ float in_as_bf16<float>(const float* p) {
-  return bf16_to_f32(f32_to_bf16(*p));
-}
-template <>
-__device__ __forceinline__ float in_as_bf16<uint16_t>(const uint16_t* p) {
-  return bf16_to_f32(*p);
-}
-
-// one thread per (row, 8 consecutive outputs); products of two bf16 values
-// are exact in fp32, sums fp32 in k order
-template <typename InT, typename OutT>
-__global__ __launch_bounds__(256) void smallk_kernel(const InT* __restrict__ in, int64_t ld_in,
-                                                     const uint16_t* __restrict__ W, int64_t ldw,
-                                                     const float* __restrict__ bias, OutT* __restrict__ C,
-                                                     int64_t ldc, int M, int N, int K, int relu) {
-  const int n8 = (N + 7) / 8;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)M * n8) return;
-  const int m = (int)(t / n8);
-  const int nb = (int)(t - (int64_t)m * n8) * 8;
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  const InT* row = in + (int64_t)m * ld_in;
-  for (int k = 0; k < K; ++k) {
-    const float x = in_as_bf16<InT>(row + k);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (nb + j < N) acc[j] = __builtin_fmaf(x, bf16_to_f32(W[(int64_t)(nb + j) * ldw + k]), acc[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (nb + j < N) {
-      float v = acc[j] + bias[nb + j];
-      if (relu) v = relu_f(v);
-      store_out(&C[(int64_t)m * ldc + nb + j], v);
-    }
-  }
+// Any layout (unaligned rows or odd leading dimensions): element-wise loads.
+template <typename OutT, bool PARTIAL>
+void launch_generic(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
+                    int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
+  const int tm = (M + 127) / 128, tn = (N + 127) / 128;
+  hipLaunchKernelGGL((gemm_bf16_generic_kernel<128, 128, false, OutT, PARTIAL>), dim3(tm * tn, 1, splits), dim3(256),
+                     0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu, tn, k_per_split);
 }
 
 // ---------------------------------------------------------------- GEMV (N == 1)
@@ -310,16 +473,17 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, void* C,
               int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s) {
   if (M <= 0 || N <= 0) return DLRM_OK;
-  const bool vec = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0;
-  const int kps = (int)round_up(K, BK);
+  const bool fast = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0 && lda >= K && ldw >= K &&
+                    (int64_t)256 * lda < ((int64_t)1 << 31) && (int64_t)256 * ldw < ((int64_t)1 << 31);
+  const int kps = (int)round_up(K > 0 ? K : 1, 64);
   if (out_bf16) {
     auto* c = static_cast<uint16_t*>(C);
-    if (vec) pick_tile<true, uint16_t, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
-    else pick_tile<false, uint16_t, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+    if (fast) pick_fast<uint16_t, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+    else launch_generic<uint16_t, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
   } else {
     auto* c = static_cast<float*>(C);
-    if (vec) pick_tile<true, float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
-    else pick_tile<false, float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+    if (fast) pick_fast<float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+    else launch_generic<float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
   }
   return launch_status();
 }
@@ -327,10 +491,11 @@ int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, co
 int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M, int N,
                      int K, int splits, hipStream_t s) {
   if (M <= 0 || N <= 0) return DLRM_OK;
-  const bool vec = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0;
-  const int kps = (int)round_up(ceil_div(K, splits), BK);
-  if (vec) pick_tile<true, float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
-  else pick_tile<false, float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
+  const bool fast = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0 && lda >= K && ldw >= K &&
+                    (int64_t)256 * lda < ((int64_t)1 << 31) && (int64_t)256 * ldw < ((int64_t)1 << 31);
+  const int kps = (int)round_up(ceil_div(K > 0 ? K : 1, splits), 64);
+  if (fast) pick_fast<float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
+  else launch_generic<float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
   return launch_status();
 }
 
@@ -340,29 +505,6 @@ int reduce_splits(const float* part, int splits, int M, int N, const float* bias
   if (MN <= 0) return DLRM_OK;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)ceil_div(MN, 256)), dim3(256), 0, s, part, splits, M, N,
                      bias, C, ldc, (int)relu);
-  return launch_status();
-}
-
-int gemm_smallk(const void* in, bool in_bf16, int64_t ld_in, const uint16_t* W, int64_t ldw, const float* bias,
-                void* C, int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s) {
-  const int64_t threads = (int64_t)M * ceil_div(N, 8);
-  if (threads <= 0) return DLRM_OK;
-  const dim3 grid((unsigned)ceil_div(threads, 256)), block(256);
-  if (in_bf16) {
-    if (out_bf16)
-      hipLaunchKernelGGL((smallk_kernel<uint16_t, uint16_t>), grid, block, 0, s, static_cast<const uint16_t*>(in),
-                         ld_in, W, ldw, bias, static_cast<uint16_t*>(C), ldc, M, N, K, (int)relu);
-    else
-      hipLaunchKernelGGL((smallk_kernel<uint16_t, float>), grid, block, 0, s, static_cast<const uint16_t*>(in), ld_in,
-                         W, ldw, bias, static_cast<float*>(C), ldc, M, N, K, (int)relu);
-  } else {
-    if (out_bf16)
-      hipLaunchKernelGGL((smallk_kernel<float, uint16_t>), grid, block, 0, s, static_cast<const float*>(in), ld_in, W,
-                         ldw, bias, static_cast<uint16_t*>(C), ldc, M, N, K, (int)relu);
-    else
-      hipLaunchKernelGGL((smallk_kernel<float, float>), grid, block, 0, s, static_cast<const float*>(in), ld_in, W,
-                         ldw, bias, static_cast<float*>(C), ldc, M, N, K, (int)relu);
-  }
   return launch_status();
 }
 

@@ -16,11 +16,6 @@ int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t 
 int reduce_splits(const float* part, int splits, int M, int N, const float* bias, float* C, int64_t ldc,
                   bool relu, hipStream_t s);
 
-// First layer with fp32 or bf16 input and small K: inputs rounded to bf16,
-// fp32 sums over k ascending.  Output bf16 or fp32.
-int gemm_smallk(const void* in, bool in_bf16, int64_t ld_in, const uint16_t* W, int64_t ldw, const float* bias,
-                void* C, int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s);
-
 // N == 1 layer: out[m] = sum_k A[m][k] w[k] + bias; prob = sigmoid(out).
 int gemv_bf16(const uint16_t* A, int64_t lda, const uint16_t* w, const float* bias, float* out, int64_t ldo,
               float* prob, int M, int K, bool relu, hipStream_t s);

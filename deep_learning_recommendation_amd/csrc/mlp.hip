@@ -234,10 +234,16 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
     return rc;
   }
 
-  // bf16 network: layer 0's input rounded once into the workspace
+  // bf16 network: an fp32 input is rounded once into the workspace; a bf16
+  // input is read in place unless it must be kept for the backward pass
   uint16_t* act0 = reinterpret_cast<uint16_t*>(wsb + lay.act_off[0]);
+  const uint16_t* in0 = act0;
+  int64_t ld0 = lay.act_ld[0];
   if (in_dtype == DLRM_F32) {
     rc = convert_to_bf16(static_cast<const float*>(in), in_ld, act0, lay.act_ld[0], M, dims[0], stream);
+  } else if (!save_acts) {
+    in0 = static_cast<const uint16_t*>(in);
+    ld0 = in_ld;
   } else {
     const int Cpad = (int)lay.act_ld[0];
     const int64_t total = (int64_t)M * Cpad;
@@ -249,16 +255,14 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
     const int fi = dims[l], fo = dims[l + 1];
     const bool last = (l == L - 1);
     const bool relu = !last || last_act == DLRM_ACT_RELU;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(wsb + lay.act_off[l]);
-    const int64_t ld_src = lay.act_ld[l];
+    const uint16_t* src = l == 0 ? in0 : reinterpret_cast<const uint16_t*>(wsb + lay.act_off[l]);
+    const int64_t ld_src = l == 0 ? ld0 : lay.act_ld[l];
     const uint16_t* w = static_cast<const uint16_t*>(W[l]);
     const int64_t wl = w_ld ? w_ld[l] : fi;
     void* dst = last ? static_cast<void*>(out) : static_cast<void*>(wsb + lay.act_off[l + 1]);
     const int64_t ld_dst = last ? out_ld : lay.act_ld[l + 1];
     if (last && fo == 1)
       rc = gemv_bf16(src, ld_src, w, bias[l], out, out_ld, prob, M, fi, relu, stream);
-    else if (fi <= 32)
-      rc = gemm_smallk(src, true, ld_src, w, wl, bias[l], dst, ld_dst, !last, M, fo, fi, relu, stream);
     else
       rc = gemm_bf16(src, ld_src, w, wl, bias[l], dst, ld_dst, !last, M, fo, fi, relu, stream);
   }

@@ -177,7 +177,10 @@ def indices_offsets(w: Workload, batch: int = 0):
 def mlp_params(w: Workload, which: str):
     """Weights and biases of the bottom ("bottom") or top ("top") MLP.
 
-    W_l ~ N(0, 2/fan_in) as [out][in] row-major; b_l ~ U(-1/sqrt(fan_in), +).
+    W_l ~ N(0, 2/(fan_in + fan_out)) (Glorot normal) as [out][in] row-major;
+    b_l ~ U(-1/sqrt(fan_in), +1/sqrt(fan_in)).  Glorot scaling keeps the
+    logits of log-normal dense inputs O(1); see the rounding-sensitivity note
+    in the design document.
     For bf16 MLPs the weights are drawn in fp32 and stored as bf16 (round to
     nearest even, by torch); ``W`` then holds the fp32 values of those bf16
     numbers and ``W_bits`` their uint16 encodings.
@@ -190,7 +193,7 @@ def mlp_params(w: Workload, which: str):
     for l in range(len(dims) - 1):
         fi, fo = dims[l], dims[l + 1]
         g = R.stream_rng(w.seed, S_W, sid, l)
-        W = (g.standard_normal(size=(fo, fi)) * math.sqrt(2.0 / fi)).astype(np.float32)
+        W = (g.standard_normal(size=(fo, fi)) * math.sqrt(2.0 / (fi + fo))).astype(np.float32)
         gb = R.stream_rng(w.seed, S_B, sid, l)
         b = gb.uniform(-1.0 / math.sqrt(fi), 1.0 / math.sqrt(fi), size=fo).astype(np.float32)
         bits = None

@@ -108,4 +108,5 @@ def test_mlp_params_bf16_exact():
         back = (bits.astype(np.uint32) << 16).view(np.float32)
         assert np.array_equal(back, Wf)
         fan_in = Wf.shape[1]
-        assert abs(Wf.std() - math.sqrt(2 / fan_in)) < 0.2 * math.sqrt(2 / fan_in)
+        sd = math.sqrt(2 / (fan_in + Wf.shape[0]))
+        assert abs(Wf.std() - sd) < 0.2 * sd
