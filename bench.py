@@ -171,12 +171,11 @@ def main():
 
         mark("bottom_mlp")
         D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
-                       model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.X, n * d, None,
+                       model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.x0, model.x0_ld, None,
                        model.ws_bot, w.train)
-        mark("embbag")
-        D.dlrm_embbag_fwd(model.table_ptrs, w.K, d, idx, off, w.B, model.X, n * d, d)
-        mark("interact")
-        D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
+        mark("embbag_interact")
+        D.dlrm_embbag_interact_fwd(model.x0, model.x0_ld, model.table_ptrs, w.K, d, idx, off, w.B, model.top_in,
+                                   model.top_ld)
         mark("top_mlp")
         D.dlrm_mlp_fwd(model.top_in, model.top_ld, w.B, model.top.dims, model.top.Ws, model.top.w_ld,
                        model.top.biases, model.top.w_dtype, D.DLRM_ACT_NONE, model.logit, 1, model.prob,
@@ -187,7 +186,7 @@ def main():
             D.dlrm_mlp_bwd(w.B, model.top.dims, model.top.Ws, model.top.w_ld, D.DLRM_ACT_NONE, model.ws_top,
                            model.logit, 1, model.dlogit, 1, model.dW_top, model.db_top, None, 0, model.ws_top_bwd)
             D.dlrm_mlp_bwd(w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld, D.DLRM_ACT_RELU,
-                           model.ws_bot, model.X, n * d, G, n * d, model.dW_bot, model.db_bot, None, 0,
+                           model.ws_bot, model.x0, model.x0_ld, G, n * d, model.dW_bot, model.db_bot, None, 0,
                            model.ws_bot_bwd)
             mark("sparse_bwd_sgd")
             D.dlrm_embbag_bwd_sgd(model.table_ptrs, w.K, d, w.rows, idx, off, w.B, nnz, G, n * d, d, w.lr,
@@ -211,10 +210,20 @@ def main():
     value = w.B * args.steps / elapsed
     breakdown = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in call_t.items()}
     nnz_mean = float(np.mean([b[5] for b in dbatches]))
-    gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean)
-    g_ms = breakdown.get("embbag", gather_t.mean_ms())
+    if model is None:
+        kname, key = "embbag_fwd_kernel", None
+        gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean)
+        g_ms = gather_t.mean_ms()
+    else:
+        # fused pooled lookup + interaction: every looked-up row, indices and
+        # offsets, the dense rows it reads and the packed top-MLP rows it writes
+        kname, key = "interact_mfma_kernel<fused>", "embbag_interact"
+        esz = model.top_in.element_size()
+        gbytes = (gather_bytes(w.K, w.B, w.d, nnz_mean) - 4 * w.K * w.B * w.d + 4 * w.B * w.d +
+                  esz * w.B * model.top_ld)
+        g_ms = breakdown[key]
     achieved = gbytes / (g_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "embbag_fwd_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes_per_launch": int(gbytes), "avg_launch_ms": round(g_ms, 4)}
 

@@ -28,6 +28,7 @@ _SIGNATURES = {
     "dlrm_last_hip_error": (ctypes.c_int, []),
     "dlrm_embbag_fwd": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I64, _P, _I64, _I64, _P]),
     "dlrm_interact_fwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I32, _I64, _P]),
+    "dlrm_embbag_interact_fwd": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I64, _P]),
     "dlrm_mlp_workspace_size": (_SZ, [_I64, _I32, _P, _I32, _I32]),
     "dlrm_mlp_fwd": (ctypes.c_int, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _SZ,
                                     _I32, _P]),
@@ -126,6 +127,13 @@ def dlrm_embbag_fwd(table_ptrs, K: int, d: int, indices, offsets, B: int, out, o
 def dlrm_interact_fwd(X, B: int, n: int, d: int, x_ld: int, out, out_ld: int, stream=None) -> None:
     _check("dlrm_interact_fwd", lib().dlrm_interact_fwd(_ptr(X), B, n, d, x_ld, _ptr(out), _dtype_code(out), out_ld,
                                                          _stream(stream)))
+
+
+def dlrm_embbag_interact_fwd(x_dense, xd_ld: int, table_ptrs, K: int, d: int, indices, offsets, B: int, out,
+                             out_ld: int, stream=None) -> None:
+    _check("dlrm_embbag_interact_fwd", lib().dlrm_embbag_interact_fwd(_ptr(x_dense), xd_ld, _ptr(table_ptrs), K, d,
+                                                                       _ptr(indices), _ptr(offsets), B, _ptr(out),
+                                                                       _dtype_code(out), out_ld, _stream(stream)))
 
 
 def dlrm_mlp_workspace_size(B: int, dims, w_dtype: int, save_acts: bool) -> int:

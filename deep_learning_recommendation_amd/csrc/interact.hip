@@ -13,7 +13,8 @@
 // v_mfma_f32_16x16x4_f32 for the tile's rows and the B operand for X^T, so
 // Gram block (I, J) is a chain of 4*ceil(d/16) MFMAs on register data, with
 // the k order permuted inside each chunk (fp32 sums in any order meet the
-// d*u error bound).  Only blocks with J <= I are computed.  fp32 MFMA runs
+// d*u error bound).  Only blocks with J <= I are computed.  The packed output
+// row is assembled in LDS and written with full 16-byte stores.  fp32 MFMA runs
 // at twice the rate of unpacked fp32 VALU FMAs, so it wins even where
 // padding to 16 rows wastes part of a block.  The kernel is bound by HBM
 // (reading X, writing the packed rows).
@@ -31,17 +32,135 @@ __device__ __forceinline__ void put4(uint16_t* p, f4 v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
-template <int NT, int DC, typename OutT>
-__global__ __launch_bounds__(256) void interact_mfma_kernel(const float* __restrict__ X, int64_t B, int n, int d,
-                                                            int64_t x_ld, OutT* __restrict__ out, int64_t out_ld,
-                                                            int pad_end) {
-  const int lane = threadIdx.x & 63;
-  const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= B) return;  // whole wave
-  const float* __restrict__ xb = X + b * x_ld;
-  OutT* __restrict__ ob = out + b * out_ld;
-  const int r16 = lane & 15, g = lane >> 4;
+// Where the rows of X come from: a materialised X, or (fused path) row 0
+// from the bottom MLP output and rows 1..K pooled on the fly from the tables.
+struct RowSource {
+  const float* X;                 // X (plain) or x_dense rows (fused)
+  int64_t x_ld;
+  const float* const* tables;     // fused only
+  const int64_t* idx;
+  const int64_t* off;
+};
 
+// Gram blocks of one sample held in registers (x[t][c]: rows t*16 + lane%16,
+// columns c*16 + 4*(lane/16) .. +3) into the sample's packed output row `ob`
+// (in LDS): dense vector first, then the strict lower triangle row by row,
+// then zeros up to pad_end.  The k loop is outermost so the MFMAs of all
+// blocks (J <= I) interleave as independent accumulation chains; a single
+// block is split into two partial chains.  Lanes whose (i, j) is not a kept
+// pair write to a dummy slot past the row, so the stores need no branches.
+template <int NT, int DC, typename OutT>
+__device__ __forceinline__ void gram_row(f4 (&x)[NT][DC], int n, int d, int pad_end, OutT* ob, int lane) {
+  const int r16 = lane & 15, g = lane >> 4;
+  if (r16 == 0) {  // row 0 lives in lanes 0, 16, 32, 48 of tile 0
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const int kk = c * 16 + 4 * g;
+      if (kk < d) put4(ob + kk, x[0][c]);
+    }
+  }
+  const int dummy = pad_end;  // one spare element after the row
+  // D[i][j] of block (I, J): lane holds i = 4*(l/16) + r, j = l % 16
+  auto store_block = [&](int I, int J, f4 v) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = I * 16 + 4 * g + r;
+      const int j = J * 16 + r16;
+      const int at = (i < n && j < i) ? d + i * (i - 1) / 2 + j : dummy;
+      put(ob + at, v[r]);
+    }
+  };
+  if constexpr (NT <= 2) {
+    // every block live at once: NT(NT+1)/2 independent chains (two partial
+    // chains when there is a single block)
+    constexpr int NB = NT * (NT + 1) / 2;
+    constexpr int NCH = NB == 1 ? 2 : 1;
+    f4 acc[NB][NCH];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int h = 0; h < NCH; ++h) acc[q][h] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        int q = 0;
+#pragma unroll
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+          for (int J = 0; J <= I; ++J, ++q)
+            acc[q][s % NCH] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[I][c][s], x[J][c][s], acc[q][s % NCH], 0, 0, 0);
+      }
+    }
+    int q = 0;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J, ++q) store_block(I, J, NCH == 2 ? acc[q][0] + acc[q][NCH - 1] : acc[q][0]);
+  } else {
+    // one block row at a time (bounded accumulator registers): I + 1 chains,
+    // two partial chains for I = 0
+#pragma unroll
+    for (int I = 0; I < NT; ++I) {
+      f4 acc[NT + 1];
+#pragma unroll
+      for (int J = 0; J <= NT; ++J) acc[J] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float a = x[I][c][s];
+          if (I == 0) {
+            acc[s & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x[0][c][s], acc[s & 1], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int J = 0; J <= I; ++J) acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x[J][c][s], acc[J], 0, 0, 0);
+          }
+        }
+      }
+      if (I == 0) {
+        store_block(0, 0, acc[0] + acc[1]);
+      } else {
+#pragma unroll
+        for (int J = 0; J <= I; ++J) store_block(I, J, acc[J]);
+      }
+    }
+  }
+  const int end = d + n * (n - 1) / 2;
+  for (int col = end + lane; col < pad_end; col += 64) put(ob + col, 0.f);
+}
+
+// Copy a wave's finished row from LDS to global memory in 16-byte (or
+// 8-byte) chunks.
+__device__ __forceinline__ void row_out(const char* rowb, char* dst, int bytes, int wide, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int off = 0;
+  if (wide) {
+    for (off = lane * 16; off + 16 <= bytes; off += 64 * 16)
+      *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(rowb + off);
+    off = bytes & ~15;
+  }
+  for (int o = off + lane * 8; o + 8 <= bytes; o += 64 * 8)
+    *reinterpret_cast<uint2*>(dst + o) = *reinterpret_cast<const uint2*>(rowb + o);
+  // the row buffer is reused by this wave's next sample
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Materialised X: one wave per sample.
+template <int NT, int DC, typename OutT>
+__global__ __launch_bounds__(256) void interact_mfma_kernel(RowSource src, int64_t B, int n, int d,
+                                                            OutT* __restrict__ out, int64_t out_ld, int pad_end,
+                                                            int row_bytes, int wide) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (b >= B) return;  // whole wave
+  char* rowb = smem + wave * row_bytes;
+  const int r16 = lane & 15, g = lane >> 4;
+  const float* __restrict__ xb = src.X + b * src.x_ld;
   f4 x[NT][DC];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -57,44 +176,95 @@ __global__ __launch_bounds__(256) void interact_mfma_kernel(const float* __restr
       }
     }
   }
+  gram_row<NT, DC, OutT>(x, n, d, pad_end, reinterpret_cast<OutT*>(rowb), lane);
+  row_out(rowb, reinterpret_cast<char*>(out + b * out_ld), pad_end * (int)sizeof(OutT), wide, lane);
+}
 
-  // dense vector first: row 0 lives in lanes 0, 16, 32, 48 of tile 0
-  if (r16 == 0) {
+// Fused pooled lookup + interaction: one wave per sample.  Row 0 is the
+// dense vector, row 1 + k the pooled bag (k, b), summed in bag order from +0
+// exactly as the standalone lookup.  All bag offsets of the sample are read
+// first, then all first indices, then all rows, so each dependent step has
+// every load of the sample in flight.
+template <int NT, int DC, typename OutT>
+__global__ __launch_bounds__(256) void fused_kernel(RowSource src, int64_t B, int n, int d, OutT* __restrict__ out,
+                                                    int64_t out_ld, int pad_end, int row_bytes, int wide) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (b >= B) return;  // whole wave
+  char* rowb = smem + wave * row_bytes;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t* __restrict__ off = src.off;
+  const int64_t* __restrict__ idx = src.idx;
+  const float* __restrict__ x0 = src.X + b * src.x_ld;
+
+  int64_t pb[NT];
+  int len[NT];
+  const float* tb[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = t * 16 + r16;
+    len[t] = 0;
+    pb[t] = 0;
+    tb[t] = nullptr;
+    if (row >= 1 && row < n) {
+      const int64_t bag = (int64_t)(row - 1) * B + b;
+      pb[t] = off[bag];
+      len[t] = (int)(off[bag + 1] - pb[t]);
+      tb[t] = src.tables[row - 1];
+    }
+  }
+  int64_t r0[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) r0[t] = len[t] > 0 ? idx[pb[t]] : 0;
+
+  f4 x[NT][DC];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = t * 16 + r16;
+    const float* rp = tb[t] + r0[t] * (int64_t)d;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const int kk = c * 16 + 4 * g;
-      if (kk < d) put4(ob + kk, x[0][c]);
-    }
-  }
-
-#pragma unroll
-  for (int I = 0; I < NT; ++I) {
-    f4 acc[NT];
-#pragma unroll
-    for (int J = 0; J <= I; ++J) acc[J] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float a = x[I][c][s];
-#pragma unroll
-        for (int J = 0; J <= I; ++J) acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x[J][c][s], acc[J], 0, 0, 0);
-      }
-    }
-    // D[i][j] of block (I, J): lane holds i = 4*(l/16) + r, j = l % 16
-#pragma unroll
-    for (int J = 0; J <= I; ++J) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = I * 16 + 4 * g + r;
-        const int j = J * 16 + r16;
-        if (i < n && j < i) put(ob + d + i * (i - 1) / 2 + j, acc[J][r]);
+      x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
+      if (kk < d) {
+        if (row == 0) {
+          const float4 v = *reinterpret_cast<const float4*>(x0 + kk);
+          x[t][c] = f4{v.x, v.y, v.z, v.w};
+        } else if (len[t] > 0) {
+          const float4 v = *reinterpret_cast<const float4*>(rp + kk);
+          x[t][c][0] = 0.f + v.x;
+          x[t][c][1] = 0.f + v.y;
+          x[t][c][2] = 0.f + v.z;
+          x[t][c][3] = 0.f + v.w;
+        }
       }
     }
   }
-
-  const int end = d + n * (n - 1) / 2;
-  for (int col = end + lane; col < pad_end; col += 64) put(ob + col, 0.f);
+  int maxlen = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) maxlen = len[t] > maxlen ? len[t] : maxlen;
+  for (int q = 1; q < maxlen; ++q) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (q < len[t]) {
+        const float* rp = tb[t] + idx[pb[t] + q] * (int64_t)d;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const int kk = c * 16 + 4 * g;
+          if (kk < d) {
+            const float4 v = *reinterpret_cast<const float4*>(rp + kk);
+            x[t][c][0] = x[t][c][0] + v.x;
+            x[t][c][1] = x[t][c][1] + v.y;
+            x[t][c][2] = x[t][c][2] + v.z;
+            x[t][c][3] = x[t][c][3] + v.w;
+          }
+        }
+      }
+    }
+  }
+  gram_row<NT, DC, OutT>(x, n, d, pad_end, reinterpret_cast<OutT*>(rowb), lane);
+  row_out(rowb, reinterpret_cast<char*>(out + b * out_ld), pad_end * (int)sizeof(OutT), wide, lane);
 }
 
 // Any shape: one thread per (sample, output column).  fp32 FMA chain.
@@ -124,44 +294,58 @@ __global__ __launch_bounds__(256) void interact_generic_kernel(const float* __re
   put(out + b * out_ld + col, v);
 }
 
-template <int NT, int DC, typename OutT>
-void launch_mfma(const float* X, int64_t B, int n, int d, int64_t x_ld, OutT* out, int64_t out_ld, int pad_end,
+template <int NT, int DC, typename OutT, bool FUSED>
+void launch_mfma(const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end,
                  hipStream_t s) {
-  hipLaunchKernelGGL((interact_mfma_kernel<NT, DC, OutT>), dim3((unsigned)ceil_div(B, 4)), dim3(256), 0, s, X, B, n,
-                     d, x_ld, out, out_ld, pad_end);
+  // row buffer: pad_end elements plus one spare element for masked stores
+  const int row_bytes = (int)round_up((int64_t)(pad_end + 1) * (int64_t)sizeof(OutT), 16);
+  int spb = 65536 / row_bytes;  // samples (waves) per block within 64 KB of LDS
+  spb = spb < 1 ? 1 : (spb > 4 ? 4 : spb);
+  const int wide = ((out_ld * (int64_t)sizeof(OutT)) % 16) == 0;
+  if (FUSED)
+    hipLaunchKernelGGL((fused_kernel<NT, DC, OutT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb),
+                       (size_t)spb * row_bytes, s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
+  else
+    hipLaunchKernelGGL((interact_mfma_kernel<NT, DC, OutT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb),
+                       (size_t)spb * row_bytes, s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
 }
 
-template <int DC, typename OutT>
-bool dispatch_nt(int NT, const float* X, int64_t B, int n, int d, int64_t x_ld, OutT* out, int64_t out_ld,
-                 int pad_end, hipStream_t s) {
+template <int DC, typename OutT, bool FUSED>
+bool dispatch_nt(int NT, const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end,
+                 hipStream_t s) {
   // x[NT][DC] must fit in 128 registers per lane: NT * DC <= 32
   constexpr int kMaxNT = (32 / DC) < 8 ? (32 / DC) : 8;
   if (NT > kMaxNT) return false;
   switch (NT) {
-    case 1: launch_mfma<1, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true;
-    case 2: launch_mfma<2, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true;
-    case 3: if constexpr (kMaxNT >= 3) { launch_mfma<3, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true; } break;
-    case 4: if constexpr (kMaxNT >= 4) { launch_mfma<4, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true; } break;
-    case 5: if constexpr (kMaxNT >= 5) { launch_mfma<5, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true; } break;
-    case 6: if constexpr (kMaxNT >= 6) { launch_mfma<6, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true; } break;
-    case 7: if constexpr (kMaxNT >= 7) { launch_mfma<7, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true; } break;
-    case 8: if constexpr (kMaxNT >= 8) { launch_mfma<8, DC>(X, B, n, d, x_ld, out, out_ld, pad_end, s); return true; } break;
+    case 1: launch_mfma<1, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true;
+    case 2: launch_mfma<2, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true;
+    case 3: if constexpr (kMaxNT >= 3) { launch_mfma<3, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 4: if constexpr (kMaxNT >= 4) { launch_mfma<4, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 5: if constexpr (kMaxNT >= 5) { launch_mfma<5, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 6: if constexpr (kMaxNT >= 6) { launch_mfma<6, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 7: if constexpr (kMaxNT >= 7) { launch_mfma<7, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 8: if constexpr (kMaxNT >= 8) { launch_mfma<8, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
   }
+  return false;
+}
+
+template <typename OutT, bool FUSED>
+bool dispatch(const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end, hipStream_t s) {
+  const int NT = (n + 15) / 16;
+  const int dc = (d + 15) / 16;
+  if (dc <= 1) return dispatch_nt<1, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 2) return dispatch_nt<2, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 4) return dispatch_nt<4, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 8) return dispatch_nt<8, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 16) return dispatch_nt<16, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
   return false;
 }
 
 template <typename OutT>
 void run(const float* X, int64_t B, int n, int d, int64_t x_ld, OutT* out, int64_t out_ld, int pad_end,
          hipStream_t s) {
-  const int NT = (n + 15) / 16;
-  const int dc = (d + 15) / 16;
-  bool done = false;
-  if (dc <= 1) done = dispatch_nt<1>(NT, X, B, n, d, x_ld, out, out_ld, pad_end, s);
-  else if (dc <= 2) done = dispatch_nt<2>(NT, X, B, n, d, x_ld, out, out_ld, pad_end, s);
-  else if (dc <= 4) done = dispatch_nt<4>(NT, X, B, n, d, x_ld, out, out_ld, pad_end, s);
-  else if (dc <= 8) done = dispatch_nt<8>(NT, X, B, n, d, x_ld, out, out_ld, pad_end, s);
-  else if (dc <= 16) done = dispatch_nt<16>(NT, X, B, n, d, x_ld, out, out_ld, pad_end, s);
-  if (!done) {
+  const RowSource src{X, x_ld, nullptr, nullptr, nullptr};
+  if (!dispatch<OutT, false>(src, B, n, d, out, out_ld, pad_end, s)) {
     const int64_t total = B * (int64_t)pad_end;
     hipLaunchKernelGGL((interact_generic_kernel<OutT>), dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, X, B,
                        n, d, x_ld, out, out_ld, pad_end);
@@ -186,5 +370,27 @@ extern "C" int dlrm_interact_fwd(const float* X, int64_t B, int32_t n, int32_t d
     run<float>(X, B, n, d, x_ld, static_cast<float*>(out), out_ld, pad_end, stream);
   else
     run<uint16_t>(X, B, n, d, x_ld, static_cast<uint16_t*>(out), out_ld, pad_end, stream);
+  return launch_status();
+}
+
+extern "C" int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, const float* const* tables, int32_t K,
+                                        int32_t d, const int64_t* indices, const int64_t* offsets, int64_t B,
+                                        void* out, int32_t out_dtype, int64_t out_ld, hipStream_t stream) {
+  if (!x_dense || !tables || !indices || !offsets || !out || K < 1 || B < 1) return DLRM_E_INVALID;
+  const int n = K + 1;
+  if (n > 128 || d < 4 || d > 256 || (d % 4) != 0) return DLRM_E_INVALID;
+  if (out_dtype != DLRM_F32 && out_dtype != DLRM_BF16) return DLRM_E_INVALID;
+  const int64_t width = d + (int64_t)n * (n - 1) / 2;
+  if (xd_ld < d || (xd_ld % 4) != 0 || !aligned16(x_dense)) return DLRM_E_INVALID;
+  if (out_ld < width || (out_ld % 4) != 0 || !aligned16(out)) return DLRM_E_INVALID;
+  if (ceil_div(B, 4) > 0x7fffffffLL || B * out_ld > (int64_t)1 << 40) return DLRM_E_UNSUPPORTED;
+  const int pad_end = (int)(round_up(width, 8) < out_ld ? round_up(width, 8) : out_ld);
+  const RowSource src{x_dense, xd_ld, tables, indices, offsets};
+  bool ok;
+  if (out_dtype == DLRM_F32)
+    ok = dispatch<float, true>(src, B, n, d, static_cast<float*>(out), out_ld, pad_end, stream);
+  else
+    ok = dispatch<uint16_t, true>(src, B, n, d, static_cast<uint16_t*>(out), out_ld, pad_end, stream);
+  if (!ok) return DLRM_E_UNSUPPORTED;  // (K + 1) x d does not fit the register-resident layout
   return launch_status();
 }

@@ -4,10 +4,12 @@ Holds device buffers (torch tensors: memory only) and orders the C-ABI
 calls on one stream; it performs no arithmetic itself.
 
 Forward ([SU] "briansu.co DLRM", How it works and Key equations):
-  1. dlrm_mlp_fwd(bottom)   dense [B][13] -> X[:, 0, :]          (fp32)
+  1. dlrm_mlp_fwd(bottom)   dense [B][13] -> x_dense              (fp32)
   2. dlrm_embbag_fwd        bags of K tables -> X[:, 1..K, :]     (fp32)
   3. dlrm_interact_fwd      X -> [x_dense, tril(X X^T)]           (bf16 row)
   4. dlrm_mlp_fwd(top)      -> logit, sigmoid(logit)
+With ``fused`` (the default) steps 2 and 3 are one dlrm_embbag_interact_fwd
+call and X never goes to memory; without it x_dense is row 0 of X.
 Training step (sum-pooled tables, row-wise SGD):
   forward with saved activations, dlrm_bce_grad, dlrm_mlp_bwd(top),
   dlrm_mlp_bwd(bottom) seeded by the X row-0 gradient, and
@@ -58,17 +60,25 @@ class DLRM:
     """Device state and call sequence for one batch size."""
 
     def __init__(self, B: int, K: int, d: int, rows, tables, bottom: MLPParams, top: MLPParams, train: bool = False,
-                 device="cuda"):
+                 device="cuda", fused: bool = True):
         self.B, self.K, self.d, self.n = B, K, d, K + 1
         self.rows = [int(r) for r in rows]
         self.tables = tables
         self.table_ptrs = C.device_pointer_array(tables)
         self.bottom, self.top = bottom, top
         self.train = train
+        self.fused = fused
         n, dev = self.n, device
         self.P = n * (n - 1) // 2
         self.top_w = d + self.P
-        self.X = torch.empty((B, n, d), dtype=torch.float32, device=dev)
+        if fused:
+            self.X = None
+            self.x0 = torch.empty((B, d), dtype=torch.float32, device=dev)
+            self.x0_ld = d
+        else:
+            self.X = torch.empty((B, n, d), dtype=torch.float32, device=dev)
+            self.x0 = self.X
+            self.x0_ld = n * d
         top_dtype = torch.bfloat16 if top.w_dtype == C.DLRM_BF16 else torch.float32
         self.top_ld = _round_up(self.top_w, 8) if top_dtype == torch.bfloat16 else _round_up(self.top_w, 4)
         self.top_in = torch.empty((B, self.top_ld), dtype=top_dtype, device=dev)
@@ -97,10 +107,14 @@ class DLRM:
         B, n, d = self.B, self.n, self.d
         save = self.train
         C.dlrm_mlp_fwd(dense, dense.shape[1], B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld,
-                       self.bottom.biases, self.bottom.w_dtype, C.DLRM_ACT_RELU, self.X, n * d, None, self.ws_bot,
-                       save, stream)
-        C.dlrm_embbag_fwd(self.table_ptrs, self.K, d, indices, offsets, B, self.X, n * d, d, stream)
-        C.dlrm_interact_fwd(self.X, B, n, d, n * d, self.top_in, self.top_ld, stream)
+                       self.bottom.biases, self.bottom.w_dtype, C.DLRM_ACT_RELU, self.x0, self.x0_ld, None,
+                       self.ws_bot, save, stream)
+        if self.fused:
+            C.dlrm_embbag_interact_fwd(self.x0, self.x0_ld, self.table_ptrs, self.K, d, indices, offsets, B,
+                                       self.top_in, self.top_ld, stream)
+        else:
+            C.dlrm_embbag_fwd(self.table_ptrs, self.K, d, indices, offsets, B, self.X, n * d, d, stream)
+            C.dlrm_interact_fwd(self.X, B, n, d, n * d, self.top_in, self.top_ld, stream)
         C.dlrm_mlp_fwd(self.top_in, self.top_ld, B, self.top.dims, self.top.Ws, self.top.w_ld, self.top.biases,
                        self.top.w_dtype, C.DLRM_ACT_NONE, self.logit, 1, self.prob, self.ws_top, save, stream)
         return self.logit, self.prob
@@ -118,7 +132,7 @@ class DLRM:
         C.dlrm_bce_grad(self.logit, 1, labels, B, self.dlogit, stream)
         C.dlrm_mlp_bwd(B, self.top.dims, self.top.Ws, self.top.w_ld, C.DLRM_ACT_NONE, self.ws_top, self.logit, 1,
                        self.dlogit, 1, self.dW_top, self.db_top, None, 0, self.ws_top_bwd, stream)
-        C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.X,
-                       n * d, G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
+        C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.x0,
+                       self.x0_ld, G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
         C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, G, n * d, d, lr,
                               self.sparse_workspace(nnz), stream)

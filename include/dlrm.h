@@ -107,6 +107,27 @@ int dlrm_interact_fwd(const float* X, int64_t B, int32_t n, int32_t d, int64_t x
                       int32_t out_dtype, int64_t out_ld, hipStream_t stream);
 
 /*
+ * Fused pooled lookup and interaction (forward).
+ * The same result as dlrm_embbag_fwd into X rows 1..K followed by
+ * dlrm_interact_fwd, with X row 0 = x_dense, but X never goes to memory:
+ * each sample's K pooled rows are summed straight into the registers that
+ * feed the Gram MFMAs.  Pooled values are bit-identical to dlrm_embbag_fwd
+ * (fp32, bag order, from +0) and the output bit-identical to the two-call
+ * path.  ([SU] Limitations & trade-offs: the model is memory-bound, so the
+ * round trip of X through HBM is the cost this call removes.)
+ *
+ *   x_dense  fp32 [B][xd_ld], d floats per sample (the bottom MLP output).
+ *   tables, K, d, indices, offsets, B: as dlrm_embbag_fwd.
+ *   out, out_dtype, out_ld: as dlrm_interact_fwd with n = K + 1.
+ *   Limits:  K + 1 <= 128, d % 4 == 0, 4 <= d <= 256, and
+ *            ceil((K+1)/16) * ceil(d/16) <= 32 (register-resident layout);
+ *            DLRM_E_UNSUPPORTED otherwise.
+ */
+int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, const float* const* tables, int32_t K, int32_t d,
+                             const int64_t* indices, const int64_t* offsets, int64_t B, void* out, int32_t out_dtype,
+                             int64_t out_ld, hipStream_t stream);
+
+/*
  * Multilayer perceptron, forward.
  * [EXPL] Key Method Details, "Bottom MLP" (FC layers with ReLU, output
  * width d) and "Top MLP" (FC layers with ReLU ending in a sigmoid); [SU] Key

@@ -42,7 +42,7 @@ def oracle_forward(w, dense, idx, off, bottom, top, samples=None, tables=None):
     return X, top_in, logit[:, 0], prob
 
 
-def device_model(w, train=False, tables=None, batch=0):
+def device_model(w, train=False, tables=None, batch=0, fused=True):
     """Pipeline state on the GPU for workload ``w`` (tables filled on device)."""
     from deep_learning_recommendation_amd import pipeline as PL
 
@@ -53,7 +53,7 @@ def device_model(w, train=False, tables=None, batch=0):
     top = W.mlp_params(w, "top")
     bp = PL.make_mlp(w.bottom, [p[0] for p in bottom], [p[2] for p in bottom], bf16)
     tp = PL.make_mlp(w.top, [p[0] for p in top], [p[2] for p in top], bf16)
-    model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=train)
+    model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=train, fused=fused)
     return model, bottom, top
 
 
@@ -75,3 +75,13 @@ def interaction_tolerance(X):
 
 def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
+
+
+def bf16_row_tolerance(X, ref_row):
+    """Bound for a bf16 top-MLP input row against the oracle's fp32 row:
+    the device's fp32 value lies within tol = 1e-5 sum|x_i x_j| (pairs) or is
+    exact (dense part), then one bf16 rounding adds at most 2**-8 of it."""
+    d = X.shape[2]
+    tol = np.zeros_like(ref_row, dtype=np.float64)
+    tol[:, d:d + interaction_tolerance(X).shape[1]] = interaction_tolerance(X)
+    return tol + 2.0 ** -8 * (np.abs(ref_row.astype(np.float64)) + tol) + 1e-30

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import oracle
-from dlrm_cases import DEV, banner, bits, interaction_tolerance, to_dev
+from dlrm_cases import DEV, banner, bf16_row_tolerance, bits, interaction_tolerance, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +61,8 @@ def test_interact_bf16_output():
     got, width = _run(X, torch.bfloat16)
     ref = oracle.interact_fwd(X)
     ref_b = torch.from_numpy(ref).to(torch.bfloat16).float().numpy()
-    # each value is the bf16 rounding of an fp32 result within the fp32 bound:
-    # at most one bf16 ulp from the oracle's rounding
-    ulp = np.abs(ref_b) * 2.0 ** -7 + 1e-30
-    assert np.all(np.abs(got[:, :width] - ref_b) <= ulp)
+    # each value is the bf16 rounding of an fp32 result within the fp32 bound
+    assert np.all(np.abs(got[:, :width] - ref) <= bf16_row_tolerance(X, ref))
     assert (got[:, :width] == ref_b).mean() > 0.99
 
 
@@ -80,3 +78,51 @@ def test_interact_workload_shapes_full_batch():
         tol = interaction_tolerance(X[rows])
         assert np.all(np.abs(got[rows, d:width].astype(np.float64) - ref[:, d:]) <= tol)
         assert np.array_equal(bits(got[rows, :d]), bits(ref[:, :d]))
+
+
+@pytest.mark.parametrize("K,d,out_bf16", [(8, 16, False), (26, 128, True), (26, 128, False), (100, 64, True),
+                                          (8, 128, True), (3, 12, False), (31, 64, True)])
+def test_fused_gather_interaction(K, d, out_bf16):
+    """dlrm_embbag_interact_fwd against dlrm_embbag_fwd + dlrm_interact_fwd on
+    the GPU (bit for bit) and against the oracle (pooled rows exact, pairs
+    within the dot-product bound), on ragged multi-hot bags with empty ones."""
+    import deep_learning_recommendation_amd as D
+
+    B = 203
+    n = K + 1
+    banner(f"fused gather+interaction K={K} d={d} bf16={out_bf16}")
+    g = np.random.default_rng(K * 100 + d)
+    rows = [int(x) for x in g.integers(5, 300, size=K)]
+    lens = g.integers(0, 6, size=K * B)
+    off = np.zeros(K * B + 1, dtype=np.int64)
+    np.cumsum(lens, out=off[1:])
+    idx = np.concatenate([g.integers(0, rows[k], off[(k + 1) * B] - off[k * B]) for k in range(K)]).astype(np.int64)
+    tabs = [(g.standard_normal((rows[k], d)) * 0.3).astype(np.float32) for k in range(K)]
+    x0 = g.standard_normal((B, d)).astype(np.float32)
+    tdev = [to_dev(t) for t in tabs]
+    ptrs = D.device_pointer_array(tdev)
+    width = d + n * (n - 1) // 2
+    ld = ((width + 7) // 8) * 8
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    # two-call path
+    X = torch.zeros((B, n, d), dtype=torch.float32, device=DEV)
+    X[:, 0, :] = to_dev(x0)
+    D.dlrm_embbag_fwd(ptrs, K, d, to_dev(idx), to_dev(off), B, X, n * d, d)
+    two = torch.full((B, ld), 3.0, dtype=dt, device=DEV)
+    D.dlrm_interact_fwd(X, B, n, d, n * d, two, ld)
+    one = torch.full((B, ld), 5.0, dtype=dt, device=DEV)
+    D.dlrm_embbag_interact_fwd(to_dev(x0), d, ptrs, K, d, to_dev(idx), to_dev(off), B, one, ld)
+    torch.cuda.synchronize()
+    vt = torch.int16 if out_bf16 else torch.int32
+    assert torch.equal(one.view(vt), two.view(vt))
+    # oracle
+    E = oracle.embbag_fwd(tabs, idx, off, B).reshape(B, K, d)
+    Xr = np.concatenate([x0[:, None, :], E], axis=1)
+    ref = oracle.interact_fwd(Xr)
+    got = one.float().cpu().numpy()
+    if out_bf16:
+        assert np.all(np.abs(got[:, :width] - ref) <= bf16_row_tolerance(Xr, ref))
+    else:
+        assert np.array_equal(bits(got[:, :d]), bits(ref[:, :d]))
+        assert np.all(np.abs(got[:, d:width].astype(np.float64) - ref[:, d:]) <= interaction_tolerance(Xr))
+    assert np.all(got[:, width:] == 0)

@@ -96,6 +96,35 @@ def test_mlp_identity_layers_exact():
     assert np.array_equal(out.cpu().numpy(), np.maximum(x, 0))
 
 
+def test_device_bf16_rounding_matches_torch():
+    # fp32 input -> bf16 rounding on the device (the layer-0 conversion),
+    # then an identity layer (one exact nonzero product per output): the fp32
+    # output must be the nearest-even bf16 of the input, bit for bit, for
+    # ties of both parities and values across the normal range.  (The bf16
+    # MFMA reads subnormal operands as zero, so the identity layer cannot
+    # show the rounding of values below 2**-126.)
+    import deep_learning_recommendation_amd as D  # noqa: F401
+
+    banner("device bf16 rounding")
+    g = np.random.default_rng(4)
+    vals = [np.ldexp(g.random(48) + 1.0, int(e)) for e in range(-126, 127, 3)]
+    ties = np.array([0x3F808000, 0x3F818000, 0x40008000, 0x00818000, 0x00808000, 0x7F7F7FFF, 0x3F80FFFF],
+                    dtype=np.uint32).view(np.float32)
+    x = np.concatenate(vals + [ties, [1.0, 3.0e38]]).astype(np.float32)  # no signed zero: -0 + (+0 products) = +0
+    x = np.concatenate([x, -x])
+    d = 64
+    x = np.concatenate([x, np.zeros((-len(x)) % d, np.float32)]).reshape(-1, d)
+    I = np.eye(d, dtype=np.float32)
+    mp = _mlp_dev((d, d), [(I, None, np.zeros(d, np.float32))], True)
+    out, _, _ = _fwd(mp, x, False)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    got = out.cpu().numpy()
+    bad = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+    detail = [(hex(int(x.view(np.uint32).flat[i])), hex(int(got.view(np.uint32).flat[i])),
+               hex(int(ref.view(np.uint32).flat[i]))) for i in bad[:8]]
+    assert bad.size == 0, f"{bad.size} mismatches (input, device, reference): {detail}"
+
+
 @pytest.mark.parametrize("which", ["bottom", "top"])
 def test_mlp_bf16_backward(which):
     import deep_learning_recommendation_amd as D
