@@ -41,6 +41,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i's bytes land at lds + 16 * i; lds must be
+// the same for every lane of the wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
+}
+
+// Keeps the compiler from moving memory accesses across this point.
+__device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
+
 // Scratch carving: 256-byte aligned sub-buffers of a caller workspace.
 struct Carver {
   char* base;

@@ -44,12 +44,6 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Fast path: 16-byte aligned operands with lda, ldw multiples of 8.
 //
 // Tiles move from global memory straight into LDS with global_load_lds_dwordx4

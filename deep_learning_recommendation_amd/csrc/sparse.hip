@@ -14,9 +14,12 @@
 //   4. one fused kernel: each segment's gradient sum over its occurrences in
 //      sorted order (fp32, from +0) and the update T <- T - lr * g.
 // Hot rows (Zipf heads with 10^5 occurrences) make step 4's longest serial
-// chain the latency floor; segments of at least kHot occurrences are taken
-// by dedicated waves that split the row's columns one per lane and are
-// dispatched before the rest.
+// chain the latency floor.  Segments of at least kHot occurrences go to a
+// producer/consumer kernel: per (segment, 64-column slice) one wave adds, one
+// column per lane, from an LDS ring that seven other waves keep filled with
+// direct global-to-LDS loads, so the serial adds never wait on memory.  Hot
+// items are handed out longest first.  The remaining (short) segments take
+// one lane group each.
 #include "common.hpp"
 
 namespace dlrm {
@@ -27,33 +30,40 @@ constexpr int RITEMS = 16;             // keys per thread per tile
 constexpr int RTILE = RT * RITEMS;     // 4096 keys per tile
 constexpr int SCAN_ITEMS = 8;
 constexpr int SCAN_TILE = 256 * SCAN_ITEMS;
-constexpr int kHot = 512;              // occurrences from which a segment is "hot"
-constexpr int kHeavyBlocks = 256;      // blocks (4 waves each) reserved for hot segments
+constexpr int kHot = 128;              // occurrences from which a segment is "hot"
+constexpr int kHotBlocks = 256;        // persistent blocks of the hot kernel (one per CU)
+constexpr int kHB = 64;                // occurrences per LDS ring slot
+constexpr int kSlots = 8;              // ring slots (8 x 64 x 64 x 4 B = 128 KB)
+constexpr int kLoaders = 7;            // loader waves per hot block (plus one adder)
 constexpr int kLightBlocks = 2048;
 
 // ------------------------------------------------------------------ keys
 
+// Each thread takes 8 consecutive positions: one binary search in the
+// offsets for the first position's bag, then a forward walk.
+constexpr int KEY_ITEMS = 8;
 __global__ __launch_bounds__(256) void build_keys_kernel(const int64_t* __restrict__ idx,
                                                          const int64_t* __restrict__ off, int64_t KB, int64_t B,
-                                                         int row_bits, uint32_t* __restrict__ keys,
+                                                         int64_t n, int row_bits, uint32_t* __restrict__ keys,
                                                          int32_t* __restrict__ vals) {
-  __shared__ int64_t s_off[257];
-  const int64_t kb0 = (int64_t)blockIdx.x * 256;
-  const int nb = (int)min((int64_t)256, KB - kb0);
-  for (int j = threadIdx.x; j <= nb; j += blockDim.x) s_off[j] = off[kb0 + j];
-  __syncthreads();
-  const int64_t p0 = s_off[0], p1 = s_off[nb];
-  for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
-    int lo = 0, hi = nb - 1;  // largest j with s_off[j] <= p
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= p) lo = mid;
-      else hi = mid - 1;
+  const int64_t p0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * KEY_ITEMS;
+  if (p0 >= n) return;
+  int64_t lo = 0, hi = KB - 1;  // largest kb with off[kb] <= p0
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= p0) lo = mid;
+    else hi = mid - 1;
+  }
+  int64_t kb = lo, next = off[kb + 1];
+#pragma unroll
+  for (int i = 0; i < KEY_ITEMS; ++i) {
+    const int64_t p = p0 + i;
+    if (p < n) {
+      while (next <= p) next = off[++kb + 1];
+      const int64_t k = kb / B;
+      keys[p] = ((uint32_t)k << row_bits) | (uint32_t)idx[p];
+      vals[p] = (int32_t)(kb - k * B);
     }
-    const int64_t kb = kb0 + lo;
-    const int64_t k = kb / B;
-    keys[p] = ((uint32_t)k << row_bits) | (uint32_t)idx[p];
-    vals[p] = (int32_t)(kb - k * B);
   }
 }
 
@@ -222,6 +232,7 @@ __global__ __launch_bounds__(256) void scan_apply_array_kernel(const uint32_t* _
 __global__ __launch_bounds__(256) void scan_apply_heads_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                                const uint32_t* __restrict__ bsum,
                                                                int32_t* __restrict__ seg_start,
+                                                               uint32_t* __restrict__ seg_key,
                                                                const uint32_t* __restrict__ nseg) {
   __shared__ uint32_t s_wave[4];
   const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
@@ -236,7 +247,10 @@ __global__ __launch_bounds__(256) void scan_apply_heads_kernel(const uint32_t* _
   uint32_t run = bsum[blockIdx.x] + block_exclusive_scan(s, s_wave, &total);
 #pragma unroll
   for (int i = 0; i < SCAN_ITEMS; ++i) {
-    if (v[i]) seg_start[run] = (int32_t)(base + i);
+    if (v[i]) {
+      seg_start[run] = (int32_t)(base + i);
+      seg_key[run] = keys[base + i];
+    }
     run += v[i];
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) seg_start[*nseg] = (int32_t)n;
@@ -246,66 +260,245 @@ __global__ __launch_bounds__(256) void find_hot_kernel(const int32_t* __restrict
                                                        const uint32_t* __restrict__ nseg, int32_t* __restrict__ hot,
                                                        uint32_t* __restrict__ nhot) {
   const uint32_t U = *nseg;
-  for (uint32_t s = blockIdx.x * blockDim.x + threadIdx.x; s < U; s += gridDim.x * blockDim.x) {
-    if (seg_start[s + 1] - seg_start[s] >= kHot) hot[atomicAdd(nhot, 1u)] = (int32_t)s;
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint32_t stride = gridDim.x * blockDim.x;
+  // every lane of a wave runs the same number of iterations (ballots below)
+  for (uint32_t s0 = blockIdx.x * blockDim.x; s0 < U; s0 += stride) {
+    const uint32_t s = s0 + threadIdx.x;
+    const bool is_hot = s < U && seg_start[s + 1] - seg_start[s] >= kHot;
+    const uint64_t m = __ballot(is_hot);
+    if (m == 0ull) continue;
+    uint32_t at = 0;
+    if (lane == __ffsll((long long)m) - 1) at = atomicAdd(nhot, (uint32_t)__popcll(m));
+    at = __shfl(at, __ffsll((long long)m) - 1, 64);
+    if (is_hot) hot[at + __popcll(m & below)] = (int32_t)s;
+  }
+}
+
+// One block: hot segments regrouped by floor(log2(length)), longest group
+// first, so the longest serial chains start first (order inside a group is
+// arbitrary; every segment's result is independent of it).
+__global__ __launch_bounds__(256) void order_hot_kernel(const int32_t* __restrict__ seg_start,
+                                                        const int32_t* __restrict__ hot,
+                                                        const uint32_t* __restrict__ nhot,
+                                                        int32_t* __restrict__ ordered) {
+  __shared__ uint32_t cnt[32];
+  const uint32_t n = *nhot;
+  if (threadIdx.x < 32) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int32_t h = hot[i];
+    atomicAdd(&cnt[31 - __clz(seg_start[h + 1] - seg_start[h])], 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t c = cnt[b];
+      cnt[b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int32_t h = hot[i];
+    ordered[atomicAdd(&cnt[31 - __clz(seg_start[h + 1] - seg_start[h])], 1u)] = h;
   }
 }
 
 // ------------------------------------------------------------------ reduce + SGD
 
-template <int V>
-__global__ __launch_bounds__(256) void segment_sgd_kernel(float* const* __restrict__ tables, int d, int g_log2,
-                                                          int row_bits, const uint32_t* __restrict__ keys,
-                                                          const int32_t* __restrict__ bags,
-                                                          const int32_t* __restrict__ seg_start,
-                                                          const uint32_t* __restrict__ nseg,
-                                                          const int32_t* __restrict__ hot,
-                                                          const uint32_t* __restrict__ nhot,
-                                                          const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
-                                                          float lr) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Hand-over flags in LDS, read and written as workgroup-scope atomics so
+// that every access really goes to LDS and stays in program order.
+__device__ __forceinline__ int32_t lds_load(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Hot segments.  A block (8 waves) takes (segment, 64-column slice) items
+// from a global counter.  Wave 0 is the adder: lane j owns column j of the
+// slice and adds the occurrences in sorted order, reading them from LDS.
+// Waves 1..7 are loaders: block t of the segment (occurrences 64t..64t+63)
+// goes to ring slot (running block number) mod kSlots, loaded by wave
+// 1 + t mod 7; each lane of a direct-to-LDS load brings 16 bytes of one
+// occurrence's slice, so a slot holds 64 occurrences x 64 columns
+// occurrence-major and the adder's reads (one column per lane) are
+// bank-conflict free.  Hand-over per slot: the loader waits until the adder
+// has finished the slot's previous block ("consumed"), loads, waits for its
+// loads and publishes the running block number in ready[slot].
+__global__ __launch_bounds__(512) void hot_sgd_kernel(float* const* __restrict__ tables, int d, int row_bits,
+                                                      const uint32_t* __restrict__ seg_key,
+                                                      const int32_t* __restrict__ bags,
+                                                      const int32_t* __restrict__ seg_start,
+                                                      const int32_t* __restrict__ hot,
+                                                      const uint32_t* __restrict__ nhot,
+                                                      const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
+                                                      float lr, uint32_t* __restrict__ next_item) {
+  __shared__ __attribute__((aligned(16))) float ring[kSlots][kHB * 64];
+  __shared__ int32_t ready[kSlots];
+  __shared__ int32_t consumed;
+  __shared__ uint32_t s_item;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < kSlots) ready[tid] = -1;
+  if (tid == 0) consumed = 0;
   const uint32_t row_mask = (row_bits >= 32) ? 0xffffffffu : ((1u << row_bits) - 1u);
-  if (blockIdx.x < kHeavyBlocks) {
-    // hot segments: one wave per (segment, 64-column slice), one column per lane
-    const int slices = (d + 63) / 64;
-    const uint32_t items = *nhot * (uint32_t)slices;
-    for (uint32_t it = blockIdx.x * 4 + wave; it < items; it += kHeavyBlocks * 4) {
-      const int32_t s = hot[it / slices];
-      const int col = (int)(it % slices) * 64 + lane;
-      const int32_t beg = seg_start[s], end = seg_start[s + 1];
-      const uint32_t key = keys[beg];
-      const int k = (int)(key >> row_bits);
-      const int64_t r = (int64_t)(key & row_mask);
-      if (col < d) {
-        const float* gcol = G + g_col0 + (int64_t)k * d + col;
-        float acc = 0.f;
-        int32_t q = beg;
-        for (; q + 8 <= end; q += 8) {
-          float v[8];
+  const int slices = (d + 63) >> 6;
+  const uint32_t items = *nhot * (uint32_t)slices;
+  int32_t base = 0;  // running block number of this block's first ring use in the current item
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) s_item = atomicAdd(next_item, 1u);
+    __syncthreads();
+    const uint32_t item = s_item;
+    if (item >= items) break;
+    const int32_t s = hot[item / slices];
+    const int col0 = (int)(item % slices) * 64;
+    const int cols = min(64, d - col0);
+    const int32_t beg = seg_start[s], end = seg_start[s + 1];
+    const uint32_t key = seg_key[s];
+    const int k = (int)(key >> row_bits);
+    const int64_t r = (int64_t)(key & row_mask);
+    const int32_t nblk = (end - beg + kHB - 1) / kHB;
+    if (wave == 0) {
+      // The adds run as one stream over the full blocks, 8 values per step,
+      // with the LDS reads issued three steps ahead (12 reads in flight,
+      // within the 15 that lgkmcnt can count).
+      constexpr int kStep = 8, kAhead = 3, kSteps = kHB / kStep;
+      const int32_t len = end - beg;
+      const int32_t nfull = len / kHB;
+      float acc = 0.f;
+      float v[4][kStep];
+      // occurrence o of a block sits in slot row 4 * (o % 16) + o / 16
+      auto step_load = [&](int32_t t, int st, float* dst) {
+        const float* blk = &ring[(base + t) & (kSlots - 1)][lane];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = gcol[(int64_t)bags[q + u] * g_ld];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) acc = acc + v[u];
+        for (int j = 0; j < kStep; ++j) {
+          const int o = st * kStep + j;
+          dst[j] = blk[(((o & 15) << 2) | (o >> 4)) * 64];
         }
-        for (; q < end; ++q) acc = acc + gcol[(int64_t)bags[q] * g_ld];
-        float* t = tables[k] + r * d + col;
+      };
+      auto wait_ready = [&](int32_t t) {
+        while (lds_load(&ready[(base + t) & (kSlots - 1)]) != base + t) __builtin_amdgcn_s_sleep(1);
+        compiler_fence();
+      };
+      auto peek = [&](int32_t t) { return lds_load(&ready[(base + t) & (kSlots - 1)]); };
+      int32_t seen = -1;
+      if (nfull > 0) {
+        wait_ready(0);
+#pragma unroll
+        for (int st = 0; st < kAhead; ++st) step_load(0, st, v[st]);
+        seen = peek(1);
+      }
+      for (int32_t t = 0; t < nfull; ++t) {
+        // the next block must be in before this one starts: its first reads
+        // are issued during this block's last steps, with no branch between;
+        // its flag was read one block earlier, so usually nothing waits here
+        const bool more = t + 1 < nfull;
+        if (more && seen != base + t + 1) wait_ready(t + 1);
+        seen = peek(t + 2);
+        const int32_t tn = more ? t + 1 : t;
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          // reads kAhead steps ahead, then this step's adds; the scheduling
+          // barrier keeps the compiler from hoisting every read to the top
+          if (st + kAhead < kSteps)
+            step_load(t, st + kAhead, v[(st + kAhead) & 3]);
+          else
+            step_load(tn, st + kAhead - kSteps, v[(st + kAhead) & 3]);
+#pragma unroll
+          for (int o = 0; o < kStep; ++o) acc = acc + v[st & 3][o];
+          __asm__ volatile("" : "+v"(acc));  // this step's adds stay in this step
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        compiler_fence();
+        if (lane == 0) lds_store(&consumed, base + t + 1);
+      }
+      if (nfull * kHB < len) {  // the last, partial block
+        const int32_t t = nfull;
+        wait_ready(t);
+        const float* blk = &ring[(base + t) & (kSlots - 1)][lane];
+        for (int o = 0; o < len - nfull * kHB; ++o) acc = acc + blk[(((o & 15) << 2) | (o >> 4)) * 64];
+        compiler_fence();
+        if (lane == 0) lds_store(&consumed, base + t + 1);
+      }
+      if (lane < cols) {
+        float* t = tables[k] + r * d + col0 + lane;
         *t = __fsub_rn(*t, __fmul_rn(lr, acc));
       }
+    } else {
+      // Loader: instruction i of a block brings occurrences i + 16 * (lane / 16)
+      // (lane % 16 = 16-byte column group), so each lane's 16 bag ids are
+      // consecutive in the sorted list; they are loaded for the loader's next
+      // block while this block's loads are in flight.
+      const int c4 = min(lane & 15, cols / 4 - 1);
+      const int sub = lane >> 4;
+      const float* gsrc = G + g_col0 + (int64_t)k * d + col0 + 4 * c4;
+      int32_t bag[16];
+      auto load_bags = [&](int32_t t) {
+        const int32_t q0 = beg + t * kHB, last = end - 1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bag[i] = bags[min(q0 + i + 16 * sub, last)];
+      };
+      int32_t t = wave - 1;
+      if (t < nblk) load_bags(t);
+      for (; t < nblk; t += kLoaders) {
+        const int32_t g = base + t;
+        const int slot = g & (kSlots - 1);
+        while (lds_load(&consumed) < g - kSlots + 1) __builtin_amdgcn_s_sleep(1);
+        compiler_fence();
+        float* dst = &ring[slot][0];
+        const int cnt = min(kHB, end - beg - t * kHB);
+        if (cnt == kHB) {  // full block: straight-line issue
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lds_dma16(gsrc + (int64_t)bag[i] * g_ld, dst + i * 256);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (i < cnt) lds_dma16(gsrc + (int64_t)bag[i] * g_ld, dst + i * 256);
+        }
+        compiler_fence();
+        if (t + kLoaders < nblk) {
+          load_bags(t + kLoaders);
+          wait_vmcnt<16>();  // this block's loads (issued before the 16 bag loads) are in LDS
+        } else {
+          wait_vmcnt<0>();
+        }
+        compiler_fence();
+        if (lane == 0) lds_store(&ready[slot], g);
+      }
     }
-    return;
+    base += nblk;
   }
-  // all other segments: a group of G lanes (float4 each) per segment
+}
+
+// Short segments: a group of 2^g_log2 lanes (V float4 each) per segment.
+// The group loads up to one bag id per lane at once, then walks the bags in
+// order with U gradient rows in flight, broadcasting each bag id from its lane.
+template <int V>
+__global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict__ tables, int d, int g_log2,
+                                                        int row_bits, const uint32_t* __restrict__ seg_key,
+                                                        const int32_t* __restrict__ bags,
+                                                        const int32_t* __restrict__ seg_start,
+                                                        const uint32_t* __restrict__ nseg,
+                                                        const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
+                                                        float lr) {
+  constexpr int U = 8 / V;
+  const int lane = threadIdx.x & 63;
+  const uint32_t row_mask = (row_bits >= 32) ? 0xffffffffu : ((1u << row_bits) - 1u);
   const int GL = 1 << g_log2;  // lanes per group
   const int gl = lane & (GL - 1);
   const int groups_per_block = 256 >> g_log2;
-  const int64_t gid = (int64_t)(blockIdx.x - kHeavyBlocks) * groups_per_block + (threadIdx.x >> g_log2);
-  const int64_t ngroups = (int64_t)(gridDim.x - kHeavyBlocks) * groups_per_block;
+  const int64_t gid = (int64_t)blockIdx.x * groups_per_block + (threadIdx.x >> g_log2);
+  const int64_t ngroups = (int64_t)gridDim.x * groups_per_block;
   const int d4 = d >> 2;
-  const uint32_t U = *nseg;
-  for (int64_t s = gid; s < U; s += ngroups) {
+  const uint32_t nsegs = *nseg;
+  for (int64_t s = gid; s < nsegs; s += ngroups) {
     const int32_t beg = seg_start[s], end = seg_start[s + 1];
+    const uint32_t key = seg_key[s];
     if (end - beg >= kHot) continue;
-    const uint32_t key = keys[beg];
     const int k = (int)(key >> row_bits);
     const int64_t r = (int64_t)(key & row_mask);
     float4* trow = reinterpret_cast<float4*>(tables[k] + r * d);
@@ -319,29 +512,32 @@ __global__ __launch_bounds__(256) void segment_sgd_kernel(float* const* __restri
     float4 acc[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    constexpr int U = 8 / V;
-    for (int32_t q = beg; q < end; q += U) {
-      float4 v[U][V];
+    for (int32_t q0 = beg; q0 < end; q0 += GL) {
+      const int m = min(GL, end - q0);
+      const int32_t my_bag = gl < m ? bags[q0 + gl] : 0;
+      for (int u0 = 0; u0 < m; u0 += U) {
+        float4 v[U][V];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = q + u < end;
-        const int64_t bag = ok ? (int64_t)bags[q + u] : 0;
-        const float4* grow = reinterpret_cast<const float4*>(gbase + bag * g_ld);
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const int c4 = gl + j * GL;
-          v[u][j] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (q + u < end) {
+        for (int u = 0; u < U; ++u) {
+          const bool ok = u0 + u < m;
+          const int64_t bag = __shfl(my_bag, ok ? u0 + u : 0, GL);
+          const float4* grow = reinterpret_cast<const float4*>(gbase + bag * g_ld);
 #pragma unroll
           for (int j = 0; j < V; ++j) {
-            acc[j].x = acc[j].x + v[u][j].x;
-            acc[j].y = acc[j].y + v[u][j].y;
-            acc[j].z = acc[j].z + v[u][j].z;
-            acc[j].w = acc[j].w + v[u][j].w;
+            const int c4 = gl + j * GL;
+            v[u][j] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (u0 + u < m) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+              acc[j].x = acc[j].x + v[u][j].x;
+              acc[j].y = acc[j].y + v[u][j].y;
+              acc[j].z = acc[j].z + v[u][j].z;
+              acc[j].w = acc[j].w + v[u][j].w;
+            }
           }
         }
       }
@@ -368,7 +564,7 @@ int bits_for(int64_t x) {  // bits needed to hold 0..x
 }
 
 struct SparseLayout {
-  size_t keys[2], vals[2], hist, bsum, seg, counters, hot, bytes;
+  size_t keys[2], vals[2], hist, bsum, seg, seg_key, counters, hot, hot_ordered, bytes;
   int64_t nblocks, hist_n, scan_nb_hist, scan_nb_keys;
 };
 
@@ -393,8 +589,10 @@ void sparse_layout(int64_t nnz, SparseLayout* L) {
   const int64_t nb = L->scan_nb_hist > L->scan_nb_keys ? L->scan_nb_hist : L->scan_nb_keys;
   L->bsum = take(4 * (size_t)nb);
   L->seg = take(4 * (size_t)(n + 1));
+  L->seg_key = take(4 * (size_t)n);
   L->counters = take(4 * 16);
   L->hot = take(4 * (size_t)(n / kHot + 1));
+  L->hot_ordered = take(4 * (size_t)(n / kHot + 1));
   L->bytes = cv.bytes();
 }
 
@@ -445,14 +643,17 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + L.hist);
   uint32_t* bsum = reinterpret_cast<uint32_t*>(w + L.bsum);
   int32_t* seg = reinterpret_cast<int32_t*>(w + L.seg);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(w + L.counters);  // [0] segments, [1] hot segments
+  uint32_t* seg_key = reinterpret_cast<uint32_t*>(w + L.seg_key);
+  // counters: [0] segments, [1] hot segments, [2] next hot item
+  uint32_t* counters = reinterpret_cast<uint32_t*>(w + L.counters);
   int32_t* hot = reinterpret_cast<int32_t*>(w + L.hot);
+  int32_t* hot_ordered = reinterpret_cast<int32_t*>(w + L.hot_ordered);
   const int n = (int)nnz;
   const int64_t KB = (int64_t)K * B;
 
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, counters, 16);
-  hipLaunchKernelGGL(build_keys_kernel, dim3((unsigned)ceil_div(KB, 256)), dim3(256), 0, stream, indices, offsets, KB,
-                     B, row_bits, keys[0], vals[0]);
+  hipLaunchKernelGGL(build_keys_kernel, dim3((unsigned)ceil_div(nnz, 256 * KEY_ITEMS)), dim3(256), 0, stream, indices,
+                     offsets, KB, B, nnz, row_bits, keys[0], vals[0]);
   const int key_bits = row_bits + table_bits;
   const int passes = (key_bits + 7) / 8;
   const int nblocks = (int)L.nblocks;
@@ -474,22 +675,28 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
                      HeadIn{keys[cur]}, (int64_t)n, bsum);
   hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, bsum, (int)L.scan_nb_keys, &counters[0]);
   hipLaunchKernelGGL(scan_apply_heads_kernel, dim3((unsigned)L.scan_nb_keys), dim3(256), 0, stream, keys[cur],
-                     (int64_t)n, bsum, seg, &counters[0]);
+                     (int64_t)n, bsum, seg, seg_key, &counters[0]);
   hipLaunchKernelGGL(find_hot_kernel, dim3(1024), dim3(256), 0, stream, seg, &counters[0], hot, &counters[1]);
-  // per-segment sums and the in-place update
+  hipLaunchKernelGGL(order_hot_kernel, dim3(1), dim3(256), 0, stream, seg, hot, &counters[1], hot_ordered);
+  // per-segment sums and the in-place update: long segments, then short ones
+  hipLaunchKernelGGL(hot_sgd_kernel, dim3(kHotBlocks), dim3(512), 0, stream, tables, d, row_bits, seg_key,
+                     vals[cur], seg, hot_ordered, &counters[1], G, g_ld, g_col0, lr, &counters[2]);
+  // short segments: half as many lanes as float4 columns (two float4 per
+  // lane), at most 64
   const int d4 = d / 4;
-  int g_log2 = 0;
-  while ((1 << g_log2) < d4 && g_log2 < 6) ++g_log2;
+  int l2 = 0;
+  while ((1 << l2) < d4) ++l2;
+  const int g_log2 = l2 > 0 ? (l2 - 1 < 6 ? l2 - 1 : 6) : 0;
   const int V = (d4 + (1 << g_log2) - 1) >> g_log2;
-  const dim3 grid(kHeavyBlocks + kLightBlocks), block(256);
+  const dim3 grid(kLightBlocks), block(256);
   if (V == 1)
-    hipLaunchKernelGGL((segment_sgd_kernel<1>), grid, block, 0, stream, tables, d, g_log2, row_bits, keys[cur],
-                       vals[cur], seg, &counters[0], hot, &counters[1], G, g_ld, g_col0, lr);
+    hipLaunchKernelGGL((light_sgd_kernel<1>), grid, block, 0, stream, tables, d, g_log2, row_bits, seg_key,
+                       vals[cur], seg, &counters[0], G, g_ld, g_col0, lr);
   else if (V == 2)
-    hipLaunchKernelGGL((segment_sgd_kernel<2>), grid, block, 0, stream, tables, d, g_log2, row_bits, keys[cur],
-                       vals[cur], seg, &counters[0], hot, &counters[1], G, g_ld, g_col0, lr);
+    hipLaunchKernelGGL((light_sgd_kernel<2>), grid, block, 0, stream, tables, d, g_log2, row_bits, seg_key,
+                       vals[cur], seg, &counters[0], G, g_ld, g_col0, lr);
   else
-    hipLaunchKernelGGL((segment_sgd_kernel<4>), grid, block, 0, stream, tables, d, g_log2, row_bits, keys[cur],
-                       vals[cur], seg, &counters[0], hot, &counters[1], G, g_ld, g_col0, lr);
+    hipLaunchKernelGGL((light_sgd_kernel<4>), grid, block, 0, stream, tables, d, g_log2, row_bits, seg_key,
+                       vals[cur], seg, &counters[0], G, g_ld, g_col0, lr);
   return launch_status();
 }

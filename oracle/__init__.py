@@ -157,6 +157,7 @@ def embbag_bwd_sgd(tables, idx, offsets, B: int, G, g_col0: int, lr: float, L=No
     rows = np.array([t.shape[0] for t in tables], dtype=np.int64)
     idx, offsets = _c(idx, np.int64), _c(offsets, np.int64)
     G = _c(G, np.float32).reshape(B, -1)
+    assert 0 <= g_col0 and g_col0 + K * d <= G.shape[1], "G has no room for K blocks of d columns at g_col0"
     L.oracle_embbag_bwd_sgd(_ptr_array(tables), _ptr(rows), K, d, _ptr(idx), _ptr(offsets), B, _ptr(G),
                             G.shape[1], g_col0, ctypes.c_float(lr))
     return tables

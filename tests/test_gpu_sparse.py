@@ -53,7 +53,58 @@ def test_sparse_sgd_random_bitexact(d, K, hot):
         assert np.array_equal(bits(tabs_dev[k].cpu().numpy()), bits(ref[k]))
     if hot:
         counts = np.bincount(idx[off[0]:off[B]], minlength=rows[0])
-        assert counts.max() >= 512  # the hot path was exercised
+        assert counts.max() >= 128  # the hot path was exercised
+
+
+def _hot_case(g, B, L, rows, counts):
+    """Indices of one table: row i occurs counts[i] times, the remaining
+    positions fall uniformly on the other rows; positions are shuffled."""
+    n = B * L
+    fixed = np.repeat(np.arange(len(counts)), counts)
+    rest = g.integers(len(counts), rows, n - len(fixed))
+    r = np.concatenate([fixed, rest])
+    g.shuffle(r)
+    return r
+
+
+@pytest.mark.parametrize("d", [4, 64, 100, 132, 256, 1024])
+def test_sparse_sgd_hot_segment_lengths(d):
+    """Segments at and around the hot-path threshold and its 64-occurrence
+    blocks (127, 128, 129, 191, 192, 193), one long segment of 20000
+    occurrences, and column slices of 64 with a ragged last slice."""
+    B, L, K = 4096, 8, 2
+    rows = [5000, 3000]
+    banner(f"sparse sgd hot segment lengths d={d}")
+    g = np.random.default_rng(100 + d)
+    counts = [[20000, 127, 128, 129, 191, 192, 193, 64, 65, 1], [1000, 256, 257, 300, 128, 5]]
+    idx = np.concatenate([_hot_case(g, B, L, rows[k], counts[k]) for k in range(K)]).astype(np.int64)
+    off = np.arange(K * B + 1, dtype=np.int64) * L
+    tabs = [g.standard_normal((rows[k], d)).astype(np.float32) for k in range(K)]
+    G = (g.standard_normal((B, (K + 1) * d)) * 0.01).astype(np.float32)
+    tabs_dev = [to_dev(t) for t in tabs]
+    _run_sgd(tabs_dev, rows, idx, off, B, d, G, d, 0.01)
+    ref = [t.copy() for t in tabs]
+    oracle.embbag_bwd_sgd(ref, idx, off, B, G, d, 0.01)
+    for k in range(K):
+        assert np.array_equal(bits(tabs_dev[k].cpu().numpy()), bits(ref[k])), k
+
+
+def test_sparse_sgd_many_hot_segments():
+    """About a thousand segments of ~200 occurrences each: far more hot
+    items than blocks, so every block runs many items through its ring."""
+    B, L, K, d = 2048, 100, 1, 128
+    rows = [1000]
+    banner("sparse sgd many hot segments")
+    g = np.random.default_rng(7)
+    idx = g.integers(0, rows[0], B * L).astype(np.int64)
+    off = np.arange(K * B + 1, dtype=np.int64) * L
+    tabs = [g.standard_normal((rows[0], d)).astype(np.float32)]
+    G = (g.standard_normal((B, d)) * 0.01).astype(np.float32)
+    tabs_dev = [to_dev(t) for t in tabs]
+    _run_sgd(tabs_dev, rows, idx, off, B, d, G, 0, 0.01)
+    ref = [t.copy() for t in tabs]
+    oracle.embbag_bwd_sgd(ref, idx, off, B, G, 0, 0.01)
+    assert np.array_equal(bits(tabs_dev[0].cpu().numpy()), bits(ref[0]))
 
 
 def test_sparse_sgd_empty_batch_is_noop():
