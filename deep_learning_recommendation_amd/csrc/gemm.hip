@@ -439,6 +439,48 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   }
 }
 
+// 64 x 64 tile, 16-byte loads and stores (rows of in and out 16-byte aligned).
+__global__ __launch_bounds__(256) void transpose_bf16_v8_kernel(const uint16_t* __restrict__ in, int64_t ldi,
+                                                                uint16_t* __restrict__ out, int64_t ldo, int R,
+                                                                int C) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int t = threadIdx.x, row = t >> 3, grp = t & 7;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = row + 32 * h, r = r0 + i, c = c0 + 8 * grp;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < R) {
+      if (c + 8 <= C) {
+        v = *reinterpret_cast<const uint4*>(in + (int64_t)r * ldi + c);
+      } else if (c < C) {
+        uint16_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = (c + q < C) ? in[(int64_t)r * ldi + c + q] : (uint16_t)0;
+        v = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                       e[6] | ((uint32_t)e[7] << 16));
+      }
+    }
+    *reinterpret_cast<uint4*>(&tile[i][8 * grp]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = row + 32 * h, c = c0 + i, r = r0 + 8 * grp;  // out row c, elements r .. r+7
+    if (c >= C || r >= R) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)tile[8 * grp + 2 * q][i] | ((uint32_t)tile[8 * grp + 2 * q + 1][i] << 16);
+    if (r + 8 <= R) {
+      *reinterpret_cast<uint4*>(out + (int64_t)c * ldo + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (r + q < R) out[(int64_t)c * ldo + r + q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void convert_bf16_kernel(const float* __restrict__ in, int64_t ldi,
                                                            uint16_t* __restrict__ out, int64_t ldo, int R, int C,
                                                            int Cpad) {
@@ -522,8 +564,11 @@ int gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const flo
 
 int transpose_bf16(const uint16_t* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int R, int C, hipStream_t s) {
   if (R <= 0 || C <= 0) return DLRM_OK;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)ceil_div(C, 64), (unsigned)ceil_div(R, 64)), dim3(256), 0,
-                     s, in, ld_in, out, ld_out, R, C);
+  const dim3 grid((unsigned)ceil_div(C, 64), (unsigned)ceil_div(R, 64));
+  if ((ld_in % 8) == 0 && (ld_out % 8) == 0 && aligned16(in) && aligned16(out))
+    hipLaunchKernelGGL(transpose_bf16_v8_kernel, grid, dim3(256), 0, s, in, ld_in, out, ld_out, R, C);
+  else
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, in, ld_in, out, ld_out, R, C);
   return launch_status();
 }
 

@@ -90,43 +90,75 @@ __device__ __forceinline__ bool positive<uint16_t>(const uint16_t* p) {
   return bf16_to_f32(*p) > 0.f;
 }
 
-// delta = g * 1[y > 0] (or g), stored as bf16 [B][ldd]
+// One pass over the upstream gradient of a layer: delta = g * 1[y > 0] (or
+// g) rounded to bf16 and stored row-major [B][ldd] (for the input gradient)
+// and transposed [N][ldt] (for the weight gradient, K = batch contiguous),
+// plus fp32 column sums of delta per 64-row chunk (for the bias gradient).
+// Block: 64 rows x 256 columns; wave w takes rows w, w+4, ..., lane l the
+// columns l, l+64, l+128, l+192, so every global access is coalesced.
+constexpr int kDRows = 64, kDCols = 256;
 template <typename YT>
-__global__ __launch_bounds__(256) void delta_kernel(const float* __restrict__ g, int64_t ldg,
-                                                    const YT* __restrict__ y, int64_t ldy, int relu,
-                                                    uint16_t* __restrict__ dlt, int64_t ldd, int B, int N) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)B * N) return;
-  const int b = (int)(t / N), o = (int)(t - (int64_t)b * N);
-  float v = g[(int64_t)b * ldg + o];
-  if (relu && !positive<YT>(y + (int64_t)b * ldy + o)) v = 0.f;
-  dlt[(int64_t)b * ldd + o] = f32_to_bf16(v);
-}
-
-// db partials: part[chunk][o] = sum over rows of the chunk of masked g (fp32, row order)
-template <typename YT>
-__global__ __launch_bounds__(256) void colsum_partial_kernel(const float* __restrict__ g, int64_t ldg,
-                                                             const YT* __restrict__ y, int64_t ldy, int relu,
-                                                             float* __restrict__ part, int B, int N, int rows_per) {
-  const int o = blockIdx.x * blockDim.x + threadIdx.x;
-  if (o >= N) return;
-  const int r0 = blockIdx.y * rows_per, r1 = min(B, r0 + rows_per);
-  float s = 0.f;
-  for (int b = r0; b < r1; ++b) {
-    float v = g[(int64_t)b * ldg + o];
-    if (relu && !positive<YT>(y + (int64_t)b * ldy + o)) v = 0.f;
-    s = s + v;
+__global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__ g, int64_t ldg,
+                                                       const YT* __restrict__ y, int64_t ldy, int relu,
+                                                       uint16_t* __restrict__ dlt, int64_t ldd,
+                                                       uint16_t* __restrict__ dltT, int64_t ldt,
+                                                       float* __restrict__ part, int B, int N) {
+  __shared__ uint16_t tile[kDRows][kDCols + 2];
+  __shared__ float red[4][kDCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * kDCols, r0 = blockIdx.y * kDRows;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = wave; i < kDRows; i += 4) {
+    const int r = r0 + i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int cl = lane + 64 * e, c = c0 + cl;
+      float v = 0.f;
+      if (r < B && c < N) {
+        v = g[(int64_t)r * ldg + c];
+        if (relu && !positive<YT>(y + (int64_t)r * ldy + c)) v = 0.f;
+      }
+      const uint16_t h = f32_to_bf16(v);
+      tile[i][cl] = h;
+      sum[e] = sum[e] + v;
+      if (r < B && c < N) dlt[(int64_t)r * ldd + c] = h;
+    }
   }
-  part[(int64_t)blockIdx.y * N + o] = s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[wave][lane + 64 * e] = sum[e];
+  __syncthreads();
+  {
+    const int cl = threadIdx.x, c = c0 + cl;
+    if (c < N) part[(int64_t)blockIdx.y * N + c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+    if (c < N) {
+      // column c of the tile is row c of delta^T: 64 rows, 8 per 16-byte store
+      uint16_t* dst = dltT + (int64_t)c * ldt + r0;
+#pragma unroll
+      for (int j = 0; j < kDRows / 8; ++j) {
+        if (r0 + 8 * j >= B) break;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = (uint32_t)tile[8 * j + 2 * q][cl] | ((uint32_t)tile[8 * j + 2 * q + 1][cl] << 16);
+        *reinterpret_cast<uint4*>(dst + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
 }
 
+// db[o] = sum of the per-chunk partials: 64 columns per block, wave w sums
+// chunks w, w+4, ... and the four wave sums are added in wave order.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int chunks, int N,
                                                            float* __restrict__ db) {
-  const int o = blockIdx.x * blockDim.x + threadIdx.x;
-  if (o >= N) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int o = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int c = 0; c < chunks; ++c) s = s + part[(int64_t)c * N + o];
-  db[o] = s;
+  if (o < N)
+    for (int c = wave; c < chunks; c += 4) s = s + part[(int64_t)c * N + o];
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && o < N) db[o] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 __global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__ logit, int64_t ld,
@@ -142,7 +174,6 @@ struct BwdLayout {
   int64_t ld_dlt, ld_B, splits_max;
 };
 
-constexpr int kColChunks = 32;
 constexpr int kMaxSplits = 16;
 
 bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
@@ -174,7 +205,7 @@ bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
   lay->xT = take(2 * (size_t)(wmax * lay->ld_B));
   lay->wT = take(2 * (size_t)(wmax * lay->ld_dlt));
   lay->part = take(4 * (size_t)(kMaxSplits * prod));
-  lay->dbp = take(4 * (size_t)(kColChunks * wfo));
+  lay->dbp = take(4 * (size_t)(ceil_div(B, kDRows) * wfo));
   lay->bytes = cv.bytes();
   return true;
 }
@@ -305,8 +336,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
   float* part = reinterpret_cast<float*>(w + bl.part);
   float* dbp = reinterpret_cast<float*>(w + bl.dbp);
   const int M = (int)B;
-  const int rows_per = (int)ceil_div(B, kColChunks);
-  const int chunks = (int)ceil_div(B, rows_per);
+  const int chunks = (int)ceil_div(B, kDRows);
 
   const float* g = dY;
   int64_t ldg = dy_ld;
@@ -314,28 +344,22 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
   for (int l = L - 1; l >= 0 && rc == DLRM_OK; --l) {
     const int fi = dims[l], fo = dims[l + 1];
     const bool relu = (l < L - 1) || last_act == DLRM_ACT_RELU;
-    const int64_t total = (int64_t)M * fo;
-    const dim3 g1((unsigned)ceil_div(total, 256)), b1(256);
-    const dim3 gc((unsigned)ceil_div(fo, 256), (unsigned)chunks);
-    // 1. delta (bf16) and db
+    const dim3 b1(256), gd((unsigned)ceil_div(fo, kDCols), (unsigned)chunks);
+    // 1. delta (bf16, both layouts) and the bias-gradient partials
     if (l == L - 1) {
       const float* y = relu ? out : g;  // mask source unused when relu == 0
       const int64_t ldy = relu ? out_ld : ldg;
-      hipLaunchKernelGGL((delta_kernel<float>), g1, b1, 0, stream, g, ldg, y, ldy, (int)relu, dlt, bl.ld_dlt, M, fo);
-      hipLaunchKernelGGL((colsum_partial_kernel<float>), gc, b1, 0, stream, g, ldg, y, ldy, (int)relu, dbp, M, fo,
-                         rows_per);
+      hipLaunchKernelGGL((delta_db_kernel<float>), gd, b1, 0, stream, g, ldg, y, ldy, (int)relu, dlt, bl.ld_dlt, dltT,
+                         bl.ld_B, dbp, M, fo);
     } else {
       const uint16_t* y = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l + 1]);
-      hipLaunchKernelGGL((delta_kernel<uint16_t>), g1, b1, 0, stream, g, ldg, y, fl.act_ld[l + 1], (int)relu, dlt,
-                         bl.ld_dlt, M, fo);
-      hipLaunchKernelGGL((colsum_partial_kernel<uint16_t>), gc, b1, 0, stream, g, ldg, y, fl.act_ld[l + 1], (int)relu,
-                         dbp, M, fo, rows_per);
+      hipLaunchKernelGGL((delta_db_kernel<uint16_t>), gd, b1, 0, stream, g, ldg, y, fl.act_ld[l + 1], (int)relu, dlt,
+                         bl.ld_dlt, dltT, bl.ld_B, dbp, M, fo);
     }
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 256)), b1, 0, stream, dbp, chunks, fo, db[l]);
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 64)), b1, 0, stream, dbp, chunks, fo, db[l]);
     if ((rc = launch_status()) != DLRM_OK) break;
     // 2. dW = delta^T x  (M = fo, N = fi, K = B), split over the batch
     const uint16_t* x = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l]);
-    if ((rc = transpose_bf16(dlt, bl.ld_dlt, dltT, bl.ld_B, M, fo, stream)) != DLRM_OK) break;
     if ((rc = transpose_bf16(x, fl.act_ld[l], xT, bl.ld_B, M, fi, stream)) != DLRM_OK) break;
     const int64_t tiles = ceil_div(fo, 128) * ceil_div(fi, 128);
     int splits = (int)ceil_div(512, tiles);

@@ -125,13 +125,12 @@ def test_device_bf16_rounding_matches_torch():
     assert bad.size == 0, f"{bad.size} mismatches (input, device, reference): {detail}"
 
 
-@pytest.mark.parametrize("which", ["bottom", "top"])
-def test_mlp_bf16_backward(which):
+@pytest.mark.parametrize("which,B", [("bottom", 520), ("top", 520), ("bottom", 517), ("top", 61)])
+def test_mlp_bf16_backward(which, B):
     import deep_learning_recommendation_amd as D
 
     w = W.get("train")
     dims = w.bottom if which == "bottom" else w.top
-    B = 520
     banner(f"mlp backward train/{which} B={B}")
     params = W.mlp_params(w, which)
     g = np.random.default_rng(21)
