@@ -9,9 +9,10 @@ full forward pass over one batch (bottom MLP, pooled lookups, interaction,
 top MLP with sigmoid); inputs are resident in HBM before timing starts.
 
 Prints one JSON line: samples/s, the roofline of the dominant kernel (the
-embedding gather: algorithmic bytes per launch over its average launch time,
-measured with HIP events on its stream), and the CPU oracle timed on a
-bounded sample of the same workload.
+fused pooled lookup + interaction kernel, or the gather alone in the
+gather microbench: algorithmic bytes per launch over its average launch
+time, measured with HIP events on its stream), and the CPU oracle timed on
+a bounded sample (about 10 s) of the same workload.
 """
 from __future__ import annotations
 
@@ -37,6 +38,29 @@ def gather_bytes(K, B, d, nnz):
     return 4 * d * nnz + 8 * nnz + 8 * (K * B + 1) + 4 * K * B * d
 
 
+def measured_traffic(key, kernel):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (profiles/hbm_traffic.json, scaled
+    by the counters' reading for a copy of known size), or None when there is
+    no record for this workload or the kernel's sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get("workloads", {}).get(key)
+    if not rec or rec.get("kernel") != kernel:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -47,6 +71,9 @@ def parse():
     p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=0, help="oracle sample size (0: automatic)")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB five times (a known-size kernel for "
+                        "calibrating hardware byte counters), then exit")
     return p.parse_args()
 
 
@@ -74,11 +101,13 @@ class Timer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
 
 
-def cpu_baseline(w, batches, bottom, top, n_samples):
+def cpu_baseline(w, batches, bottom, top, n_samples, min_seconds=10.0):
     """The oracle (as it stands) on the first n_samples of batch 0: forward
     for forward-type workloads, pooled lookups for the gather microbench,
-    the sparse update for the training step.  Row regeneration and input
-    slicing are excluded from the timed region."""
+    forward plus the sparse update for the training step.  The pass is
+    repeated until min_seconds of CPU work have run (a bounded sample);
+    row regeneration and input slicing are excluded from the timed region.
+    Returns (samples processed, seconds, threads, passes)."""
     import oracle
     from synth import workloads as W
 
@@ -89,18 +118,27 @@ def cpu_baseline(w, batches, bottom, top, n_samples):
     ws = w.scaled(B=S)
     tabs, local, _ = W.compact_rows(ws, sidx, soff)
     quant = w.mlp_dtype == "bf16"
+    G = batches[0][3].reshape(w.B, -1)[:S] if w.train else None
+
+    def one_pass():
+        E = oracle.embbag_fwd(tabs, local, soff, S)
+        if w.name != "embbag":
+            x0, _, _ = oracle.mlp_fwd(dense[:S], [p[0] for p in bottom], [p[2] for p in bottom], quant, True)
+            X = np.concatenate([x0, E], axis=1).reshape(S, w.n, w.d)
+            top_in = oracle.interact_fwd(X)
+            oracle.mlp_fwd(top_in, [p[0] for p in top], [p[2] for p in top], quant, False)
+            if w.train:
+                oracle.embbag_bwd_sgd(tabs, local, soff, S, G, w.d, w.lr)
+
+    passes = 0
     t0 = time.perf_counter()
-    E = oracle.embbag_fwd(tabs, local, soff, S)
-    if w.name not in ("embbag",):
-        x0, _, _ = oracle.mlp_fwd(dense[:S], [p[0] for p in bottom], [p[2] for p in bottom], quant, True)
-        X = np.concatenate([x0, E], axis=1).reshape(S, w.n, w.d)
-        top_in = oracle.interact_fwd(X)
-        oracle.mlp_fwd(top_in, [p[0] for p in top], [p[2] for p in top], quant, False)
-        if w.train:
-            G = batches[0][3].reshape(w.B, -1)[:S]
-            oracle.embbag_bwd_sgd(tabs, local, soff, S, G, w.d, w.lr)
-    dt = time.perf_counter() - t0
-    return S, dt, oracle.num_threads()
+    while True:
+        one_pass()
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return S * passes, dt, oracle.num_threads(), passes
 
 
 def main():
@@ -110,6 +148,16 @@ def main():
               "sharding design is documented but not built.", file=sys.stderr)
         sys.exit(1)
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}), flush=True)
+        return
 
     import deep_learning_recommendation_amd as D
     from deep_learning_recommendation_amd import pipeline as PL
@@ -217,26 +265,27 @@ def main():
     else:
         # fused pooled lookup + interaction: every looked-up row, indices and
         # offsets, the dense rows it reads and the packed top-MLP rows it writes
-        kname, key = "interact_mfma_kernel<fused>", "embbag_interact"
+        kname, key = "fused_kernel", "embbag_interact"
         esz = model.top_in.element_size()
         gbytes = (gather_bytes(w.K, w.B, w.d, nnz_mean) - 4 * w.K * w.B * w.d + 4 * w.B * w.d +
                   esz * w.B * model.top_ld)
         g_ms = breakdown[key]
     achieved = gbytes / (g_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name + ("_uniform" if args.uniform else ""), kname)
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(gbytes), "avg_launch_ms": round(g_ms, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
         ns = args.cpu_samples or {"forward": 16384, "embbag": 16384, "interaction": 512, "train": 1024,
                                   "tiny": 128}[w.name]
-        S, dt, thr = cpu_baseline(w, batches, bottom, top, ns)
+        S, dt, thr, passes = cpu_baseline(w, batches, bottom, top, ns)
         what = {"forward": "forward pass", "embbag": "pooled lookups", "interaction": "forward pass",
                 "train": "forward pass and sparse SGD update", "tiny": "forward pass"}[w.name]
         cpu = {"value": round(S / dt, 2), "unit": "samples/s", "cores": thr, "kind": "oracle",
-               "sample": f"{what} of the first {S} samples of batch 0 ({dt:.1f} s; tables regenerated for the "
-                         f"touched rows only, outside the timed region)"}
+               "sample": f"{what} of the first {S // passes} samples of batch 0, repeated {passes} times "
+                         f"({dt:.1f} s; tables regenerated for the touched rows only, outside the timed region)"}
 
     cfg = {"workload": w.name, "batch": w.B, "tables": w.K, "d": w.d, "rows_total": int(sum(w.rows)),
            "bag": f"{w.bag}:{w.bag_len}", "index": f"{w.index_dist}" + (f"({w.alpha})" if w.index_dist == "zipf" else ""),
