@@ -126,46 +126,99 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int r32 = lane & 31, half = lane >> 5;
-  if (nk > 0) issue(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    const char* st = smem + (kt & 1) * STAGE;
-    if (kt + 1 < nk) issue(kt + 1);
+  // zero columns [valid, BK) of every A and W row of a partial last k-tile
+  auto zero_tail = [&](int kt) {
     const int valid = kend - (kbeg + kt * BK);
-    if (valid < BK) {
-      // last k-tile is partial: zero columns [valid, BK) of every A and W row
-      char* wst = smem + (kt & 1) * STAGE;
-      for (int e = tid; e < (BM + BN) * 8; e += NWAVES * 64) {
-        const int row = e >> 3, c = e & 7;
-        if (c * 8 + 8 > valid) {
-          uint16_t* p = reinterpret_cast<uint16_t*>(wst + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
+    if (valid >= BK) return;
+    char* wst = smem + (kt & 1) * STAGE;
+    for (int e = tid; e < (BM + BN) * 8; e += NWAVES * 64) {
+      const int row = e >> 3, c = e & 7;
+      if (c * 8 + 8 > valid) {
+        uint16_t* p = reinterpret_cast<uint16_t*>(wst + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
 #pragma unroll
-          for (int x = 0; x < 8; ++x)
-            if (c * 8 + x >= valid) p[x] = 0;
-        }
+        for (int x = 0; x < 8; ++x)
+          if (c * 8 + x >= valid) p[x] = 0;
       }
-      __syncthreads();
+    }
+    __syncthreads();
+  };
+  // MFMA operands of k-step ks of the tile in stage st, double-buffered in
+  // registers: the reads of step ks+1 are in flight during the MFMAs of ks
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto load_frags = [&](const char* st, int ks, int buf) {
+    const int c = 2 * ks + half;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WM + i * 32 + r32;
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
     }
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = 2 * ks + half;
-      bf16x8 a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + r32;
-        a[i] = *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WN + j * 32 + r32;
-        b[j] = *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < TN; ++j) {
+      const int row = wn * WN + j * 32 + r32;
+      fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
     }
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  // Pipeline: tiles kt and kt+1 sit in the two LDS stages.  At the last
+  // k-step of tile kt every wave has read its operands of stage kt & 1, so
+  // after one barrier (which also sees tile kt+1 landed) the loads of tile
+  // kt+2 go into that stage and the first operands of tile kt+1 are read
+  // before the last MFMAs of tile kt run.
+  if (nk > 0) issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 0) {
+    if (nk > 1) wait_vmcnt<A_INS + B_INS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (nk == 1) zero_tail(0);
+    load_frags(smem, 0, 0);
+  }
+  // k-steps 0..2 of the tile in stage st: read the next step's operands,
+  // then this step's MFMAs (the scheduling barriers keep that order)
+  auto first_steps = [&](const char* st) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+      load_frags(st, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(ks & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // hand-over from tile kt to tile kt+1 (see above), then the last MFMAs of kt
+  auto turn = [&](int kt, bool load_next, bool zero_next) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage kt & 1 are done
+    wait_vmcnt<0>();                      // tile kt+1 has landed (this wave's share)
+    __builtin_amdgcn_s_barrier();
+    if (load_next) issue(kt + 2);
+    if (zero_next) zero_tail(kt + 1);
+    load_frags(smem + ((kt + 1) & 1) * STAGE, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the steady state has no branch, so every wait is an exact count; the
+  // epilogue's kernel arguments are read here so that no scalar load is
+  // pending in the loop (that would turn every LDS wait into lgkmcnt(0))
+  __asm__ volatile("" : "+s"(bias), "+s"(C), "+s"(ldc));
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) {
+    first_steps(smem + (kt & 1) * STAGE);
+    turn(kt, true, false);
+  }
+  if (kt + 1 < nk) {
+    first_steps(smem + (kt & 1) * STAGE);
+    turn(kt, false, true);
+    ++kt;
+  }
+  if (kt < nk) {
+    first_steps(smem + (kt & 1) * STAGE);
+    mfmas(1);
   }
 
   // D layout of a 32x32 block: lane l holds column l % 32 and rows

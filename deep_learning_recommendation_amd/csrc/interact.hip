@@ -49,6 +49,19 @@ struct RowSource {
 // blocks (J <= I) interleave as independent accumulation chains; a single
 // block is split into two partial chains.  Lanes whose (i, j) is not a kept
 // pair write to a dummy slot past the row, so the stores need no branches.
+// 16-byte load through a global-address-space pointer (a plain pointer that
+// came out of memory would otherwise turn into a flat load)
+__device__ __forceinline__ f4 ld4(const float* p) { return *(const __attribute__((address_space(1))) f4*)(p); }
+
+// Pointer select with both operands computed up front: keeps the compiler
+// from moving the address arithmetic into a branch (a branch before a load
+// makes the loads after it wait for every load before it).
+__device__ __forceinline__ const float* pick(bool c, const float* a, const float* b) {
+  uint64_t ua = reinterpret_cast<uint64_t>(a), ub = reinterpret_cast<uint64_t>(b);
+  __asm__ volatile("" : "+v"(ua), "+v"(ub));
+  return reinterpret_cast<const float*>(c ? ua : ub);
+}
+
 template <int NT, int DC, typename OutT>
 __device__ __forceinline__ void gram_row(f4 (&x)[NT][DC], int n, int d, int pad_end, OutT* ob, int lane) {
   const int r16 = lane & 15, g = lane >> 4;
@@ -161,21 +174,24 @@ __global__ __launch_bounds__(256) void interact_mfma_kernel(RowSource src, int64
   char* rowb = smem + wave * row_bytes;
   const int r16 = lane & 15, g = lane >> 4;
   const float* __restrict__ xb = src.X + b * src.x_ld;
+  // every load is issued (rows past n re-read row 0, columns past d the last
+  // four) and masked afterwards, so that the loads go out back to back
   f4 x[NT][DC];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = t * 16 + r16;
+    const float* rp = xb + (int64_t)(row < n ? row : 0) * d;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const int kk = c * 16 + 4 * g;
-      if (row < n && kk < d) {
-        const float4 v = *reinterpret_cast<const float4*>(xb + (int64_t)row * d + kk);
-        x[t][c] = f4{v.x, v.y, v.z, v.w};
-      } else {
-        x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
-      }
+      x[t][c] = ld4(rp + (kk < d ? kk : d - 4));
     }
   }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      if (!(t * 16 + r16 < n && c * 16 + 4 * g < d)) x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
   gram_row<NT, DC, OutT>(x, n, d, pad_end, reinterpret_cast<OutT*>(rowb), lane);
   row_out(rowb, reinterpret_cast<char*>(out + b * out_ld), pad_end * (int)sizeof(OutT), wide, lane);
 }
@@ -186,7 +202,8 @@ __global__ __launch_bounds__(256) void interact_mfma_kernel(RowSource src, int64
 // first, then all first indices, then all rows, so each dependent step has
 // every load of the sample in flight.
 template <int NT, int DC, typename OutT>
-__global__ __launch_bounds__(256) void fused_kernel(RowSource src, int64_t B, int n, int d, OutT* __restrict__ out,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT * (4 * DC + 12) <= 112 ? 4 : 2))) void fused_kernel(
+    RowSource src, int64_t B, int n, int d, OutT* __restrict__ out,
                                                     int64_t out_ld, int pad_end, int row_bytes, int wide) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -198,67 +215,78 @@ __global__ __launch_bounds__(256) void fused_kernel(RowSource src, int64_t B, in
   const int64_t* __restrict__ idx = src.idx;
   const float* __restrict__ x0 = src.X + b * src.x_ld;
 
+  // Every load below is issued unconditionally from a valid address (lanes
+  // with nothing to load read the offsets array or the dense row) and masked
+  // afterwards: with no branch between them the loads of one level go out
+  // back to back instead of one memory latency each.
   int64_t pb[NT];
   int len[NT];
   const float* tb[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = t * 16 + r16;
-    len[t] = 0;
-    pb[t] = 0;
-    tb[t] = nullptr;
-    if (row >= 1 && row < n) {
-      const int64_t bag = (int64_t)(row - 1) * B + b;
-      pb[t] = off[bag];
-      len[t] = (int)(off[bag + 1] - pb[t]);
-      tb[t] = src.tables[row - 1];
-    }
+    const bool bagrow = row >= 1 && row < n;
+    const int64_t bag = bagrow ? (int64_t)(row - 1) * B + b : 0;
+    const int64_t o0 = off[bag], o1 = off[bag + 1];
+    pb[t] = o0;
+    len[t] = bagrow ? (int)(o1 - o0) : 0;
+    tb[t] = src.tables[bagrow ? row - 1 : 0];
   }
   int64_t r0[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) r0[t] = len[t] > 0 ? idx[pb[t]] : 0;
+  for (int t = 0; t < NT; ++t) r0[t] = *(len[t] > 0 ? idx + pb[t] : off);
 
+  // first row of every bag (0 + row, the sum's start) and the dense row
   f4 x[NT][DC];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = t * 16 + r16;
-    const float* rp = tb[t] + r0[t] * (int64_t)d;
+    const float* rp = pick(row != 0 && len[t] > 0, tb[t] + r0[t] * (int64_t)d, x0);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const int kk = c * 16 + 4 * g;
-      x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
-      if (kk < d) {
-        if (row == 0) {
-          const float4 v = *reinterpret_cast<const float4*>(x0 + kk);
-          x[t][c] = f4{v.x, v.y, v.z, v.w};
-        } else if (len[t] > 0) {
-          const float4 v = *reinterpret_cast<const float4*>(rp + kk);
-          x[t][c][0] = 0.f + v.x;
-          x[t][c][1] = 0.f + v.y;
-          x[t][c][2] = 0.f + v.z;
-          x[t][c][3] = 0.f + v.w;
-        }
+      x[t][c] = ld4(rp + (kk < d ? kk : d - 4));
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = t * 16 + r16;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const bool live = c * 16 + 4 * g < d;
+      if (row == 0) {
+        if (!live) x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
+      } else if (len[t] > 0 && live) {
+        x[t][c] = f4{0.f + x[t][c][0], 0.f + x[t][c][1], 0.f + x[t][c][2], 0.f + x[t][c][3]};
+      } else {
+        x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
+  // remaining bag positions, in order; the index of position q+1 is loaded
+  // while the rows of position q are in flight
   int maxlen = 0;
 #pragma unroll
   for (int t = 0; t < NT; ++t) maxlen = len[t] > maxlen ? len[t] : maxlen;
-  for (int q = 1; q < maxlen; ++q) {
+  if (maxlen > 1) {
+    int64_t rq[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (q < len[t]) {
-        const float* rp = tb[t] + idx[pb[t] + q] * (int64_t)d;
+    for (int t = 0; t < NT; ++t) rq[t] = *(1 < len[t] ? idx + pb[t] + 1 : off);
+    for (int q = 1; q < maxlen; ++q) {
+      const float* rp[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) rp[t] = pick(q < len[t], tb[t] + rq[t] * (int64_t)d, x0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) rq[t] = *(q + 1 < len[t] ? idx + pb[t] + q + 1 : off);
+      // x is never -0 here (every sum starts from +0), so adding +0 for a
+      // finished bag leaves it bit for bit unchanged
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
           const int kk = c * 16 + 4 * g;
-          if (kk < d) {
-            const float4 v = *reinterpret_cast<const float4*>(rp + kk);
-            x[t][c][0] = x[t][c][0] + v.x;
-            x[t][c][1] = x[t][c][1] + v.y;
-            x[t][c][2] = x[t][c][2] + v.z;
-            x[t][c][3] = x[t][c][3] + v.w;
-          }
+          const f4 v = ld4(rp[t] + (kk < d ? kk : d - 4));
+          x[t][c] = x[t][c] + ((q < len[t] && kk < d) ? v : f4{0.f, 0.f, 0.f, 0.f});
         }
       }
     }
