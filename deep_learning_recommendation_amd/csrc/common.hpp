@@ -57,6 +57,19 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
 // Keeps the compiler from moving memory accesses across this point.
 __device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
 
+// Compute units of the current device (queried once per device).
+inline int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 1;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
 // Scratch carving: 256-byte aligned sub-buffers of a caller workspace.
 struct Carver {
   char* base;

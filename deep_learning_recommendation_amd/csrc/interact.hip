@@ -201,98 +201,138 @@ __global__ __launch_bounds__(256) void interact_mfma_kernel(RowSource src, int64
 // exactly as the standalone lookup.  All bag offsets of the sample are read
 // first, then all first indices, then all rows, so each dependent step has
 // every load of the sample in flight.
+// Register budget per lane: the rows (4 per column chunk and tile), bag
+// metadata, and for the persistent form the next sample's metadata.  Small
+// shapes run persistent (metadata of sample b + stride loaded during sample
+// b) at 4 waves per SIMD; larger ones one sample per wave, where the extra
+// metadata would cost a wave of occupancy (measured slower).
+template <int NT, int DC>
+constexpr bool fused_persistent() { return NT <= 2 && NT * DC <= 8; }
+template <int NT, int DC>
+constexpr int fused_waves() {
+  return fused_persistent<NT, DC>() ? 4 : (NT * (4 * DC + 12) < 112 ? 4 : 2);
+}
+
 template <int NT, int DC, typename OutT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT * (4 * DC + 12) <= 112 ? 4 : 2))) void fused_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves<NT, DC>()))) void fused_kernel(
     RowSource src, int64_t B, int n, int d, OutT* __restrict__ out,
                                                     int64_t out_ld, int pad_end, int row_bytes, int wide) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 6);
+  int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
   if (b >= B) return;  // whole wave
   char* rowb = smem + wave * row_bytes;
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t* __restrict__ off = src.off;
   const int64_t* __restrict__ idx = src.idx;
-  const float* __restrict__ x0 = src.X + b * src.x_ld;
 
   // Every load below is issued unconditionally from a valid address (lanes
   // with nothing to load read the offsets array or the dense row) and masked
   // afterwards: with no branch between them the loads of one level go out
-  // back to back instead of one memory latency each.
-  int64_t pb[NT];
-  int len[NT];
+  // back to back instead of one memory latency each.  The wave walks the
+  // samples b, b + stride, ...; the bag offsets of the next sample are loaded
+  // with this sample's rows and its first indices during this sample's Gram
+  // matrix, so only the row loads wait on memory.
   const float* tb[NT];
+  bool bagrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = t * 16 + r16;
-    const bool bagrow = row >= 1 && row < n;
-    const int64_t bag = bagrow ? (int64_t)(row - 1) * B + b : 0;
-    const int64_t o0 = off[bag], o1 = off[bag + 1];
-    pb[t] = o0;
-    len[t] = bagrow ? (int)(o1 - o0) : 0;
-    tb[t] = src.tables[bagrow ? row - 1 : 0];
+    bagrow[t] = row >= 1 && row < n;
+    tb[t] = src.tables[bagrow[t] ? row - 1 : 0];
   }
-  int64_t r0[NT];
+  auto load_offsets = [&](int64_t s, int64_t (&o0)[NT], int64_t (&o1)[NT]) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) r0[t] = *(len[t] > 0 ? idx + pb[t] : off);
-
-  // first row of every bag (0 + row, the sum's start) and the dense row
-  f4 x[NT][DC];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int row = t * 16 + r16;
-    const float* rp = pick(row != 0 && len[t] > 0, tb[t] + r0[t] * (int64_t)d, x0);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const int kk = c * 16 + 4 * g;
-      x[t][c] = ld4(rp + (kk < d ? kk : d - 4));
+    for (int t = 0; t < NT; ++t) {
+      const int64_t bag = (bagrow[t] && s < B) ? (int64_t)(t * 16 + r16 - 1) * B + s : 0;
+      o0[t] = off[bag];
+      o1[t] = off[bag + 1];
     }
+  };
+  int64_t pb[NT], r0[NT];
+  int len[NT];
+  auto take_meta = [&](int64_t s, const int64_t (&o0)[NT], const int64_t (&o1)[NT], int64_t (&p)[NT],
+                       int (&l)[NT], int64_t (&r)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      p[t] = o0[t];
+      l[t] = (bagrow[t] && s < B) ? (int)(o1[t] - o0[t]) : 0;
+      r[t] = *(l[t] > 0 ? idx + p[t] : off);
+    }
+  };
+  {
+    int64_t o0[NT], o1[NT];
+    load_offsets(b, o0, o1);
+    take_meta(b, o0, o1, pb, len, r0);
   }
+  for (;;) {
+    const float* __restrict__ x0 = src.X + b * src.x_ld;
+    // first row of every bag (0 + row, the sum's start) and the dense row
+    f4 x[NT][DC];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int row = t * 16 + r16;
+    for (int t = 0; t < NT; ++t) {
+      const int row = t * 16 + r16;
+      const float* rp = pick(row != 0 && len[t] > 0, tb[t] + r0[t] * (int64_t)d, x0);
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const bool live = c * 16 + 4 * g < d;
-      if (row == 0) {
-        if (!live) x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
-      } else if (len[t] > 0 && live) {
-        x[t][c] = f4{0.f + x[t][c][0], 0.f + x[t][c][1], 0.f + x[t][c][2], 0.f + x[t][c][3]};
-      } else {
-        x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < DC; ++c) {
+        const int kk = c * 16 + 4 * g;
+        x[t][c] = ld4(rp + (kk < d ? kk : d - 4));
       }
     }
-  }
-  // remaining bag positions, in order; the index of position q+1 is loaded
-  // while the rows of position q are in flight
-  int maxlen = 0;
+    constexpr bool kPersist = fused_persistent<NT, DC>();
+    const int64_t bn = kPersist ? b + stride : B;
+    int64_t o0n[NT], o1n[NT];
+    if constexpr (kPersist) load_offsets(bn, o0n, o1n);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) maxlen = len[t] > maxlen ? len[t] : maxlen;
-  if (maxlen > 1) {
-    int64_t rq[NT];
+    for (int t = 0; t < NT; ++t) {
+      const int row = t * 16 + r16;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) rq[t] = *(1 < len[t] ? idx + pb[t] + 1 : off);
-    for (int q = 1; q < maxlen; ++q) {
-      const float* rp[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) rp[t] = pick(q < len[t], tb[t] + rq[t] * (int64_t)d, x0);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) rq[t] = *(q + 1 < len[t] ? idx + pb[t] + q + 1 : off);
-      // x is never -0 here (every sum starts from +0), so adding +0 for a
-      // finished bag leaves it bit for bit unchanged
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const int kk = c * 16 + 4 * g;
-          const f4 v = ld4(rp[t] + (kk < d ? kk : d - 4));
-          x[t][c] = x[t][c] + ((q < len[t] && kk < d) ? v : f4{0.f, 0.f, 0.f, 0.f});
+      for (int c = 0; c < DC; ++c) {
+        const bool live = c * 16 + 4 * g < d;
+        if (row == 0) {
+          if (!live) x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
+        } else if (len[t] > 0 && live) {
+          x[t][c] = f4{0.f + x[t][c][0], 0.f + x[t][c][1], 0.f + x[t][c][2], 0.f + x[t][c][3]};
+        } else {
+          x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
         }
       }
     }
+    // remaining bag positions, in order; the index of position q+1 is loaded
+    // while the rows of position q are in flight
+    int maxlen = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) maxlen = len[t] > maxlen ? len[t] : maxlen;
+    if (maxlen > 1) {
+      int64_t rq[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) rq[t] = *(1 < len[t] ? idx + pb[t] + 1 : off);
+      for (int q = 1; q < maxlen; ++q) {
+        const float* rp[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) rp[t] = pick(q < len[t], tb[t] + rq[t] * (int64_t)d, x0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) rq[t] = *(q + 1 < len[t] ? idx + pb[t] + q + 1 : off);
+        // x is never -0 here (every sum starts from +0), so adding +0 for a
+        // finished bag leaves it bit for bit unchanged
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int c = 0; c < DC; ++c) {
+            const int kk = c * 16 + 4 * g;
+            const f4 v = ld4(rp[t] + (kk < d ? kk : d - 4));
+            x[t][c] = x[t][c] + ((q < len[t] && kk < d) ? v : f4{0.f, 0.f, 0.f, 0.f});
+          }
+        }
+      }
+    }
+    if constexpr (kPersist) take_meta(bn, o0n, o1n, pb, len, r0);  // next sample's first indices, in flight during the Gram matrix
+    gram_row<NT, DC, OutT>(x, n, d, pad_end, reinterpret_cast<OutT*>(rowb), lane);
+    row_out(rowb, reinterpret_cast<char*>(out + b * out_ld), pad_end * (int)sizeof(OutT), wide, lane);
+    if (bn >= B) break;
+    b = bn;
   }
-  gram_row<NT, DC, OutT>(x, n, d, pad_end, reinterpret_cast<OutT*>(rowb), lane);
-  row_out(rowb, reinterpret_cast<char*>(out + b * out_ld), pad_end * (int)sizeof(OutT), wide, lane);
 }
 
 // Any shape: one thread per (sample, output column).  fp32 FMA chain.
@@ -330,9 +370,18 @@ void launch_mfma(const RowSource& src, int64_t B, int n, int d, OutT* out, int64
   int spb = 65536 / row_bytes;  // samples (waves) per block within 64 KB of LDS
   spb = spb < 1 ? 1 : (spb > 4 ? 4 : spb);
   const int wide = ((out_ld * (int64_t)sizeof(OutT)) % 16) == 0;
-  if (FUSED)
-    hipLaunchKernelGGL((fused_kernel<NT, DC, OutT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb),
-                       (size_t)spb * row_bytes, s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
+  if (FUSED) {
+    // persistent waves: as many blocks as stay resident, each wave walking
+    // the samples with the grid's stride
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fused_kernel<NT, DC, OutT>),
+                                                     64 * spb, (size_t)spb * row_bytes) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    int64_t grid = ceil_div(B, spb);
+    if (fused_persistent<NT, DC>() && grid > (int64_t)per_cu * device_cu_count()) grid = (int64_t)per_cu * device_cu_count();
+    hipLaunchKernelGGL((fused_kernel<NT, DC, OutT>), dim3((unsigned)grid), dim3(64 * spb), (size_t)spb * row_bytes,
+                       s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
+  }
   else
     hipLaunchKernelGGL((interact_mfma_kernel<NT, DC, OutT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb),
                        (size_t)spb * row_bytes, s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
