@@ -54,6 +54,17 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
 }
 
+// The same 16-byte direct-to-LDS load, issued through inline assembly so the
+// compiler's wait-count model does not see an LDS write: with the builtin it
+// turns every later LDS-read wait into lgkmcnt(0), exposing each operand read
+// of a GEMM k-step.  The asm has no register outputs; completion is still
+// vmcnt, which the caller waits for explicitly (followed by a barrier and a
+// compiler fence) before any wave reads the destination.
+__device__ __forceinline__ void lds_dma16_opaque(const void* src, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(a) : "memory");
+}
+
 // Keeps the compiler from moving memory accesses across this point.
 __device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
 

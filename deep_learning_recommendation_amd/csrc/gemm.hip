@@ -56,21 +56,28 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
 // (their results are never stored); columns past K in the last k-tile are
 // zeroed in LDS before use.  The bf16 epilogue goes through LDS so that every
 // global store is a full 16-byte chunk.
-template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL>
+template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, OutT* __restrict__ C, int64_t ldc, int M, int N, int K, int relu, int tiles_n,
     int k_per_split) {
-  constexpr int BK = 64;
+  static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
   constexpr int RB = BK * 2;                      // bytes per tile row
+  constexpr int CPR = BK / 8;                     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                   // rows per 1 KB load instruction
+  constexpr int KS = BK / 16;                     // MFMA k-steps per tile
   constexpr int WAVES_N = BN / WN, NWAVES = (BM / WM) * WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_INS = BM * RB / 1024 / NWAVES, B_INS = BN * RB / 1024 / NWAVES;
+  constexpr int A_INS = BM * RB / 1024 / NWAVES, B_INS = BN * RB / 1024 / NWAVES, INS = A_INS + B_INS;
   constexpr int STAGE = (BM + BN) * RB;
   constexpr int EPI_LS = WN * 2 + 16;             // epilogue LDS row stride (bytes)
   constexpr int EPI = BM * (BN / WN) * EPI_LS;
-  constexpr int SMEM = (2 * STAGE > EPI) ? 2 * STAGE : EPI;
+  constexpr int SMEM = (S * STAGE > EPI) ? S * STAGE : EPI;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  // chunk swizzle: the 16 lanes that one LDS cycle serves read 16 rows of
+  // one logical chunk; XOR-ing the chunk with row bits above the rows that
+  // share a bank group spreads them over all 64 banks
+  auto swz = [](int row) { return CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave - (wave / WAVES_N) * WAVES_N;
@@ -84,37 +91,32 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int kpad = (kend + 7) & ~7;
 
-  // this lane's DMA rows: instruction j of wave w fills rows (w*INS + j)*8 + lane/8
-  const int lrow = lane >> 3, lpc = lane & 7;
+  // this lane's DMA rows: instruction j of wave w fills rows (w*INS + j)*RPI + lane/CPR
+  const int lrow = lane / CPR, lpc = lane % CPR;
   const uint16_t* a_row[A_INS];
   const uint16_t* b_row[B_INS];
   int a_c[A_INS], b_c[B_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
-    const int row = (wave * A_INS + j) * 8 + lrow;
+    const int row = (wave * A_INS + j) * RPI + lrow;
     a_row[j] = A + (int64_t)min(m0 + row, M - 1) * lda;
-    a_c[j] = (lpc ^ ((row >> 1) & 7)) * 8;
+    a_c[j] = (lpc ^ swz(row)) * 8;
   }
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
-    const int row = (wave * B_INS + j) * 8 + lrow;
+    const int row = (wave * B_INS + j) * RPI + lrow;
     b_row[j] = W + (int64_t)min(n0 + row, N - 1) * ldw;
-    b_c[j] = (lpc ^ ((row >> 1) & 7)) * 8;
+    b_c[j] = (lpc ^ swz(row)) * 8;
   }
   auto issue = [&](int kt) {
-    char* st = smem + (kt & 1) * STAGE;
+    char* st = smem + (kt % S) * STAGE;
     const int k0 = kbeg + kt * BK;
 #pragma unroll
     for (int j = 0; j < A_INS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(a_row[j] + min(k0 + a_c[j], kpad - 8)),
-                                       (void __attribute__((address_space(3)))*)(st + (wave * A_INS + j) * 1024), 16,
-                                       0, 0);
+      lds_dma16_opaque(a_row[j] + min(k0 + a_c[j], kpad - 8), st + (wave * A_INS + j) * 1024);
 #pragma unroll
     for (int j = 0; j < B_INS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(b_row[j] + min(k0 + b_c[j], kpad - 8)),
-                                       (void __attribute__((address_space(3)))*)(st + BM * RB +
-                                                                                 (wave * B_INS + j) * 1024),
-                                       16, 0, 0);
+      lds_dma16_opaque(b_row[j] + min(k0 + b_c[j], kpad - 8), st + BM * RB + (wave * B_INS + j) * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -130,11 +132,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
   auto zero_tail = [&](int kt) {
     const int valid = kend - (kbeg + kt * BK);
     if (valid >= BK) return;
-    char* wst = smem + (kt & 1) * STAGE;
-    for (int e = tid; e < (BM + BN) * 8; e += NWAVES * 64) {
-      const int row = e >> 3, c = e & 7;
+    char* wst = smem + (kt % S) * STAGE;
+    for (int e = tid; e < (BM + BN) * CPR; e += NWAVES * 64) {
+      const int row = e / CPR, c = e % CPR;
       if (c * 8 + 8 > valid) {
-        uint16_t* p = reinterpret_cast<uint16_t*>(wst + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
+        uint16_t* p = reinterpret_cast<uint16_t*>(wst + row * RB + ((c ^ swz(row)) * 16));
 #pragma unroll
         for (int x = 0; x < 8; ++x)
           if (c * 8 + x >= valid) p[x] = 0;
@@ -150,12 +152,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = wm * WM + i * 32 + r32;
-      fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ swz(row)) * 16));
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int row = wn * WN + j * 32 + r32;
-      fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ ((row >> 1) & 7)) * 16));
+      fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ swz(row)) * 16));
     }
   };
   auto mfmas = [&](int buf) {
@@ -165,41 +167,55 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
   };
-  // Pipeline: tiles kt and kt+1 sit in the two LDS stages.  At the last
-  // k-step of tile kt every wave has read its operands of stage kt & 1, so
-  // after one barrier (which also sees tile kt+1 landed) the loads of tile
-  // kt+2 go into that stage and the first operands of tile kt+1 are read
-  // before the last MFMAs of tile kt run.
-  if (nk > 0) issue(0);
-  if (nk > 1) issue(1);
+  // Pipeline: tiles kt .. kt+S-1 sit in the S LDS stages (tile t in stage
+  // t % S).  At the last k-step of tile kt every wave has read its operands
+  // of stage kt % S, so after one barrier (which also sees tile kt+1 landed)
+  // the loads of tile kt+S go into that stage and the first operands of tile
+  // kt+1 are read before the last MFMAs of tile kt run.
+  auto wait_tiles = [&](int younger) {  // at most `younger` tiles' loads still in flight
+    if constexpr (S >= 4) {
+      if (younger >= 3) { wait_vmcnt<3 * INS>(); return; }
+    }
+    if constexpr (S >= 3) {
+      if (younger >= 2) { wait_vmcnt<2 * INS>(); return; }
+    }
+    if (younger >= 1) { wait_vmcnt<INS>(); return; }
+    wait_vmcnt<0>();
+  };
+  const int pre = nk < S ? nk : S;
+#pragma unroll
+  for (int t = 0; t < S; ++t)
+    if (t < nk) issue(t);
   if (nk > 0) {
-    if (nk > 1) wait_vmcnt<A_INS + B_INS>();
-    else wait_vmcnt<0>();
+    wait_tiles(pre - 1);
     __builtin_amdgcn_s_barrier();
+    compiler_fence();
     if (nk == 1) zero_tail(0);
     load_frags(smem, 0, 0);
   }
-  // k-steps 0..2 of the tile in stage st: read the next step's operands,
+  // k-steps 0..KS-2 of the tile in stage st: read the next step's operands,
   // then this step's MFMAs (the scheduling barriers keep that order)
   auto first_steps = [&](const char* st) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+    for (int ks = 0; ks < KS - 1; ++ks) {
       load_frags(st, ks + 1, (ks + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(ks & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  constexpr int LAST = (KS - 1) & 1;  // register buffer of the last k-step
   // hand-over from tile kt to tile kt+1 (see above), then the last MFMAs of kt
-  auto turn = [&](int kt, bool load_next, bool zero_next) {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage kt & 1 are done
-    wait_vmcnt<0>();                      // tile kt+1 has landed (this wave's share)
+  auto turn = [&](int kt, bool load_next, bool zero_next, int younger) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage kt % S are done
+    wait_tiles(younger);                  // tile kt+1 has landed (this wave's share)
     __builtin_amdgcn_s_barrier();
-    if (load_next) issue(kt + 2);
+    compiler_fence();
+    if (load_next) issue(kt + S);
     if (zero_next) zero_tail(kt + 1);
-    load_frags(smem + ((kt + 1) & 1) * STAGE, 0, 0);
+    load_frags(smem + ((kt + 1) % S) * STAGE, 0, (LAST + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
+    mfmas(LAST);
     __builtin_amdgcn_sched_barrier(0);
   };
   // the steady state has no branch, so every wait is an exact count; the
@@ -207,18 +223,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
   // pending in the loop (that would turn every LDS wait into lgkmcnt(0))
   __asm__ volatile("" : "+s"(bias), "+s"(C), "+s"(ldc));
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) {
-    first_steps(smem + (kt & 1) * STAGE);
-    turn(kt, true, false);
+  for (; kt + S < nk; ++kt) {
+    first_steps(smem + (kt % S) * STAGE);
+    turn(kt, true, false, S - 2);
   }
-  if (kt + 1 < nk) {
-    first_steps(smem + (kt & 1) * STAGE);
-    turn(kt, false, true);
-    ++kt;
+#pragma unroll
+  for (int r = 0; r < S - 1; ++r) {  // at most S - 1 tiles remain after the steady state
+    if (kt + 1 < nk) {
+      first_steps(smem + (kt % S) * STAGE);
+      const int younger = nk - 2 - kt;
+      turn(kt, false, kt + 2 == nk, younger < S - 2 ? younger : S - 2);
+      ++kt;
+    }
   }
   if (kt < nk) {
-    first_steps(smem + (kt & 1) * STAGE);
-    mfmas(1);
+    first_steps(smem + (kt % S) * STAGE);
+    mfmas(LAST);
   }
 
   // D layout of a 32x32 block: lane l holds column l % 32 and rows
@@ -278,12 +298,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
   }
 }
 
-template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL>
+template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2>
 void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
                  int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL>), dim3(tm * tn, 1, splits),
+  hipLaunchKernelGGL((gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S>), dim3(tm * tn, 1, splits),
                      dim3(threads), 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu, tn, k_per_split);
 }
 
@@ -296,8 +316,9 @@ void pick_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, c
   // fp32 stores with bias would exceed 256 registers in the 256 x 256 tile
   constexpr bool kWide = sizeof(OutT) == 2 || PARTIAL;
   if (kWide && t256x256 >= 256)
-    launch_fast<256, 256, 128, 64, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split,
-                                                  s);
+    // 32-wide k-tiles in four stages: three tiles of loads in flight
+    launch_fast<256, 256, 128, 64, OutT, PARTIAL, 32, 4>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits,
+                                                         k_per_split, s);
   else if (t256x128 >= 256)
     launch_fast<256, 128, 64, 64, OutT, PARTIAL>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits, k_per_split,
                                                  s);
