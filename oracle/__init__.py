@@ -50,6 +50,7 @@ def _bind(L):
     L.oracle_bf16_round.argtypes = [_P, _P, _I64]
     L.oracle_embbag_fwd.argtypes = [_P, _I32, _I32, _P, _P, _I64, _P, _I64, _I64]
     L.oracle_interact_fwd.argtypes = [_P, _I64, _I32, _I32, _I64, _P, _I64]
+    L.oracle_interact_bwd.argtypes = [_P, _I64, _I32, _I32, _I64, _P, _I64, _P, _I64]
     L.oracle_mlp_fwd.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P]
     L.oracle_mlp_bwd.argtypes = [_I64, _I32, _P, _P, _P, _I32, _P, _P, _P, _P]
     L.oracle_embbag_bwd_sgd.argtypes = [_P, _P, _I32, _I32, _P, _P, _I64, _P, _I64, _I64, ctypes.c_float]
@@ -112,6 +113,19 @@ def interact_fwd(X, L=None) -> np.ndarray:
     out = np.zeros((B, d + n * (n - 1) // 2), dtype=np.float32)
     L.oracle_interact_fwd(_ptr(X), B, n, d, n * d, _ptr(out), out.shape[1])
     return out
+
+
+def interact_bwd(X, g, L=None) -> np.ndarray:
+    """X [B][n][d], g [B][d + n(n-1)/2] (gradient of the top-MLP input row)
+    -> dX [B][n][d]."""
+    L = L or lib()
+    X = _c(X, np.float32)
+    B, n, d = X.shape
+    g = _c(g, np.float32).reshape(B, -1)
+    assert g.shape[1] >= d + n * (n - 1) // 2
+    dX = np.zeros((B, n, d), dtype=np.float32)
+    L.oracle_interact_bwd(_ptr(X), B, n, d, n * d, _ptr(g), g.shape[1], _ptr(dX), n * d)
+    return dX
 
 
 def mlp_fwd(x, Ws, bs, quant_bf16: bool, last_relu: bool, save_acts: bool = False, L=None):

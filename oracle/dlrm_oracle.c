@@ -126,6 +126,39 @@ void oracle_interact_fwd(const float* X, int64_t B, int32_t n, int32_t d, int64_
 }
 
 /*
+ * Interaction, backward (the training pass through the interaction above).
+ * [SU] Key equations, Interaction and Output define the forward map
+ * X -> y = [X_0, Z]; [EXPL] Key Method Details, Loss: the model is trained
+ * on binary cross-entropy, so the top MLP hands back g = dL/dy.  By the
+ * chain rule, each kept pair value Z_ij = <X_i, X_j> (j < i) sends
+ * g_ij * X_j to row i and g_ij * X_i to row j, and the dense copy sends g_c
+ * to row 0:
+ *   dX[i][c] = [i == 0] g[c] + sum over j != i of g_pair(i, j) * X[j][c]
+ * with g_pair(i, j) = g[d + a(a-1)/2 + b], a = max(i, j), b = min(i, j).
+ * Every term is an exact product accumulated in fp64, rounded once to fp32.
+ */
+void oracle_interact_bwd(const float* X, int64_t B, int32_t n, int32_t d, int64_t x_ld, const float* g, int64_t g_ld,
+                         float* dX, int64_t dx_ld) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < B; ++b) {
+    const float* xr = X + b * x_ld;
+    const float* gb = g + b * g_ld;
+    float* o = dX + b * dx_ld;
+    for (int32_t i = 0; i < n; ++i) {
+      for (int32_t c = 0; c < d; ++c) {
+        double s = (i == 0) ? (double)gb[c] : 0.0;
+        for (int32_t j = 0; j < n; ++j) {
+          if (j == i) continue;
+          const int32_t a = i > j ? i : j, e = i > j ? j : i;
+          s += (double)gb[d + (int64_t)a * (a - 1) / 2 + e] * (double)xr[(int64_t)j * d + c];
+        }
+        o[(int64_t)i * d + c] = (float)s;
+      }
+    }
+  }
+}
+
+/*
  * Multilayer perceptron, forward.
  * [EXPL] Key Method Details, "Bottom MLP": fully connected layers with ReLU
  * whose output has dimension d.  "Top MLP": fully connected layers with ReLU

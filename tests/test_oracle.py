@@ -211,6 +211,67 @@ def test_interact_orthogonal_and_identical_rows(orc):
     assert np.allclose(z, float((v.astype(np.float64) ** 2).sum()), rtol=1e-6) and np.all(z == z[0])
 
 
+def test_interact_bwd_against_autograd(orc):
+    # the interaction's forward map built from torch ops in fp64, differentiated
+    # by autograd: dL/dX for L = sum(g * [X_0, tril(X X^T)])
+    rng = np.random.default_rng(11)
+    B, n, d = 5, 27, 32
+    X = rng.standard_normal((B, n, d)).astype(np.float32)
+    g = rng.standard_normal((B, d + n * (n - 1) // 2)).astype(np.float32)
+    Xt = torch.from_numpy(X.astype(np.float64)).requires_grad_(True)
+    ii, jj = np.tril_indices(n, -1)
+    gram = torch.bmm(Xt, Xt.transpose(1, 2))
+    y = torch.cat([Xt[:, 0, :], gram[:, ii, jj]], dim=1)
+    (y * torch.from_numpy(g.astype(np.float64))).sum().backward()
+    ref = Xt.grad.numpy()
+    got = orc.interact_bwd(X, g)
+    # one fp32 rounding of an fp64 sum
+    mag = np.abs(ref) + 1e-30
+    assert np.all(np.abs(got - ref) <= 2.0 ** -24 * mag + 1e-12)
+
+
+def test_interact_bwd_finite_differences(orc):
+    # central differences of the oracle's own forward, L(X) = sum(g * y(X)),
+    # on small integer-valued inputs where y is exact in fp32
+    rng = np.random.default_rng(12)
+    B, n, d = 2, 6, 5
+    X = rng.integers(-3, 4, size=(B, n, d)).astype(np.float32)
+    g = rng.integers(-2, 3, size=(B, d + n * (n - 1) // 2)).astype(np.float32)
+    got = orc.interact_bwd(X, g)
+
+    def loss(Xv):
+        return float((orc.interact_fwd(Xv).astype(np.float64) * g).sum())
+
+    h = 0.5  # L is quadratic in X: central differences are exact for any h
+    for b in range(B):
+        for i in range(n):
+            for c in range(d):
+                Xp, Xm = X.copy(), X.copy()
+                Xp[b, i, c] += h
+                Xm[b, i, c] -= h
+                fd = (loss(Xp) - loss(Xm)) / (2 * h)
+                assert fd == got[b, i, c], (b, i, c, fd, got[b, i, c])
+
+
+def test_interact_bwd_structure(orc):
+    rng = np.random.default_rng(13)
+    B, n, d = 3, 9, 16
+    X = rng.standard_normal((B, n, d)).astype(np.float32)
+    P = n * (n - 1) // 2
+    # no pair gradient: only the dense row receives the dense part of g
+    g = np.zeros((B, d + P), np.float32)
+    g[:, :d] = rng.standard_normal((B, d))
+    dX = orc.interact_bwd(X, g)
+    assert np.array_equal(dX[:, 0], g[:, :d]) and np.all(dX[:, 1:] == 0)
+    # a single pair (i, j) = (4, 2) with weight 1: rows 4 and 2 receive X_2 and X_4
+    g = np.zeros((B, d + P), np.float32)
+    g[:, d + 4 * 3 // 2 + 2] = 1.0
+    dX = orc.interact_bwd(X, g)
+    assert np.array_equal(dX[:, 4], X[:, 2]) and np.array_equal(dX[:, 2], X[:, 4])
+    others = [r for r in range(n) if r not in (2, 4)]
+    assert np.all(dX[:, others] == 0)
+
+
 # --------------------------------------------------------------------------- MLP
 
 def test_bf16_round_against_torch(orc):

@@ -29,6 +29,14 @@ MUTANTS = {
                                  ["test_interact_integer_X_exact_against_integer_gram"]),
     "interact_dense_row_missing": ("for (int32_t c = 0; c < d; ++c) o[c] = x[c];", "",
                                    ["test_interact_integer_X_exact_against_integer_gram", "test_hand_example_forward_and_sgd"]),
+    "interact_bwd_lower_half_only": ("if (j == i) continue;", "if (j >= i) continue;",
+                                     ["test_interact_bwd_structure", "test_interact_bwd_against_autograd"]),
+    "interact_bwd_no_dense_part": ("double s = (i == 0) ? (double)gb[c] : 0.0;", "double s = 0.0;",
+                                   ["test_interact_bwd_structure", "test_interact_bwd_finite_differences"]),
+    "interact_bwd_reversed_pair_index": ("gb[d + (int64_t)a * (a - 1) / 2 + e]", "gb[d + (int64_t)a * (a - 1) / 2 + (a - 1 - e)]",
+                                         ["test_interact_bwd_structure", "test_interact_bwd_against_autograd"]),
+    "interact_bwd_own_row": ("(double)xr[(int64_t)j * d + c]", "(double)xr[(int64_t)i * d + c]",
+                             ["test_interact_bwd_structure", "test_interact_bwd_finite_differences"]),
     "mlp_drops_bias": ("float y = (float)(s + (double)bias[l][o]);", "float y = (float)s;",
                        ["test_mlp_against_torch_linear", "test_hand_example_forward_and_sgd"]),
     "mlp_relu_on_logit": ("const int relu = (l < L - 1) || last_relu;\n        for (int32_t o = 0; o < fo; ++o) {\n          const float* w",
