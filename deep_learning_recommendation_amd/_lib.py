@@ -29,6 +29,7 @@ _SIGNATURES = {
     "dlrm_embbag_fwd": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I64, _P, _I64, _I64, _P]),
     "dlrm_interact_fwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I32, _I64, _P]),
     "dlrm_embbag_interact_fwd": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I64, _P]),
+    "dlrm_interact_bwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I64, _P, _I64, _P]),
     "dlrm_mlp_workspace_size": (_SZ, [_I64, _I32, _P, _I32, _I32]),
     "dlrm_mlp_fwd": (ctypes.c_int, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _SZ,
                                     _I32, _P]),
@@ -134,6 +135,11 @@ def dlrm_embbag_interact_fwd(x_dense, xd_ld: int, table_ptrs, K: int, d: int, in
     _check("dlrm_embbag_interact_fwd", lib().dlrm_embbag_interact_fwd(_ptr(x_dense), xd_ld, _ptr(table_ptrs), K, d,
                                                                        _ptr(indices), _ptr(offsets), B, _ptr(out),
                                                                        _dtype_code(out), out_ld, _stream(stream)))
+
+
+def dlrm_interact_bwd(X, B: int, n: int, d: int, x_ld: int, g, g_ld: int, dX, dx_ld: int, stream=None) -> None:
+    _check("dlrm_interact_bwd", lib().dlrm_interact_bwd(_ptr(X), B, n, d, x_ld, _ptr(g), g_ld, _ptr(dX), dx_ld,
+                                                         _stream(stream)))
 
 
 def dlrm_mlp_workspace_size(B: int, dims, w_dtype: int, save_acts: bool) -> int:

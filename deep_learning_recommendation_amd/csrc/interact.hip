@@ -406,6 +406,100 @@ bool dispatch_nt(int NT, const RowSource& src, int64_t B, int n, int d, OutT* ou
   return false;
 }
 
+// ------------------------------------------------------------------ backward
+// One wave per sample.  The sample's X rows and pair gradients are staged in
+// LDS (row stride d + 16 floats, so the four 16-lane groups of an MFMA
+// operand read hit distinct banks); then dX = S X with S the symmetric
+// n x n matrix of pair gradients (zero diagonal) runs on fp32 MFMA 16x16x4:
+// A operand S[i][j] (lane: i = 16I + l%16, j = 4ks + l/16), B operand X[j][c]
+// (lane: j = 4ks + l/16, c = 16ct + l%16), D rows 16I + 4(l/16) + r.
+template <int CT>
+__global__ __launch_bounds__(256) void interact_bwd_kernel(const float* __restrict__ X, int64_t B, int n, int d,
+                                                           int64_t x_ld, const float* __restrict__ g, int64_t g_ld,
+                                                           float* __restrict__ dX, int64_t dx_ld, int xs,
+                                                           int wave_floats) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (b >= B) return;  // whole wave
+  float* xsm = sm + (int64_t)wave * wave_floats;  // [n][xs]
+  const int P = n * (n - 1) / 2;
+  float* psm = xsm + n * xs;                      // [P]
+  const float* __restrict__ xb = X + b * x_ld;
+  const float* __restrict__ gb = g + b * g_ld;
+  const int d4 = d >> 2;
+  for (int e = lane; e < n * d4; e += 64) {
+    const int row = e / d4, c4 = e - row * d4;
+    *reinterpret_cast<float4*>(xsm + row * xs + 4 * c4) = *reinterpret_cast<const float4*>(xb + row * d + 4 * c4);
+  }
+  for (int e = lane; e < P; e += 64) psm[e] = gb[d + e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const int r16 = lane & 15, q = lane >> 4;
+  const int NT = (n + 15) >> 4, KS = (n + 3) >> 2;
+  for (int I = 0; I < NT; ++I) {
+    const int i = 16 * I + r16;
+    f4 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks) {
+      const int j = 4 * ks + q;
+      // S[i][j]: zero on the diagonal and outside n (read from a clamped,
+      // valid address and masked)
+      const int hi = i > j ? i : j, lo = i > j ? j : i;
+      const bool live = i < n && j < n && i != j;
+      const int pidx = live ? hi * (hi - 1) / 2 + lo : 0;
+      const float sv = psm[P > 0 ? pidx : 0];
+      const float a = live ? sv : 0.f;
+      const int jr = j < n ? j : n - 1;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const float xv = xsm[jr * xs + 16 * ct + r16];
+        const float bv = j < n ? xv : 0.f;
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[ct], 0, 0, 0);
+      }
+    }
+    float* __restrict__ ob = dX + b * dx_ld;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c = 16 * ct + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * I + 4 * q + r;
+        if (row < n && c < d) ob[row * d + c] = acc[ct][r] + (row == 0 ? gb[c] : 0.f);
+      }
+    }
+  }
+}
+
+constexpr int kBwdLdsMax = 160 * 1024;  // LDS of one workgroup on gfx950
+
+inline int bwd_wave_floats(int n, int d) { return (int)round_up((int64_t)n * (d + 16) + (int64_t)n * (n - 1) / 2, 4); }
+
+template <int CT>
+int launch_bwd(const float* X, int64_t B, int n, int d, int64_t x_ld, const float* g, int64_t g_ld, float* dX,
+               int64_t dx_ld, hipStream_t s) {
+  const int xs = d + 16;
+  const int wave_floats = bwd_wave_floats(n, d);
+  int spb = (int)(65536 / ((int64_t)wave_floats * 4));  // waves per block within 64 KB of LDS
+  spb = spb < 1 ? 1 : (spb > 4 ? 4 : spb);
+  const size_t lds = (size_t)spb * wave_floats * 4;
+  if (lds > 65536) {  // one large sample per block: allow the full LDS once
+    static bool raised = false;
+    if (!raised) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(interact_bwd_kernel<CT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLdsMax) != hipSuccess)
+        return DLRM_E_HIP;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL((interact_bwd_kernel<CT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb), lds, s, X, B, n,
+                     d, x_ld, g, g_ld, dX, dx_ld, xs, wave_floats);
+  return DLRM_OK;
+}
+
 template <typename OutT, bool FUSED>
 bool dispatch(const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end, hipStream_t s) {
   const int NT = (n + 15) / 16;
@@ -470,4 +564,21 @@ extern "C" int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, con
     ok = dispatch<uint16_t, true>(src, B, n, d, static_cast<uint16_t*>(out), out_ld, pad_end, stream);
   if (!ok) return DLRM_E_UNSUPPORTED;  // (K + 1) x d does not fit the register-resident layout
   return launch_status();
+}
+
+extern "C" int dlrm_interact_bwd(const float* X, int64_t B, int32_t n, int32_t d, int64_t x_ld, const float* g,
+                                 int64_t g_ld, float* dX, int64_t dx_ld, hipStream_t stream) {
+  if (!X || !g || !dX) return DLRM_E_INVALID;
+  if (B < 1 || n < 2 || n > 128 || d < 4 || d > 256 || (d % 4) != 0) return DLRM_E_INVALID;
+  if (x_ld < (int64_t)n * d || (x_ld % 4) != 0 || !aligned16(X)) return DLRM_E_INVALID;
+  if (g_ld < (int64_t)d + (int64_t)n * (n - 1) / 2 || dx_ld < (int64_t)n * d) return DLRM_E_INVALID;
+  if ((int64_t)bwd_wave_floats(n, d) * 4 > kBwdLdsMax) return DLRM_E_UNSUPPORTED;
+  const int ct = (d + 15) / 16;
+  int rc;
+  if (ct <= 1) rc = launch_bwd<1>(X, B, n, d, x_ld, g, g_ld, dX, dx_ld, stream);
+  else if (ct <= 2) rc = launch_bwd<2>(X, B, n, d, x_ld, g, g_ld, dX, dx_ld, stream);
+  else if (ct <= 4) rc = launch_bwd<4>(X, B, n, d, x_ld, g, g_ld, dX, dx_ld, stream);
+  else if (ct <= 8) rc = launch_bwd<8>(X, B, n, d, x_ld, g, g_ld, dX, dx_ld, stream);
+  else rc = launch_bwd<16>(X, B, n, d, x_ld, g, g_ld, dX, dx_ld, stream);
+  return rc != DLRM_OK ? rc : launch_status();
 }

@@ -98,6 +98,9 @@ class DLRM:
             self.db_top = [torch.empty((o,), dtype=torch.float32, device=dev) for o in top.dims[1:]]
             self.dlogit = torch.empty((B,), dtype=torch.float32, device=dev)
             self.ws_sparse = None
+            if not fused:  # full backward chain: gradient of the top input row, then of X
+                self.g_top = torch.empty((B, self.top_w), dtype=torch.float32, device=dev)
+                self.G = torch.empty((B, n, d), dtype=torch.float32, device=dev)
 
     @staticmethod
     def _ws(nbytes: int):
@@ -135,4 +138,21 @@ class DLRM:
         C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.x0,
                        self.x0_ld, G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
         C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, G, n * d, d, lr,
+                              self.sparse_workspace(nnz), stream)
+
+    def backward_chain(self, labels, indices, offsets, nnz: int, lr: float, stream=None):
+        """The whole training backward from the loss: BCE seed, top MLP (with
+        the gradient of its input row), interaction backward to the gradient
+        of X, then the bottom MLP from row 0 and the sparse SGD update from
+        rows 1..K.  Needs the materialised X (fused=False)."""
+        if self.fused or not self.train:
+            raise ValueError("backward_chain needs a training model built with fused=False")
+        B, n, d = self.B, self.n, self.d
+        C.dlrm_bce_grad(self.logit, 1, labels, B, self.dlogit, stream)
+        C.dlrm_mlp_bwd(B, self.top.dims, self.top.Ws, self.top.w_ld, C.DLRM_ACT_NONE, self.ws_top, self.logit, 1,
+                       self.dlogit, 1, self.dW_top, self.db_top, self.g_top, self.top_w, self.ws_top_bwd, stream)
+        C.dlrm_interact_bwd(self.X, B, n, d, n * d, self.g_top, self.top_w, self.G, n * d, stream)
+        C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.x0,
+                       self.x0_ld, self.G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
+        C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, self.G, n * d, d, lr,
                               self.sparse_workspace(nnz), stream)

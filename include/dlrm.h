@@ -107,6 +107,30 @@ int dlrm_interact_fwd(const float* X, int64_t B, int32_t n, int32_t d, int64_t x
                       int32_t out_dtype, int64_t out_ld, hipStream_t stream);
 
 /*
+ * Pairwise dot-product interaction, backward.
+ * The training pass through the interaction above: [SU] Key equations,
+ * Interaction and Output give the forward map X -> [X_0, Z]; the model is
+ * trained on binary cross-entropy ([EXPL] Key Method Details, Loss), so the
+ * top MLP returns g, the gradient of its input row, and by the chain rule
+ *   dX[i][c] = [i == 0] g[c] + sum over j != i of g_pair(i, j) * X[j][c],
+ *   g_pair(i, j) = g[d + a(a-1)/2 + b], a = max(i, j), b = min(i, j).
+ * dX rows 1..n-1 are the gradients of the pooled embeddings (the input of
+ * dlrm_embbag_bwd_sgd), row 0 the gradient of the bottom MLP's output.
+ *
+ *   X        fp32, sample b's forward input at X + b*x_ld, rows of d floats
+ *            (x_ld >= n*d, x_ld % 4 == 0, 16-byte aligned).
+ *   g        fp32, sample b's gradient row at g + b*g_ld, g_ld >= d + n(n-1)/2.
+ *   dX       fp32 out, sample b's rows at dX + b*dx_ld (dx_ld >= n*d).
+ *   Accuracy: fp32 products and accumulation
+ *            (|err| <= n u (sum over j of |g_pair(i, j) X[j][c]| + |g[c]|)).
+ *   Limits:  2 <= n <= 128, d % 4 == 0, 4 <= d <= 256, and one sample's
+ *            n (d + 16) + n(n-1)/2 floats within the 160 KB of LDS
+ *            (DLRM_E_UNSUPPORTED otherwise, e.g. n = 128 with d = 256).
+ */
+int dlrm_interact_bwd(const float* X, int64_t B, int32_t n, int32_t d, int64_t x_ld, const float* g, int64_t g_ld,
+                      float* dX, int64_t dx_ld, hipStream_t stream);
+
+/*
  * Fused pooled lookup and interaction (forward).
  * The same result as dlrm_embbag_fwd into X rows 1..K followed by
  * dlrm_interact_fwd, with X row 0 = x_dense, but X never goes to memory:

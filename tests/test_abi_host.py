@@ -63,6 +63,23 @@ def test_interact_argument_checks(lib):
     assert f(FAKE, 4, 129, 16, 129 * 16, FAKE, C.DLRM_F32, 9000, NULL) == C.DLRM_E_INVALID
 
 
+def test_interact_bwd_argument_checks(lib):
+    P = ctypes.c_void_p
+    x, g, dx = P(16), P(16), P(16)  # never dereferenced: every case fails before a launch
+    bad = [
+        (None, 4, 9, 16, 144, g, 52, dx, 144),      # null X
+        (x, 4, 1, 16, 16, g, 16, dx, 16),           # n < 2
+        (x, 4, 9, 18, 162, g, 54, dx, 162),         # d % 4
+        (x, 4, 9, 16, 140, g, 52, dx, 144),         # x_ld < n*d
+        (x, 4, 9, 16, 144, g, 51, dx, 144),         # g_ld < d + n(n-1)/2
+        (x, 4, 9, 16, 144, g, 52, dx, 143),         # dx_ld < n*d
+    ]
+    for args in bad:
+        assert lib.dlrm_interact_bwd(*args, None) == -1, args
+    # n = 128 with d = 256 does not fit one workgroup's LDS
+    assert lib.dlrm_interact_bwd(x, 1, 128, 256, 128 * 256, g, 256 + 128 * 127 // 2, dx, 128 * 256, None) == -4
+
+
 def test_mlp_workspace_and_checks(lib):
     dims = (ctypes.c_int32 * 4)(13, 512, 256, 128)
     a = lib.dlrm_mlp_workspace_size(32768, 3, dims, C.DLRM_BF16, 0)

@@ -113,3 +113,39 @@ def test_train_step_scaled():
     for l in range(len(rW)):
         g = model.dW_top[l].cpu().numpy()
         assert np.linalg.norm(g - rW[l]) <= 2e-2 * np.linalg.norm(rW[l]), l
+
+
+def test_train_full_backward_chain_scaled():
+    """Loss -> top MLP (input gradient) -> interaction backward -> bottom MLP
+    and sparse SGD.  The gradient of X against the oracle's chain within the
+    MLP-backward tolerance (the top MLP's bf16 backward dominates); the table
+    update from the device's own X gradient bit-exact."""
+    w = W.get("train").scaled(B=512, rows=50_000)
+    banner("train full backward chain scaled")
+    model, bottom, top = device_model(w, train=True, fused=False)
+    dense, idx, off = W.dense(w), *W.indices_offsets(w)
+    y = W.labels(w)
+    idx_d, off_d = to_dev(idx), to_dev(off)
+    model.forward(to_dev(dense), idx_d, off_d)
+    model.backward_chain(to_dev(y), idx_d, off_d, int(off[-1]), w.lr)
+    torch.cuda.synchronize()
+    G = model.G.cpu().numpy()
+    # oracle chain
+    X, top_in, logit, prob = oracle_forward(w, dense, idx, off, bottom, top)
+    _, _, acts = oracle.mlp_fwd(top_in, [p[0] for p in top], [p[2] for p in top], True, False, save_acts=True)
+    dY = ((prob - y) / w.B).astype(np.float32).reshape(-1, 1)
+    _, _, g_top = oracle.mlp_bwd([p[0] for p in top], acts, dY, False, want_dx=True)
+    G_ref = oracle.interact_bwd(X, g_top)
+    assert np.linalg.norm(G - G_ref) <= 2e-2 * np.linalg.norm(G_ref)
+    # the sparse update consumed rows 1..K of the device's G: bit-exact
+    tabs, local, row_ids = W.compact_rows(w, idx, off)
+    oracle.embbag_bwd_sgd(tabs, local, off, w.B, G.reshape(w.B, -1), w.d, w.lr)
+    for k in range(w.K):
+        got = model.tables[k][torch.from_numpy(row_ids[k]).to(DEV)].cpu().numpy()
+        assert np.array_equal(bits(got), bits(tabs[k])), k
+    # bottom MLP weight gradients from row 0 of the device's G
+    _, _, acts_b = oracle.mlp_fwd(dense, [p[0] for p in bottom], [p[2] for p in bottom], True, True, save_acts=True)
+    rW, _, _ = oracle.mlp_bwd([p[0] for p in bottom], acts_b, G[:, 0, :], True)
+    for l in range(len(rW)):
+        g = model.dW_bot[l].cpu().numpy()
+        assert np.linalg.norm(g - rW[l]) <= 2e-2 * np.linalg.norm(rW[l]), l

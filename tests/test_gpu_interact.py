@@ -126,3 +126,66 @@ def test_fused_gather_interaction(K, d, out_bf16):
         assert np.array_equal(bits(got[:, :d]), bits(ref[:, :d]))
         assert np.all(np.abs(got[:, d:width].astype(np.float64) - ref[:, d:]) <= interaction_tolerance(Xr))
     assert np.all(got[:, width:] == 0)
+
+
+# ------------------------------------------------------------------ backward
+
+def _run_bwd(X, g):
+    import deep_learning_recommendation_amd as D
+
+    B, n, d = X.shape
+    dX = torch.full((B, n * d), 7.0, dtype=torch.float32, device=DEV)
+    D.dlrm_interact_bwd(to_dev(X), B, n, d, n * d, to_dev(g), g.shape[1], dX, n * d)
+    torch.cuda.synchronize()
+    return dX.cpu().numpy().reshape(B, n, d)
+
+
+def _bwd_bound(X, g):
+    # fp32 accumulation of n products per output: n u (sum |g_pair X| + |g_dense|)
+    n = X.shape[1]
+    mag = oracle.interact_bwd(np.abs(X), np.abs(g)).astype(np.float64)
+    return (n + 2) * 2.0 ** -24 * mag + 1e-30
+
+
+BWD_SHAPES = [(2, 4), (9, 16), (9, 128), (17, 32), (27, 128), (33, 64), (101, 64), (128, 64), (5, 12), (27, 100),
+              (101, 128), (128, 128), (64, 256)]
+
+
+@pytest.mark.parametrize("n,d", BWD_SHAPES)
+def test_interact_bwd_within_bound(n, d):
+    B = 37
+    banner(f"interact bwd n={n} d={d}")
+    rng = np.random.default_rng(1000 + n * 7 + d)
+    X = rng.standard_normal((B, n, d)).astype(np.float32)
+    g = rng.standard_normal((B, d + n * (n - 1) // 2)).astype(np.float32)
+    got = _run_bwd(X, g)
+    ref = oracle.interact_bwd(X, g)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= _bwd_bound(X, g))
+    # and the "1e-5 relative" reading against the sum of magnitudes
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= 1e-5 * oracle.interact_bwd(np.abs(X), np.abs(g)) + 1e-30)
+
+
+@pytest.mark.parametrize("n,d", [(9, 16), (27, 128), (101, 64)])
+def test_interact_bwd_integer_exact(n, d):
+    # small integers: every product and partial sum is exact in fp32, so any
+    # accumulation order gives the oracle's value; pins the S and X index maps
+    B = 9
+    banner(f"interact bwd integer n={n} d={d}")
+    rng = np.random.default_rng(n + d)
+    X = rng.integers(-4, 5, size=(B, n, d)).astype(np.float32)
+    g = rng.integers(-3, 4, size=(B, d + n * (n - 1) // 2)).astype(np.float32)
+    assert np.array_equal(bits(_run_bwd(X, g)), bits(oracle.interact_bwd(X, g)))
+
+
+def test_interact_bwd_workload_shapes_full_batch():
+    for (B, n, d) in [(8192, 9, 128), (32768, 27, 128), (16384, 101, 64)]:
+        banner(f"interact bwd full batch B={B} n={n} d={d}")
+        rng = np.random.default_rng(B + n)
+        X = (rng.standard_normal((B, n, d)) * 0.1).astype(np.float32)
+        g = (rng.standard_normal((B, d + n * (n - 1) // 2)) * 1e-3).astype(np.float32)
+        got = _run_bwd(X, g)
+        rows = np.random.default_rng(1).choice(B, 64, replace=False)
+        rows[-1] = B - 1
+        ref = oracle.interact_bwd(X[rows], g[rows])
+        bound = 1e-5 * oracle.interact_bwd(np.abs(X[rows]), np.abs(g[rows])) + 1e-30
+        assert np.all(np.abs(got[rows].astype(np.float64) - ref) <= bound)
