@@ -69,6 +69,10 @@ def parse():
     p.add_argument("--workload", default="forward", choices=["forward", "embbag", "interaction", "train", "tiny"])
     p.add_argument("--batches", type=int, default=2, help="distinct input batches rotated over the steps")
     p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
+    p.add_argument("--chain", action="store_true",
+                   help="training workload only: the whole backward from the BCE loss (top MLP input gradient, "
+                        "interaction backward, bottom MLP and sparse update from the real X gradient) instead of "
+                        "the synthetic upstream gradient G")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-samples", type=int, default=0, help="oracle sample size (0: automatic)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -101,10 +105,12 @@ class Timer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
 
 
-def cpu_baseline(w, batches, bottom, top, n_samples, min_seconds=10.0):
+def cpu_baseline(w, batches, bottom, top, n_samples, chain=False, min_seconds=10.0):
     """The oracle (as it stands) on the first n_samples of batch 0: forward
     for forward-type workloads, pooled lookups for the gather microbench,
-    forward plus the sparse update for the training step.  The pass is
+    forward plus the sparse update for the training step (with ``chain``:
+    forward with saved activations, the BCE seed, both MLP backwards, the
+    interaction backward and the sparse update from its X gradient).  The pass is
     repeated until min_seconds of CPU work have run (a bounded sample);
     row regeneration and input slicing are excluded from the timed region.
     Returns (samples processed, seconds, threads, passes)."""
@@ -119,8 +125,25 @@ def cpu_baseline(w, batches, bottom, top, n_samples, min_seconds=10.0):
     tabs, local, _ = W.compact_rows(ws, sidx, soff)
     quant = w.mlp_dtype == "bf16"
     G = batches[0][3].reshape(w.B, -1)[:S] if w.train else None
+    y = batches[0][4][:S] if w.train else None
+
+    def chain_pass():
+        E = oracle.embbag_fwd(tabs, local, soff, S)
+        Wb, bb = [p[0] for p in bottom], [p[2] for p in bottom]
+        Wt, bt = [p[0] for p in top], [p[2] for p in top]
+        x0, _, acts_b = oracle.mlp_fwd(dense[:S], Wb, bb, quant, True, save_acts=True)
+        X = np.concatenate([x0, E], axis=1).reshape(S, w.n, w.d)
+        top_in = oracle.interact_fwd(X)
+        _, prob, acts_t = oracle.mlp_fwd(top_in, Wt, bt, quant, False, save_acts=True)
+        dY = ((prob - y) / S).astype(np.float32).reshape(-1, 1)
+        _, _, g_top = oracle.mlp_bwd(Wt, acts_t, dY, False, want_dx=True)
+        GX = oracle.interact_bwd(X, g_top).reshape(S, -1)
+        oracle.mlp_bwd(Wb, acts_b, GX[:, :w.d], True)
+        oracle.embbag_bwd_sgd(tabs, local, soff, S, GX, w.d, w.lr)
 
     def one_pass():
+        if chain:
+            return chain_pass()
         E = oracle.embbag_fwd(tabs, local, soff, S)
         if w.name != "embbag":
             x0, _, _ = oracle.mlp_fwd(dense[:S], [p[0] for p in bottom], [p[2] for p in bottom], quant, True)
@@ -166,6 +189,9 @@ def main():
     import dataclasses
 
     w = W.get(args.workload)
+    if args.chain and not w.train:
+        print("--chain applies to the training workload only", file=sys.stderr)
+        sys.exit(1)
     if args.uniform:
         w = dataclasses.replace(w, index_dist="uniform")
     t_setup = time.perf_counter()
@@ -189,7 +215,7 @@ def main():
     if w.bottom:
         bp = PL.make_mlp(w.bottom, [p[0] for p in bottom], [p[2] for p in bottom], bf16)
         tp = PL.make_mlp(w.top, [p[0] for p in top], [p[2] for p in top], bf16)
-        model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=w.train)
+        model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=w.train, fused=not args.chain)
         if w.train:
             model.sparse_workspace(max(b[5] for b in dbatches))
     else:
@@ -217,6 +243,8 @@ def main():
             if timed:
                 ev[name] = gather_t.start(stream)
 
+        if args.chain:
+            return chain_step(model, dense, idx, off, y, nnz, mark, ev, timed)
         mark("bottom_mlp")
         D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
                        model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.x0, model.x0_ld, None,
@@ -240,10 +268,40 @@ def main():
             D.dlrm_embbag_bwd_sgd(model.table_ptrs, w.K, d, w.rows, idx, off, w.B, nnz, G, n * d, d, w.lr,
                                   model.ws_sparse)
         mark("end")
+        record(ev, timed)
+
+    def record(ev, timed):
         if timed:
             names = list(ev)
             for a, b in zip(names[:-1], names[1:]):
                 call_t.setdefault(a, []).append((ev[a], ev[b]))
+
+    def chain_step(m, dense, idx, off, y, nnz, mark, ev, timed):
+        """Forward with X materialised, then the backward from the loss."""
+        n, d, B = m.n, m.d, w.B
+        mark("bottom_mlp")
+        D.dlrm_mlp_fwd(dense, dense.shape[1], B, m.bottom.dims, m.bottom.Ws, m.bottom.w_ld, m.bottom.biases,
+                       m.bottom.w_dtype, D.DLRM_ACT_RELU, m.x0, m.x0_ld, None, m.ws_bot, True)
+        mark("embbag")
+        D.dlrm_embbag_fwd(m.table_ptrs, w.K, d, idx, off, B, m.X, n * d, d)
+        mark("interact")
+        D.dlrm_interact_fwd(m.X, B, n, d, n * d, m.top_in, m.top_ld)
+        mark("top_mlp")
+        D.dlrm_mlp_fwd(m.top_in, m.top_ld, B, m.top.dims, m.top.Ws, m.top.w_ld, m.top.biases, m.top.w_dtype,
+                       D.DLRM_ACT_NONE, m.logit, 1, m.prob, m.ws_top, True)
+        mark("top_bwd")
+        D.dlrm_bce_grad(m.logit, 1, y, B, m.dlogit)
+        D.dlrm_mlp_bwd(B, m.top.dims, m.top.Ws, m.top.w_ld, D.DLRM_ACT_NONE, m.ws_top, m.logit, 1, m.dlogit, 1,
+                       m.dW_top, m.db_top, m.g_top, m.top_w, m.ws_top_bwd)
+        mark("interact_bwd")
+        D.dlrm_interact_bwd(m.X, B, n, d, n * d, m.g_top, m.top_w, m.G, n * d)
+        mark("bottom_bwd")
+        D.dlrm_mlp_bwd(B, m.bottom.dims, m.bottom.Ws, m.bottom.w_ld, D.DLRM_ACT_RELU, m.ws_bot, m.x0, m.x0_ld,
+                       m.G, n * d, m.dW_bot, m.db_bot, None, 0, m.ws_bot_bwd)
+        mark("sparse_bwd_sgd")
+        D.dlrm_embbag_bwd_sgd(m.table_ptrs, w.K, d, w.rows, idx, off, B, nnz, m.G, n * d, d, w.lr, m.ws_sparse)
+        mark("end")
+        record(ev, timed)
 
     for i in range(args.warmup):
         step(i, False)
@@ -258,10 +316,10 @@ def main():
     value = w.B * args.steps / elapsed
     breakdown = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in call_t.items()}
     nnz_mean = float(np.mean([b[5] for b in dbatches]))
-    if model is None:
+    if model is None or args.chain:
         kname, key = "embbag_fwd_kernel", None
         gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean)
-        g_ms = gather_t.mean_ms()
+        g_ms = gather_t.mean_ms() if model is None else breakdown["embbag"]
     else:
         # fused pooled lookup + interaction: every looked-up row, indices and
         # offsets, the dense rows it reads and the packed top-MLP rows it writes
@@ -271,7 +329,7 @@ def main():
                   esz * w.B * model.top_ld)
         g_ms = breakdown[key]
     achieved = gbytes / (g_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w.name + ("_uniform" if args.uniform else ""), kname)
+    traffic = measured_traffic(w.name + ("_uniform" if args.uniform else "") + ("_chain" if args.chain else ""), kname)
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(gbytes), "avg_launch_ms": round(g_ms, 4)}
@@ -280,9 +338,11 @@ def main():
     if not args.no_cpu_baseline:
         ns = args.cpu_samples or {"forward": 16384, "embbag": 16384, "interaction": 512, "train": 1024,
                                   "tiny": 128}[w.name]
-        S, dt, thr, passes = cpu_baseline(w, batches, bottom, top, ns)
+        S, dt, thr, passes = cpu_baseline(w, batches, bottom, top, ns, chain=args.chain)
         what = {"forward": "forward pass", "embbag": "pooled lookups", "interaction": "forward pass",
                 "train": "forward pass and sparse SGD update", "tiny": "forward pass"}[w.name]
+        if args.chain:
+            what = "forward pass and the whole backward from the loss with the sparse SGD update"
         cpu = {"value": round(S / dt, 2), "unit": "samples/s", "cores": thr, "kind": "oracle",
                "sample": f"{what} of the first {S // passes} samples of batch 0, repeated {passes} times "
                          f"({dt:.1f} s; tables regenerated for the touched rows only, outside the timed region)"}
@@ -291,6 +351,8 @@ def main():
            "bag": f"{w.bag}:{w.bag_len}", "index": f"{w.index_dist}" + (f"({w.alpha})" if w.index_dist == "zipf" else ""),
            "bottom_mlp": "-".join(map(str, w.bottom)), "top_mlp": "-".join(map(str, w.top)),
            "mlp_dtype": w.mlp_dtype, "table_dtype": "f32", "batches_rotated": args.batches}
+    if w.train:
+        cfg["upstream_grad"] = "from the loss (interaction backward)" if args.chain else "synthetic G"
     res = {"metric": METRIC, "value": round(value, 1), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32+bf16" if w.mlp_dtype == "bf16" else "f32", "data": "synthetic",
