@@ -6,12 +6,10 @@
 // the natural layout of a fully connected layer y = x W^T.  gfx950 bf16 MFMA
 // v_mfma_f32_32x32x16_bf16: each lane feeds 8 consecutive k of one row of A
 // (row l % 32, k (l / 32) * 8) and of W, so both operands are read from LDS
-// with one 16-byte ds_read per fragment.  Block tile BM x BN x 64 with four
-// waves in a 2 x 2 grid (wave tiles up to 128 x 128, accumulators in AGPRs),
-// LDS rows padded by 16 bytes (conflict-free 16-byte reads), double-buffered
-// LDS with the next k-tile's global loads in flight during the MFMAs.  Tiles
-// are walked N-fastest and block ids are regrouped so that the tiles sharing
-// an A panel land on one XCD (one L2).
+// with one 16-byte ds_read per fragment.  The fast kernel (16-byte aligned
+// operands) is persistent, loads tiles straight from global memory into LDS,
+// keeps its accumulators in registers and writes C from registers; a
+// generic kernel covers any other layout.
 #include "gemm.hpp"
 
 namespace dlrm {
@@ -48,19 +46,35 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
 //
 // Tiles move from global memory straight into LDS with global_load_lds_dwordx4
 // (no register staging): each wave instruction fills one contiguous 1 KB
-// block of LDS, i.e. 8 rows of a 64-wide bf16 k-slice.  Inside a row the
-// eight 16-byte chunks are XOR-swizzled (physical chunk = chunk ^ ((row >> 1)
-// & 7)) so that the 16 lanes that one LDS cycle serves read 16 distinct bank
-// groups.  Two LDS stages: the loads of k-tile kt+1 run during the MFMAs of
-// k-tile kt; one barrier per k-tile.  Rows past M or N re-read the last row
-// (their results are never stored); columns past K in the last k-tile are
-// zeroed in LDS before use.  The bf16 epilogue goes through LDS so that every
-// global store is a full 16-byte chunk.
+// block of LDS, i.e. 1 KB / (2 BK) rows of a BK-wide bf16 k-slice.  Inside a
+// row the 16-byte chunks are XOR-swizzled with row bits so that the 16 lanes
+// that one LDS cycle serves read distinct bank groups.  S LDS stages: the
+// loads of k-tiles kt+1 .. kt+S-1 run during the MFMAs of k-tile kt; one
+// barrier per k-tile.  Rows past M or N re-read the last row (their results
+// are never stored); columns past K in the last k-tile are zeroed in LDS.
+//
+// The MFMA takes the W fragment as its first operand, so each accumulator
+// block holds a 32 x 32 piece of C transposed: lane l owns row l % 32 of C
+// and, for every group of four registers, four consecutive columns.  The
+// epilogue therefore needs no LDS: bias, ReLU and bf16 rounding run in
+// registers, one cross-half lane swap (v_permlane32_swap) gives each lane
+// eight consecutive columns, and every store is 16 bytes.
+//
+// The kernel is persistent: a grid of at most (resident workgroups per CU x
+// CUs) walks the tiles, and the first k-tiles of the next tile are already
+// loading into LDS while the epilogue of the current tile runs.  Tiles are
+// walked N-fastest; with a grid and tile count divisible by 8, each XCD
+// (workgroup b runs on XCD b % 8) takes one contiguous range of tiles, so
+// the tiles that share an A panel share one L2.
+// Waves per SIMD the register budget allows: wave tiles of 128 x 128 keep
+// 256 accumulators and run one wave per SIMD, smaller ones two.
+constexpr int fast_waves_per_eu(int WM, int WN) { return WM * WN > 128 * 64 ? 1 : 2; }
+
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_kernel(
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(fast_waves_per_eu(WM, WN)))) void gemm_bf16_fast_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, OutT* __restrict__ C, int64_t ldc, int M, int N, int K, int relu, int tiles_n,
-    int k_per_split) {
+    int tiles, int k_per_split, int vec_out) {
   static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
   constexpr int RB = BK * 2;                      // bytes per tile row
   constexpr int CPR = BK / 8;                     // 16-byte chunks per row
@@ -70,10 +84,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_INS = BM * RB / 1024 / NWAVES, B_INS = BN * RB / 1024 / NWAVES, INS = A_INS + B_INS;
   constexpr int STAGE = (BM + BN) * RB;
-  constexpr int EPI_LS = WN * 2 + 16;             // epilogue LDS row stride (bytes)
-  constexpr int EPI = BM * (BN / WN) * EPI_LS;
-  constexpr int SMEM = (S * STAGE > EPI) ? S * STAGE : EPI;
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
   // chunk swizzle: the 16 lanes that one LDS cycle serves read 16 rows of
   // one logical chunk; XOR-ing the chunk with row bits above the rows that
   // share a bank group spreads them over all 64 banks
@@ -81,33 +92,44 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave - (wave / WAVES_N) * WAVES_N;
-  int bid = blockIdx.x;
-  const int total = gridDim.x;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  const int tile_m = bid / tiles_n, tile_n = bid - tile_m * tiles_n;
-  const int m0 = tile_m * BM, n0 = tile_n * BN;
   const int kbeg = (int)blockIdx.z * k_per_split;
   const int kend = min(K, kbeg + k_per_split);
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int kpad = (kend + 7) & ~7;
 
+  // this workgroup's tiles: first, first + stride, ... below end
+  const int G = gridDim.x;
+  int tile = blockIdx.x, stride = G, end = tiles;
+  if ((tiles & 7) == 0 && (G & 7) == 0) {
+    const int per = tiles >> 3, x = blockIdx.x & 7;
+    tile = x * per + (blockIdx.x >> 3);
+    stride = G >> 3;
+    end = (x + 1) * per;
+  }
+  if (tile >= end) return;
+
   // this lane's DMA rows: instruction j of wave w fills rows (w*INS + j)*RPI + lane/CPR
   const int lrow = lane / CPR, lpc = lane % CPR;
-  const uint16_t* a_row[A_INS];
-  const uint16_t* b_row[B_INS];
-  int a_c[A_INS], b_c[B_INS];
+  int a_r[A_INS], b_r[B_INS], a_c[A_INS], b_c[B_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
-    const int row = (wave * A_INS + j) * RPI + lrow;
-    a_row[j] = A + (int64_t)min(m0 + row, M - 1) * lda;
-    a_c[j] = (lpc ^ swz(row)) * 8;
+    a_r[j] = (wave * A_INS + j) * RPI + lrow;
+    a_c[j] = (lpc ^ swz(a_r[j])) * 8;
   }
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
-    const int row = (wave * B_INS + j) * RPI + lrow;
-    b_row[j] = W + (int64_t)min(n0 + row, N - 1) * ldw;
-    b_c[j] = (lpc ^ swz(row)) * 8;
+    b_r[j] = (wave * B_INS + j) * RPI + lrow;
+    b_c[j] = (lpc ^ swz(b_r[j])) * 8;
   }
+  const uint16_t* a_row[A_INS];
+  const uint16_t* b_row[B_INS];
+  auto rows_of = [&](int t, const uint16_t** ar, const uint16_t** br) {
+    const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) ar[j] = A + (int64_t)min(tm * BM + a_r[j], M - 1) * lda;
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) br[j] = W + (int64_t)min(tn * BN + b_r[j], N - 1) * ldw;
+  };
   auto issue = [&](int kt) {
     char* st = smem + (kt % S) * STAGE;
     const int k0 = kbeg + kt * BK;
@@ -120,13 +142,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
   };
 
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
   const int r32 = lane & 31, half = lane >> 5;
   // zero columns [valid, BK) of every A and W row of a partial last k-tile
   auto zero_tail = [&](int kt) {
@@ -165,13 +180,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
   };
   // Pipeline: tiles kt .. kt+S-1 sit in the S LDS stages (tile t in stage
   // t % S).  At the last k-step of tile kt every wave has read its operands
   // of stage kt % S, so after one barrier (which also sees tile kt+1 landed)
   // the loads of tile kt+S go into that stage and the first operands of tile
-  // kt+1 are read before the last MFMAs of tile kt run.
+  // kt+1 are read before the last MFMAs of tile kt run.  Waits count this
+  // wave's vector-memory operations, which complete in issue order; the
+  // epilogue stores of the previous tile, issued after this tile's first
+  // loads, only make the first waits of a tile wait a little longer.
   auto wait_tiles = [&](int younger) {  // at most `younger` tiles' loads still in flight
     if constexpr (S >= 4) {
       if (younger >= 3) { wait_vmcnt<3 * INS>(); return; }
@@ -182,17 +200,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
     if (younger >= 1) { wait_vmcnt<INS>(); return; }
     wait_vmcnt<0>();
   };
-  const int pre = nk < S ? nk : S;
-#pragma unroll
-  for (int t = 0; t < S; ++t)
-    if (t < nk) issue(t);
-  if (nk > 0) {
-    wait_tiles(pre - 1);
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    if (nk == 1) zero_tail(0);
-    load_frags(smem, 0, 0);
-  }
   // k-steps 0..KS-2 of the tile in stage st: read the next step's operands,
   // then this step's MFMAs (the scheduling barriers keep that order)
   auto first_steps = [&](const char* st) {
@@ -221,90 +228,195 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_bf16_fast_ker
   // the steady state has no branch, so every wait is an exact count; the
   // epilogue's kernel arguments are read here so that no scalar load is
   // pending in the loop (that would turn every LDS wait into lgkmcnt(0))
-  __asm__ volatile("" : "+s"(bias), "+s"(C), "+s"(ldc));
-  int kt = 0;
-  for (; kt + S < nk; ++kt) {
-    first_steps(smem + (kt % S) * STAGE);
-    turn(kt, true, false, S - 2);
-  }
+  __asm__ volatile("" : "+s"(bias), "+s"(C), "+s"(ldc), "+s"(vec_out), "+s"(relu));
+  const int pre = nk < S ? nk : S;
+  rows_of(tile, a_row, b_row);
 #pragma unroll
-  for (int r = 0; r < S - 1; ++r) {  // at most S - 1 tiles remain after the steady state
-    if (kt + 1 < nk) {
-      first_steps(smem + (kt % S) * STAGE);
-      const int younger = nk - 2 - kt;
-      turn(kt, false, kt + 2 == nk, younger < S - 2 ? younger : S - 2);
-      ++kt;
-    }
-  }
-  if (kt < nk) {
-    first_steps(smem + (kt % S) * STAGE);
-    mfmas(LAST);
-  }
+  for (int t = 0; t < S; ++t)
+    if (t < nk) issue(t);
 
-  // D layout of a 32x32 block: lane l holds column l % 32 and rows
-  // 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
-  constexpr bool kBf16Out = sizeof(OutT) == 2 && !PARTIAL;
-  const bool staged = kBf16Out && m0 + BM <= M && n0 + BN <= N && (ldc % 8) == 0 &&
-                      (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
-  if (staged) {
-    __syncthreads();  // all waves are done reading the k-tiles
-    char* ep = smem + (wm * WM * (BN / WN) + wn * WM) * EPI_LS;  // this wave's WM x WN region
+  while (true) {
+    const int m0 = (tile / tiles_n) * BM, n0 = (tile - (tile / tiles_n) * tiles_n) * BN;
+    // Block (tm, tn) of the accumulators: lane l holds C row
+    // m0 + wm*WM + tm*32 + l%32 and, in register v, column
+    // n0 + wn*WN + tn*32 + 8*(v/4) + 4*(l/32) + v%4.  The accumulators start
+    // from the bias (zero for partial sums), so the MFMAs add the products to it.
+    const int rowb = m0 + wm * WM + r32, colb = n0 + wn * WN + 4 * half;
+    const bool with_bias = !PARTIAL && bias != nullptr;
+    if (with_bias && n0 + (wn + 1) * WN <= N) {  // this wave's columns all exist
+      const float* bp = bias + colb;
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const float bj = bias != nullptr ? bias[n0 + wn * WN + tn * 32 + r32] : 0.f;
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int i = tm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          float val = acc[tm][tn][v] + bj;
-          if (relu) val = relu_f(val);
-          *reinterpret_cast<uint16_t*>(ep + i * EPI_LS + (tn * 32 + r32) * 2) = f32_to_bf16(val);
+          const float b0 = bp[j * 32 + 8 * (v >> 2) + (v & 3)];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) acc[i][j][v] = b0;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int col = colb + j * 32 + 8 * (v >> 2) + (v & 3);
+          const float b0 = (with_bias && col < N) ? bias[col] : 0.f;
+#pragma unroll
+          for (int i = 0; i < TM; ++i) acc[i][j][v] = b0;
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (region is wave-private)
-    constexpr int CH = WN / 8;            // 16-byte chunks per row
-#pragma unroll
-    for (int it = 0; it < WM * CH / 64; ++it) {
-      const int e = it * 64 + lane;
-      const int row = e / CH, ch = e - (e / CH) * CH;
-      const uint4 v = *reinterpret_cast<const uint4*>(ep + row * EPI_LS + ch * 16);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(C) + (int64_t)(m0 + wm * WM + row) * ldc + n0 + wn * WN +
-                                ch * 8) = v;
+    if (nk > 0) {
+      wait_tiles(pre - 1);
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      if (nk == 1) zero_tail(0);
+      load_frags(smem, 0, 0);
     }
-    return;
-  }
+    int kt = 0;
+    for (; kt + S < nk; ++kt) {
+      first_steps(smem + (kt % S) * STAGE);
+      turn(kt, true, false, S - 2);
+    }
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int j = n0 + wn * WN + tn * 32 + r32;
-    const float bj = (!PARTIAL && bias != nullptr && j < N) ? bias[j] : 0.f;
+    for (int r = 0; r < S - 1; ++r) {  // at most S - 1 tiles remain after the steady state
+      if (kt + 1 < nk) {
+        first_steps(smem + (kt % S) * STAGE);
+        const int younger = nk - 2 - kt;
+        turn(kt, false, kt + 2 == nk, younger < S - 2 ? younger : S - 2);
+        ++kt;
+      }
+    }
+    if (kt < nk) {
+      first_steps(smem + (kt % S) * STAGE);
+      mfmas(LAST);
+    }
+
+    const int next = tile + stride;
+    if (next < end) {
+      // every wave's LDS reads of this tile are done: the next tile's first
+      // k-tiles load while this tile's epilogue runs
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      rows_of(next, a_row, b_row);
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
+      for (int t = 0; t < S; ++t)
+        if (t < nk) issue(t);
+    }
+
+    const bool full = m0 + BM <= M && n0 + BN <= N && vec_out;
+    if constexpr (sizeof(OutT) == 2 && !PARTIAL) {
+      if (full) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) {
+            uint32_t pk[4][2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                float v0 = acc[tm][tn][4 * g + 2 * h];
+                float v1 = acc[tm][tn][4 * g + 2 * h + 1];
+                if (relu) {
+                  v0 = relu_f(v0);
+                  v1 = relu_f(v1);
+                }
+                pk[g][h] = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+              }
+            // lanes 0-31 gather columns 0-7 and 16-23 of the block, lanes 32-63 columns 8-15 and 24-31
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const auto s01 = __builtin_amdgcn_permlane32_swap(pk[0][h], pk[1][h], false, false);
+              const auto s23 = __builtin_amdgcn_permlane32_swap(pk[2][h], pk[3][h], false, false);
+              pk[0][h] = s01[0];
+              pk[1][h] = s01[1];
+              pk[2][h] = s23[0];
+              pk[3][h] = s23[1];
+            }
+            uint16_t* c = reinterpret_cast<uint16_t*>(C) + (int64_t)(rowb + tm * 32) * ldc + n0 + wn * WN + tn * 32 +
+                          8 * half;
+            *reinterpret_cast<uint4*>(c) = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);
+            *reinterpret_cast<uint4*>(c + 16) = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);
+          }
+        goto tile_done;
+      }
+    }
+    if constexpr (sizeof(OutT) == 4) {
+      if (full) {  // four consecutive fp32 columns per register group: 16-byte stores
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int j = colb + tn * 32 + 8 * g;
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+              float o[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                o[q] = acc[tm][tn][4 * g + q];
+                if (!PARTIAL && relu) o[q] = relu_f(o[q]);
+              }
+              const int64_t i = rowb + tm * 32;
+              float* dst = reinterpret_cast<float*>(C) + (PARTIAL ? ((int64_t)blockIdx.z * M + i) : i) * ldc + j;
+              *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+          }
+        goto tile_done;
+      }
+    }
+    // edge tiles and unaligned outputs: element stores
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int i = m0 + wm * WM + tm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (i < M && j < N) {
-          float val = acc[tm][tn][v];
-          if (PARTIAL) {
-            C[((int64_t)blockIdx.z * M + i) * ldc + j] = val;
-          } else {
-            val = val + bj;
-            if (relu) val = relu_f(val);
-            store_out(&C[(int64_t)i * ldc + j], val);
+        const int j = colb + tn * 32 + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int i = rowb + tm * 32;
+          if (i < M && j < N) {
+            float val = acc[tm][tn][v];
+            if (PARTIAL) {
+              C[((int64_t)blockIdx.z * M + i) * ldc + j] = val;
+            } else {
+              if (relu) val = relu_f(val);
+              store_out(&C[(int64_t)i * ldc + j], val);
+            }
           }
         }
       }
-    }
+  tile_done:
+    if (next >= end) break;
+    tile = next;
   }
+}
+
+// Resident workgroups per CU of one fast-kernel instance (queried once).
+template <typename Kern>
+int fast_occupancy(Kern kern, int threads) {
+  static int cached = 0;
+  if (cached == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, 0) != hipSuccess || v < 1) v = 1;
+    cached = v;
+  }
+  return cached;
 }
 
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2>
 void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
                  int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int tiles = tm * tn;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S>), dim3(tm * tn, 1, splits),
-                     dim3(threads), 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu, tn, k_per_split);
+  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S>;
+  const int slots = fast_occupancy(kern, threads) * device_cu_count();
+  int grid = slots / (splits > 0 ? splits : 1);
+  if (grid > 8) grid &= ~7;  // a multiple of 8 keeps the per-XCD tile ranges
+  grid = grid < 1 ? 1 : (grid < tiles ? grid : tiles);
+  constexpr int VW = 16 / (int)sizeof(OutT);
+  const int vec_out = (ldc % VW) == 0 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+  hipLaunchKernelGGL(kern, dim3(grid, 1, splits), dim3(threads), 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu,
+                     tn, tiles, k_per_split, vec_out);
 }
 
 // Tile choice: the largest block tile that still gives every CU a tile.
@@ -313,9 +425,7 @@ void pick_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, c
                int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
   const int64_t t256x256 = ceil_div(M, 256) * ceil_div(N, 256) * splits;
   const int64_t t256x128 = ceil_div(M, 256) * ceil_div(N, 128) * splits;
-  // fp32 stores with bias would exceed 256 registers in the 256 x 256 tile
-  constexpr bool kWide = sizeof(OutT) == 2 || PARTIAL;
-  if (kWide && t256x256 >= 256)
+  if (t256x256 >= 256)
     // 32-wide k-tiles in four stages: three tiles of loads in flight
     launch_fast<256, 256, 128, 64, OutT, PARTIAL, 32, 4>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits,
                                                          k_per_split, s);

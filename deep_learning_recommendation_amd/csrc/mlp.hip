@@ -79,6 +79,258 @@ __global__ __launch_bounds__(256) void copy_bf16_kernel(const uint16_t* __restri
   out[(int64_t)r * ldo + c] = c < C ? in[(int64_t)r * ldi + c] : (uint16_t)0;
 }
 
+// ------------------------------------------------------------------ fused bottom MLP
+//
+// A three-layer bf16 network K0 (<= 16) -> 512 -> 256 -> 128 with ReLU after
+// the hidden layers (the bottom-MLP shape 13-512-256-128) in one kernel.  A
+// workgroup of eight waves owns 128 rows: it rounds its fp32 input rows to
+// bf16, keeps the 128 x 512 hidden activations and then the 128 x 256 ones
+// in LDS (bf16, the rounding points of the layer-by-layer path), and writes
+// only the fp32 output rows (and, for training, the bf16 activations the
+// backward pass reads).  Weights are read straight from global memory (L2
+// resident) as MFMA fragments, a few k-steps ahead.  As in the GEMM, the W
+// fragment is the first MFMA operand, so each lane owns one row and groups of
+// four consecutive columns; accumulators start from the bias.
+constexpr int kF3Rows = 128, kF3D1 = 512, kF3D2 = 256, kF3D3 = 128, kF3K0 = 16;
+constexpr int kF3Lds = kF3Rows * kF3D1 * 2;  // 128 KB: the first hidden layer, later the second
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8_t gld8(const uint16_t* p) {
+  return *(const __attribute__((address_space(1))) bf16x8_t*)(p);
+}
+// byte offset of 16-byte chunk c of row r in an LDS matrix with `cpr` chunks
+// per row; the chunk index is XOR-ed with the row's low four bits so that the
+// 16 rows one LDS cycle serves hit distinct banks
+__device__ __forceinline__ int f3_off(int r, int c, int cpr) { return (r * cpr + (c ^ (r & 15))) * 16; }
+
+// bias + optional ReLU, bf16 rounding and the cross-half swap of one 32 x 32
+// accumulator block: returns the two 16-byte chunks this lane owns, columns
+// 8*(l/32) .. +7 and 16 + 8*(l/32) .. +7 of the block
+__device__ __forceinline__ void f3_pack(const f32x16_t& a, bool relu, uint4& lo, uint4& hi) {
+  uint32_t pk[4][2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float v0 = a[4 * g + 2 * h], v1 = a[4 * g + 2 * h + 1];
+      if (relu) {
+        v0 = v0 > 0.f ? v0 : 0.f;
+        v1 = v1 > 0.f ? v1 : 0.f;
+      }
+      pk[g][h] = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto s01 = __builtin_amdgcn_permlane32_swap(pk[0][h], pk[1][h], false, false);
+    const auto s23 = __builtin_amdgcn_permlane32_swap(pk[2][h], pk[3][h], false, false);
+    pk[0][h] = s01[0];
+    pk[1][h] = s01[1];
+    pk[2][h] = s23[0];
+    pk[3][h] = s23[1];
+  }
+  lo = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);
+  hi = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);
+}
+
+// acc[tm][tn] += sum over K of W-fragments x LDS A-fragments; W rows
+// w_rows[tn] (already offset by this lane's 8 k), A rows in LDS with `cpr`
+// chunks per row.  The W fragments of the next P - 1 k-steps and the A
+// fragments of the next k-step are in flight during each step's MFMAs (the
+// scheduling barriers keep the loads ahead of the MFMAs).
+template <int TM, int TN, int KSTEPS, int P>
+__device__ __forceinline__ void f3_layer(f32x16_t (&acc)[TM][TN], const uint16_t* const (&w_rows)[TN],
+                                         const char* lds, int cpr, int row0, int r32, int half) {
+  static_assert(KSTEPS % P == 0, "whole prefetch rounds");
+  bf16x8_t wb[P][TN], af[2][TM];
+#pragma unroll
+  for (int p = 0; p < P - 1; ++p)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) wb[p][tn] = gld8(w_rows[tn] + p * 16);
+  auto read_a = [&](int ks, int buf) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int r = row0 + tm * 32 + r32;
+      af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(lds + f3_off(r, 2 * ks + half, cpr));
+    }
+  };
+  read_a(0, 0);
+  for (int ks0 = 0; ks0 < KSTEPS; ks0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int ks = ks0 + p;
+      const int ahead = ks + P - 1 < KSTEPS ? ks + P - 1 : KSTEPS - 1;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) wb[(p + P - 1) % P][tn] = gld8(w_rows[tn] + ahead * 16);
+      read_a(ks + 1 < KSTEPS ? ks + 1 : KSTEPS - 1, (p + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[p][tn], af[p & 1][tm], acc[tm][tn], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(512) void mlp3_fused_kernel(
+    const float* __restrict__ in, int64_t in_ld, int K0, int M, const uint16_t* __restrict__ W1, int64_t w1_ld,
+    const float* __restrict__ b1, const uint16_t* __restrict__ W2, int64_t w2_ld, const float* __restrict__ b2,
+    const uint16_t* __restrict__ W3, int64_t w3_ld, const float* __restrict__ b3, int relu3, float* __restrict__ out,
+    int64_t out_ld, int vec_out, uint16_t* __restrict__ act0, int64_t ld0, uint16_t* __restrict__ act1,
+    uint16_t* __restrict__ act2) {
+  extern __shared__ __attribute__((aligned(16))) char f3_smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
+  const int m0 = blockIdx.x * kF3Rows;
+  const int rowl = wm * 64 + r32;           // local row of block tm = 0
+
+  // ---- layer 1: K0 -> 512.  Wave tile 64 x 128, one k-step of 16.
+  {
+    bf16x8_t a1[2];
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int row = min(m0 + rowl + tm * 32, M - 1);
+      const float* src = in + (int64_t)row * in_ld;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = half * 8 + 2 * q;
+        const uint16_t lo = k < K0 ? f32_to_bf16(src[k]) : (uint16_t)0;
+        const uint16_t hi = k + 1 < K0 ? f32_to_bf16(src[k + 1]) : (uint16_t)0;
+        w[q] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      const uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
+      a1[tm] = *reinterpret_cast<const bf16x8_t*>(&u);
+      // the rounded input rows are layer 1's saved input (the first 4 waves store them)
+      if (act0 != nullptr && wn == 0 && m0 + rowl + tm * 32 < M && half * 8 < ld0)
+        *reinterpret_cast<uint4*>(act0 + (int64_t)(m0 + rowl + tm * 32) * ld0 + half * 8) = u;
+    }
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const float* bp = b1 + wn * 128 + tn * 32 + 4 * half;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float b = bp[8 * (v >> 2) + (v & 3)];
+        acc[0][tn][v] = b;
+        acc[1][tn][v] = b;
+      }
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      // W1 row, k = 8*half .. +7; columns at or past K0 read as zero
+      const uint16_t* wr = W1 + (int64_t)(wn * 128 + tn * 32 + r32) * w1_ld + half * 8;
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (half * 8 < K0) {
+        u = *reinterpret_cast<const uint4*>(wr);
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = half * 8 + 2 * q;
+          if (k >= K0) w[q] = 0u;
+          else if (k + 1 >= K0) w[q] &= 0xffffu;
+        }
+        u = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      const bf16x8_t wb = *reinterpret_cast<const bf16x8_t*>(&u);
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm) acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, a1[tm], acc[tm][tn], 0, 0, 0);
+    }
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        uint4 lo, hi;
+        f3_pack(acc[tm][tn], true, lo, hi);
+        const int r = rowl + tm * 32, c = (wn * 128 + tn * 32) / 8 + half;  // 16-byte chunk of the row
+        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c, 64)) = lo;
+        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c + 2, 64)) = hi;
+        if (act1 != nullptr && m0 + r < M) {
+          uint16_t* g = act1 + (int64_t)(m0 + r) * kF3D1 + c * 8;
+          *reinterpret_cast<uint4*>(g) = lo;
+          *reinterpret_cast<uint4*>(g + 16) = hi;
+        }
+      }
+  }
+  __syncthreads();
+
+  // ---- layer 2: 512 -> 256.  Wave tile 64 x 64, 32 k-steps.
+  {
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+      const float* bp = b2 + wn * 64 + tn * 32 + 4 * half;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float b = bp[8 * (v >> 2) + (v & 3)];
+        acc[0][tn][v] = b;
+        acc[1][tn][v] = b;
+      }
+    }
+    const uint16_t* const wr[2] = {W2 + (int64_t)(wn * 64 + r32) * w2_ld + half * 8,
+                                   W2 + (int64_t)(wn * 64 + 32 + r32) * w2_ld + half * 8};
+    f3_layer<2, 2, kF3D1 / 16, 8>(acc, wr, f3_smem, 64, wm * 64, r32, half);
+    __syncthreads();  // every wave is done reading the first hidden layer
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) {
+        uint4 lo, hi;
+        f3_pack(acc[tm][tn], true, lo, hi);
+        const int r = rowl + tm * 32, c = (wn * 64 + tn * 32) / 8 + half;
+        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c, 32)) = lo;
+        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c + 2, 32)) = hi;
+        if (act2 != nullptr && m0 + r < M) {
+          uint16_t* g = act2 + (int64_t)(m0 + r) * kF3D2 + c * 8;
+          *reinterpret_cast<uint4*>(g) = lo;
+          *reinterpret_cast<uint4*>(g + 16) = hi;
+        }
+      }
+  }
+  __syncthreads();
+
+  // ---- layer 3: 256 -> 128, fp32 out.  Wave tile 64 x 32, 16 k-steps.
+  {
+    f32x16_t acc[2][1];
+    {
+      const float* bp = b3 + wn * 32 + 4 * half;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float b = bp[8 * (v >> 2) + (v & 3)];
+        acc[0][0][v] = b;
+        acc[1][0][v] = b;
+      }
+    }
+    const uint16_t* const wr[1] = {W3 + (int64_t)(wn * 32 + r32) * w3_ld + half * 8};
+    f3_layer<2, 1, kF3D2 / 16, 8>(acc, wr, f3_smem, 32, wm * 64, r32, half);
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int row = m0 + rowl + tm * 32;
+      if (row >= M) continue;
+      float* o = out + (int64_t)row * out_ld + wn * 32 + 4 * half;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = acc[tm][0][4 * g + q];
+          if (relu3) v[q] = v[q] > 0.f ? v[q] : 0.f;
+        }
+        if (vec_out) {
+          *reinterpret_cast<float4*>(o + 8 * g) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[8 * g + q] = v[q];
+        }
+      }
+    }
+  }
+}
+
 template <typename YT>
 __device__ __forceinline__ bool positive(const YT* p);
 template <>
@@ -263,6 +515,35 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
       ld_src = ld_dst;
     }
     return rc;
+  }
+
+  // the bottom-MLP shape K0 (<= 16) -> 512 -> 256 -> 128 with aligned
+  // weights runs as one fused kernel
+  if (in_dtype == DLRM_F32 && L == 3 && dims[0] <= kF3K0 && dims[1] == kF3D1 && dims[2] == kF3D2 &&
+      dims[3] == kF3D3 && w_ld != nullptr) {
+    bool ok = true;
+    for (int l = 0; l < 3; ++l) ok = ok && aligned16(W[l]) && (w_ld[l] % 8) == 0;
+    if (ok) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+      static bool raised[64] = {false};
+      if (!raised[dev]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(mlp3_fused_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kF3Lds) != hipSuccess)
+          return DLRM_E_HIP;
+        raised[dev] = true;
+      }
+      const int vec_out = (out_ld % 4) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+      uint16_t* a0 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[0]) : nullptr;
+      uint16_t* a1 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[1]) : nullptr;
+      uint16_t* a2 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[2]) : nullptr;
+      hipLaunchKernelGGL(mlp3_fused_kernel, dim3((unsigned)ceil_div(B, kF3Rows)), dim3(512), kF3Lds, stream,
+                         static_cast<const float*>(in), in_ld, dims[0], M, static_cast<const uint16_t*>(W[0]),
+                         (int64_t)w_ld[0], bias[0], static_cast<const uint16_t*>(W[1]), (int64_t)w_ld[1], bias[1],
+                         static_cast<const uint16_t*>(W[2]), (int64_t)w_ld[2], bias[2],
+                         (int)(last_act == DLRM_ACT_RELU), out, out_ld, vec_out, a0, lay.act_ld[0], a1, a2);
+      return launch_status();
+    }
   }
 
   // bf16 network: an fp32 input is rounded once into the workspace; a bf16

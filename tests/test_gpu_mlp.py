@@ -169,3 +169,74 @@ def test_mlp_bf16_backward(which, B):
         assert rel(dWs[l].cpu().numpy(), rW[l]) <= 2e-2, (l, rel(dWs[l].cpu().numpy(), rW[l]))
         assert rel(dbs[l].cpu().numpy(), rb[l]) <= 2e-2, (l, rel(dbs[l].cpu().numpy(), rb[l]))
     assert rel(dX.cpu().numpy(), rX) <= 2e-2
+
+
+def _bf16_params(dims, seed):
+    """Glorot-normal weights stored as bf16 (their fp32 values), U(+-1/sqrt(fan_in)) biases."""
+    g = np.random.default_rng(seed)
+    out = []
+    for fi, fo in zip(dims[:-1], dims[1:]):
+        Wf = (g.standard_normal((fo, fi)) * np.sqrt(2.0 / (fi + fo))).astype(np.float32)
+        Wf = torch.from_numpy(Wf).to(torch.bfloat16).to(torch.float32).numpy()
+        b = g.uniform(-1 / np.sqrt(fi), 1 / np.sqrt(fi), fo).astype(np.float32)
+        out.append((Wf, None, b))
+    return out
+
+
+@pytest.mark.parametrize("K0,B,last_relu", [(13, 1000, True), (13, 128, False), (5, 257, True), (16, 3, True),
+                                            (1, 131, True), (9, 1, False)])
+def test_mlp_three_layer_bottom_shape(K0, B, last_relu):
+    """Networks K0 -> 512 -> 256 -> 128 (the bottom-MLP shape, which runs as
+    one fused kernel): ragged batches, narrow inputs, with and without the
+    last ReLU; with saved activations the output is bit-identical and the
+    backward from them matches the oracle."""
+    import deep_learning_recommendation_amd as D
+
+    dims = (K0, 512, 256, 128)
+    banner(f"mlp three-layer bottom shape K0={K0} B={B} relu={last_relu}")
+    params = _bf16_params(dims, 100 + K0 + B)
+    x = np.random.default_rng(K0 * 7 + B).lognormal(0, 1, (B, K0)).astype(np.float32)
+    mp = _mlp_dev(dims, params, True)
+    out, _, _ = _fwd(mp, x, last_relu)
+    ref, _, acts = oracle.mlp_fwd(x, [p[0] for p in params], [p[2] for p in params], True, last_relu, save_acts=True)
+    got = out.cpu().numpy()
+    err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert err <= 1e-2, err
+    assert np.max(np.abs(got - ref)) <= 2e-2 * max(1.0, np.abs(ref).max())
+    # saved activations: same output bits, and the backward reads them correctly
+    out_s, _, ws = _fwd(mp, x, last_relu, save=True)
+    assert torch.equal(out_s, out)
+    dY = np.random.default_rng(5).standard_normal((B, 128)).astype(np.float32) * 0.1
+    dW = [torch.empty((o, i), dtype=torch.float32, device=DEV) for i, o in zip(dims[:-1], dims[1:])]
+    db = [torch.empty((o,), dtype=torch.float32, device=DEV) for o in dims[1:]]
+    wsb = torch.empty((max(256, D.dlrm_mlp_bwd_workspace_size(B, dims)),), dtype=torch.uint8, device=DEV)
+    D.dlrm_mlp_bwd(B, dims, mp.Ws, mp.w_ld, D.DLRM_ACT_RELU if last_relu else D.DLRM_ACT_NONE, ws, out_s, 128,
+                   to_dev(dY), 128, dW, db, None, 0, wsb)
+    torch.cuda.synchronize()
+    rW, rb, _ = oracle.mlp_bwd([p[0] for p in params], acts, dY, last_relu)
+    for l in range(3):
+        g = dW[l].cpu().numpy()
+        assert np.linalg.norm(g - rW[l]) <= 2e-2 * max(np.linalg.norm(rW[l]), 1e-30), l
+
+
+def test_mlp_three_layer_bottom_shape_strided_output():
+    """Output rows with a leading dimension that is not a multiple of 4
+    (element stores) inside a wider buffer: the columns around the block
+    stay untouched."""
+    import deep_learning_recommendation_amd as D
+
+    dims, B, ld = (13, 512, 256, 128), 300, 131
+    banner("mlp three-layer bottom shape, strided output")
+    params = _bf16_params(dims, 7)
+    x = np.random.default_rng(8).lognormal(0, 1, (B, 13)).astype(np.float32)
+    mp = _mlp_dev(dims, params, True)
+    out = torch.full((B, ld), 7.0, dtype=torch.float32, device=DEV)
+    ws = torch.empty((max(256, D.dlrm_mlp_workspace_size(B, dims, mp.w_dtype, False)),), dtype=torch.uint8,
+                     device=DEV)
+    D.dlrm_mlp_fwd(to_dev(x), 13, B, dims, mp.Ws, mp.w_ld, mp.biases, mp.w_dtype, D.DLRM_ACT_RELU, out, ld, None,
+                   ws, False)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.mlp_fwd(x, [p[0] for p in params], [p[2] for p in params], True, True)
+    got = out.cpu().numpy()
+    assert np.all(got[:, 128:] == 7.0)
+    assert np.linalg.norm(got[:, :128] - ref) <= 1e-2 * np.linalg.norm(ref)
