@@ -83,43 +83,56 @@ __global__ __launch_bounds__(256) void copy_bf16_kernel(const uint16_t* __restri
 //
 // A three-layer bf16 network K0 (<= 16) -> 512 -> 256 -> 128 with ReLU after
 // the hidden layers (the bottom-MLP shape 13-512-256-128) in one kernel.  A
-// workgroup of eight waves owns 128 rows: it rounds its fp32 input rows to
-// bf16, keeps the 128 x 512 hidden activations and then the 128 x 256 ones
-// in LDS (bf16, the rounding points of the layer-by-layer path), and writes
-// only the fp32 output rows (and, for training, the bf16 activations the
-// backward pass reads).  Weights are read straight from global memory (L2
-// resident) as MFMA fragments, a few k-steps ahead.  As in the GEMM, the W
-// fragment is the first MFMA operand, so each lane owns one row and groups of
-// four consecutive columns; accumulators start from the bias.
+// workgroup of four waves (one per SIMD) owns 128 rows, each wave 32 of
+// them, and every activation of a wave's rows stays in its registers: with
+// the W fragment as the first MFMA operand, a lane holds one row and groups
+// of four consecutive output columns, and after bias, ReLU, bf16 rounding
+// and one cross-half lane swap (v_permlane32_swap) each lane holds eight
+// consecutive columns -- exactly the operand layout of the next layer's
+// MFMA (row l % 32, k = 8 * (l / 32) .. +7 of each 16-wide k-step).  The
+// rounding points are those of the layer-by-layer path (input, hidden
+// activations in bf16; fp32 accumulation; fp32 output).
+//
+// The weights of layers 2 and 3 stream through a ring of four 32 KB LDS
+// stages, loaded straight from global memory (global_load_lds_dwordx4,
+// coalesced rows): ten chunks, eight of W2 (64 k x 256 rows) and two of W3
+// (128 k x 128 rows), three in flight ahead of the one being used.  Layer
+// 1's weights (512 x K0) are read as fragments from global memory.  The
+// output rows are written in fp32; for training the bf16 input and hidden
+// activations the backward pass reads are written as well.
 constexpr int kF3Rows = 128, kF3D1 = 512, kF3D2 = 256, kF3D3 = 128, kF3K0 = 16;
-constexpr int kF3Lds = kF3Rows * kF3D1 * 2;  // 128 KB: the first hidden layer, later the second
+constexpr int kF3Stage = 32768, kF3Ring = 4 * kF3Stage;
+constexpr int kF3Lds = kF3Ring + 4096;  // the ring, then the three bias vectors (2 KB, 1 KB, 512 B)
+constexpr int kF3Chunks = 10;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ bf16x8_t gld8(const uint16_t* p) {
-  return *(const __attribute__((address_space(1))) bf16x8_t*)(p);
-}
-// byte offset of 16-byte chunk c of row r in an LDS matrix with `cpr` chunks
-// per row; the chunk index is XOR-ed with the row's low four bits so that the
-// 16 rows one LDS cycle serves hit distinct banks
-__device__ __forceinline__ int f3_off(int r, int c, int cpr) { return (r * cpr + (c ^ (r & 15))) * 16; }
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// bias + optional ReLU, bf16 rounding and the cross-half swap of one 32 x 32
-// accumulator block: returns the two 16-byte chunks this lane owns, columns
-// 8*(l/32) .. +7 and 16 + 8*(l/32) .. +7 of the block
+// row pieces (16 bytes) of chunk c: W2 rows hold 64 k (8 pieces), W3 rows
+// 128 k (16); a row's pieces are XOR-swizzled so that the 16 lanes one LDS
+// cycle serves (16 consecutive rows, one logical piece) hit distinct banks
+__device__ __forceinline__ int f3_cpr(int c) { return c < 8 ? 8 : 16; }
+__device__ __forceinline__ int f3_swz(int row, int cpr) { return cpr == 8 ? ((row >> 1) & 7) : (row & 15); }
+
+// bf16 rounding, optional ReLU and the cross-half swap of one 32 x 32
+// accumulator block: lo = columns 8*(l/32) .. +7, hi = columns 16 + 8*(l/32)
+// .. +7.  The ReLU acts on the rounded pair (a sign test: negative values
+// and -0 become +0), which equals rounding the ReLU output for every
+// non-NaN value.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t p) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, p), s16x2{0, 0}));
+}
 __device__ __forceinline__ void f3_pack(const f32x16_t& a, bool relu, uint4& lo, uint4& hi) {
   uint32_t pk[4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float v0 = a[4 * g + 2 * h], v1 = a[4 * g + 2 * h + 1];
-      if (relu) {
-        v0 = v0 > 0.f ? v0 : 0.f;
-        v1 = v1 > 0.f ? v1 : 0.f;
-      }
-      pk[g][h] = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+      const uint32_t p = pack_bf16x2(a[4 * g + 2 * h], a[4 * g + 2 * h + 1]);
+      pk[g][h] = relu ? relu_bf16x2(p) : p;
     }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -134,199 +147,242 @@ __device__ __forceinline__ void f3_pack(const f32x16_t& a, bool relu, uint4& lo,
   hi = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);
 }
 
-// acc[tm][tn] += sum over K of W-fragments x LDS A-fragments; W rows
-// w_rows[tn] (already offset by this lane's 8 k), A rows in LDS with `cpr`
-// chunks per row.  The W fragments of the next P - 1 k-steps and the A
-// fragments of the next k-step are in flight during each step's MFMAs (the
-// scheduling barriers keep the loads ahead of the MFMAs).
-template <int TM, int TN, int KSTEPS, int P>
-__device__ __forceinline__ void f3_layer(f32x16_t (&acc)[TM][TN], const uint16_t* const (&w_rows)[TN],
-                                         const char* lds, int cpr, int row0, int r32, int half) {
-  static_assert(KSTEPS % P == 0, "whole prefetch rounds");
-  bf16x8_t wb[P][TN], af[2][TM];
+// accumulators of one 32 x 32 block start from the bias (in LDS): register
+// v is column col0 + 8*(v/4) + 4*(l/32) + v%4
+__device__ __forceinline__ void f3_bias(f32x16_t& acc, const char* b, int col0, int half) {
 #pragma unroll
-  for (int p = 0; p < P - 1; ++p)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) wb[p][tn] = gld8(w_rows[tn] + p * 16);
-  auto read_a = [&](int ks, int buf) {
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int r = row0 + tm * 32 + r32;
-      af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(lds + f3_off(r, 2 * ks + half, cpr));
-    }
-  };
-  read_a(0, 0);
-  for (int ks0 = 0; ks0 < KSTEPS; ks0 += P) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int ks = ks0 + p;
-      const int ahead = ks + P - 1 < KSTEPS ? ks + P - 1 : KSTEPS - 1;
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) wb[(p + P - 1) % P][tn] = gld8(w_rows[tn] + ahead * 16);
-      read_a(ks + 1 < KSTEPS ? ks + 1 : KSTEPS - 1, (p + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[p][tn], af[p & 1][tm], acc[tm][tn], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int g = 0; g < 4; ++g) {
+    const float4 v = *reinterpret_cast<const float4*>(b + (col0 + 8 * g + 4 * half) * 4);
+    acc[4 * g] = v.x;
+    acc[4 * g + 1] = v.y;
+    acc[4 * g + 2] = v.z;
+    acc[4 * g + 3] = v.w;
   }
 }
 
-__global__ __launch_bounds__(512) void mlp3_fused_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp3_fused_kernel(
     const float* __restrict__ in, int64_t in_ld, int K0, int M, const uint16_t* __restrict__ W1, int64_t w1_ld,
     const float* __restrict__ b1, const uint16_t* __restrict__ W2, int64_t w2_ld, const float* __restrict__ b2,
     const uint16_t* __restrict__ W3, int64_t w3_ld, const float* __restrict__ b3, int relu3, float* __restrict__ out,
     int64_t out_ld, int vec_out, uint16_t* __restrict__ act0, int64_t ld0, uint16_t* __restrict__ act1,
     uint16_t* __restrict__ act2) {
-  extern __shared__ __attribute__((aligned(16))) char f3_smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ __attribute__((aligned(1024))) char f3_smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, half = lane >> 5;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
-  const int m0 = blockIdx.x * kF3Rows;
-  const int rowl = wm * 64 + r32;           // local row of block tm = 0
+  const int row = blockIdx.x * kF3Rows + wave * 32 + r32;  // this lane's row (all layers)
+  const bool row_ok = row < M;
 
-  // ---- layer 1: K0 -> 512.  Wave tile 64 x 128, one k-step of 16.
+  // chunk c of the weight ring into stage c % 4: 32 instructions of 1 KB,
+  // eight per wave; instruction j of wave w fills rows (8w + j) * (64 / cpr) ..
+  auto issue = [&](int c) {
+    char* st = f3_smem + (c & 3) * kF3Stage;
+    const int cpr = f3_cpr(c), rpi = 64 / cpr;
+    const uint16_t* base = c < 8 ? W2 : W3;
+    const int64_t ld = c < 8 ? w2_ld : w3_ld;
+    const int k0 = c < 8 ? c * 64 : (c - 8) * 128;
+    const int lrow = lane / cpr, lpc = lane % cpr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = (wave * 8 + j) * rpi + lrow;
+      lds_dma16_opaque(base + (int64_t)n * ld + k0 + (lpc ^ f3_swz(n, cpr)) * 8, st + (wave * 8 + j) * 1024);
+    }
+  };
+  // the B fragments of k-step ks of chunk c for output blocks tn0 .. tn0+TN-1
+  auto read_b = [&](int c, int ks, bf16x8_t* fb, int tn0, int TN) {
+    const char* st = f3_smem + (c & 3) * kF3Stage;
+    const int cpr = f3_cpr(c);
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int tn = tn0 + t;
+      const int n = tn * 32 + r32;
+      fb[t] = *reinterpret_cast<const bf16x8_t*>(st + n * cpr * 16 + (((2 * ks + half) ^ f3_swz(n, cpr)) * 16));
+    }
+  };
+  // wait until at most `younger` chunks issued after the awaited one are still in flight
+  auto wait_younger = [&](int younger) {
+    if (younger >= 4) wait_vmcnt<32>();
+    else if (younger == 3) wait_vmcnt<24>();
+    else if (younger == 2) wait_vmcnt<16>();
+    else if (younger == 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+  };
+
+  // bias vectors into LDS first (one 1 KB instruction per wave; lanes past
+  // the end of b3 re-read its start into the padding)
   {
-    bf16x8_t a1[2];
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
-      const int row = min(m0 + rowl + tm * 32, M - 1);
-      const float* src = in + (int64_t)row * in_ld;
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = half * 8 + 2 * q;
-        const uint16_t lo = k < K0 ? f32_to_bf16(src[k]) : (uint16_t)0;
-        const uint16_t hi = k + 1 < K0 ? f32_to_bf16(src[k + 1]) : (uint16_t)0;
-        w[q] = (uint32_t)lo | ((uint32_t)hi << 16);
-      }
-      const uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
-      a1[tm] = *reinterpret_cast<const bf16x8_t*>(&u);
-      // the rounded input rows are layer 1's saved input (the first 4 waves store them)
-      if (act0 != nullptr && wn == 0 && m0 + rowl + tm * 32 < M && half * 8 < ld0)
-        *reinterpret_cast<uint4*>(act0 + (int64_t)(m0 + rowl + tm * 32) * ld0 + half * 8) = u;
-    }
-    f32x16_t acc[2][4];
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-      const float* bp = b1 + wn * 128 + tn * 32 + 4 * half;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float b = bp[8 * (v >> 2) + (v & 3)];
-        acc[0][tn][v] = b;
-        acc[1][tn][v] = b;
-      }
-    }
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-      // W1 row, k = 8*half .. +7; columns at or past K0 read as zero
-      const uint16_t* wr = W1 + (int64_t)(wn * 128 + tn * 32 + r32) * w1_ld + half * 8;
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (half * 8 < K0) {
-        u = *reinterpret_cast<const uint4*>(wr);
-        uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int k = half * 8 + 2 * q;
-          if (k >= K0) w[q] = 0u;
-          else if (k + 1 >= K0) w[q] &= 0xffffu;
-        }
-        u = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      const bf16x8_t wb = *reinterpret_cast<const bf16x8_t*>(&u);
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm) acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, a1[tm], acc[tm][tn], 0, 0, 0);
-    }
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        uint4 lo, hi;
-        f3_pack(acc[tm][tn], true, lo, hi);
-        const int r = rowl + tm * 32, c = (wn * 128 + tn * 32) / 8 + half;  // 16-byte chunk of the row
-        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c, 64)) = lo;
-        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c + 2, 64)) = hi;
-        if (act1 != nullptr && m0 + r < M) {
-          uint16_t* g = act1 + (int64_t)(m0 + r) * kF3D1 + c * 8;
-          *reinterpret_cast<uint4*>(g) = lo;
-          *reinterpret_cast<uint4*>(g + 16) = hi;
-        }
-      }
+    char* ba = f3_smem + kF3Ring;
+    const int off = wave * 1024 + lane * 16;
+    const float* src = off < 2048 ? b1 + off / 4 : off < 3072 ? b2 + (off - 2048) / 4 : off < 3584 ? b3 + (off - 3072) / 4 : b3;
+    lds_dma16_opaque(src, ba + wave * 1024);
   }
-  __syncthreads();
-
-  // ---- layer 2: 512 -> 256.  Wave tile 64 x 64, 32 k-steps.
+  // ---- operands of layer 1 in registers: this lane's input row (k = 8*(l/32)
+  // .. +7, bf16) and the W1 fragments of the 16 output blocks (rows 32b + l%32,
+  // the same k; columns at or past K0 read as zero).  Branch-free, so that
+  // every load is in flight at once: out-of-range positions re-read an
+  // in-range one and are masked afterwards.
+  float x[8];
   {
-    f32x16_t acc[2][2];
+    const float* src = in + (int64_t)(row_ok ? row : M - 1) * in_ld;
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
-      const float* bp = b2 + wn * 64 + tn * 32 + 4 * half;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float b = bp[8 * (v >> 2) + (v & 3)];
-        acc[0][tn][v] = b;
-        acc[1][tn][v] = b;
-      }
+    for (int q = 0; q < 8; ++q) {
+      const int k = half * 8 + q;
+      x[q] = src[k < K0 ? k : K0 - 1];
     }
-    const uint16_t* const wr[2] = {W2 + (int64_t)(wn * 64 + r32) * w2_ld + half * 8,
-                                   W2 + (int64_t)(wn * 64 + 32 + r32) * w2_ld + half * 8};
-    f3_layer<2, 2, kF3D1 / 16, 8>(acc, wr, f3_smem, 64, wm * 64, r32, half);
-    __syncthreads();  // every wave is done reading the first hidden layer
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
-        uint4 lo, hi;
-        f3_pack(acc[tm][tn], true, lo, hi);
-        const int r = rowl + tm * 32, c = (wn * 64 + tn * 32) / 8 + half;
-        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c, 32)) = lo;
-        *reinterpret_cast<uint4*>(f3_smem + f3_off(r, c + 2, 32)) = hi;
-        if (act2 != nullptr && m0 + r < M) {
-          uint16_t* g = act2 + (int64_t)(m0 + r) * kF3D2 + c * 8;
-          *reinterpret_cast<uint4*>(g) = lo;
-          *reinterpret_cast<uint4*>(g + 16) = hi;
-        }
-      }
   }
-  __syncthreads();
-
-  // ---- layer 3: 256 -> 128, fp32 out.  Wave tile 64 x 32, 16 k-steps.
-  {
-    f32x16_t acc[2][1];
-    {
-      const float* bp = b3 + wn * 32 + 4 * half;
+  uint4 w1f[kF3D1 / 32];
+  const int w1k = half * 8 < K0 ? half * 8 : 0;  // an in-range start for lanes whose k is all masked
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float b = bp[8 * (v >> 2) + (v & 3)];
-        acc[0][0][v] = b;
-        acc[1][0][v] = b;
+  for (int b = 0; b < kF3D1 / 32; ++b)
+    w1f[b] = *reinterpret_cast<const uint4*>(W1 + (int64_t)(b * 32 + r32) * w1_ld + w1k);
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+  uint32_t win[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k = half * 8 + 2 * q;
+    const uint32_t lo = k < K0 ? (uint32_t)f32_to_bf16(x[2 * q]) : 0u;
+    const uint32_t hi = k + 1 < K0 ? (uint32_t)f32_to_bf16(x[2 * q + 1]) : 0u;
+    win[q] = lo | (hi << 16);
+  }
+#pragma unroll
+  for (int b = 0; b < kF3D1 / 32; ++b) {
+    uint32_t x[4] = {w1f[b].x, w1f[b].y, w1f[b].z, w1f[b].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = half * 8 + 2 * q;
+      x[q] = k >= K0 ? 0u : (k + 1 >= K0 ? (x[q] & 0xffffu) : x[q]);
+    }
+    w1f[b] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+  // the plain loads and the bias vectors have landed before any chunk is
+  // issued, so no later wait of the compiler's covers a chunk
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  issue(0);
+  issue(1);
+  issue(2);
+  issue(3);
+  const char* bias1 = f3_smem + kF3Ring;
+  const char* bias2 = bias1 + 2048;
+  const char* bias3 = bias1 + 3072;
+
+  // ---- layer 1: K0 -> 512, 16 output blocks of 32 columns, one k-step
+  uint4 h1[32];  // bf16 layer-1 activations in layer-2 operand order (k-step s = h1[s])
+  {
+    const uint4 ua = make_uint4(win[0], win[1], win[2], win[3]);
+    if (act0 != nullptr && row_ok && half * 8 < ld0) *reinterpret_cast<uint4*>(act0 + (int64_t)row * ld0 + half * 8) = ua;
+    const bf16x8_t a1 = as_bf16x8(ua);
+    // four blocks at a time, so that four independent MFMA and packing
+    // chains interleave
+#pragma unroll
+    for (int b0 = 0; b0 < kF3D1 / 32; b0 += 4) {
+      f32x16_t acc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f3_bias(acc[j], bias1, (b0 + j) * 32, half);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w1f[b0 + j]), a1, acc[j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f3_pack(acc[j], true, h1[2 * (b0 + j)], h1[2 * (b0 + j) + 1]);
+    }
+    if (act1 != nullptr && row_ok) {
+      uint16_t* g = act1 + (int64_t)row * kF3D1 + 8 * half;
+#pragma unroll
+      for (int b = 0; b < kF3D1 / 32; ++b) {
+        *reinterpret_cast<uint4*>(g + b * 32) = h1[2 * b];
+        *reinterpret_cast<uint4*>(g + b * 32 + 16) = h1[2 * b + 1];
       }
     }
-    const uint16_t* const wr[1] = {W3 + (int64_t)(wn * 32 + r32) * w3_ld + half * 8};
-    f3_layer<2, 1, kF3D2 / 16, 8>(acc, wr, f3_smem, 32, wm * 64, r32, half);
+  }
+
+  // ---- layer 2: 512 -> 256 (chunks 0 .. 7, four k-steps each, 8 output blocks)
+  f32x16_t acc2[8];
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
-      const int row = m0 + rowl + tm * 32;
-      if (row >= M) continue;
-      float* o = out + (int64_t)row * out_ld + wn * 32 + 4 * half;
+  for (int tn = 0; tn < 8; ++tn) f3_bias(acc2[tn], bias2, tn * 32, half);
+  bf16x8_t fb[2][8];
+  wait_younger(3);  // chunk 0
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  read_b(0, 0, fb[0], 0, 8);
+  int buf = 0;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v[4];
+  for (int c = 0; c < 8; ++c) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = acc[tm][0][4 * g + q];
-          if (relu3) v[q] = v[q] > 0.f ? v[q] : 0.f;
-        }
-        if (vec_out) {
-          *reinterpret_cast<float4*>(o + 8 * g) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) o[8 * g + q] = v[q];
-        }
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) {
+        read_b(c, ks + 1, fb[buf ^ 1], 0, 8);
+      } else {
+        // hand-over to chunk c+1: after the barrier every wave's reads of
+        // chunk c are done, so chunk c+4 can load into its stage.  Layer 3
+        // starts with both of its chunks resident.
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        wait_younger(c < 7 ? (7 - c < 2 ? 7 - c : 2) : 0);
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        if (c + 4 < kF3Chunks) issue(c + 4);
+        if (c < 7) read_b(c + 1, 0, fb[buf ^ 1], 0, 8);
+        else read_b(8, 0, fb[buf ^ 1], 0, 2);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8_t a = as_bf16x8(h1[c * 4 + ks]);
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn) acc2[tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][tn], a, acc2[tn], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      buf ^= 1;
+    }
+  }
+  // layer 2's activations become layer 3's operands
+  uint4 h2[16];
+#pragma unroll
+  for (int tn = 0; tn < 8; ++tn) f3_pack(acc2[tn], true, h2[2 * tn], h2[2 * tn + 1]);
+  if (act2 != nullptr && row_ok) {
+    uint16_t* g = act2 + (int64_t)row * kF3D2 + 8 * half;
+#pragma unroll
+    for (int tn = 0; tn < 8; ++tn) {
+      *reinterpret_cast<uint4*>(g + tn * 32) = h2[2 * tn];
+      *reinterpret_cast<uint4*>(g + tn * 32 + 16) = h2[2 * tn + 1];
+    }
+  }
+
+  // ---- layer 3: 256 -> 128 in two halves of 64 columns (chunks 8 and 9
+  // hold k 0-127 and 128-255); each half's fp32 rows are stored while the
+  // next half computes
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x16_t acc3[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f3_bias(acc3[j], bias3, (2 * hf + j) * 32, half);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks < 15) read_b(8 + ((ks + 1) >> 3), (ks + 1) & 7, fb[buf ^ 1], 2 * hf, 2);
+      else if (hf == 0) read_b(8, 0, fb[buf ^ 1], 2, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8_t a = as_bf16x8(h2[ks]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc3[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], a, acc3[j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      buf ^= 1;
+    }
+    if (row_ok) {
+      float* o = out + (int64_t)row * out_ld + 4 * half;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] = acc3[j][4 * g + q];
+            if (relu3) v[q] = v[q] > 0.f ? v[q] : 0.f;
+          }
+          float* d = o + (2 * hf + j) * 32 + 8 * g;
+          if (vec_out) {
+            *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) d[q] = v[q];
+          }
+        }
     }
   }
 }
@@ -522,7 +578,7 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
   if (in_dtype == DLRM_F32 && L == 3 && dims[0] <= kF3K0 && dims[1] == kF3D1 && dims[2] == kF3D2 &&
       dims[3] == kF3D3 && w_ld != nullptr) {
     bool ok = true;
-    for (int l = 0; l < 3; ++l) ok = ok && aligned16(W[l]) && (w_ld[l] % 8) == 0;
+    for (int l = 0; l < 3; ++l) ok = ok && aligned16(W[l]) && aligned16(bias[l]) && (w_ld[l] % 8) == 0;
     if (ok) {
       int dev = 0;
       if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -537,7 +593,7 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
       uint16_t* a0 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[0]) : nullptr;
       uint16_t* a1 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[1]) : nullptr;
       uint16_t* a2 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[2]) : nullptr;
-      hipLaunchKernelGGL(mlp3_fused_kernel, dim3((unsigned)ceil_div(B, kF3Rows)), dim3(512), kF3Lds, stream,
+      hipLaunchKernelGGL(mlp3_fused_kernel, dim3((unsigned)ceil_div(B, kF3Rows)), dim3(256), kF3Lds, stream,
                          static_cast<const float*>(in), in_ld, dims[0], M, static_cast<const uint16_t*>(W[0]),
                          (int64_t)w_ld[0], bias[0], static_cast<const uint16_t*>(W[1]), (int64_t)w_ld[1], bias[1],
                          static_cast<const uint16_t*>(W[2]), (int64_t)w_ld[2], bias[2],
