@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--workload", default="forward", choices=["forward", "embbag", "interaction", "train", "tiny"])
     p.add_argument("--batches", type=int, default=2, help="distinct input batches rotated over the steps")
     p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "two-call"],
+                   help="pooled lookup + interaction: one fused call, two calls (X materialised), or auto (fused "
+                        "for short bags)")
     p.add_argument("--chain", action="store_true",
                    help="training workload only: the whole backward from the BCE loss (top MLP input gradient, "
                         "interaction backward, bottom MLP and sparse update from the real X gradient) instead of "
@@ -215,7 +218,11 @@ def main():
     if w.bottom:
         bp = PL.make_mlp(w.bottom, [p[0] for p in bottom], [p[2] for p in bottom], bf16)
         tp = PL.make_mlp(w.top, [p[0] for p in top], [p[2] for p in top], bf16)
-        model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=w.train, fused=not args.chain)
+        fused = {"auto": "auto", "fused": True, "two-call": False}[args.path]
+        if args.chain and fused is True:
+            print("--chain needs X: use --path auto or two-call", file=sys.stderr)
+            sys.exit(1)
+        model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=w.train, fused=fused)
         if w.train:
             model.sparse_workspace(max(b[5] for b in dbatches))
     else:
@@ -249,9 +256,15 @@ def main():
         D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
                        model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.x0, model.x0_ld, None,
                        model.ws_bot, w.train)
-        mark("embbag_interact")
-        D.dlrm_embbag_interact_fwd(model.x0, model.x0_ld, model.table_ptrs, w.K, d, idx, off, w.B, model.top_in,
-                                   model.top_ld)
+        if model.use_fused(nnz):
+            mark("embbag_interact")
+            D.dlrm_embbag_interact_fwd(model.x0, model.x0_ld, model.table_ptrs, w.K, d, idx, off, w.B, model.top_in,
+                                       model.top_ld)
+        else:
+            mark("embbag")
+            D.dlrm_embbag_fwd(model.table_ptrs, w.K, d, idx, off, w.B, model.X, n * d, d)
+            mark("interact")
+            D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
         mark("top_mlp")
         D.dlrm_mlp_fwd(model.top_in, model.top_ld, w.B, model.top.dims, model.top.Ws, model.top.w_ld,
                        model.top.biases, model.top.w_dtype, D.DLRM_ACT_NONE, model.logit, 1, model.prob,
@@ -316,7 +329,7 @@ def main():
     value = w.B * args.steps / elapsed
     breakdown = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in call_t.items()}
     nnz_mean = float(np.mean([b[5] for b in dbatches]))
-    if model is None or args.chain:
+    if model is None or "embbag" in breakdown:
         kname, key = "embbag_fwd_kernel", None
         gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean)
         g_ms = gather_t.mean_ms() if model is None else breakdown["embbag"]

@@ -8,8 +8,12 @@ Forward ([SU] "briansu.co DLRM", How it works and Key equations):
   2. dlrm_embbag_fwd        bags of K tables -> X[:, 1..K, :]     (fp32)
   3. dlrm_interact_fwd      X -> [x_dense, tril(X X^T)]           (bf16 row)
   4. dlrm_mlp_fwd(top)      -> logit, sigmoid(logit)
-With ``fused`` (the default) steps 2 and 3 are one dlrm_embbag_interact_fwd
-call and X never goes to memory; without it x_dense is row 0 of X.
+With ``fused=True`` steps 2 and 3 are one dlrm_embbag_interact_fwd call and
+X never goes to memory; with ``fused=False`` x_dense is row 0 of X and the
+two calls run separately.  ``fused="auto"`` (the default) keeps X and picks
+per batch: the fused call for short bags, where the lookups are latency-bound
+and skipping X's write and re-read pays, the two calls for long bags, where
+the standalone lookup keeps more rows in flight (measured crossover below).
 Training step (sum-pooled tables, row-wise SGD):
   forward with saved activations, dlrm_bce_grad, dlrm_mlp_bwd(top),
   dlrm_mlp_bwd(bottom) seeded by the X row-0 gradient, and
@@ -56,22 +60,28 @@ def make_mlp(dims, weights, biases, bf16: bool, device="cuda") -> MLPParams:
     return MLPParams(tuple(int(x) for x in dims), Ws, lds, bs, C.DLRM_BF16 if bf16 else C.DLRM_F32)
 
 
+# Mean bag length up to which "auto" takes the fused lookup + interaction.
+AUTO_FUSED_MAX_MEAN_BAG = 2.0
+
+
 class DLRM:
     """Device state and call sequence for one batch size."""
 
     def __init__(self, B: int, K: int, d: int, rows, tables, bottom: MLPParams, top: MLPParams, train: bool = False,
-                 device="cuda", fused: bool = True):
+                 device="cuda", fused="auto"):
         self.B, self.K, self.d, self.n = B, K, d, K + 1
         self.rows = [int(r) for r in rows]
         self.tables = tables
         self.table_ptrs = C.device_pointer_array(tables)
         self.bottom, self.top = bottom, top
         self.train = train
+        if fused not in (True, False, "auto"):
+            raise ValueError("fused must be True, False or 'auto'")
         self.fused = fused
         n, dev = self.n, device
         self.P = n * (n - 1) // 2
         self.top_w = d + self.P
-        if fused:
+        if fused is True:
             self.X = None
             self.x0 = torch.empty((B, d), dtype=torch.float32, device=dev)
             self.x0_ld = d
@@ -98,7 +108,7 @@ class DLRM:
             self.db_top = [torch.empty((o,), dtype=torch.float32, device=dev) for o in top.dims[1:]]
             self.dlogit = torch.empty((B,), dtype=torch.float32, device=dev)
             self.ws_sparse = None
-            if not fused:  # full backward chain: gradient of the top input row, then of X
+            if fused is not True:  # full backward chain: gradient of the top input row, then of X
                 self.g_top = torch.empty((B, self.top_w), dtype=torch.float32, device=dev)
                 self.G = torch.empty((B, n, d), dtype=torch.float32, device=dev)
 
@@ -106,13 +116,19 @@ class DLRM:
     def _ws(nbytes: int):
         return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device="cuda")
 
+    def use_fused(self, nnz: int) -> bool:
+        """Whether a batch of nnz lookups takes the fused lookup + interaction."""
+        if self.fused == "auto":
+            return nnz <= AUTO_FUSED_MAX_MEAN_BAG * self.K * self.B
+        return bool(self.fused)
+
     def forward(self, dense, indices, offsets, stream=None):
         B, n, d = self.B, self.n, self.d
         save = self.train
         C.dlrm_mlp_fwd(dense, dense.shape[1], B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld,
                        self.bottom.biases, self.bottom.w_dtype, C.DLRM_ACT_RELU, self.x0, self.x0_ld, None,
                        self.ws_bot, save, stream)
-        if self.fused:
+        if self.use_fused(indices.numel()):
             C.dlrm_embbag_interact_fwd(self.x0, self.x0_ld, self.table_ptrs, self.K, d, indices, offsets, B,
                                        self.top_in, self.top_ld, stream)
         else:
@@ -144,9 +160,12 @@ class DLRM:
         """The whole training backward from the loss: BCE seed, top MLP (with
         the gradient of its input row), interaction backward to the gradient
         of X, then the bottom MLP from row 0 and the sparse SGD update from
-        rows 1..K.  Needs the materialised X (fused=False)."""
-        if self.fused or not self.train:
-            raise ValueError("backward_chain needs a training model built with fused=False")
+        rows 1..K.  Needs X (a model built with fused=False or "auto") and
+        the two-call forward of this batch."""
+        if self.fused is True or not self.train:
+            raise ValueError("backward_chain needs a training model built with fused=False or 'auto'")
+        if self.use_fused(indices.numel()):
+            raise ValueError("backward_chain needs X: this batch's forward took the fused path")
         B, n, d = self.B, self.n, self.d
         C.dlrm_bce_grad(self.logit, 1, labels, B, self.dlogit, stream)
         C.dlrm_mlp_bwd(B, self.top.dims, self.top.Ws, self.top.w_ld, C.DLRM_ACT_NONE, self.ws_top, self.logit, 1,

@@ -149,3 +149,17 @@ def test_train_full_backward_chain_scaled():
     for l in range(len(rW)):
         g = model.dW_bot[l].cpu().numpy()
         assert np.linalg.norm(g - rW[l]) <= 2e-2 * np.linalg.norm(rW[l]), l
+
+
+@pytest.mark.parametrize("name,expect_fused", [("forward", True), ("interaction", False), ("train", False)])
+def test_forward_auto_path(name, expect_fused):
+    """fused="auto" takes the fused call for one-index bags and the two calls
+    for longer bags; either way the logits equal the explicit path's bits."""
+    w = W.get(name).scaled(B=700, rows=8_000)
+    banner(f"forward auto path {name}")
+    auto, _, _ = device_model(w, fused="auto")
+    dense, idx, off = _forward(w, auto)
+    assert auto.use_fused(int(off[-1])) == expect_fused
+    ref, _, _ = device_model(w, tables=auto.tables, fused=expect_fused)
+    _forward(w, ref)
+    assert np.array_equal(auto.logit.cpu().numpy().view(np.uint32), ref.logit.cpu().numpy().view(np.uint32))
