@@ -60,17 +60,18 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
 // registers, one cross-half lane swap (v_permlane32_swap) gives each lane
 // eight consecutive columns, and every store is 16 bytes.
 //
-// The kernel is persistent: a grid of at most (resident workgroups per CU x
-// CUs) walks the tiles, and the first k-tiles of the next tile are already
-// loading into LDS while the epilogue of the current tile runs.  Tiles are
-// walked N-fastest; with a grid and tile count divisible by 8, each XCD
-// (workgroup b runs on XCD b % 8) takes one contiguous range of tiles, so
-// the tiles that share an A panel share one L2.
+// With PERSIST a grid of at most (resident workgroups per CU x CUs) walks
+// the tiles, and the first k-tiles of the next tile load into LDS while the
+// epilogue of the current tile runs; without it each workgroup takes one
+// tile (measured 2-4% faster on the MLP shapes, so that is what the MLPs
+// use).  Tiles are walked N-fastest; with a grid and tile count divisible by
+// 8, each XCD (workgroup b runs on XCD b % 8) takes one contiguous range of
+// tiles, so the tiles that share an A panel share one L2.
 // Waves per SIMD the register budget allows: wave tiles of 128 x 128 keep
 // 256 accumulators and run one wave per SIMD, smaller ones two.
 constexpr int fast_waves_per_eu(int WM, int WN) { return WM * WN > 128 * 64 ? 1 : 2; }
 
-template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S>
+template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S, bool PERSIST>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(fast_waves_per_eu(WM, WN)))) void gemm_bf16_fast_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, OutT* __restrict__ C, int64_t ldc, int M, int N, int K, int relu, int tiles_n,
@@ -290,7 +291,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
       mfmas(LAST);
     }
 
-    const int next = tile + stride;
+    const int next = PERSIST ? tile + stride : end;
     if (next < end) {
       // every wave's LDS reads of this tile are done: the next tile's first
       // k-tiles load while this tile's epilogue runs
@@ -402,17 +403,20 @@ int fast_occupancy(Kern kern, int threads) {
   return cached;
 }
 
-template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2>
+template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2, bool PERSIST = false>
 void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
                  int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int tiles = tm * tn;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S>;
-  const int slots = fast_occupancy(kern, threads) * device_cu_count();
-  int grid = slots / (splits > 0 ? splits : 1);
-  if (grid > 8) grid &= ~7;  // a multiple of 8 keeps the per-XCD tile ranges
-  grid = grid < 1 ? 1 : (grid < tiles ? grid : tiles);
+  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S, PERSIST>;
+  int grid = tiles;
+  if constexpr (PERSIST) {
+    const int slots = fast_occupancy(kern, threads) * device_cu_count();
+    grid = slots / (splits > 0 ? splits : 1);
+    if (grid > 8) grid &= ~7;  // a multiple of 8 keeps the per-XCD tile ranges
+    grid = grid < 1 ? 1 : (grid < tiles ? grid : tiles);
+  }
   constexpr int VW = 16 / (int)sizeof(OutT);
   const int vec_out = (ldc % VW) == 0 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
   hipLaunchKernelGGL(kern, dim3(grid, 1, splits), dim3(threads), 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu,
