@@ -33,8 +33,10 @@ constexpr int SCAN_TILE = 256 * SCAN_ITEMS;
 constexpr int kHot = 128;              // occurrences from which a segment is "hot"
 constexpr int kHotBlocks = 256;        // persistent blocks of the hot kernel (one per CU)
 constexpr int kHB = 64;                // occurrences per LDS ring slot
-constexpr int kSlots = 8;              // ring slots (8 x 64 x 64 x 4 B = 128 KB)
-constexpr int kLoaders = 7;            // loader waves per hot block (plus one adder)
+constexpr int kSlots = 8;              // ring slots
+constexpr int kRS = kHB + 4;           // floats per column row of a slot (padded: conflict-free 16-byte reads)
+constexpr int kLoaders = 6;            // loader waves per hot block (plus one adder)
+constexpr int kAdder = 3;              // the adder's wave index: alone on its SIMD when waves go round-robin
 constexpr int kLightBlocks = 2048;
 
 // ------------------------------------------------------------------ keys
@@ -318,18 +320,21 @@ __device__ __forceinline__ void lds_store(int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Hot segments.  A block (8 waves) takes (segment, 64-column slice) items
-// from a global counter.  Wave 0 is the adder: lane j owns column j of the
+// Hot segments.  A block (7 waves) takes (segment, 64-column slice) items
+// from a global counter.  Wave kAdder is the adder (the only wave on its
+// SIMD when the waves are placed round-robin): lane j owns column j of the
 // slice and adds the occurrences in sorted order, reading them from LDS.
-// Waves 1..7 are loaders: block t of the segment (occurrences 64t..64t+63)
-// goes to ring slot (running block number) mod kSlots, loaded by wave
-// 1 + t mod 7; each lane of a direct-to-LDS load brings 16 bytes of one
-// occurrence's slice, so a slot holds 64 occurrences x 64 columns
-// occurrence-major and the adder's reads (one column per lane) are
-// bank-conflict free.  Hand-over per slot: the loader waits until the adder
-// has finished the slot's previous block ("consumed"), loads, waits for its
-// loads and publishes the running block number in ready[slot].
-__global__ __launch_bounds__(512) void hot_sgd_kernel(float* const* __restrict__ tables, int d, int row_bits,
+// The other six waves are loaders: block t of the segment (occurrences
+// 64t..64t+63) goes to ring slot (running block number) mod kSlots, loaded
+// by loader t mod 6.  A slot is column-major (column c's 64 occurrences are
+// contiguous, rows padded to kRS floats), so the adder reads four
+// consecutive occurrences of its column with one 16-byte LDS read.  A loader lane loads a 4 x 4 piece
+// (4 occurrences x 4 columns) of the block into registers, transposes it
+// and writes four 16-byte column pieces.  Hand-over per slot: the loader
+// waits until the adder has finished the slot's previous block
+// ("consumed"), writes, and publishes the running block number in
+// ready[slot].
+__global__ __launch_bounds__(64 * (kLoaders + 1)) void hot_sgd_kernel(float* const* __restrict__ tables, int d, int row_bits,
                                                       const uint32_t* __restrict__ seg_key,
                                                       const int32_t* __restrict__ bags,
                                                       const int32_t* __restrict__ seg_start,
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(512) void hot_sgd_kernel(float* const* __restrict__
                                                       const uint32_t* __restrict__ nhot,
                                                       const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
                                                       float lr, uint32_t* __restrict__ next_item) {
-  __shared__ __attribute__((aligned(16))) float ring[kSlots][kHB * 64];
+  __shared__ __attribute__((aligned(16))) float ring[kSlots][64 * kRS];
   __shared__ int32_t ready[kSlots];
   __shared__ int32_t consumed;
   __shared__ uint32_t s_item;
@@ -362,112 +367,147 @@ __global__ __launch_bounds__(512) void hot_sgd_kernel(float* const* __restrict__
     const int k = (int)(key >> row_bits);
     const int64_t r = (int64_t)(key & row_mask);
     const int32_t nblk = (end - beg + kHB - 1) / kHB;
-    if (wave == 0) {
-      // The adds run as one stream over the full blocks, 8 values per step,
-      // with the LDS reads issued three steps ahead (12 reads in flight,
-      // within the 15 that lgkmcnt can count).
-      constexpr int kStep = 8, kAhead = 3, kSteps = kHB / kStep;
+    if (wave == kAdder) {
+      // The adds run as one stream over the full blocks, 16 values (four
+      // 16-byte LDS reads) per step, with the reads issued three steps
+      // ahead: twelve reads in flight (lgkmcnt counts up to 15).  Measured
+      // on one wave, wider steps keep the adder closest to its add rate.
+      constexpr int kStep = 16, kAhead = 3, kSteps = kHB / kStep, kBufs = 4, kReads = kStep / 4;
       const int32_t len = end - beg;
       const int32_t nfull = len / kHB;
       float acc = 0.f;
-      float v[4][kStep];
-      // occurrence o of a block sits in slot row 4 * (o % 16) + o / 16
+      float v[kBufs][kStep];
+      // occurrences kStep * st .. + kStep - 1 of this lane's column
       auto step_load = [&](int32_t t, int st, float* dst) {
-        const float* blk = &ring[(base + t) & (kSlots - 1)][lane];
+        const float* p = &ring[(base + t) & (kSlots - 1)][lane * kRS + st * kStep];
 #pragma unroll
-        for (int j = 0; j < kStep; ++j) {
-          const int o = st * kStep + j;
-          dst[j] = blk[(((o & 15) << 2) | (o >> 4)) * 64];
+        for (int q = 0; q < kStep; q += 4) {
+          const float4 a = *reinterpret_cast<const float4*>(p + q);
+          dst[q] = a.x;
+          dst[q + 1] = a.y;
+          dst[q + 2] = a.z;
+          dst[q + 3] = a.w;
         }
       };
       auto wait_ready = [&](int32_t t) {
         while (lds_load(&ready[(base + t) & (kSlots - 1)]) != base + t) __builtin_amdgcn_s_sleep(1);
         compiler_fence();
       };
-      auto peek = [&](int32_t t) { return lds_load(&ready[(base + t) & (kSlots - 1)]); };
-      int32_t seen = -1;
+      // The next block's flag is read with a plain LDS load just before its
+      // first data reads and checked at the end of this block.  One wave's
+      // LDS accesses execute in order and a loader writes its flag only
+      // after its data writes have completed, so a flag that shows the block
+      // proves the data reads after it saw the data; otherwise (rare) those
+      // reads are repeated once the flag is up.  Plain accesses keep the
+      // compiler's waits exact (an atomic or a loop-carried use would drain
+      // every read in flight).
+      auto flag = [&](int32_t t) { return ready[(base + t) & (kSlots - 1)]; };
       if (nfull > 0) {
         wait_ready(0);
 #pragma unroll
         for (int st = 0; st < kAhead; ++st) step_load(0, st, v[st]);
-        seen = peek(1);
       }
       for (int32_t t = 0; t < nfull; ++t) {
-        // the next block must be in before this one starts: its first reads
-        // are issued during this block's last steps, with no branch between;
-        // its flag was read one block earlier, so usually nothing waits here
         const bool more = t + 1 < nfull;
-        if (more && seen != base + t + 1) wait_ready(t + 1);
-        seen = peek(t + 2);
         const int32_t tn = more ? t + 1 : t;
+        int32_t fl = base + tn;
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
           // reads kAhead steps ahead, then this step's adds; the scheduling
           // barrier keeps the compiler from hoisting every read to the top
+          if (st + kAhead == kSteps) {
+            compiler_fence();
+            fl = flag(tn);
+            compiler_fence();
+          }
           if (st + kAhead < kSteps)
-            step_load(t, st + kAhead, v[(st + kAhead) & 3]);
+            step_load(t, st + kAhead, v[(st + kAhead) & (kBufs - 1)]);
           else
-            step_load(tn, st + kAhead - kSteps, v[(st + kAhead) & 3]);
+            step_load(tn, st + kAhead - kSteps, v[(st + kAhead) & (kBufs - 1)]);
+          // this step's values were read kAhead steps ago: the kAhead * kReads
+          // younger reads (and at most one flag access) may still be in flight
+          __builtin_amdgcn_s_waitcnt(0xc07f & ~0x0f00 | ((kAhead * kReads) << 8));
 #pragma unroll
-          for (int o = 0; o < kStep; ++o) acc = acc + v[st & 3][o];
+          for (int o = 0; o < kStep; ++o) acc = acc + v[st & (kBufs - 1)][o];
           __asm__ volatile("" : "+v"(acc));  // this step's adds stay in this step
           __builtin_amdgcn_sched_barrier(0);
         }
         compiler_fence();
-        if (lane == 0) lds_store(&consumed, base + t + 1);
+        if (lane == 0) consumed = base + t + 1;
+        if (more && fl != base + t + 1) {  // the next block's first reads came too early
+          wait_ready(t + 1);
+#pragma unroll
+          for (int st = 0; st < kAhead; ++st) step_load(t + 1, st, v[st]);
+        }
       }
       if (nfull * kHB < len) {  // the last, partial block
         const int32_t t = nfull;
         wait_ready(t);
-        const float* blk = &ring[(base + t) & (kSlots - 1)][lane];
-        for (int o = 0; o < len - nfull * kHB; ++o) acc = acc + blk[(((o & 15) << 2) | (o >> 4)) * 64];
+        const float* col = &ring[(base + t) & (kSlots - 1)][lane * kRS];
+        for (int o = 0; o < len - nfull * kHB; ++o) acc = acc + col[o];
         compiler_fence();
-        if (lane == 0) lds_store(&consumed, base + t + 1);
+        if (lane == 0) consumed = base + t + 1;
       }
       if (lane < cols) {
         float* t = tables[k] + r * d + col0 + lane;
         *t = __fsub_rn(*t, __fmul_rn(lr, acc));
       }
     } else {
-      // Loader: instruction i of a block brings occurrences i + 16 * (lane / 16)
-      // (lane % 16 = 16-byte column group), so each lane's 16 bag ids are
-      // consecutive in the sorted list; they are loaded for the loader's next
-      // block while this block's loads are in flight.
-      const int c4 = min(lane & 15, cols / 4 - 1);
-      const int sub = lane >> 4;
+      // Loader: lane (c4, sub) = (lane / 4, lane % 4) brings columns
+      // 4 c4 .. 4 c4 + 3 of occurrences 4 (sub + 4 m) + r (m, r = 0..3): 16
+      // global loads of 16 bytes, each 4 x 4 piece transposed in registers
+      // and written as four 16-byte column pieces.  Three blocks of the
+      // wave are in flight: while block t is written to its slot, the rows
+      // of its next block (t + kLoaders) are loading and the bag ids of the
+      // one after.
+      const int c4 = min(lane >> 2, cols / 4 - 1);
+      const int sub = lane & 3;
       const float* gsrc = G + g_col0 + (int64_t)k * d + col0 + 4 * c4;
-      int32_t bag[16];
-      auto load_bags = [&](int32_t t) {
+      auto occ = [&](int i) { return 4 * (sub + 4 * (i >> 2)) + (i & 3); };
+      auto load_bags = [&](int32_t t, int32_t (&bag)[16]) {
         const int32_t q0 = beg + t * kHB, last = end - 1;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) bag[i] = bags[min(q0 + i + 16 * sub, last)];
+        for (int i = 0; i < 16; ++i) bag[i] = bags[min(q0 + occ(i), last)];
       };
-      int32_t t = wave - 1;
-      if (t < nblk) load_bags(t);
+      // rows of a partial block past its end re-read its last row (bag ids
+      // were clamped); the adder never reads them
+      auto load_rows = [&](const int32_t (&bag)[16], float4 (&v)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const float4*>(gsrc + (int64_t)bag[i] * g_ld);
+      };
+      int32_t t = wave < kAdder ? wave : wave - 1;
+      int32_t bag[16];
+      float4 v[16];
+      if (t < nblk) {
+        load_bags(t, bag);
+        load_rows(bag, v);
+        if (t + kLoaders < nblk) load_bags(t + kLoaders, bag);
+      }
       for (; t < nblk; t += kLoaders) {
         const int32_t g = base + t;
         const int slot = g & (kSlots - 1);
+        float4 vn[16];
+        if (t + kLoaders < nblk) {
+          load_rows(bag, vn);
+          if (t + 2 * kLoaders < nblk) load_bags(t + 2 * kLoaders, bag);
+        }
         while (lds_load(&consumed) < g - kSlots + 1) __builtin_amdgcn_s_sleep(1);
         compiler_fence();
         float* dst = &ring[slot][0];
-        const int cnt = min(kHB, end - beg - t * kHB);
-        if (cnt == kHB) {  // full block: straight-line issue
 #pragma unroll
-          for (int i = 0; i < 16; ++i) lds_dma16(gsrc + (int64_t)bag[i] * g_ld, dst + i * 256);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (i < cnt) lds_dma16(gsrc + (int64_t)bag[i] * g_ld, dst + i * 256);
+        for (int m = 0; m < 4; ++m) {
+          const float4 a = v[4 * m], b = v[4 * m + 1], c = v[4 * m + 2], e = v[4 * m + 3];
+          float* p = dst + (4 * c4) * kRS + 4 * (sub + 4 * m);
+          *reinterpret_cast<float4*>(p) = make_float4(a.x, b.x, c.x, e.x);
+          *reinterpret_cast<float4*>(p + kRS) = make_float4(a.y, b.y, c.y, e.y);
+          *reinterpret_cast<float4*>(p + 2 * kRS) = make_float4(a.z, b.z, c.z, e.z);
+          *reinterpret_cast<float4*>(p + 3 * kRS) = make_float4(a.w, b.w, c.w, e.w);
         }
-        compiler_fence();
-        if (t + kLoaders < nblk) {
-          load_bags(t + kLoaders);
-          wait_vmcnt<16>();  // this block's loads (issued before the 16 bag loads) are in LDS
-        } else {
-          wait_vmcnt<0>();
-        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slot is written before its flag
         compiler_fence();
         if (lane == 0) lds_store(&ready[slot], g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = vn[i];
       }
     }
     base += nblk;
@@ -679,7 +719,7 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
   hipLaunchKernelGGL(find_hot_kernel, dim3(1024), dim3(256), 0, stream, seg, &counters[0], hot, &counters[1]);
   hipLaunchKernelGGL(order_hot_kernel, dim3(1), dim3(256), 0, stream, seg, hot, &counters[1], hot_ordered);
   // per-segment sums and the in-place update: long segments, then short ones
-  hipLaunchKernelGGL(hot_sgd_kernel, dim3(kHotBlocks), dim3(512), 0, stream, tables, d, row_bits, seg_key,
+  hipLaunchKernelGGL(hot_sgd_kernel, dim3(kHotBlocks), dim3(64 * (kLoaders + 1)), 0, stream, tables, d, row_bits, seg_key,
                      vals[cur], seg, hot_ordered, &counters[1], G, g_ld, g_col0, lr, &counters[2]);
   // short segments: half as many lanes as float4 columns (two float4 per
   // lane), at most 64
