@@ -9,14 +9,21 @@
 // Kernel design (gfx950): one wave per sample.  The sample's n x d matrix is
 // loaded straight into registers as 16-row tiles: lane l holds rows
 // T*16 + (l % 16) and, for every 16-wide k chunk, the four consecutive
-// columns 4*(l / 16) .. +3.  That is exactly the A operand of
-// v_mfma_f32_16x16x4_f32 for the tile's rows and the B operand for X^T, so
-// Gram block (I, J) is a chain of 4*ceil(d/16) MFMAs on register data, with
-// the k order permuted inside each chunk (fp32 sums in any order meet the
-// d*u error bound).  Only blocks with J <= I are computed.  The packed output
-// row is assembled in LDS and written with full 16-byte stores.  fp32 MFMA runs
-// at twice the rate of unpacked fp32 VALU FMAs, so it wins even where
-// padding to 16 rows wastes part of a block.  The kernel is bound by HBM
+// columns 4*(l / 16) .. +3.  Two chunks side by side give each lane eight
+// values of one row, the operand shape of v_mfma_f32_16x16x32_bf16 (the k
+// order inside the 32 columns is permuted, identically for both operands).
+//
+// Precision: the inputs are fp32 and the pairs need about fp32 accuracy, but
+// bf16 MFMA runs at 16 times the fp32 MFMA rate.  Every value is split
+// exactly into three bf16 parts, v = h + m + l (h: the top 8 significant
+// bits by truncation, m: the top 8 of the remainder, l: the rest, which has
+// at most 8 significant bits), and the Gram block sums the six products
+// hh, hm, mh, hl, mm, lh with fp32 accumulation.  Each bf16 product is exact
+// in fp32; the dropped terms ml, lm, ll are below 2^-20 |a b|, so with the
+// fp32 accumulation error the result stays within a few 1e-6 of
+// sum_c |x_ic x_jc|.  Six bf16 products cost 6/16 of one fp32 MFMA pass.
+// Only blocks with J <= I are computed.  The packed output row is assembled
+// in LDS and written with full 16-byte stores.  The kernel is bound by HBM
 // (reading X, writing the packed rows).
 #include "common.hpp"
 
@@ -24,6 +31,47 @@ namespace dlrm {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Exact split of eight fp32 values (a then b) into bf16 parts h + m + l.
+// Both subtractions are exact (each operand pair shares a binade), and the
+// final remainder has at most 8 significant bits, so it is a bf16 value.
+struct Parts {
+  bf16x8 h, m, l;
+};
+__device__ __forceinline__ Parts split3(f4 a, f4 b) {
+  uint32_t hb[8], mb[8], lb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float v = k < 4 ? a[k] : b[k - 4];
+    const uint32_t u = __float_as_uint(v);
+    const float r1 = v - __uint_as_float(u & 0xffff0000u);
+    const uint32_t ur = __float_as_uint(r1);
+    const float r2 = r1 - __uint_as_float(ur & 0xffff0000u);
+    hb[k] = u;
+    mb[k] = ur;
+    lb[k] = __float_as_uint(r2);
+  }
+  u32x4 h, m, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = (hb[2 * i] >> 16) | (hb[2 * i + 1] & 0xffff0000u);
+    m[i] = (mb[2 * i] >> 16) | (mb[2 * i + 1] & 0xffff0000u);
+    l[i] = (lb[2 * i] >> 16) | (lb[2 * i + 1] & 0xffff0000u);
+  }
+  return Parts{__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, m), __builtin_bit_cast(bf16x8, l)};
+}
+
+// acc += the six significant products of the split rows p (tile I) and q (tile J)
+__device__ __forceinline__ f4 gram6(const Parts& p, const Parts& q, f4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p.l, q.h, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p.h, q.l, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p.m, q.m, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p.m, q.h, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p.h, q.m, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(p.h, q.h, acc, 0, 0, 0);
+}
 
 __device__ __forceinline__ void put(float* p, float v) { *p = v; }
 __device__ __forceinline__ void put(uint16_t* p, float v) { *p = f32_to_bf16(v); }
@@ -83,9 +131,14 @@ __device__ __forceinline__ void gram_row(f4 (&x)[NT][DC], int n, int d, int pad_
       put(ob + at, v[r]);
     }
   };
+  // chunk pairs (2p, 2p + 1); an odd last chunk pairs with zeros
+  constexpr int DP = (DC + 1) / 2;
+  auto parts = [&](int t, int p) {
+    return split3(x[t][2 * p], 2 * p + 1 < DC ? x[t][2 * p + 1] : f4{0.f, 0.f, 0.f, 0.f});
+  };
   if constexpr (NT <= 2) {
-    // every block live at once: NT(NT+1)/2 independent chains (two partial
-    // chains when there is a single block)
+    // every block live at once, the rows split one chunk pair at a time; a
+    // single block runs as two partial chains
     constexpr int NB = NT * (NT + 1) / 2;
     constexpr int NCH = NB == 1 ? 2 : 1;
     f4 acc[NB][NCH];
@@ -94,16 +147,15 @@ __device__ __forceinline__ void gram_row(f4 (&x)[NT][DC], int n, int d, int pad_
 #pragma unroll
       for (int h = 0; h < NCH; ++h) acc[q][h] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
+    for (int p = 0; p < DP; ++p) {
+      Parts xs[NT];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        int q = 0;
+      for (int t = 0; t < NT; ++t) xs[t] = parts(t, p);
+      int q = 0;
 #pragma unroll
-        for (int I = 0; I < NT; ++I)
+      for (int I = 0; I < NT; ++I)
 #pragma unroll
-          for (int J = 0; J <= I; ++J, ++q)
-            acc[q][s % NCH] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[I][c][s], x[J][c][s], acc[q][s % NCH], 0, 0, 0);
-      }
+        for (int J = 0; J <= I; ++J, ++q) acc[q][p % NCH] = gram6(xs[I], xs[J], acc[q][p % NCH]);
     }
     int q = 0;
 #pragma unroll
@@ -111,32 +163,24 @@ __device__ __forceinline__ void gram_row(f4 (&x)[NT][DC], int n, int d, int pad_
 #pragma unroll
       for (int J = 0; J <= I; ++J, ++q) store_block(I, J, NCH == 2 ? acc[q][0] + acc[q][NCH - 1] : acc[q][0]);
   } else {
-    // one block row at a time (bounded accumulator registers): I + 1 chains,
-    // two partial chains for I = 0
+    // all rows split once, then one block row at a time (bounded
+    // accumulator registers)
+    Parts xs[NT][DP];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int p = 0; p < DP; ++p) xs[t][p] = parts(t, p);
 #pragma unroll
     for (int I = 0; I < NT; ++I) {
-      f4 acc[NT + 1];
+      f4 acc[NT];
 #pragma unroll
-      for (int J = 0; J <= NT; ++J) acc[J] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int J = 0; J < NT; ++J) acc[J] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
+      for (int p = 0; p < DP; ++p)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float a = x[I][c][s];
-          if (I == 0) {
-            acc[s & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x[0][c][s], acc[s & 1], 0, 0, 0);
-          } else {
+        for (int J = 0; J <= I; ++J) acc[J] = gram6(xs[I][p], xs[J][p], acc[J]);
 #pragma unroll
-            for (int J = 0; J <= I; ++J) acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x[J][c][s], acc[J], 0, 0, 0);
-          }
-        }
-      }
-      if (I == 0) {
-        store_block(0, 0, acc[0] + acc[1]);
-      } else {
-#pragma unroll
-        for (int J = 0; J <= I; ++J) store_block(I, J, acc[J]);
-      }
+      for (int J = 0; J <= I; ++J) store_block(I, J, acc[J]);
     }
   }
   const int end = d + n * (n - 1) / 2;
@@ -162,9 +206,11 @@ __device__ __forceinline__ void row_out(const char* rowb, char* dst, int bytes, 
   __builtin_amdgcn_wave_barrier();
 }
 
-// Materialised X: one wave per sample.
+// Materialised X: one wave per sample, at least two waves per SIMD (the
+// split rows of the largest shapes would otherwise take the whole register
+// file).
 template <int NT, int DC, typename OutT>
-__global__ __launch_bounds__(256) void interact_mfma_kernel(RowSource src, int64_t B, int n, int d,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void interact_mfma_kernel(RowSource src, int64_t B, int n, int d,
                                                             OutT* __restrict__ out, int64_t out_ld, int pad_end,
                                                             int row_bytes, int wide) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
