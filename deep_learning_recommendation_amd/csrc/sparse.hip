@@ -22,6 +22,8 @@
 // one lane group each.
 #include "common.hpp"
 
+#include <mutex>
+
 namespace dlrm {
 namespace {
 
@@ -517,6 +519,10 @@ __global__ __launch_bounds__(64 * (kLoaders + 1)) void hot_sgd_kernel(float* con
 // Short segments: a group of 2^g_log2 lanes (V float4 each) per segment.
 // The group loads up to one bag id per lane at once, then walks the bags in
 // order with U gradient rows in flight, broadcasting each bag id from its lane.
+// Waves take chunks of kLightChunk segments per group from a shared counter,
+// so the blocks that become resident early (beside the hot kernel) and late
+// (after its short items end) share the work as they come.
+constexpr int kLightChunk = 16;
 template <int V>
 __global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict__ tables, int d, int g_log2,
                                                         int row_bits, const uint32_t* __restrict__ seg_key,
@@ -524,74 +530,82 @@ __global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict
                                                         const int32_t* __restrict__ seg_start,
                                                         const uint32_t* __restrict__ nseg,
                                                         const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
-                                                        float lr) {
+                                                        float lr, uint32_t* __restrict__ next) {
   constexpr int U = 8 / V;
   const int lane = threadIdx.x & 63;
   const uint32_t row_mask = (row_bits >= 32) ? 0xffffffffu : ((1u << row_bits) - 1u);
   const int GL = 1 << g_log2;  // lanes per group
   const int gl = lane & (GL - 1);
-  const int groups_per_block = 256 >> g_log2;
-  const int64_t gid = (int64_t)blockIdx.x * groups_per_block + (threadIdx.x >> g_log2);
-  const int64_t ngroups = (int64_t)gridDim.x * groups_per_block;
+  const int wgroups = 64 >> g_log2;  // groups per wave
+  const int grp = lane >> g_log2;
   const int d4 = d >> 2;
   const uint32_t nsegs = *nseg;
-  for (int64_t s = gid; s < nsegs; s += ngroups) {
-    const int32_t beg = seg_start[s], end = seg_start[s + 1];
-    const uint32_t key = seg_key[s];
-    if (end - beg >= kHot) continue;
-    const int k = (int)(key >> row_bits);
-    const int64_t r = (int64_t)(key & row_mask);
-    float4* trow = reinterpret_cast<float4*>(tables[k] + r * d);
-    float4 tv[V];
+  const uint32_t per_wave = (uint32_t)(wgroups * kLightChunk);
+  for (;;) {
+    uint32_t c0 = 0;
+    if (lane == 0) c0 = atomicAdd(next, per_wave);
+    c0 = (uint32_t)__shfl((int)c0, 0, 64);
+    if (c0 >= nsegs) break;  // whole wave
+    for (int i = 0; i < kLightChunk; ++i) {
+      const uint32_t s = c0 + (uint32_t)(i * wgroups + grp);
+      if (s >= nsegs) break;  // whole group (later segments of the chunk are past the end too)
+      const int32_t beg = seg_start[s], end = seg_start[s + 1];
+      const uint32_t key = seg_key[s];
+      if (end - beg >= kHot) continue;
+      const int k = (int)(key >> row_bits);
+      const int64_t r = (int64_t)(key & row_mask);
+      float4* trow = reinterpret_cast<float4*>(tables[k] + r * d);
+      float4 tv[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int c4 = gl + j * GL;
-      tv[j] = c4 < d4 ? trow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const float* gbase = G + g_col0 + (int64_t)k * d;
-    float4 acc[V];
+      for (int j = 0; j < V; ++j) {
+        const int c4 = gl + j * GL;
+        tv[j] = c4 < d4 ? trow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      const float* gbase = G + g_col0 + (int64_t)k * d;
+      float4 acc[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int32_t q0 = beg; q0 < end; q0 += GL) {
-      const int m = min(GL, end - q0);
-      const int32_t my_bag = gl < m ? bags[q0 + gl] : 0;
-      for (int u0 = 0; u0 < m; u0 += U) {
-        float4 v[U][V];
+      for (int j = 0; j < V; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int32_t q0 = beg; q0 < end; q0 += GL) {
+        const int m = min(GL, end - q0);
+        const int32_t my_bag = gl < m ? bags[q0 + gl] : 0;
+        for (int u0 = 0; u0 < m; u0 += U) {
+          float4 v[U][V];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const bool ok = u0 + u < m;
-          const int64_t bag = __shfl(my_bag, ok ? u0 + u : 0, GL);
-          const float4* grow = reinterpret_cast<const float4*>(gbase + bag * g_ld);
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            const int c4 = gl + j * GL;
-            v[u][j] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (u0 + u < m) {
+          for (int u = 0; u < U; ++u) {
+            const bool ok = u0 + u < m;
+            const int64_t bag = __shfl(my_bag, ok ? u0 + u : 0, GL);
+            const float4* grow = reinterpret_cast<const float4*>(gbase + bag * g_ld);
 #pragma unroll
             for (int j = 0; j < V; ++j) {
-              acc[j].x = acc[j].x + v[u][j].x;
-              acc[j].y = acc[j].y + v[u][j].y;
-              acc[j].z = acc[j].z + v[u][j].z;
-              acc[j].w = acc[j].w + v[u][j].w;
+              const int c4 = gl + j * GL;
+              v[u][j] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (u0 + u < m) {
+#pragma unroll
+              for (int j = 0; j < V; ++j) {
+                acc[j].x = acc[j].x + v[u][j].x;
+                acc[j].y = acc[j].y + v[u][j].y;
+                acc[j].z = acc[j].z + v[u][j].z;
+                acc[j].w = acc[j].w + v[u][j].w;
+              }
             }
           }
         }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int c4 = gl + j * GL;
-      if (c4 < d4) {
-        float4 o;
-        o.x = __fsub_rn(tv[j].x, __fmul_rn(lr, acc[j].x));
-        o.y = __fsub_rn(tv[j].y, __fmul_rn(lr, acc[j].y));
-        o.z = __fsub_rn(tv[j].z, __fmul_rn(lr, acc[j].z));
-        o.w = __fsub_rn(tv[j].w, __fmul_rn(lr, acc[j].w));
-        trow[c4] = o;
+      for (int j = 0; j < V; ++j) {
+        const int c4 = gl + j * GL;
+        if (c4 < d4) {
+          float4 o;
+          o.x = __fsub_rn(tv[j].x, __fmul_rn(lr, acc[j].x));
+          o.y = __fsub_rn(tv[j].y, __fmul_rn(lr, acc[j].y));
+          o.z = __fsub_rn(tv[j].z, __fmul_rn(lr, acc[j].z));
+          o.w = __fsub_rn(tv[j].w, __fmul_rn(lr, acc[j].w));
+          trow[c4] = o;
+        }
       }
     }
   }
@@ -636,10 +650,35 @@ void sparse_layout(int64_t nnz, SparseLayout* L) {
   L->bytes = cv.bytes();
 }
 
+// A second stream per device (default priority) for the short segments,
+// which run beside the hot-segment kernel: that kernel's critical path is a
+// few serial chains on a few CUs while the rest of the chip would idle.
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    streams[dev] = s;
+  }
+  return streams[dev];
+}
+
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
 }
 
+}  // namespace
+}  // namespace dlrm
+
+namespace dlrm {
+namespace {
+int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_key, const int32_t* vals,
+                 const int32_t* seg, const int32_t* hot_ordered, uint32_t* counters, const float* G, int64_t g_ld,
+                 int64_t g_col0, float lr, hipStream_t stream, hipStream_t side);
 }  // namespace
 }  // namespace dlrm
 
@@ -684,7 +723,7 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
   uint32_t* bsum = reinterpret_cast<uint32_t*>(w + L.bsum);
   int32_t* seg = reinterpret_cast<int32_t*>(w + L.seg);
   uint32_t* seg_key = reinterpret_cast<uint32_t*>(w + L.seg_key);
-  // counters: [0] segments, [1] hot segments, [2] next hot item
+  // counters: [0] segments, [1] hot segments, [2] next hot item, [3] next short-segment chunk
   uint32_t* counters = reinterpret_cast<uint32_t*>(w + L.counters);
   int32_t* hot = reinterpret_cast<int32_t*>(w + L.hot);
   int32_t* hot_ordered = reinterpret_cast<int32_t*>(w + L.hot_ordered);
@@ -718,9 +757,37 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
                      (int64_t)n, bsum, seg, seg_key, &counters[0]);
   hipLaunchKernelGGL(find_hot_kernel, dim3(1024), dim3(256), 0, stream, seg, &counters[0], hot, &counters[1]);
   hipLaunchKernelGGL(order_hot_kernel, dim3(1), dim3(256), 0, stream, seg, hot, &counters[1], hot_ordered);
-  // per-segment sums and the in-place update: long segments, then short ones
+  if (launch_status() != DLRM_OK) return DLRM_E_HIP;
+  // per-segment sums and the in-place update: the long segments on `stream`,
+  // the short ones (disjoint rows) on the side stream at the same time, joined
+  // back into `stream` before returning
+  hipStream_t side = side_stream();
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (!side || hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return DLRM_E_HIP;
+  if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipEventDestroy(fork);
+    return DLRM_E_HIP;
+  }
+  int rc = DLRM_OK;
+  if (hipEventRecord(fork, stream) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess) rc = DLRM_E_HIP;
+  if (rc == DLRM_OK) rc = sgd_segments(tables, d, row_bits, seg_key, vals[cur], seg, hot_ordered, counters, G, g_ld,
+                                       g_col0, lr, stream, side);
+  // the join is recorded even after a failed launch, so `stream` never
+  // waits on an event that was not recorded
+  if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(stream, join, 0) != hipSuccess) rc = DLRM_E_HIP;
+  (void)hipEventDestroy(fork);
+  (void)hipEventDestroy(join);
+  return rc;
+}
+
+namespace dlrm {
+namespace {
+int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_key, const int32_t* vals,
+                 const int32_t* seg, const int32_t* hot_ordered, uint32_t* counters, const float* G, int64_t g_ld,
+                 int64_t g_col0, float lr, hipStream_t stream, hipStream_t side) {
   hipLaunchKernelGGL(hot_sgd_kernel, dim3(kHotBlocks), dim3(64 * (kLoaders + 1)), 0, stream, tables, d, row_bits, seg_key,
-                     vals[cur], seg, hot_ordered, &counters[1], G, g_ld, g_col0, lr, &counters[2]);
+                     vals, seg, hot_ordered, &counters[1], G, g_ld, g_col0, lr, &counters[2]);
+  if (launch_status() != DLRM_OK) return DLRM_E_HIP;
   // short segments: half as many lanes as float4 columns (two float4 per
   // lane), at most 64
   const int d4 = d / 4;
@@ -730,13 +797,15 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
   const int V = (d4 + (1 << g_log2) - 1) >> g_log2;
   const dim3 grid(kLightBlocks), block(256);
   if (V == 1)
-    hipLaunchKernelGGL((light_sgd_kernel<1>), grid, block, 0, stream, tables, d, g_log2, row_bits, seg_key,
-                       vals[cur], seg, &counters[0], G, g_ld, g_col0, lr);
+    hipLaunchKernelGGL((light_sgd_kernel<1>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg,
+                       &counters[0], G, g_ld, g_col0, lr, &counters[3]);
   else if (V == 2)
-    hipLaunchKernelGGL((light_sgd_kernel<2>), grid, block, 0, stream, tables, d, g_log2, row_bits, seg_key,
-                       vals[cur], seg, &counters[0], G, g_ld, g_col0, lr);
+    hipLaunchKernelGGL((light_sgd_kernel<2>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg,
+                       &counters[0], G, g_ld, g_col0, lr, &counters[3]);
   else
-    hipLaunchKernelGGL((light_sgd_kernel<4>), grid, block, 0, stream, tables, d, g_log2, row_bits, seg_key,
-                       vals[cur], seg, &counters[0], G, g_ld, g_col0, lr);
+    hipLaunchKernelGGL((light_sgd_kernel<4>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg,
+                       &counters[0], G, g_ld, g_col0, lr, &counters[3]);
   return launch_status();
 }
+}  // namespace
+}  // namespace dlrm
