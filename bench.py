@@ -239,7 +239,7 @@ def main():
         dense, idx, off, G, y, nnz = dbatches[i % len(dbatches)]
         if model is None:
             e0 = gather_t.start(stream) if timed else None
-            D.dlrm_embbag_fwd(ptrs, w.K, w.d, idx, off, w.B, out, w.K * w.d, 0)
+            D.dlrm_embbag_fwd(ptrs, w.K, w.d, idx, off, w.B, out, w.K * w.d, 0, nnz=nnz)
             if timed:
                 gather_t.stop(e0, stream)
             return
@@ -262,7 +262,7 @@ def main():
                                        model.top_ld)
         else:
             mark("embbag")
-            D.dlrm_embbag_fwd(model.table_ptrs, w.K, d, idx, off, w.B, model.X, n * d, d)
+            D.dlrm_embbag_fwd(model.table_ptrs, w.K, d, idx, off, w.B, model.X, n * d, d, nnz=nnz)
             mark("interact")
             D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
         mark("top_mlp")
@@ -296,7 +296,7 @@ def main():
         D.dlrm_mlp_fwd(dense, dense.shape[1], B, m.bottom.dims, m.bottom.Ws, m.bottom.w_ld, m.bottom.biases,
                        m.bottom.w_dtype, D.DLRM_ACT_RELU, m.x0, m.x0_ld, None, m.ws_bot, True)
         mark("embbag")
-        D.dlrm_embbag_fwd(m.table_ptrs, w.K, d, idx, off, B, m.X, n * d, d)
+        D.dlrm_embbag_fwd(m.table_ptrs, w.K, d, idx, off, B, m.X, n * d, d, nnz=nnz)
         mark("interact")
         D.dlrm_interact_fwd(m.X, B, n, d, n * d, m.top_in, m.top_ld)
         mark("top_mlp")

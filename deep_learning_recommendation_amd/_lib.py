@@ -26,7 +26,7 @@ _SIGNATURES = {
     "dlrm_abi_version": (ctypes.c_int, []),
     "dlrm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "dlrm_last_hip_error": (ctypes.c_int, []),
-    "dlrm_embbag_fwd": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I64, _P, _I64, _I64, _P]),
+    "dlrm_embbag_fwd": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "dlrm_interact_fwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I32, _I64, _P]),
     "dlrm_embbag_interact_fwd": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I64, _P]),
     "dlrm_interact_bwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I64, _P, _I64, _P]),
@@ -120,8 +120,9 @@ def dlrm_abi_version() -> int:
 
 
 def dlrm_embbag_fwd(table_ptrs, K: int, d: int, indices, offsets, B: int, out, out_ld: int, out_col0: int = 0,
-                    stream=None) -> None:
-    _check("dlrm_embbag_fwd", lib().dlrm_embbag_fwd(_ptr(table_ptrs), K, d, _ptr(indices), _ptr(offsets), B,
+                    stream=None, nnz: int = -1) -> None:
+    """nnz: offsets[K*B] when known on the host (sizes the work split), else -1."""
+    _check("dlrm_embbag_fwd", lib().dlrm_embbag_fwd(_ptr(table_ptrs), K, d, _ptr(indices), _ptr(offsets), B, nnz,
                                                      _ptr(out), out_ld, out_col0, _stream(stream)))
 
 

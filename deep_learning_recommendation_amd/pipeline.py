@@ -132,7 +132,8 @@ class DLRM:
             C.dlrm_embbag_interact_fwd(self.x0, self.x0_ld, self.table_ptrs, self.K, d, indices, offsets, B,
                                        self.top_in, self.top_ld, stream)
         else:
-            C.dlrm_embbag_fwd(self.table_ptrs, self.K, d, indices, offsets, B, self.X, n * d, d, stream)
+            C.dlrm_embbag_fwd(self.table_ptrs, self.K, d, indices, offsets, B, self.X, n * d, d, stream,
+                              nnz=indices.numel())
             C.dlrm_interact_fwd(self.X, B, n, d, n * d, self.top_in, self.top_ld, stream)
         C.dlrm_mlp_fwd(self.top_in, self.top_ld, B, self.top.dims, self.top.Ws, self.top.w_ld, self.top.biases,
                        self.top.w_dtype, C.DLRM_ACT_NONE, self.logit, 1, self.prob, self.ws_top, save, stream)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define DLRM_ABI_VERSION 1
+#define DLRM_ABI_VERSION 2
 
 enum {
   DLRM_OK = 0,
@@ -75,6 +75,9 @@ int dlrm_last_hip_error(void);
  *   indices  int64 [nnz], table-major.
  *   offsets  int64 [K*B + 1], non-decreasing, offsets[0] = 0: bag (k, b)
  *            owns indices[offsets[k*B+b] .. offsets[k*B+b+1]).
+ *   nnz      offsets[K*B] if the caller knows it on the host, else -1: it
+ *            only sizes the work split (bags per lane group) and never
+ *            bounds a read.
  *   out      fp32; bag (k, b) is written to
  *            out[b*out_ld + out_col0 + k*d + c], c < d (out_ld >= out_col0
  *            + K*d; out and out_ld*4, out_col0*4 must keep 16-byte alignment).
@@ -83,7 +86,7 @@ int dlrm_last_hip_error(void);
  *   Limits:  d % 4 == 0, 4 <= d <= 1024, K >= 1, B >= 1.
  */
 int dlrm_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const int64_t* indices,
-                    const int64_t* offsets, int64_t B, float* out, int64_t out_ld, int64_t out_col0,
+                    const int64_t* offsets, int64_t B, int64_t nnz, float* out, int64_t out_ld, int64_t out_col0,
                     hipStream_t stream);
 
 /*

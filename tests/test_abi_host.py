@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_strings(lib):
-    assert C.dlrm_abi_version() == 1
+    assert C.dlrm_abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert lib.dlrm_strerror(code)
     assert lib.dlrm_last_hip_error() == 0
@@ -47,12 +47,12 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
 
 def test_embbag_argument_checks(lib):
     f = lib.dlrm_embbag_fwd
-    assert f(NULL, 8, 16, FAKE, FAKE, 128, FAKE, 8 * 16, 0, NULL) == C.DLRM_E_INVALID
-    assert f(FAKE, 8, 6, FAKE, FAKE, 128, FAKE, 8 * 6, 0, NULL) == C.DLRM_E_INVALID     # d % 4
-    assert f(FAKE, 8, 2048, FAKE, FAKE, 128, FAKE, 8 * 2048, 0, NULL) == C.DLRM_E_INVALID  # d > 1024
-    assert f(FAKE, 8, 16, FAKE, FAKE, 128, FAKE, 8 * 16 - 4, 0, NULL) == C.DLRM_E_INVALID  # out_ld too small
-    assert f(FAKE, 0, 16, FAKE, FAKE, 128, FAKE, 16, 0, NULL) == C.DLRM_E_INVALID
-    assert f(FAKE, 8, 16, FAKE, FAKE, 128, ctypes.c_void_p(0x10004), 128, 0, NULL) == C.DLRM_E_INVALID  # alignment
+    assert f(NULL, 8, 16, FAKE, FAKE, 128, -1, FAKE, 8 * 16, 0, NULL) == C.DLRM_E_INVALID
+    assert f(FAKE, 8, 6, FAKE, FAKE, 128, -1, FAKE, 8 * 6, 0, NULL) == C.DLRM_E_INVALID     # d % 4
+    assert f(FAKE, 8, 2048, FAKE, FAKE, 128, -1, FAKE, 8 * 2048, 0, NULL) == C.DLRM_E_INVALID  # d > 1024
+    assert f(FAKE, 8, 16, FAKE, FAKE, 128, -1, FAKE, 8 * 16 - 4, 0, NULL) == C.DLRM_E_INVALID  # out_ld too small
+    assert f(FAKE, 0, 16, FAKE, FAKE, 128, -1, FAKE, 16, 0, NULL) == C.DLRM_E_INVALID
+    assert f(FAKE, 8, 16, FAKE, FAKE, 128, -1, ctypes.c_void_p(0x10004), 128, 0, NULL) == C.DLRM_E_INVALID  # alignment
 
 
 def test_interact_argument_checks(lib):

@@ -12,14 +12,17 @@ from synth import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _run(tables_dev, idx, off, B, d, out_ld=None, col0=0):
+def _run(tables_dev, idx, off, B, d, out_ld=None, col0=0, nnz=None):
+    """nnz: None passes offsets[K*B] (the bench's call), -1 leaves the work
+    split to the bag count alone."""
     import deep_learning_recommendation_amd as D
 
     K = len(tables_dev)
     out_ld = K * d if out_ld is None else out_ld
     out = torch.full((B, out_ld), float("nan"), dtype=torch.float32, device=DEV)
     ptrs = D.device_pointer_array(tables_dev)
-    D.dlrm_embbag_fwd(ptrs, K, d, to_dev(idx), to_dev(off), B, out, out_ld, col0)
+    nnz = int(off[-1]) if nnz is None else nnz
+    D.dlrm_embbag_fwd(ptrs, K, d, to_dev(idx), to_dev(off), B, out, out_ld, col0, nnz=nnz)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -36,11 +39,13 @@ def _rand_case(seed, K, B, d, rows, max_len, empty_frac=0.1):
 
 
 @pytest.mark.parametrize("d", [4, 16, 64, 128, 132, 256, 260, 1024])
-def test_embbag_random_ragged_bitexact(d):
+@pytest.mark.parametrize("max_len,nnz_known", [(45, True), (45, False), (2, True), (300, True)])
+def test_embbag_random_ragged_bitexact(d, max_len, nnz_known):
+    """Bag lengths set the bags per lane group (1 .. G - 1) when nnz is given."""
     K, B = 3, 701  # B not a multiple of any chunk size: ragged tail
-    banner(f"embbag random d={d} K={K} B={B}")
-    tabs, idx, off = _rand_case(d, K, B, d, [50, 333, 7], 45)
-    got = _run([to_dev(t) for t in tabs], idx, off, B, d)
+    banner(f"embbag random d={d} K={K} B={B} max_len={max_len} nnz_known={nnz_known}")
+    tabs, idx, off = _rand_case(d + max_len, K, B, d, [50, 333, 7], max_len)
+    got = _run([to_dev(t) for t in tabs], idx, off, B, d, nnz=None if nnz_known else -1)
     ref = oracle.embbag_fwd(tabs, idx, off, B)
     assert np.array_equal(bits(got), bits(ref))
 
@@ -106,7 +111,8 @@ def test_embbag_full_size_sampled(name):
     idx, off = W.indices_offsets(w)
     tabs_dev = SD.make_tables(w)
     out = torch.empty((w.B, w.K * w.d), dtype=torch.float32, device=DEV)
-    D.dlrm_embbag_fwd(D.device_pointer_array(tabs_dev), w.K, w.d, to_dev(idx), to_dev(off), w.B, out, w.K * w.d, 0)
+    D.dlrm_embbag_fwd(D.device_pointer_array(tabs_dev), w.K, w.d, to_dev(idx), to_dev(off), w.B, out, w.K * w.d, 0,
+                      nnz=len(idx))
     torch.cuda.synchronize()
     samples = np.sort(np.random.default_rng(1).choice(w.B, 512, replace=False))
     samples[-1] = w.B - 1  # include the ragged end

@@ -107,7 +107,7 @@ def test_fused_gather_interaction(K, d, out_bf16):
     # two-call path
     X = torch.zeros((B, n, d), dtype=torch.float32, device=DEV)
     X[:, 0, :] = to_dev(x0)
-    D.dlrm_embbag_fwd(ptrs, K, d, to_dev(idx), to_dev(off), B, X, n * d, d)
+    D.dlrm_embbag_fwd(ptrs, K, d, to_dev(idx), to_dev(off), B, X, n * d, d, nnz=len(idx))
     two = torch.full((B, ld), 3.0, dtype=dt, device=DEV)
     D.dlrm_interact_fwd(X, B, n, d, n * d, two, ld)
     one = torch.full((B, ld), 5.0, dtype=dt, device=DEV)
