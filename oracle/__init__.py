@@ -49,6 +49,7 @@ def _bind(L):
     L.oracle_set_threads.argtypes = [ctypes.c_int]
     L.oracle_bf16_round.argtypes = [_P, _P, _I64]
     L.oracle_embbag_fwd.argtypes = [_P, _I32, _I32, _P, _P, _I64, _P, _I64, _I64]
+    L.oracle_embbag_fwd_lp.argtypes = [_P, _I32, _P, _I32, _I32, _P, _P, _I64, _P, _I64, _I64]
     L.oracle_interact_fwd.argtypes = [_P, _I64, _I32, _I32, _I64, _P, _I64]
     L.oracle_interact_bwd.argtypes = [_P, _I64, _I32, _I32, _I64, _P, _I64, _P, _I64]
     L.oracle_mlp_fwd.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P]
@@ -102,6 +103,31 @@ def embbag_fwd(tables, idx, offsets, B: int, out=None, out_ld=None, out_col0: in
     out_ld = out.shape[1] if out_ld is None else out_ld
     ptrs = _ptr_array(tables)
     L.oracle_embbag_fwd(ptrs, K, d, _ptr(idx), _ptr(offsets), B, _ptr(out), out_ld, out_col0)
+    return out
+
+
+def embbag_fwd_lp(tables, dtype: str, idx, offsets, B: int, scale_bias=None, out=None, out_ld=None, out_col0: int = 0,
+                  L=None) -> np.ndarray:
+    """Sum-pooled bags from low-precision rows: dtype "bf16" (tables are
+    uint16 arrays of bf16 bit patterns) or "int8" (int8 tables with
+    ``scale_bias[k]`` float32 [m_k][2] = per-row scale and bias)."""
+    L = L or lib()
+    code = {"bf16": 1, "int8": 2}[dtype]
+    tables = [_c(t, np.uint16 if code == 1 else np.int8) for t in tables]
+    K, d = len(tables), tables[0].shape[1]
+    idx, offsets = _c(idx, np.int64), _c(offsets, np.int64)
+    assert offsets.shape[0] == K * B + 1
+    sbp = None
+    if code == 2:
+        scale_bias = [_c(a, np.float32) for a in scale_bias]
+        assert all(a.shape == (t.shape[0], 2) for a, t in zip(scale_bias, tables))
+        sbp = _ptr_array(scale_bias)
+    if out is None:
+        out_ld = K * d if out_ld is None else out_ld
+        out = np.zeros((B, out_ld), dtype=np.float32)
+    out_ld = out.shape[1] if out_ld is None else out_ld
+    L.oracle_embbag_fwd_lp(_ptr_array(tables), code, sbp, K, d, _ptr(idx), _ptr(offsets), B, _ptr(out), out_ld,
+                           out_col0)
     return out
 
 

@@ -95,6 +95,47 @@ void oracle_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const i
 }
 
 /*
+ * Embedding lookup with sum pooling from low-precision table rows.
+ * The explainer's citation list (Evaluation & Benchmarks) carries the note
+ * that quantisation pays where a problem is bandwidth-bound, as
+ * recommendation is; the pages fix no format, so two plain ones are read
+ * here.  Every stored value is first turned into an fp32 number v, then the
+ * bag is pooled exactly as oracle_embbag_fwd (fp32, ascending position,
+ * from +0.0f):
+ *   dtype 1 (bf16):  v = the bf16 value widened to fp32 (exact: the 16 bits
+ *                    become the high half of the fp32 word).
+ *   dtype 2 (int8):  v = fl(fl(s * q) + z) with the row's fp32 scale s and
+ *                    bias z (sb[k][2r], sb[k][2r+1]): the product is rounded
+ *                    to fp32, then the sum.
+ */
+static float lp_value(const void* table, const float* sb, int32_t dtype, int64_t r, int32_t d, int32_t c) {
+  if (dtype == 1) {
+    const uint16_t h = ((const uint16_t*)table)[r * d + c];
+    const uint32_t u = (uint32_t)h << 16;
+    float v;
+    memcpy(&v, &u, sizeof v);
+    return v;
+  }
+  const int8_t q = ((const int8_t*)table)[r * d + c];
+  const float prod = sb[2 * r] * (float)q;
+  return prod + sb[2 * r + 1];
+}
+
+void oracle_embbag_fwd_lp(const void* const* tables, int32_t dtype, const float* const* sb, int32_t K, int32_t d,
+                          const int64_t* idx, const int64_t* off, int64_t B, float* out, int64_t out_ld,
+                          int64_t out_col0) {
+  const int64_t bags = (int64_t)K * B;
+#pragma omp parallel for schedule(static)
+  for (int64_t kb = 0; kb < bags; ++kb) {
+    const int64_t k = kb / B, b = kb % B;
+    float* o = out + b * out_ld + out_col0 + k * (int64_t)d;
+    for (int32_t c = 0; c < d; ++c) o[c] = +0.0f;
+    for (int64_t pos = off[kb]; pos < off[kb + 1]; ++pos)
+      for (int32_t c = 0; c < d; ++c) o[c] = o[c] + lp_value(tables[k], sb ? sb[k] : 0, dtype, idx[pos], d, c);
+  }
+}
+
+/*
  * Pairwise dot-product interaction and concatenation.
  * [SU] Key equations, Interaction: Z = tril(X X^T), X = [x_dense; e_1; ...; e_K]
  * of shape (K+1) x d.  [EXPL] Key Method Details, "Interaction layer": only

@@ -25,6 +25,11 @@ def lib():
         _lib.synth_fill_table.restype = ctypes.c_int
         _lib.synth_fill_table.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
                                           ctypes.c_float, ctypes.c_void_p]
+        _lib.synth_fill_table_bf16.restype = ctypes.c_int
+        _lib.synth_fill_table_bf16.argtypes = _lib.synth_fill_table.argtypes
+        _lib.synth_fill_table_i8.restype = ctypes.c_int
+        _lib.synth_fill_table_i8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_uint64, ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p]
     return _lib
 
 
@@ -52,3 +57,30 @@ def make_tables(w, device="cuda", seed: int | None = None):
         fill_table(t, seed, k)
         out.append(t)
     return out
+
+
+def make_tables_lp(w, dtype: str, device="cuda", seed: int | None = None):
+    """Low-precision tables of workload ``w``: ``dtype`` "bf16" gives K
+    int16 tensors of bf16 bit patterns (``synth.rng.table_rows_bf16``) and
+    ``None``; "int8" gives K int8 tensors and K float32 [m_k][2] (scale,
+    bias) tensors (``synth.rng.table_rows_i8``)."""
+    import torch
+
+    seed = w.seed if seed is None else seed
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    tabs, sbs = [], []
+    for k in range(w.K):
+        rows, a = w.rows[k], float(R.table_scale(w.rows[k]))
+        if dtype == "bf16":
+            t = torch.empty((rows, w.d), dtype=torch.int16, device=device)
+            rc = lib().synth_fill_table_bf16(ctypes.c_void_p(t.data_ptr()), rows, w.d, R.table_key(seed, k), a, s)
+        else:
+            t = torch.empty((rows, w.d), dtype=torch.int8, device=device)
+            sb = torch.empty((rows, 2), dtype=torch.float32, device=device)
+            rc = lib().synth_fill_table_i8(ctypes.c_void_p(t.data_ptr()), ctypes.c_void_p(sb.data_ptr()), rows, w.d,
+                                           R.table_key(seed, k), R.scale_bias_key(seed, k), a, s)
+            sbs.append(sb)
+        if rc != 0:
+            raise RuntimeError(f"synth fill ({dtype}) failed with code {rc}")
+        tabs.append(t)
+    return tabs, (sbs if dtype == "int8" else None)

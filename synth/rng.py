@@ -78,6 +78,47 @@ def table_rows(seed: int, table: int, rows: int, row_ids: np.ndarray, d: int) ->
     return (table_scale(rows) * t).astype(np.float32)
 
 
+def table_rows_bf16(seed: int, table: int, rows: int, row_ids: np.ndarray, d: int) -> np.ndarray:
+    """bf16 table rows (uint16 bit patterns): the high half of each fp32
+    value of ``table_rows``."""
+    return (table_rows(seed, table, rows, row_ids, d).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def scale_bias_key(seed: int, table: int) -> int:
+    """State of the per-row (scale, bias) stream of an int8 table."""
+    return fmix_int(table_key(seed, table) ^ 0xD6E8FEB86659FD93)
+
+
+def table_rows_i8(seed: int, table: int, rows: int, row_ids: np.ndarray, d: int):
+    """int8 table rows and their fp32 (scale, bias) pairs.
+
+    q(r, c) is the top byte, as a signed value, of output ``r*d + c + 1`` of
+    the table's state.  Row r's scale is ``a * ((0.5 + u1) * 2**-7)`` and its
+    bias ``a * ((2 u2 - 1) * 2**-3)``, u1 = (h1 >> 41) 2**-23 and
+    u2 = (h2 >> 40) 2**-24 from outputs 2r + 1 and 2r + 2 of the row-parameter
+    state: the factors after ``a`` are exact, so each is one fp32 rounding,
+    as in the device fill.
+    """
+    row_ids = np.asarray(row_ids, dtype=np.int64)
+    key = np.uint64(table_key(seed, table))
+    e = (row_ids[:, None] * d + np.arange(d, dtype=np.int64)[None, :]).astype(np.uint64)
+    with np.errstate(over="ignore"):
+        h = fmix(key + (e + np.uint64(1)) * GAMMA)
+    q = (h >> np.uint64(56)).astype(np.uint8).view(np.int8)
+    k2 = np.uint64(scale_bias_key(seed, table))
+    r = row_ids.astype(np.uint64)
+    with np.errstate(over="ignore"):
+        h1 = fmix(k2 + (np.uint64(2) * r + np.uint64(1)) * GAMMA)
+        h2 = fmix(k2 + (np.uint64(2) * r + np.uint64(2)) * GAMMA)
+    u1 = (h1 >> np.uint64(41)).astype(np.float32) * np.float32(2.0 ** -23)
+    f1 = (np.float32(0.5) + u1) * np.float32(2.0 ** -7)
+    top = (h2 >> np.uint64(40)).astype(np.int64)
+    f2 = (top * 2 - (1 << 24)).astype(np.float32) * np.float32(2.0 ** -27)
+    a = table_scale(rows)
+    sb = np.stack([a * f1, a * f2], axis=1).astype(np.float32)
+    return np.ascontiguousarray(q), sb
+
+
 class FeistelPermutation:
     """Seeded bijection of [0, m) built from a 4-round balanced Feistel network
     on the smallest even bit width covering m, with cycle walking."""

@@ -146,6 +146,72 @@ def test_embbag_empty_bag_is_positive_zero(orc):
     assert np.all(out[1] == -6.0)
 
 
+# --------------------------------------------------------------------------- low-precision table rows
+
+def test_embbag_lp_bf16_is_exact_widening(orc):
+    """bf16 rows widen exactly: tables whose fp32 values have zero low halves
+    give, stored as their high halves, the fp32 lookup's result bit for bit."""
+    g = np.random.default_rng(11)
+    K, B, d, rows = 3, 40, 12, [9, 30, 5]
+    f32 = [g.standard_normal((m, d)).astype(np.float32) for m in rows]
+    f32 = [(t.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32) for t in f32]
+    b16 = [(t.view(np.uint32) >> np.uint32(16)).astype(np.uint16) for t in f32]
+    idx, off = _rand_bags(g, K, B, rows, 7)
+    got = orc.embbag_fwd_lp(b16, "bf16", idx, off, B)
+    ref = orc.embbag_fwd(f32, idx, off, B)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_embbag_lp_int8_unit_scale_is_integer_sum(orc):
+    """Scale 1 and bias 0: every pooled value is the integer sum of the bag's
+    bytes (exact in fp32 at these sizes), by brute force in int64."""
+    g = np.random.default_rng(12)
+    K, B, d, rows = 2, 33, 8, [17, 6]
+    q = [g.integers(-128, 128, size=(m, d)).astype(np.int8) for m in rows]
+    sb = [np.tile(np.array([1.0, 0.0], np.float32), (m, 1)) for m in rows]
+    idx, off = _rand_bags(g, K, B, rows, 9)
+    got = orc.embbag_fwd_lp(q, "int8", idx, off, B, scale_bias=sb)
+    for k in range(K):
+        for b in range(B):
+            a, e = off[k * B + b], off[k * B + b + 1]
+            want = q[k][idx[a:e]].astype(np.int64).sum(axis=0) if e > a else np.zeros(d, np.int64)
+            assert np.array_equal(got[b, k * d:(k + 1) * d], want.astype(np.float32))
+
+
+def test_embbag_lp_int8_two_roundings(orc):
+    """(s * q) + z is rounded after the product and again after the sum: with
+    s = 1 + 2^-23, q = 127, z = -127 the product 127 + 127 * 2^-23 rounds to
+    127 + 2^-16 (the fp32 spacing at 127 is 2^-17), so the value is exactly
+    2^-16; a fused multiply-add would give 127 * 2^-23.  A bag of the row twice
+    pools to 2^-15."""
+    s = np.float32(1.0 + 2.0 ** -23)
+    q = [np.full((1, 4), 127, np.int8)]
+    sb = [np.array([[s, -127.0]], np.float32)]
+    off = np.array([0, 1, 3], dtype=np.int64)
+    idx = np.array([0, 0, 0], dtype=np.int64)
+    got = orc.embbag_fwd_lp(q, "int8", idx, off, 2, scale_bias=sb)
+    assert np.all(got[0] == np.float32(2.0 ** -16))
+    assert np.all(got[1] == np.float32(2.0 ** -15))
+    assert 2.0 ** -16 != 127 * 2.0 ** -23
+
+
+def test_embbag_lp_int8_affine_dyadic(orc):
+    """Dyadic scale and bias: (q / 8) + 1/2 is exact, so the pooled values
+    equal the exact rational sums."""
+    from fractions import Fraction
+
+    g = np.random.default_rng(13)
+    K, B, d, rows = 1, 25, 4, [11]
+    q = [g.integers(-128, 128, size=(rows[0], d)).astype(np.int8)]
+    sb = [np.tile(np.array([0.125, 0.5], np.float32), (rows[0], 1))]
+    idx, off = _rand_bags(g, K, B, rows, 6)
+    got = orc.embbag_fwd_lp(q, "int8", idx, off, B, scale_bias=sb)
+    for b in range(B):
+        for c in range(d):
+            want = sum((Fraction(int(q[0][r, c]), 8) + Fraction(1, 2) for r in idx[off[b]:off[b + 1]]), Fraction(0))
+            assert Fraction(float(got[b, c])) == want
+
+
 # --------------------------------------------------------------------------- interaction
 
 @pytest.mark.parametrize("n,d", [(9, 16), (27, 128), (101, 64), (2, 4), (1, 8)])

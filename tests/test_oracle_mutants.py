@@ -48,6 +48,14 @@ MUTANTS = {
                              ["test_mlp_bwd_against_autograd", "test_mlp_bwd_finite_differences"]),
     "mlp_bwd_transposed_weight": ("(double)W[l][(int64_t)o * fi + i]", "(double)W[l][(int64_t)(i % fo) * fi + (o % fi)]",
                                   ["test_mlp_bwd_against_autograd"]),
+    "lp_int8_fused_multiply_add": ("const float prod = sb[2 * r] * (float)q;\n  return prod + sb[2 * r + 1];",
+                                   "return fmaf(sb[2 * r], (float)q, sb[2 * r + 1]);",
+                                   ["test_embbag_lp_int8_two_roundings"]),
+    "lp_int8_drops_bias": ("return prod + sb[2 * r + 1];", "return prod;", ["test_embbag_lp_int8_affine_dyadic"]),
+    "lp_int8_unsigned_bytes": ("const int8_t q = ((const int8_t*)table)", "const uint8_t q = ((const uint8_t*)table)",
+                               ["test_embbag_lp_int8_unit_scale_is_integer_sum"]),
+    "lp_bf16_low_half": ("const uint32_t u = (uint32_t)h << 16;", "const uint32_t u = (uint32_t)h;",
+                         ["test_embbag_lp_bf16_is_exact_widening"]),
     "sgd_wrong_sign": ("T[r * (int64_t)d + c] - step", "T[r * (int64_t)d + c] + step",
                        ["test_sparse_sgd_single_occurrence_and_untouched", "test_sparse_sgd_dyadic_exact"]),
     "sgd_ignores_table_slot": ("G + b * g_ld + g_col0 + (int64_t)k * d", "G + b * g_ld + g_col0",
