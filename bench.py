@@ -32,10 +32,14 @@ BF16_PEAK_TFLOPS = 2500.0
 METRIC = "DLRM fwd samples/s at 1 GPU; EmbeddingBag HBM GB/s as % of peak"
 
 
-def gather_bytes(K, B, d, nnz):
-    """Algorithmic bytes of one pooled-lookup launch: every looked-up row,
-    the int64 indices and offsets, and the pooled output."""
-    return 4 * d * nnz + 8 * nnz + 8 * (K * B + 1) + 4 * K * B * d
+ROW_BYTES = {"f32": lambda d: 4 * d, "bf16": lambda d: 2 * d, "int8": lambda d: d + 8}  # int8: + (scale, bias)
+
+
+def gather_bytes(K, B, d, nnz, table_dtype="f32"):
+    """Algorithmic bytes of one pooled-lookup launch: every looked-up row
+    (with its scale and bias for int8 rows), the int64 indices and offsets,
+    and the fp32 pooled output."""
+    return ROW_BYTES[table_dtype](d) * nnz + 8 * nnz + 8 * (K * B + 1) + 4 * K * B * d
 
 
 def measured_traffic(key, kernel):
@@ -69,6 +73,9 @@ def parse():
     p.add_argument("--workload", default="forward", choices=["forward", "embbag", "interaction", "train", "tiny"])
     p.add_argument("--batches", type=int, default=2, help="distinct input batches rotated over the steps")
     p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
+    p.add_argument("--table-dtype", default="f32", choices=["f32", "bf16", "int8"],
+                   help="gather microbenchmark only: table rows stored as fp32, bf16, or int8 with a per-row scale "
+                        "and bias (dlrm_embbag_fwd_lp)")
     p.add_argument("--path", default="auto", choices=["auto", "fused", "two-call"],
                    help="pooled lookup + interaction: one fused call, two calls (X materialised), or auto (fused "
                         "for short bags)")
@@ -108,7 +115,7 @@ class Timer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
 
 
-def cpu_baseline(w, batches, bottom, top, n_samples, chain=False, min_seconds=10.0):
+def cpu_baseline(w, batches, bottom, top, n_samples, chain=False, min_seconds=10.0, table_dtype="f32"):
     """The oracle (as it stands) on the first n_samples of batch 0: forward
     for forward-type workloads, pooled lookups for the gather microbench,
     forward plus the sparse update for the training step (with ``chain``:
@@ -125,7 +132,15 @@ def cpu_baseline(w, batches, bottom, top, n_samples, chain=False, min_seconds=10
     samples = np.arange(S)
     sidx, soff = W.sub_bags(idx, off, w.K, w.B, samples)
     ws = w.scaled(B=S)
-    tabs, local, _ = W.compact_rows(ws, sidx, soff)
+    tabs, local, row_ids = W.compact_rows(ws, sidx, soff)
+    lp = table_dtype
+    if lp != "f32":
+        from synth import rng as R
+        if lp == "bf16":
+            tabs, sbs = [R.table_rows_bf16(w.seed, k, w.rows[k], row_ids[k], w.d) for k in range(w.K)], None
+        else:
+            pairs = [R.table_rows_i8(w.seed, k, w.rows[k], row_ids[k], w.d) for k in range(w.K)]
+            tabs, sbs = [p[0] for p in pairs], [p[1] for p in pairs]
     quant = w.mlp_dtype == "bf16"
     G = batches[0][3].reshape(w.B, -1)[:S] if w.train else None
     y = batches[0][4][:S] if w.train else None
@@ -147,6 +162,9 @@ def cpu_baseline(w, batches, bottom, top, n_samples, chain=False, min_seconds=10
     def one_pass():
         if chain:
             return chain_pass()
+        if lp != "f32":
+            oracle.embbag_fwd_lp(tabs, lp, local, soff, S, scale_bias=sbs)
+            return
         E = oracle.embbag_fwd(tabs, local, soff, S)
         if w.name != "embbag":
             x0, _, _ = oracle.mlp_fwd(dense[:S], [p[0] for p in bottom], [p[2] for p in bottom], quant, True)
@@ -197,9 +215,16 @@ def main():
         sys.exit(1)
     if args.uniform:
         w = dataclasses.replace(w, index_dist="uniform")
+    lp = args.table_dtype
+    if lp != "f32" and w.name != "embbag":
+        print("--table-dtype applies to the gather microbenchmark (--workload embbag) only", file=sys.stderr)
+        sys.exit(1)
     t_setup = time.perf_counter()
     dev = "cuda"
-    tables = SD.make_tables(w)
+    if lp == "f32":
+        tables, sbs = SD.make_tables(w), None
+    else:
+        tables, sbs = SD.make_tables_lp(w, lp)
     bf16 = w.mlp_dtype == "bf16"
     bottom = W.mlp_params(w, "bottom") if w.bottom else None
     top = W.mlp_params(w, "top") if w.top else None
@@ -227,6 +252,8 @@ def main():
             model.sparse_workspace(max(b[5] for b in dbatches))
     else:
         ptrs = D.device_pointer_array(tables)
+        sbp = D.device_pointer_array(sbs) if sbs is not None else None
+        lp_code = {"bf16": D.DLRM_BF16, "int8": D.DLRM_I8}.get(lp)
         out = torch.empty((w.B, w.K * w.d), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
@@ -239,7 +266,10 @@ def main():
         dense, idx, off, G, y, nnz = dbatches[i % len(dbatches)]
         if model is None:
             e0 = gather_t.start(stream) if timed else None
-            D.dlrm_embbag_fwd(ptrs, w.K, w.d, idx, off, w.B, out, w.K * w.d, 0, nnz=nnz)
+            if lp == "f32":
+                D.dlrm_embbag_fwd(ptrs, w.K, w.d, idx, off, w.B, out, w.K * w.d, 0, nnz=nnz)
+            else:
+                D.dlrm_embbag_fwd_lp(ptrs, lp_code, sbp, w.K, w.d, idx, off, w.B, out, w.K * w.d, 0, nnz=nnz)
             if timed:
                 gather_t.stop(e0, stream)
             return
@@ -331,7 +361,7 @@ def main():
     nnz_mean = float(np.mean([b[5] for b in dbatches]))
     if model is None or "embbag" in breakdown:
         kname, key = "embbag_fwd_kernel", None
-        gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean)
+        gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean, lp)
         g_ms = gather_t.mean_ms() if model is None else breakdown["embbag"]
     else:
         # fused pooled lookup + interaction: every looked-up row, indices and
@@ -342,7 +372,8 @@ def main():
                   esz * w.B * model.top_ld)
         g_ms = breakdown[key]
     achieved = gbytes / (g_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w.name + ("_uniform" if args.uniform else "") + ("_chain" if args.chain else ""), kname)
+    traffic = measured_traffic(w.name + ("_uniform" if args.uniform else "") + ("_chain" if args.chain else "") +
+                               ("" if lp == "f32" else "_" + lp), kname)
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(gbytes), "avg_launch_ms": round(g_ms, 4)}
@@ -351,11 +382,13 @@ def main():
     if not args.no_cpu_baseline:
         ns = args.cpu_samples or {"forward": 16384, "embbag": 16384, "interaction": 512, "train": 1024,
                                   "tiny": 128}[w.name]
-        S, dt, thr, passes = cpu_baseline(w, batches, bottom, top, ns, chain=args.chain)
+        S, dt, thr, passes = cpu_baseline(w, batches, bottom, top, ns, chain=args.chain, table_dtype=lp)
         what = {"forward": "forward pass", "embbag": "pooled lookups", "interaction": "forward pass",
                 "train": "forward pass and sparse SGD update", "tiny": "forward pass"}[w.name]
         if args.chain:
             what = "forward pass and the whole backward from the loss with the sparse SGD update"
+        if lp != "f32":
+            what = f"pooled lookups from {lp} rows"
         cpu = {"value": round(S / dt, 2), "unit": "samples/s", "cores": thr, "kind": "oracle",
                "sample": f"{what} of the first {S // passes} samples of batch 0, repeated {passes} times "
                          f"({dt:.1f} s; tables regenerated for the touched rows only, outside the timed region)"}
@@ -363,7 +396,7 @@ def main():
     cfg = {"workload": w.name, "batch": w.B, "tables": w.K, "d": w.d, "rows_total": int(sum(w.rows)),
            "bag": f"{w.bag}:{w.bag_len}", "index": f"{w.index_dist}" + (f"({w.alpha})" if w.index_dist == "zipf" else ""),
            "bottom_mlp": "-".join(map(str, w.bottom)), "top_mlp": "-".join(map(str, w.top)),
-           "mlp_dtype": w.mlp_dtype, "table_dtype": "f32", "batches_rotated": args.batches}
+           "mlp_dtype": w.mlp_dtype, "table_dtype": lp, "batches_rotated": args.batches}
     if w.train:
         cfg["upstream_grad"] = "from the loss (interaction backward)" if args.chain else "synthetic G"
     res = {"metric": METRIC, "value": round(value, 1), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdlrm.so")
 
 DLRM_OK, DLRM_E_INVALID, DLRM_E_WORKSPACE, DLRM_E_HIP, DLRM_E_UNSUPPORTED = 0, -1, -2, -3, -4
-DLRM_F32, DLRM_BF16 = 0, 1
+DLRM_F32, DLRM_BF16, DLRM_I8 = 0, 1, 2
 DLRM_ACT_NONE, DLRM_ACT_RELU = 0, 1
 
 _P = ctypes.c_void_p
@@ -27,6 +27,7 @@ _SIGNATURES = {
     "dlrm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "dlrm_last_hip_error": (ctypes.c_int, []),
     "dlrm_embbag_fwd": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I64, _I64, _P, _I64, _I64, _P]),
+    "dlrm_embbag_fwd_lp": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "dlrm_interact_fwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I32, _I64, _P]),
     "dlrm_embbag_interact_fwd": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I64, _P]),
     "dlrm_interact_bwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I64, _P, _I64, _P]),
@@ -124,6 +125,16 @@ def dlrm_embbag_fwd(table_ptrs, K: int, d: int, indices, offsets, B: int, out, o
     """nnz: offsets[K*B] when known on the host (sizes the work split), else -1."""
     _check("dlrm_embbag_fwd", lib().dlrm_embbag_fwd(_ptr(table_ptrs), K, d, _ptr(indices), _ptr(offsets), B, nnz,
                                                      _ptr(out), out_ld, out_col0, _stream(stream)))
+
+
+def dlrm_embbag_fwd_lp(table_ptrs, table_dtype: int, scale_bias_ptrs, K: int, d: int, indices, offsets, B: int, out,
+                       out_ld: int, out_col0: int = 0, stream=None, nnz: int = -1) -> None:
+    """Low-precision table rows: table_dtype DLRM_BF16, or DLRM_I8 with
+    scale_bias_ptrs (K device pointers to fp32 [m_k][2]); None for bf16."""
+    sb = _ptr(scale_bias_ptrs) if scale_bias_ptrs is not None else None
+    _check("dlrm_embbag_fwd_lp", lib().dlrm_embbag_fwd_lp(_ptr(table_ptrs), table_dtype, sb, K, d, _ptr(indices),
+                                                           _ptr(offsets), B, nnz, _ptr(out), out_ld, out_col0,
+                                                           _stream(stream)))
 
 
 def dlrm_interact_fwd(X, B: int, n: int, d: int, x_ld: int, out, out_ld: int, stream=None) -> None:

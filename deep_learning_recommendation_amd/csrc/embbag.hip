@@ -31,14 +31,88 @@
 namespace dlrm {
 namespace {
 
-template <int V, int U>
-__global__ __launch_bounds__(256) void embbag_fwd_kernel(const float* const* __restrict__ tables, int32_t d,
+// Table-row formats.  A lane loads one piece of a row (kVec x 4 consecutive
+// columns) and turns it into kVec float4 when it is added:
+//   fp32: 16 bytes, 4 columns.
+//   bf16: 16 bytes, 8 columns (4 when d is not a multiple of 8), each value
+//         widened exactly.
+//   int8: 16 bytes, 16 columns (4 when d is not a multiple of 16), each value
+//         dequantised with the row's scale s and bias z as (s * q) + z, two
+//         fp32 roundings (no fused multiply-add).
+// Loads are kept raw until the add so that the rows in flight cost the same
+// registers in every format.
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float deq(uint32_t u, int sh, float2 sz) {
+  return __fadd_rn(__fmul_rn(sz.x, (float)(int8_t)(u >> sh)), sz.y);
+}
+__device__ __forceinline__ float4 deq4(uint32_t u, float2 sz) {
+  return make_float4(deq(u, 0, sz), deq(u, 8, sz), deq(u, 16, sz), deq(u, 24, sz));
+}
+struct RowF32 {
+  typedef float T;
+  typedef uint4 Raw;
+  static constexpr int kVec = 1;
+  static constexpr bool kScaled = false;
+  __device__ static Raw load(const T* row, int ch) { return *reinterpret_cast<const uint4*>(row + 4 * ch); }
+  __device__ static void decode(Raw r, float2, float4 (&o)[kVec]) {
+    o[0] = make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w));
+  }
+};
+struct RowBF16 {
+  typedef uint16_t T;
+  typedef uint2 Raw;
+  static constexpr int kVec = 1;
+  static constexpr bool kScaled = false;
+  __device__ static Raw load(const T* row, int ch) { return *reinterpret_cast<const uint2*>(row + 4 * ch); }
+  __device__ static void decode(Raw r, float2, float4 (&o)[kVec]) {
+    o[0] = make_float4(bf_lo(r.x), bf_hi(r.x), bf_lo(r.y), bf_hi(r.y));
+  }
+};
+struct RowBF16x8 {
+  typedef uint16_t T;
+  typedef uint4 Raw;
+  static constexpr int kVec = 2;
+  static constexpr bool kScaled = false;
+  __device__ static Raw load(const T* row, int ch) { return *reinterpret_cast<const uint4*>(row + 8 * ch); }
+  __device__ static void decode(Raw r, float2, float4 (&o)[kVec]) {
+    o[0] = make_float4(bf_lo(r.x), bf_hi(r.x), bf_lo(r.y), bf_hi(r.y));
+    o[1] = make_float4(bf_lo(r.z), bf_hi(r.z), bf_lo(r.w), bf_hi(r.w));
+  }
+};
+struct RowI8 {
+  typedef int8_t T;
+  typedef uint32_t Raw;
+  static constexpr int kVec = 1;
+  static constexpr bool kScaled = true;
+  __device__ static Raw load(const T* row, int ch) { return *reinterpret_cast<const uint32_t*>(row + 4 * ch); }
+  __device__ static void decode(Raw r, float2 sz, float4 (&o)[kVec]) { o[0] = deq4(r, sz); }
+};
+struct RowI8x16 {
+  typedef int8_t T;
+  typedef uint4 Raw;
+  static constexpr int kVec = 4;
+  static constexpr bool kScaled = true;
+  __device__ static Raw load(const T* row, int ch) { return *reinterpret_cast<const uint4*>(row + 16 * ch); }
+  __device__ static void decode(Raw r, float2 sz, float4 (&o)[kVec]) {
+    o[0] = deq4(r.x, sz);
+    o[1] = deq4(r.y, sz);
+    o[2] = deq4(r.z, sz);
+    o[3] = deq4(r.w, sz);
+  }
+};
+
+// NC pieces per lane (piece ch = lane-in-group + j * G), U rows in flight.
+template <int NC, int U, typename R = RowF32>
+__global__ __launch_bounds__(256) void embbag_fwd_kernel(const typename R::T* const* __restrict__ tables,
+                                                         const float* const* __restrict__ scale_bias, int32_t d,
                                                          int32_t g_log2, int32_t CB,
                                                          const int64_t* __restrict__ idx,
                                                          const int64_t* __restrict__ off, int64_t B,
                                                          int64_t chunks_per_table, int64_t total_chunks,
                                                          float* __restrict__ out, int64_t out_ld,
                                                          int64_t out_col0) {
+  constexpr int KV = R::kVec;
   const int lane = threadIdx.x & 63;
   const int G = 1 << g_log2;
   const int gl = lane & (G - 1);
@@ -52,8 +126,9 @@ __global__ __launch_bounds__(256) void embbag_fwd_kernel(const float* const* __r
   const int64_t bag0 = k * B + b0;
   // lane j of the group holds the start of bag j; lane nb holds the end of the chunk
   const int64_t my_off = off[bag0 + min(gl, nb)];
-  const float* __restrict__ T = tables[k];
-  const int d4 = d >> 2;
+  const typename R::T* __restrict__ T = tables[k];
+  const float2* __restrict__ SB = R::kScaled ? reinterpret_cast<const float2*>(scale_bias[k]) : nullptr;
+  const int npc = d / (4 * KV);  // pieces per row
 
   const int64_t P0 = __shfl(my_off, gbase, 64);
   const int64_t P1 = __shfl(my_off, gbase + nb, 64);
@@ -61,17 +136,22 @@ __global__ __launch_bounds__(256) void embbag_fwd_kernel(const float* const* __r
   int64_t cur_end = __shfl(my_off, gbase + 1, 64);
   float* obase = out + out_col0 + k * (int64_t)d;
 
-  float4 acc[V];
+  float4 acc[NC][KV];
 #pragma unroll
-  for (int j = 0; j < V; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int v = 0; v < KV; ++v) acc[j][v] = make_float4(0.f, 0.f, 0.f, 0.f);
 
   auto flush = [&]() {
     float* o = obase + (b0 + cb) * out_ld;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int c4 = gl + j * G;
-      if (c4 < d4) *reinterpret_cast<float4*>(o + 4 * c4) = acc[j];
-      acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < NC; ++j) {
+      const int ch = gl + j * G;
+#pragma unroll
+      for (int v = 0; v < KV; ++v) {
+        if (ch < npc) *reinterpret_cast<float4*>(o + 4 * (KV * ch + v)) = acc[j][v];
+        acc[j][v] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
     ++cb;
     cur_end = __shfl(my_off, gbase + min(cb + 1, nb), 64);
@@ -82,15 +162,16 @@ __global__ __launch_bounds__(256) void embbag_fwd_kernel(const float* const* __r
   for (int u = 0; u < U; ++u) ridx[u] = (P0 + u < P1) ? idx[P0 + u] : 0;
 
   for (int64_t p = P0; p < P1; p += U) {
-    float4 v[U][V];
+    typename R::Raw raw[U][NC];
+    float2 sz[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float* row = T + ridx[u] * (int64_t)d;
+      const typename R::T* row = T + ridx[u] * (int64_t)d;
+      sz[u] = (R::kScaled && p + u < P1) ? SB[ridx[u]] : make_float2(0.f, 0.f);
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const int c4 = gl + j * G;
-        v[u][j] = (p + u < P1 && c4 < d4) ? *reinterpret_cast<const float4*>(row + 4 * c4)
-                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < NC; ++j) {
+        const int ch = gl + j * G;
+        raw[u][j] = (p + u < P1 && ch < npc) ? R::load(row, ch) : typename R::Raw{};
       }
     }
     const int64_t pn = p + U;
@@ -101,11 +182,16 @@ __global__ __launch_bounds__(256) void embbag_fwd_kernel(const float* const* __r
       if (p + u < P1) {
         while (p + u >= cur_end) flush();
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-          acc[j].x = acc[j].x + v[u][j].x;
-          acc[j].y = acc[j].y + v[u][j].y;
-          acc[j].z = acc[j].z + v[u][j].z;
-          acc[j].w = acc[j].w + v[u][j].w;
+        for (int j = 0; j < NC; ++j) {
+          float4 t[KV];
+          R::decode(raw[u][j], sz[u], t);
+#pragma unroll
+          for (int v = 0; v < KV; ++v) {
+            acc[j][v].x = acc[j][v].x + t[v].x;
+            acc[j][v].y = acc[j][v].y + t[v].y;
+            acc[j][v].z = acc[j][v].z + t[v].z;
+            acc[j][v].w = acc[j][v].w + t[v].w;
+          }
         }
       }
     }
@@ -146,19 +232,17 @@ __global__ __launch_bounds__(256) void check_indices_kernel(const int64_t* __res
 
 using namespace dlrm;
 
-extern "C" int dlrm_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const int64_t* indices,
-                               const int64_t* offsets, int64_t B, int64_t nnz, float* out, int64_t out_ld,
-                               int64_t out_col0, hipStream_t stream) {
-  if (!tables || !indices || !offsets || !out) return DLRM_E_INVALID;
-  if (K < 1 || B < 1 || d < 4 || d > 1024 || (d % 4) != 0) return DLRM_E_INVALID;
-  if (out_col0 < 0 || out_ld < out_col0 + (int64_t)K * d) return DLRM_E_INVALID;
-  if (!aligned16(out) || (out_ld % 4) != 0 || (out_col0 % 4) != 0) return DLRM_E_INVALID;
-
-  const int d4 = d / 4;
+namespace dlrm {
+namespace {
+template <typename R>
+int launch_embbag(const typename R::T* const* tables, const float* const* scale_bias, int32_t K, int32_t d,
+                  const int64_t* indices, const int64_t* offsets, int64_t B, int64_t nnz, float* out, int64_t out_ld,
+                  int64_t out_col0, hipStream_t stream) {
+  const int npc = d / (4 * R::kVec);  // pieces per row, one per lane
   int g_log2 = 1;
-  while ((1 << g_log2) < d4 && g_log2 < 6) ++g_log2;
+  while ((1 << g_log2) < npc && g_log2 < 6) ++g_log2;
   const int G = 1 << g_log2;
-  const int Vneed = (d4 + G - 1) / G;  // 1..4
+  const int Vneed = (npc + G - 1) / G;  // 1..4 pieces per lane
   const int64_t bags = (int64_t)K * B;
   // CB <= G - 1; without nnz, enough chunks to fill the chip several times over
   int64_t cb = bags / 65536;
@@ -173,15 +257,54 @@ extern "C" int dlrm_embbag_fwd(const float* const* tables, int32_t K, int32_t d,
   if (blocks > 0x7fffffffLL) return DLRM_E_UNSUPPORTED;
   const dim3 grid((unsigned)blocks), block(256);
   if (Vneed == 1)
-    hipLaunchKernelGGL((embbag_fwd_kernel<1, 8>), grid, block, 0, stream, tables, d, g_log2, CB, indices, offsets, B,
-                       chunks_per_table, total, out, out_ld, out_col0);
+    hipLaunchKernelGGL((embbag_fwd_kernel<1, 8, R>), grid, block, 0, stream, tables, scale_bias, d, g_log2, CB,
+                       indices, offsets, B, chunks_per_table, total, out, out_ld, out_col0);
   else if (Vneed == 2)
-    hipLaunchKernelGGL((embbag_fwd_kernel<2, 4>), grid, block, 0, stream, tables, d, g_log2, CB, indices, offsets, B,
-                       chunks_per_table, total, out, out_ld, out_col0);
+    hipLaunchKernelGGL((embbag_fwd_kernel<2, 4, R>), grid, block, 0, stream, tables, scale_bias, d, g_log2, CB,
+                       indices, offsets, B, chunks_per_table, total, out, out_ld, out_col0);
   else
-    hipLaunchKernelGGL((embbag_fwd_kernel<4, 2>), grid, block, 0, stream, tables, d, g_log2, CB, indices, offsets, B,
-                       chunks_per_table, total, out, out_ld, out_col0);
+    hipLaunchKernelGGL((embbag_fwd_kernel<4, 2, R>), grid, block, 0, stream, tables, scale_bias, d, g_log2, CB,
+                       indices, offsets, B, chunks_per_table, total, out, out_ld, out_col0);
   return launch_status();
+}
+
+int check_embbag_args(const void* tables, int32_t K, int32_t d, const int64_t* indices, const int64_t* offsets,
+                      int64_t B, float* out, int64_t out_ld, int64_t out_col0) {
+  if (!tables || !indices || !offsets || !out) return DLRM_E_INVALID;
+  if (K < 1 || B < 1 || d < 4 || d > 1024 || (d % 4) != 0) return DLRM_E_INVALID;
+  if (out_col0 < 0 || out_ld < out_col0 + (int64_t)K * d) return DLRM_E_INVALID;
+  if (!aligned16(out) || (out_ld % 4) != 0 || (out_col0 % 4) != 0) return DLRM_E_INVALID;
+  return DLRM_OK;
+}
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int dlrm_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const int64_t* indices,
+                               const int64_t* offsets, int64_t B, int64_t nnz, float* out, int64_t out_ld,
+                               int64_t out_col0, hipStream_t stream) {
+  const int rc = check_embbag_args(tables, K, d, indices, offsets, B, out, out_ld, out_col0);
+  if (rc != DLRM_OK) return rc;
+  return launch_embbag<RowF32>(tables, nullptr, K, d, indices, offsets, B, nnz, out, out_ld, out_col0, stream);
+}
+
+extern "C" int dlrm_embbag_fwd_lp(const void* const* tables, int32_t table_dtype, const float* const* scale_bias,
+                                  int32_t K, int32_t d, const int64_t* indices, const int64_t* offsets, int64_t B,
+                                  int64_t nnz, float* out, int64_t out_ld, int64_t out_col0, hipStream_t stream) {
+  const int rc = check_embbag_args(tables, K, d, indices, offsets, B, out, out_ld, out_col0);
+  if (rc != DLRM_OK) return rc;
+  if (table_dtype == DLRM_BF16) {
+    const auto* t = reinterpret_cast<const uint16_t* const*>(tables);
+    if (d % 8 == 0) return launch_embbag<RowBF16x8>(t, nullptr, K, d, indices, offsets, B, nnz, out, out_ld, out_col0, stream);
+    return launch_embbag<RowBF16>(t, nullptr, K, d, indices, offsets, B, nnz, out, out_ld, out_col0, stream);
+  }
+  if (table_dtype == DLRM_I8) {
+    if (!scale_bias) return DLRM_E_INVALID;
+    const auto* t = reinterpret_cast<const int8_t* const*>(tables);
+    if (d % 16 == 0)
+      return launch_embbag<RowI8x16>(t, scale_bias, K, d, indices, offsets, B, nnz, out, out_ld, out_col0, stream);
+    return launch_embbag<RowI8>(t, scale_bias, K, d, indices, offsets, B, nnz, out, out_ld, out_col0, stream);
+  }
+  return DLRM_E_INVALID;
 }
 
 extern "C" int dlrm_check_indices(const int64_t* indices, const int64_t* offsets, int32_t K, int64_t B,

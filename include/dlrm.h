@@ -52,8 +52,8 @@ enum {
   DLRM_E_UNSUPPORTED = -4
 };
 
-/* element types */
-enum { DLRM_F32 = 0, DLRM_BF16 = 1 };
+/* element types (DLRM_I8: table rows only, with a per-row fp32 scale and bias) */
+enum { DLRM_F32 = 0, DLRM_BF16 = 1, DLRM_I8 = 2 };
 
 /* activation after a layer */
 enum { DLRM_ACT_NONE = 0, DLRM_ACT_RELU = 1 };
@@ -88,6 +88,27 @@ int dlrm_last_hip_error(void);
 int dlrm_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const int64_t* indices,
                     const int64_t* offsets, int64_t B, int64_t nnz, float* out, int64_t out_ld, int64_t out_col0,
                     hipStream_t stream);
+
+/*
+ * Embedding lookup with sum pooling from low-precision table rows.
+ * Quantised tables are what a bandwidth-bound recommendation model gains
+ * from (the explainer's citations in Evaluation & Benchmarks: a survey of
+ * quantisation notes it pays where the problem is bandwidth-bound, as in
+ * recommendation systems).  Each value read is first turned into fp32, then
+ * pooled exactly as dlrm_embbag_fwd (fp32, bag order, from +0.0):
+ *   DLRM_BF16  T_k is bf16 [m_k][d] (2 bytes per value): widened exactly.
+ *   DLRM_I8    T_k is int8 [m_k][d] (1 byte per value) and scale_bias[k] is
+ *              fp32 [m_k][2] = (s, z) per row: value = (s * q) + z, rounded
+ *              to fp32 after the product and again after the sum (no fused
+ *              multiply-add).
+ * Bit-exact.  Arguments as dlrm_embbag_fwd; tables hold K device pointers to
+ * 16-byte aligned tables of table_dtype; scale_bias (DLRM_I8 only, else
+ * ignored) K device pointers to 8-byte aligned fp32 [m_k][2].  Other
+ * table_dtype values: DLRM_E_INVALID.
+ */
+int dlrm_embbag_fwd_lp(const void* const* tables, int32_t table_dtype, const float* const* scale_bias, int32_t K,
+                       int32_t d, const int64_t* indices, const int64_t* offsets, int64_t B, int64_t nnz, float* out,
+                       int64_t out_ld, int64_t out_col0, hipStream_t stream);
 
 /*
  * Pairwise dot-product interaction, packed strict lower triangle, concat.

@@ -143,3 +143,108 @@ def test_check_indices_counts_bad_entries():
     D.dlrm_check_indices(to_dev(idx), to_dev(off), K, B, to_dev(rows), bad)
     torch.cuda.synchronize()
     assert int(bad.item()) == 3
+
+
+# ----------------------------------------------------------------- low-precision table rows
+
+def _run_lp(tabs_dev, sbs_dev, dtype, idx, off, B, d, nnz=None):
+    import deep_learning_recommendation_amd as D
+
+    K = len(tabs_dev)
+    out = torch.full((B, K * d), float("nan"), dtype=torch.float32, device=DEV)
+    code = D.DLRM_BF16 if dtype == "bf16" else D.DLRM_I8
+    sbp = D.device_pointer_array(sbs_dev) if sbs_dev is not None else None
+    D.dlrm_embbag_fwd_lp(D.device_pointer_array(tabs_dev), code, sbp, K, d, to_dev(idx), to_dev(off), B, out, K * d, 0,
+                         nnz=int(off[-1]) if nnz is None else nnz)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _lp_tables(g, dtype, rows, d):
+    """bf16: high halves of random fp32 values (uint16); int8: random bytes
+    with per-row scale and bias."""
+    if dtype == "bf16":
+        tabs = [(g.standard_normal((m, d)).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+                for m in rows]
+        return tabs, None
+    tabs = [g.integers(-128, 128, size=(m, d)).astype(np.int8) for m in rows]
+    sbs = [np.stack([g.uniform(1e-3, 2e-2, m), g.normal(0, 1e-2, m)], axis=1).astype(np.float32) for m in rows]
+    return tabs, sbs
+
+
+def _dev_lp(tabs, sbs):
+    td = [to_dev(t.view(np.int16) if t.dtype == np.uint16 else t) for t in tabs]
+    return td, (None if sbs is None else [to_dev(s) for s in sbs])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("d", [4, 16, 64, 128, 132, 256, 260, 1024])
+def test_embbag_lp_random_ragged_bitexact(dtype, d):
+    K, B = 3, 701
+    banner(f"embbag lp {dtype} d={d} K={K} B={B}")
+    g = np.random.default_rng(d + (7 if dtype == "int8" else 0))
+    rows = [50, 333, 7]
+    tabs, sbs = _lp_tables(g, dtype, rows, d)
+    _, idx, off = _rand_case(d + 3, K, B, d, rows, 45)
+    td, sd = _dev_lp(tabs, sbs)
+    got = _run_lp(td, sd, dtype, idx, off, B, d)
+    ref = oracle.embbag_fwd_lp(tabs, dtype, idx, off, B, scale_bias=sbs)
+    assert np.array_equal(bits(got), bits(ref))
+    got2 = _run_lp(td, sd, dtype, idx, off, B, d, nnz=-1)  # other work split, same bits
+    assert np.array_equal(bits(got2), bits(ref))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "int8"])
+def test_embbag_lp_device_fill_matches_host_generator(dtype):
+    w = W.get("tiny")
+    banner(f"embbag lp device fill {dtype}")
+    tabs_dev, sbs_dev = SD.make_tables_lp(w, dtype)
+    torch.cuda.synchronize()
+    for k in range(w.K):
+        ids = np.arange(w.rows[k])
+        if dtype == "bf16":
+            host = R.table_rows_bf16(w.seed, k, w.rows[k], ids, w.d)
+            assert np.array_equal(tabs_dev[k].cpu().numpy().view(np.uint16), host)
+        else:
+            q, sb = R.table_rows_i8(w.seed, k, w.rows[k], ids, w.d)
+            assert np.array_equal(tabs_dev[k].cpu().numpy(), q)
+            assert np.array_equal(sbs_dev[k].cpu().numpy().view(np.uint32), sb.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "int8"])
+def test_embbag_lp_full_size_sampled(dtype):
+    """The gather microbenchmark's full-size workload with bf16 / int8 rows, in
+    the benchmark's launch configuration; sampled bags against the oracle on
+    regenerated rows."""
+    w = W.get("embbag")
+    banner(f"embbag lp full size {dtype}: K={w.K} rows={w.rows[0]} B={w.B}")
+    idx, off = W.indices_offsets(w)
+    tabs_dev, sbs_dev = SD.make_tables_lp(w, dtype)
+    out = torch.empty((w.B, w.K * w.d), dtype=torch.float32, device=DEV)
+    import deep_learning_recommendation_amd as D
+
+    code = D.DLRM_BF16 if dtype == "bf16" else D.DLRM_I8
+    sbp = D.device_pointer_array(sbs_dev) if sbs_dev is not None else None
+    D.dlrm_embbag_fwd_lp(D.device_pointer_array(tabs_dev), code, sbp, w.K, w.d, to_dev(idx), to_dev(off), w.B, out,
+                         w.K * w.d, 0, nnz=len(idx))
+    torch.cuda.synchronize()
+    samples = np.sort(np.random.default_rng(2).choice(w.B, 512, replace=False))
+    samples[-1] = w.B - 1
+    got = out[torch.from_numpy(samples).to(DEV)].cpu().numpy()
+    sidx, soff = W.sub_bags(idx, off, w.K, w.B, samples)
+    S = len(samples)
+    tabs, sbs, local = [], [], np.empty_like(sidx)
+    for k in range(w.K):
+        a, b = int(soff[k * S]), int(soff[(k + 1) * S])
+        u, inv = np.unique(sidx[a:b], return_inverse=True)
+        local[a:b] = inv
+        if dtype == "bf16":
+            tabs.append(R.table_rows_bf16(w.seed, k, w.rows[k], u, w.d))
+        else:
+            q, sb = R.table_rows_i8(w.seed, k, w.rows[k], u, w.d)
+            tabs.append(q)
+            sbs.append(sb)
+    ref = oracle.embbag_fwd_lp(tabs, dtype, local, soff, S, scale_bias=sbs if dtype == "int8" else None)
+    del tabs_dev, sbs_dev
+    torch.cuda.empty_cache()
+    assert np.array_equal(bits(got), bits(ref))
