@@ -493,15 +493,16 @@ void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw,
 // Tile choice: the largest block tile that still gives every CU a tile
 // (256 x 128 only where it gives each CU two; with exactly one, 128 x 128
 // measured as fast or faster).  Deep k (a multiple of 64, at least 512) runs
-// 64-wide k-tiles in two stages, fewer barriers; shallower k 32-wide k-tiles
-// in four stages.  Every choice interleaves the operand reads with the
+// 64-wide k-tiles in two stages, fewer barriers; shallower or ragged k
+// 32-wide k-tiles in four stages.  Every choice interleaves the operand reads with the
 // MFMAs (measured 3-10% faster than reads first on every MLP shape).
 template <typename OutT, bool PARTIAL>
 void pick_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
                int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
   const int64_t t256x256 = ceil_div(M, 256) * ceil_div(N, 256) * splits;
   const int64_t t256x128 = ceil_div(M, 256) * ceil_div(N, 128) * splits;
-  const bool deep = k_per_split >= 512 && (k_per_split % 64) == 0;
+  // a partial last k-tile (K not a multiple of 64, e.g. 479) measured faster in 32-wide tiles
+  const bool deep = k_per_split >= 512 && (k_per_split % 64) == 0 && (K % 64) == 0;
   if (t256x256 >= 256 && deep)
     launch_fast<256, 256, 128, 64, OutT, PARTIAL, 64, 2, false, 2>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits,
                                                                    k_per_split, s);
