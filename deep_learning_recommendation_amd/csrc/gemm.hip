@@ -762,7 +762,14 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   if (t >= MN) return;
   const int i = (int)(t / N), j = (int)(t - (int64_t)i * N);
   float v = 0.f;
-  for (int z = 0; z < splits; ++z) v = v + part[z * MN + t];
+  for (int z0 = 0; z0 < splits; z0 += 8) {  // eight loads in flight, added in split order
+    float p[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) p[q] = (z0 + q < splits) ? part[(z0 + q) * MN + t] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (z0 + q < splits) v = v + p[q];
+  }
   if (bias) v = v + bias[j];
   if (relu) v = relu_f(v);
   C[(int64_t)i * ldc + j] = v;

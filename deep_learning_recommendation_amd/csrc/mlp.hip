@@ -403,51 +403,106 @@ __device__ __forceinline__ bool positive<uint16_t>(const uint16_t* p) {
 // and transposed [N][ldt] (for the weight gradient, K = batch contiguous),
 // plus fp32 column sums of delta per 64-row chunk (for the bias gradient).
 // Block: 64 rows x 256 columns; wave w takes rows w, w+4, ..., lane l the
-// columns l, l+64, l+128, l+192, so every global access is coalesced.
-constexpr int kDRows = 64, kDCols = 256;
+// four consecutive columns 4l .. 4l+3 (16-byte loads of g, 8- or 16-byte
+// loads of y, 8-byte stores of delta when `vec`), eight rows' loads in flight
+// before the first is used.  The column sums add the rows in the same order
+// as a one-row-at-a-time walk.
+constexpr int kDRows = 64, kDCols = 256, kDBatch = 8;
+template <typename YT>
+struct YLoad;
+template <>
+struct YLoad<float> {
+  typedef float4 V;
+  __device__ static V load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static bool pos(const V& v, int e) { return (e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w) > 0.f; }
+};
+template <>
+struct YLoad<uint16_t> {
+  typedef uint2 V;
+  __device__ static V load(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ static bool pos(const V& v, int e) {
+    const uint32_t w = (e < 2) ? v.x : v.y;
+    return bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))) > 0.f;
+  }
+};
 template <typename YT>
 __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__ g, int64_t ldg,
                                                        const YT* __restrict__ y, int64_t ldy, int relu,
                                                        uint16_t* __restrict__ dlt, int64_t ldd,
                                                        uint16_t* __restrict__ dltT, int64_t ldt,
-                                                       float* __restrict__ part, int B, int N) {
-  __shared__ uint16_t tile[kDRows][kDCols + 2];
+                                                       float* __restrict__ part, int B, int N, int vec) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kDRows][kDCols + 8];
   __shared__ float red[4][kDCols];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = blockIdx.x * kDCols, r0 = blockIdx.y * kDRows;
+  const int cl = 4 * lane, c = c0 + cl;
+  const bool full = vec && c + 4 <= N;  // this lane's four columns by vector accesses
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int i = wave; i < kDRows; i += 4) {
-    const int r = r0 + i;
+  for (int i0 = wave; i0 < kDRows; i0 += 4 * kDBatch) {
+    float4 gv[kDBatch];
+    typename YLoad<YT>::V yv[kDBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int cl = lane + 64 * e, c = c0 + cl;
-      float v = 0.f;
-      if (r < B && c < N) {
-        v = g[(int64_t)r * ldg + c];
-        if (relu && !positive<YT>(y + (int64_t)r * ldy + c)) v = 0.f;
+    for (int t = 0; t < kDBatch; ++t) {
+      const int r = r0 + i0 + 4 * t;
+      if (full && r < B) {
+        gv[t] = *reinterpret_cast<const float4*>(g + (int64_t)r * ldg + c);
+        if (relu) yv[t] = YLoad<YT>::load(y + (int64_t)r * ldy + c);
       }
-      const uint16_t h = f32_to_bf16(v);
-      tile[i][cl] = h;
-      sum[e] = sum[e] + v;
-      if (r < B && c < N) dlt[(int64_t)r * ldd + c] = h;
+    }
+#pragma unroll
+    for (int t = 0; t < kDBatch; ++t) {
+      const int i = i0 + 4 * t, r = r0 + i;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (full) {
+          v[e] = (r < B) ? (e == 0 ? gv[t].x : e == 1 ? gv[t].y : e == 2 ? gv[t].z : gv[t].w) : 0.f;
+          if (relu && r < B && !YLoad<YT>::pos(yv[t], e)) v[e] = 0.f;
+        } else {
+          v[e] = 0.f;
+          if (r < B && c + e < N) {
+            v[e] = g[(int64_t)r * ldg + c + e];
+            if (relu && !positive<YT>(y + (int64_t)r * ldy + c + e)) v[e] = 0.f;
+          }
+        }
+      }
+      uint16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(v[e]);
+        sum[e] = sum[e] + v[e];
+      }
+      *reinterpret_cast<uint2*>(&tile[i][cl]) =
+          make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      if (r < B) {
+        uint16_t* o = dlt + (int64_t)r * ldd + c;
+        if (full) {
+          *reinterpret_cast<uint2*>(o) =
+              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < N) o[e] = h[e];
+        }
+      }
     }
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) red[wave][lane + 64 * e] = sum[e];
+  for (int e = 0; e < 4; ++e) red[wave][cl + e] = sum[e];
   __syncthreads();
   {
-    const int cl = threadIdx.x, c = c0 + cl;
-    if (c < N) part[(int64_t)blockIdx.y * N + c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
-    if (c < N) {
-      // column c of the tile is row c of delta^T: 64 rows, 8 per 16-byte store
-      uint16_t* dst = dltT + (int64_t)c * ldt + r0;
+    const int cc = threadIdx.x, col = c0 + cc;
+    if (col < N) part[(int64_t)blockIdx.y * N + col] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
+    if (col < N) {
+      // column cc of the tile is row col of delta^T: 64 rows, 8 per 16-byte store
+      uint16_t* dst = dltT + (int64_t)col * ldt + r0;
 #pragma unroll
       for (int j = 0; j < kDRows / 8; ++j) {
         if (r0 + 8 * j >= B) break;
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          w[q] = (uint32_t)tile[8 * j + 2 * q][cl] | ((uint32_t)tile[8 * j + 2 * q + 1][cl] << 16);
+          w[q] = (uint32_t)tile[8 * j + 2 * q][cc] | ((uint32_t)tile[8 * j + 2 * q + 1][cc] << 16);
         *reinterpret_cast<uint4*>(dst + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
@@ -463,7 +518,14 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
   const int o = blockIdx.x * 64 + lane;
   float s = 0.f;
   if (o < N)
-    for (int c = wave; c < chunks; c += 4) s = s + part[(int64_t)c * N + o];
+    for (int c0 = wave; c0 < chunks; c0 += 32) {  // eight loads in flight, added in chunk order
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = (c0 + 4 * t < chunks) ? part[(int64_t)(c0 + 4 * t) * N + o] : 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (c0 + 4 * t < chunks) s = s + v[t];
+    }
   red[wave][lane] = s;
   __syncthreads();
   if (wave == 0 && o < N) db[o] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
@@ -683,15 +745,22 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     const bool relu = (l < L - 1) || last_act == DLRM_ACT_RELU;
     const dim3 b1(256), gd((unsigned)ceil_div(fo, kDCols), (unsigned)chunks);
     // 1. delta (bf16, both layouts) and the bias-gradient partials
+    // vector accesses: g 16-byte, delta 8-byte and y (16-byte fp32 / 8-byte bf16) aligned rows
+    auto al = [](const void* p, int64_t ld, int esz, int bytes) {
+      return (reinterpret_cast<uintptr_t>(p) % bytes) == 0 && ((ld * esz) % bytes) == 0;
+    };
+    const bool vg = al(g, ldg, 4, 16) && al(dlt, bl.ld_dlt, 2, 8);
     if (l == L - 1) {
       const float* y = relu ? out : g;  // mask source unused when relu == 0
       const int64_t ldy = relu ? out_ld : ldg;
+      const int vec = vg && al(y, ldy, 4, 16);
       hipLaunchKernelGGL((delta_db_kernel<float>), gd, b1, 0, stream, g, ldg, y, ldy, (int)relu, dlt, bl.ld_dlt, dltT,
-                         bl.ld_B, dbp, M, fo);
+                         bl.ld_B, dbp, M, fo, vec);
     } else {
       const uint16_t* y = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l + 1]);
+      const int vec = vg && al(y, fl.act_ld[l + 1], 2, 8);
       hipLaunchKernelGGL((delta_db_kernel<uint16_t>), gd, b1, 0, stream, g, ldg, y, fl.act_ld[l + 1], (int)relu, dlt,
-                         bl.ld_dlt, dltT, bl.ld_B, dbp, M, fo);
+                         bl.ld_dlt, dltT, bl.ld_B, dbp, M, fo, vec);
     }
     hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 64)), b1, 0, stream, dbp, chunks, fo, db[l]);
     if ((rc = launch_status()) != DLRM_OK) break;
