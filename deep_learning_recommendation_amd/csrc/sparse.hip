@@ -43,31 +43,25 @@ constexpr int kLightBlocks = 2048;
 
 // ------------------------------------------------------------------ keys
 
-// Each thread takes 8 consecutive positions: one binary search in the
-// offsets for the first position's bag, then a forward walk.
-constexpr int KEY_ITEMS = 8;
+// One group of G lanes per bag (G about the mean bag length, at most 64):
+// the group walks the bag's positions with stride G, so the index reads and
+// the key and bag-id writes of a wave are contiguous runs.
 __global__ __launch_bounds__(256) void build_keys_kernel(const int64_t* __restrict__ idx,
                                                          const int64_t* __restrict__ off, int64_t KB, int64_t B,
-                                                         int64_t n, int row_bits, uint32_t* __restrict__ keys,
+                                                         int g_log2, int row_bits, uint32_t* __restrict__ keys,
                                                          int32_t* __restrict__ vals) {
-  const int64_t p0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * KEY_ITEMS;
-  if (p0 >= n) return;
-  int64_t lo = 0, hi = KB - 1;  // largest kb with off[kb] <= p0
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= p0) lo = mid;
-    else hi = mid - 1;
-  }
-  int64_t kb = lo, next = off[kb + 1];
-#pragma unroll
-  for (int i = 0; i < KEY_ITEMS; ++i) {
-    const int64_t p = p0 + i;
-    if (p < n) {
-      while (next <= p) next = off[++kb + 1];
-      const int64_t k = kb / B;
-      keys[p] = ((uint32_t)k << row_bits) | (uint32_t)idx[p];
-      vals[p] = (int32_t)(kb - k * B);
-    }
+  const int G = 1 << g_log2;
+  const int64_t bag = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> g_log2;
+  if (bag >= KB) return;  // whole group
+  const int gl = threadIdx.x & (G - 1);
+  const int64_t a = off[bag], e = off[bag + 1];
+  const int64_t k = bag / B;
+  const uint32_t hi = (uint32_t)k << row_bits;
+  const int32_t b = (int32_t)(bag - k * B);
+#pragma unroll 4
+  for (int64_t p = a + gl; p < e; p += G) {
+    keys[p] = hi | (uint32_t)idx[p];
+    vals[p] = b;
   }
 }
 
@@ -79,10 +73,30 @@ __global__ __launch_bounds__(RT) void radix_hist_kernel(const uint32_t* __restri
   cnt[threadIdx.x] = 0;
   __syncthreads();
   const int base = blockIdx.x * RTILE;
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // lanes with equal digits found by eight ballots; the lowest of them adds
+  // the group's count (Zipf keys share digits, so one atomic per group
+  // instead of one per key)
+  uint32_t kv[RITEMS];
 #pragma unroll
   for (int i = 0; i < RITEMS; ++i) {
     const int p = base + i * RT + threadIdx.x;
-    if (p < n) atomicAdd(&cnt[(keys[p] >> shift) & 255u], 1u);
+    kv[i] = p < n ? keys[p] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < RITEMS; ++i) {
+    const int p = base + i * RT + threadIdx.x;
+    const bool valid = p < n;
+    const uint32_t digit = (kv[i] >> shift) & 255u;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (digit >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    if (valid && (peers & lt) == 0ull) atomicAdd(&cnt[digit], (uint32_t)__popcll(peers));
   }
   __syncthreads();
   hist[(int64_t)threadIdx.x * nblocks + blockIdx.x] = cnt[threadIdx.x];
@@ -731,8 +745,14 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
   const int64_t KB = (int64_t)K * B;
 
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, counters, 16);
-  hipLaunchKernelGGL(build_keys_kernel, dim3((unsigned)ceil_div(nnz, 256 * KEY_ITEMS)), dim3(256), 0, stream, indices,
-                     offsets, KB, B, nnz, row_bits, keys[0], vals[0]);
+  {
+    int kg = 0;  // lanes per bag: the mean bag length rounded up to a power of two, at most 64
+    while ((1LL << kg) * KB < nnz && kg < 6) ++kg;
+    const int64_t kblocks = ceil_div(KB << kg, 256);
+    if (kblocks > 0x7fffffffLL) return DLRM_E_UNSUPPORTED;
+    hipLaunchKernelGGL(build_keys_kernel, dim3((unsigned)kblocks), dim3(256), 0, stream, indices, offsets, KB, B, kg,
+                       row_bits, keys[0], vals[0]);
+  }
   const int key_bits = row_bits + table_bits;
   const int passes = (key_bits + 7) / 8;
   const int nblocks = (int)L.nblocks;
