@@ -74,8 +74,8 @@ def parse():
     p.add_argument("--batches", type=int, default=2, help="distinct input batches rotated over the steps")
     p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
     p.add_argument("--table-dtype", default="f32", choices=["f32", "bf16", "int8"],
-                   help="gather microbenchmark only: table rows stored as fp32, bf16, or int8 with a per-row scale "
-                        "and bias (dlrm_embbag_fwd_lp)")
+                   help="forward workloads: table rows stored as fp32, bf16, or int8 with a per-row scale "
+                        "and bias (dlrm_embbag_fwd_lp, dlrm_embbag_interact_fwd_lp)")
     p.add_argument("--path", default="auto", choices=["auto", "fused", "two-call"],
                    help="pooled lookup + interaction: one fused call, two calls (X materialised), or auto (fused "
                         "for short bags)")
@@ -163,9 +163,9 @@ def cpu_baseline(w, batches, bottom, top, n_samples, chain=False, min_seconds=10
         if chain:
             return chain_pass()
         if lp != "f32":
-            oracle.embbag_fwd_lp(tabs, lp, local, soff, S, scale_bias=sbs)
-            return
-        E = oracle.embbag_fwd(tabs, local, soff, S)
+            E = oracle.embbag_fwd_lp(tabs, lp, local, soff, S, scale_bias=sbs)
+        else:
+            E = oracle.embbag_fwd(tabs, local, soff, S)
         if w.name != "embbag":
             x0, _, _ = oracle.mlp_fwd(dense[:S], [p[0] for p in bottom], [p[2] for p in bottom], quant, True)
             X = np.concatenate([x0, E], axis=1).reshape(S, w.n, w.d)
@@ -216,8 +216,8 @@ def main():
     if args.uniform:
         w = dataclasses.replace(w, index_dist="uniform")
     lp = args.table_dtype
-    if lp != "f32" and w.name != "embbag":
-        print("--table-dtype applies to the gather microbenchmark (--workload embbag) only", file=sys.stderr)
+    if lp != "f32" and w.train:
+        print("--table-dtype applies to forward workloads (the sparse update needs fp32 rows)", file=sys.stderr)
         sys.exit(1)
     t_setup = time.perf_counter()
     dev = "cuda"
@@ -247,7 +247,8 @@ def main():
         if args.chain and fused is True:
             print("--chain needs X: use --path auto or two-call", file=sys.stderr)
             sys.exit(1)
-        model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=w.train, fused=fused)
+        model = PL.DLRM(w.B, w.K, w.d, w.rows, tables, bp, tp, train=w.train, fused=fused, table_dtype=lp,
+                        scale_bias=sbs)
         if w.train:
             model.sparse_workspace(max(b[5] for b in dbatches))
     else:
@@ -288,11 +289,19 @@ def main():
                        model.ws_bot, w.train)
         if model.use_fused(nnz):
             mark("embbag_interact")
-            D.dlrm_embbag_interact_fwd(model.x0, model.x0_ld, model.table_ptrs, w.K, d, idx, off, w.B, model.top_in,
-                                       model.top_ld)
+            if lp == "f32":
+                D.dlrm_embbag_interact_fwd(model.x0, model.x0_ld, model.table_ptrs, w.K, d, idx, off, w.B,
+                                           model.top_in, model.top_ld)
+            else:
+                D.dlrm_embbag_interact_fwd_lp(model.x0, model.x0_ld, model.table_ptrs, model.table_code, model.sb_ptrs,
+                                              w.K, d, idx, off, w.B, model.top_in, model.top_ld)
         else:
             mark("embbag")
-            D.dlrm_embbag_fwd(model.table_ptrs, w.K, d, idx, off, w.B, model.X, n * d, d, nnz=nnz)
+            if lp == "f32":
+                D.dlrm_embbag_fwd(model.table_ptrs, w.K, d, idx, off, w.B, model.X, n * d, d, nnz=nnz)
+            else:
+                D.dlrm_embbag_fwd_lp(model.table_ptrs, model.table_code, model.sb_ptrs, w.K, d, idx, off, w.B, model.X,
+                                     n * d, d, nnz=nnz)
             mark("interact")
             D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
         mark("top_mlp")
@@ -368,7 +377,7 @@ def main():
         # offsets, the dense rows it reads and the packed top-MLP rows it writes
         kname, key = "fused_kernel", "embbag_interact"
         esz = model.top_in.element_size()
-        gbytes = (gather_bytes(w.K, w.B, w.d, nnz_mean) - 4 * w.K * w.B * w.d + 4 * w.B * w.d +
+        gbytes = (gather_bytes(w.K, w.B, w.d, nnz_mean, lp) - 4 * w.K * w.B * w.d + 4 * w.B * w.d +
                   esz * w.B * model.top_ld)
         g_ms = breakdown[key]
     achieved = gbytes / (g_ms * 1e-3) / 1e9
@@ -388,7 +397,7 @@ def main():
         if args.chain:
             what = "forward pass and the whole backward from the loss with the sparse SGD update"
         if lp != "f32":
-            what = f"pooled lookups from {lp} rows"
+            what += f" from {lp} rows"
         cpu = {"value": round(S / dt, 2), "unit": "samples/s", "cores": thr, "kind": "oracle",
                "sample": f"{what} of the first {S // passes} samples of batch 0, repeated {passes} times "
                          f"({dt:.1f} s; tables regenerated for the touched rows only, outside the timed region)"}

@@ -28,6 +28,8 @@ _SIGNATURES = {
     "dlrm_last_hip_error": (ctypes.c_int, []),
     "dlrm_embbag_fwd": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "dlrm_embbag_fwd_lp": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _P, _I64, _I64, _P, _I64, _I64, _P]),
+    "dlrm_embbag_interact_fwd_lp": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I64,
+                                                   _P]),
     "dlrm_interact_fwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I32, _I64, _P]),
     "dlrm_embbag_interact_fwd": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _P, _P, _I64, _P, _I32, _I64, _P]),
     "dlrm_interact_bwd": (ctypes.c_int, [_P, _I64, _I32, _I32, _I64, _P, _I64, _P, _I64, _P]),
@@ -147,6 +149,14 @@ def dlrm_embbag_interact_fwd(x_dense, xd_ld: int, table_ptrs, K: int, d: int, in
     _check("dlrm_embbag_interact_fwd", lib().dlrm_embbag_interact_fwd(_ptr(x_dense), xd_ld, _ptr(table_ptrs), K, d,
                                                                        _ptr(indices), _ptr(offsets), B, _ptr(out),
                                                                        _dtype_code(out), out_ld, _stream(stream)))
+
+
+def dlrm_embbag_interact_fwd_lp(x_dense, xd_ld: int, table_ptrs, table_dtype: int, scale_bias_ptrs, K: int, d: int,
+                                indices, offsets, B: int, out, out_ld: int, stream=None) -> None:
+    sb = _ptr(scale_bias_ptrs) if scale_bias_ptrs is not None else None
+    _check("dlrm_embbag_interact_fwd_lp", lib().dlrm_embbag_interact_fwd_lp(
+        _ptr(x_dense), xd_ld, _ptr(table_ptrs), table_dtype, sb, K, d, _ptr(indices), _ptr(offsets), B, _ptr(out),
+        _dtype_code(out), out_ld, _stream(stream)))
 
 
 def dlrm_interact_bwd(X, B: int, n: int, d: int, x_ld: int, g, g_ld: int, dX, dx_ld: int, stream=None) -> None:

@@ -27,6 +27,8 @@
 // (reading X, writing the packed rows).
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace dlrm {
 namespace {
 
@@ -88,6 +90,34 @@ struct RowSource {
   const float* const* tables;     // fused only
   const int64_t* idx;
   const int64_t* off;
+  const float* const* scale_bias;  // fused from int8 rows only: per-row (scale, bias)
+};
+
+// Formats of the table rows the fused kernel reads, four columns per load:
+// fp32; bf16 (widened exactly); int8 with the row's scale s and bias z,
+// value (s * q) + z with two fp32 roundings (no fused multiply-add).
+struct FRowF32 {
+  typedef float T;
+  static constexpr bool kScaled = false;
+};
+struct FRowBF16 {
+  typedef uint16_t T;
+  static constexpr bool kScaled = false;
+  __device__ static f4 load(const T* row, int kk, float2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 u = *(const __attribute__((address_space(1))) u32x2*)(row + kk);
+    return f4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+              __uint_as_float(u[1] & 0xffff0000u)};
+  }
+};
+struct FRowI8 {
+  typedef int8_t T;
+  static constexpr bool kScaled = true;
+  __device__ static f4 load(const T* row, int kk, float2 sz) {
+    const uint32_t u = *(const __attribute__((address_space(1))) uint32_t*)(row + kk);
+    auto deq = [&](int sh) { return __fadd_rn(__fmul_rn(sz.x, (float)(int8_t)(u >> sh)), sz.y); };
+    return f4{deq(0), deq(8), deq(16), deq(24)};
+  }
 };
 
 // Gram blocks of one sample held in registers (x[t][c]: rows t*16 + lane%16,
@@ -259,10 +289,12 @@ constexpr int fused_waves() {
   return fused_persistent<NT, DC>() ? 4 : (NT * (4 * DC + 12) < 112 ? 4 : 2);
 }
 
-template <int NT, int DC, typename OutT>
+template <int NT, int DC, typename OutT, typename R = FRowF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves<NT, DC>()))) void fused_kernel(
     RowSource src, int64_t B, int n, int d, OutT* __restrict__ out,
                                                     int64_t out_ld, int pad_end, int row_bytes, int wide) {
+  constexpr bool kF32 = std::is_same<R, FRowF32>::value;
+  typedef typename R::T TT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 6);
@@ -280,13 +312,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
   // samples b, b + stride, ...; the bag offsets of the next sample are loaded
   // with this sample's rows and its first indices during this sample's Gram
   // matrix, so only the row loads wait on memory.
-  const float* tb[NT];
+  const TT* tb[NT];
+  const float2* sbt[NT];
   bool bagrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = t * 16 + r16;
     bagrow[t] = row >= 1 && row < n;
-    tb[t] = src.tables[bagrow[t] ? row - 1 : 0];
+    tb[t] = reinterpret_cast<const TT*>(src.tables[bagrow[t] ? row - 1 : 0]);
+    sbt[t] = R::kScaled ? reinterpret_cast<const float2*>(src.scale_bias[bagrow[t] ? row - 1 : 0]) : nullptr;
   }
   auto load_offsets = [&](int64_t s, int64_t (&o0)[NT], int64_t (&o1)[NT]) {
 #pragma unroll
@@ -319,11 +353,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int row = t * 16 + r16;
-      const float* rp = pick(row != 0 && len[t] > 0, tb[t] + r0[t] * (int64_t)d, x0);
+      if constexpr (kF32) {
+        const float* rp = pick(row != 0 && len[t] > 0, tb[t] + r0[t] * (int64_t)d, x0);
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const int kk = c * 16 + 4 * g;
-        x[t][c] = ld4(rp + (kk < d ? kk : d - 4));
+        for (int c = 0; c < DC; ++c) {
+          const int kk = c * 16 + 4 * g;
+          x[t][c] = ld4(rp + (kk < d ? kk : d - 4));
+        }
+      } else {
+        // table rows (row 0 of the table for lanes with no row: a valid
+        // address, masked below), and the dense row for the lanes of row 0
+        const int64_t rr = (row != 0 && len[t] > 0) ? r0[t] : 0;
+        const TT* rp = tb[t] + rr * (int64_t)d;
+        const float2 sz = R::kScaled ? sbt[t][rr] : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const int kk = c * 16 + 4 * g;
+          x[t][c] = R::load(rp, kk < d ? kk : d - 4, sz);
+        }
+        if (t == 0) {
+#pragma unroll
+          for (int c = 0; c < DC; ++c) {
+            const int kk = c * 16 + 4 * g;
+            const f4 xd = ld4(x0 + (kk < d ? kk : d - 4));
+            if (row == 0) x[0][c] = xd;
+          }
+        }
       }
     }
     constexpr bool kPersist = fused_persistent<NT, DC>();
@@ -356,8 +411,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
       for (int t = 0; t < NT; ++t) rq[t] = *(1 < len[t] ? idx + pb[t] + 1 : off);
       for (int q = 1; q < maxlen; ++q) {
         const float* rp[NT];
+        const TT* rq_row[NT];
+        float2 sz[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) rp[t] = pick(q < len[t], tb[t] + rq[t] * (int64_t)d, x0);
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (kF32) {
+            rp[t] = pick(q < len[t], tb[t] + rq[t] * (int64_t)d, x0);
+          } else {
+            const int64_t rr = q < len[t] ? rq[t] : 0;
+            rq_row[t] = tb[t] + rr * (int64_t)d;
+            sz[t] = R::kScaled ? sbt[t][rr] : make_float2(0.f, 0.f);
+          }
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) rq[t] = *(q + 1 < len[t] ? idx + pb[t] + q + 1 : off);
         // x is never -0 here (every sum starts from +0), so adding +0 for a
@@ -367,7 +432,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
 #pragma unroll
           for (int c = 0; c < DC; ++c) {
             const int kk = c * 16 + 4 * g;
-            const f4 v = ld4(rp[t] + (kk < d ? kk : d - 4));
+            const int kc = kk < d ? kk : d - 4;
+            f4 v;
+            if constexpr (kF32) v = ld4(rp[t] + kc);
+            else v = R::load(rq_row[t], kc, sz[t]);
             x[t][c] = x[t][c] + ((q < len[t] && kk < d) ? v : f4{0.f, 0.f, 0.f, 0.f});
           }
         }
@@ -408,7 +476,15 @@ __global__ __launch_bounds__(256) void interact_generic_kernel(const float* __re
   put(out + b * out_ld + col, v);
 }
 
-template <int NT, int DC, typename OutT, bool FUSED>
+template <int MODE>
+struct FRowOf { typedef FRowF32 type; };
+template <>
+struct FRowOf<2> { typedef FRowBF16 type; };
+template <>
+struct FRowOf<3> { typedef FRowI8 type; };
+
+// MODE 0: materialised X; 1: fused from fp32 rows; 2: bf16 rows; 3: int8 rows
+template <int NT, int DC, typename OutT, int MODE>
 void launch_mfma(const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end,
                  hipStream_t s) {
   // row buffer: pad_end elements plus one spare element for masked stores
@@ -416,38 +492,39 @@ void launch_mfma(const RowSource& src, int64_t B, int n, int d, OutT* out, int64
   int spb = 65536 / row_bytes;  // samples (waves) per block within 64 KB of LDS
   spb = spb < 1 ? 1 : (spb > 4 ? 4 : spb);
   const int wide = ((out_ld * (int64_t)sizeof(OutT)) % 16) == 0;
-  if (FUSED) {
+  if constexpr (MODE > 0) {
     // persistent waves: as many blocks as stay resident, each wave walking
     // the samples with the grid's stride
+    typedef typename FRowOf<MODE>::type R;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fused_kernel<NT, DC, OutT>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
+                                                     reinterpret_cast<const void*>(fused_kernel<NT, DC, OutT, R>),
                                                      64 * spb, (size_t)spb * row_bytes) != hipSuccess || per_cu < 1)
       per_cu = 1;
     int64_t grid = ceil_div(B, spb);
     if (fused_persistent<NT, DC>() && grid > (int64_t)per_cu * device_cu_count()) grid = (int64_t)per_cu * device_cu_count();
-    hipLaunchKernelGGL((fused_kernel<NT, DC, OutT>), dim3((unsigned)grid), dim3(64 * spb), (size_t)spb * row_bytes,
+    hipLaunchKernelGGL((fused_kernel<NT, DC, OutT, R>), dim3((unsigned)grid), dim3(64 * spb), (size_t)spb * row_bytes,
                        s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
-  }
-  else
+  } else
     hipLaunchKernelGGL((interact_mfma_kernel<NT, DC, OutT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb),
                        (size_t)spb * row_bytes, s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
 }
 
-template <int DC, typename OutT, bool FUSED>
+template <int DC, typename OutT, int MODE>
 bool dispatch_nt(int NT, const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end,
                  hipStream_t s) {
   // x[NT][DC] must fit in 128 registers per lane: NT * DC <= 32
   constexpr int kMaxNT = (32 / DC) < 8 ? (32 / DC) : 8;
   if (NT > kMaxNT) return false;
   switch (NT) {
-    case 1: launch_mfma<1, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true;
-    case 2: launch_mfma<2, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true;
-    case 3: if constexpr (kMaxNT >= 3) { launch_mfma<3, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
-    case 4: if constexpr (kMaxNT >= 4) { launch_mfma<4, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
-    case 5: if constexpr (kMaxNT >= 5) { launch_mfma<5, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
-    case 6: if constexpr (kMaxNT >= 6) { launch_mfma<6, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
-    case 7: if constexpr (kMaxNT >= 7) { launch_mfma<7, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
-    case 8: if constexpr (kMaxNT >= 8) { launch_mfma<8, DC, OutT, FUSED>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 1: launch_mfma<1, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true;
+    case 2: launch_mfma<2, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true;
+    case 3: if constexpr (kMaxNT >= 3) { launch_mfma<3, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 4: if constexpr (kMaxNT >= 4) { launch_mfma<4, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 5: if constexpr (kMaxNT >= 5) { launch_mfma<5, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 6: if constexpr (kMaxNT >= 6) { launch_mfma<6, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 7: if constexpr (kMaxNT >= 7) { launch_mfma<7, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
+    case 8: if constexpr (kMaxNT >= 8) { launch_mfma<8, DC, OutT, MODE>(src, B, n, d, out, out_ld, pad_end, s); return true; } break;
   }
   return false;
 }
@@ -546,23 +623,23 @@ int launch_bwd(const float* X, int64_t B, int n, int d, int64_t x_ld, const floa
   return DLRM_OK;
 }
 
-template <typename OutT, bool FUSED>
+template <typename OutT, int MODE>
 bool dispatch(const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end, hipStream_t s) {
   const int NT = (n + 15) / 16;
   const int dc = (d + 15) / 16;
-  if (dc <= 1) return dispatch_nt<1, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
-  if (dc <= 2) return dispatch_nt<2, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
-  if (dc <= 4) return dispatch_nt<4, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
-  if (dc <= 8) return dispatch_nt<8, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
-  if (dc <= 16) return dispatch_nt<16, OutT, FUSED>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 1) return dispatch_nt<1, OutT, MODE>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 2) return dispatch_nt<2, OutT, MODE>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 4) return dispatch_nt<4, OutT, MODE>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 8) return dispatch_nt<8, OutT, MODE>(NT, src, B, n, d, out, out_ld, pad_end, s);
+  if (dc <= 16) return dispatch_nt<16, OutT, MODE>(NT, src, B, n, d, out, out_ld, pad_end, s);
   return false;
 }
 
 template <typename OutT>
 void run(const float* X, int64_t B, int n, int d, int64_t x_ld, OutT* out, int64_t out_ld, int pad_end,
          hipStream_t s) {
-  const RowSource src{X, x_ld, nullptr, nullptr, nullptr};
-  if (!dispatch<OutT, false>(src, B, n, d, out, out_ld, pad_end, s)) {
+  const RowSource src{X, x_ld, nullptr, nullptr, nullptr, nullptr};
+  if (!dispatch<OutT, 0>(src, B, n, d, out, out_ld, pad_end, s)) {
     const int64_t total = B * (int64_t)pad_end;
     hipLaunchKernelGGL((interact_generic_kernel<OutT>), dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, X, B,
                        n, d, x_ld, out, out_ld, pad_end);
@@ -590,9 +667,11 @@ extern "C" int dlrm_interact_fwd(const float* X, int64_t B, int32_t n, int32_t d
   return launch_status();
 }
 
-extern "C" int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, const float* const* tables, int32_t K,
-                                        int32_t d, const int64_t* indices, const int64_t* offsets, int64_t B,
-                                        void* out, int32_t out_dtype, int64_t out_ld, hipStream_t stream) {
+namespace dlrm {
+namespace {
+// Checks shared by the fused entry points; sets *pad_end.
+int check_fused(const float* x_dense, int64_t xd_ld, const void* tables, int32_t K, int32_t d, const int64_t* indices,
+                const int64_t* offsets, int64_t B, void* out, int32_t out_dtype, int64_t out_ld, int* pad_end) {
   if (!x_dense || !tables || !indices || !offsets || !out || K < 1 || B < 1) return DLRM_E_INVALID;
   const int n = K + 1;
   if (n > 128 || d < 4 || d > 256 || (d % 4) != 0) return DLRM_E_INVALID;
@@ -601,14 +680,46 @@ extern "C" int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, con
   if (xd_ld < d || (xd_ld % 4) != 0 || !aligned16(x_dense)) return DLRM_E_INVALID;
   if (out_ld < width || (out_ld % 4) != 0 || !aligned16(out)) return DLRM_E_INVALID;
   if (ceil_div(B, 4) > 0x7fffffffLL || B * out_ld > (int64_t)1 << 40) return DLRM_E_UNSUPPORTED;
-  const int pad_end = (int)(round_up(width, 8) < out_ld ? round_up(width, 8) : out_ld);
-  const RowSource src{x_dense, xd_ld, tables, indices, offsets};
+  *pad_end = (int)(round_up(width, 8) < out_ld ? round_up(width, 8) : out_ld);
+  return DLRM_OK;
+}
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, const float* const* tables, int32_t K,
+                                        int32_t d, const int64_t* indices, const int64_t* offsets, int64_t B,
+                                        void* out, int32_t out_dtype, int64_t out_ld, hipStream_t stream) {
+  int pad_end = 0;
+  const int rc = check_fused(x_dense, xd_ld, tables, K, d, indices, offsets, B, out, out_dtype, out_ld, &pad_end);
+  if (rc != DLRM_OK) return rc;
+  const int n = K + 1;
+  const RowSource src{x_dense, xd_ld, tables, indices, offsets, nullptr};
   bool ok;
   if (out_dtype == DLRM_F32)
-    ok = dispatch<float, true>(src, B, n, d, static_cast<float*>(out), out_ld, pad_end, stream);
+    ok = dispatch<float, 1>(src, B, n, d, static_cast<float*>(out), out_ld, pad_end, stream);
   else
-    ok = dispatch<uint16_t, true>(src, B, n, d, static_cast<uint16_t*>(out), out_ld, pad_end, stream);
+    ok = dispatch<uint16_t, 1>(src, B, n, d, static_cast<uint16_t*>(out), out_ld, pad_end, stream);
   if (!ok) return DLRM_E_UNSUPPORTED;  // (K + 1) x d does not fit the register-resident layout
+  return launch_status();
+}
+
+extern "C" int dlrm_embbag_interact_fwd_lp(const float* x_dense, int64_t xd_ld, const void* const* tables,
+                                           int32_t table_dtype, const float* const* scale_bias, int32_t K, int32_t d,
+                                           const int64_t* indices, const int64_t* offsets, int64_t B, void* out,
+                                           int32_t out_dtype, int64_t out_ld, hipStream_t stream) {
+  int pad_end = 0;
+  const int rc = check_fused(x_dense, xd_ld, tables, K, d, indices, offsets, B, out, out_dtype, out_ld, &pad_end);
+  if (rc != DLRM_OK) return rc;
+  if (table_dtype != DLRM_BF16 && table_dtype != DLRM_I8) return DLRM_E_INVALID;
+  if (table_dtype == DLRM_I8 && !scale_bias) return DLRM_E_INVALID;
+  if (out_dtype != DLRM_BF16) return DLRM_E_UNSUPPORTED;  // low-precision rows feed a bf16 top MLP
+  const int n = K + 1;
+  const RowSource src{x_dense, xd_ld, reinterpret_cast<const float* const*>(tables), indices, offsets,
+                      table_dtype == DLRM_I8 ? scale_bias : nullptr};
+  uint16_t* o = static_cast<uint16_t*>(out);
+  const bool ok = table_dtype == DLRM_BF16 ? dispatch<uint16_t, 2>(src, B, n, d, o, out_ld, pad_end, stream)
+                                           : dispatch<uint16_t, 3>(src, B, n, d, o, out_ld, pad_end, stream);
+  if (!ok) return DLRM_E_UNSUPPORTED;
   return launch_status();
 }
 

@@ -68,11 +68,21 @@ class DLRM:
     """Device state and call sequence for one batch size."""
 
     def __init__(self, B: int, K: int, d: int, rows, tables, bottom: MLPParams, top: MLPParams, train: bool = False,
-                 device="cuda", fused="auto"):
+                 device="cuda", fused="auto", table_dtype: str = "f32", scale_bias=None):
+        """table_dtype "f32", or "bf16" / "int8" rows (forward only) with, for
+        int8, ``scale_bias`` = K fp32 [m_k][2] tensors."""
         self.B, self.K, self.d, self.n = B, K, d, K + 1
         self.rows = [int(r) for r in rows]
         self.tables = tables
         self.table_ptrs = C.device_pointer_array(tables)
+        if table_dtype not in ("f32", "bf16", "int8"):
+            raise ValueError("table_dtype must be 'f32', 'bf16' or 'int8'")
+        if table_dtype != "f32" and train:
+            raise ValueError("the sparse SGD update needs fp32 table rows")
+        self.table_dtype = table_dtype
+        self.table_code = {"bf16": C.DLRM_BF16, "int8": C.DLRM_I8}.get(table_dtype)
+        self.scale_bias = scale_bias
+        self.sb_ptrs = C.device_pointer_array(scale_bias) if scale_bias is not None else None
         self.bottom, self.top = bottom, top
         self.train = train
         if fused not in (True, False, "auto"):
@@ -128,12 +138,21 @@ class DLRM:
         C.dlrm_mlp_fwd(dense, dense.shape[1], B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld,
                        self.bottom.biases, self.bottom.w_dtype, C.DLRM_ACT_RELU, self.x0, self.x0_ld, None,
                        self.ws_bot, save, stream)
+        lp = self.table_dtype != "f32"
         if self.use_fused(indices.numel()):
-            C.dlrm_embbag_interact_fwd(self.x0, self.x0_ld, self.table_ptrs, self.K, d, indices, offsets, B,
-                                       self.top_in, self.top_ld, stream)
+            if lp:
+                C.dlrm_embbag_interact_fwd_lp(self.x0, self.x0_ld, self.table_ptrs, self.table_code, self.sb_ptrs,
+                                              self.K, d, indices, offsets, B, self.top_in, self.top_ld, stream)
+            else:
+                C.dlrm_embbag_interact_fwd(self.x0, self.x0_ld, self.table_ptrs, self.K, d, indices, offsets, B,
+                                           self.top_in, self.top_ld, stream)
         else:
-            C.dlrm_embbag_fwd(self.table_ptrs, self.K, d, indices, offsets, B, self.X, n * d, d, stream,
-                              nnz=indices.numel())
+            if lp:
+                C.dlrm_embbag_fwd_lp(self.table_ptrs, self.table_code, self.sb_ptrs, self.K, d, indices, offsets, B,
+                                     self.X, n * d, d, stream, nnz=indices.numel())
+            else:
+                C.dlrm_embbag_fwd(self.table_ptrs, self.K, d, indices, offsets, B, self.X, n * d, d, stream,
+                                  nnz=indices.numel())
             C.dlrm_interact_fwd(self.X, B, n, d, n * d, self.top_in, self.top_ld, stream)
         C.dlrm_mlp_fwd(self.top_in, self.top_ld, B, self.top.dims, self.top.Ws, self.top.w_ld, self.top.biases,
                        self.top.w_dtype, C.DLRM_ACT_NONE, self.logit, 1, self.prob, self.ws_top, save, stream)

@@ -176,6 +176,20 @@ int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, const float* c
                              int64_t out_ld, hipStream_t stream);
 
 /*
+ * Fused pooled lookup and interaction from low-precision table rows: the
+ * rows of dlrm_embbag_fwd_lp (bf16 widened exactly, or int8 with per-row
+ * scale and bias, two fp32 roundings) pooled and interacted exactly as
+ * dlrm_embbag_interact_fwd; bit-identical to dlrm_embbag_fwd_lp into X
+ * followed by dlrm_interact_fwd.  table_dtype and scale_bias as
+ * dlrm_embbag_fwd_lp; other arguments as dlrm_embbag_interact_fwd.  The
+ * output must be bf16 (the top MLP's input), DLRM_E_UNSUPPORTED otherwise.
+ */
+int dlrm_embbag_interact_fwd_lp(const float* x_dense, int64_t xd_ld, const void* const* tables, int32_t table_dtype,
+                                const float* const* scale_bias, int32_t K, int32_t d, const int64_t* indices,
+                                const int64_t* offsets, int64_t B, void* out, int32_t out_dtype, int64_t out_ld,
+                                hipStream_t stream);
+
+/*
  * Multilayer perceptron, forward.
  * [EXPL] Key Method Details, "Bottom MLP" (FC layers with ReLU, output
  * width d) and "Top MLP" (FC layers with ReLU ending in a sigmoid); [SU] Key

@@ -5,6 +5,7 @@ import torch
 
 import oracle
 from dlrm_cases import DEV, banner, bf16_row_tolerance, bits, device_model, oracle_forward, to_dev
+from synth import device as SD
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -163,3 +164,29 @@ def test_forward_auto_path(name, expect_fused):
     ref, _, _ = device_model(w, tables=auto.tables, fused=expect_fused)
     _forward(w, ref)
     assert np.array_equal(auto.logit.cpu().numpy().view(np.uint32), ref.logit.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "int8"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_forward_lowprec_rows_equal_widened_fp32(dtype, fused):
+    """A forward pass from bf16 / int8 table rows gives the logits, bit for bit,
+    of the same model on fp32 tables holding the decoded values (bf16 widened;
+    (s * q) + z in two fp32 roundings, computed here with separate torch ops)."""
+    from deep_learning_recommendation_amd import pipeline as PL
+
+    w = W.get("forward").scaled(B=700, rows=8_000)
+    banner(f"forward from {dtype} rows fused={fused}")
+    tabs, sbs = SD.make_tables_lp(w, dtype)
+    if dtype == "bf16":
+        f32 = [(t.to(torch.int32) << 16).view(torch.float32).contiguous() for t in tabs]
+    else:
+        f32 = [(t.to(torch.float32) * sb[:, 0:1]) + sb[:, 1:2] for t, sb in zip(tabs, sbs)]
+    ref, bottom, top = device_model(w, tables=f32, fused=fused)
+    dense, idx, off = _forward(w, ref)
+    bf16 = w.mlp_dtype == "bf16"
+    bp = PL.make_mlp(w.bottom, [p[0] for p in bottom], [p[2] for p in bottom], bf16)
+    tp = PL.make_mlp(w.top, [p[0] for p in top], [p[2] for p in top], bf16)
+    lp = PL.DLRM(w.B, w.K, w.d, w.rows, tabs, bp, tp, fused=fused, table_dtype=dtype, scale_bias=sbs)
+    _forward(w, lp)
+    assert np.array_equal(lp.logit.cpu().numpy().view(np.uint32), ref.logit.cpu().numpy().view(np.uint32))
+    assert np.array_equal(lp.top_in.view(torch.int16).cpu().numpy(), ref.top_in.view(torch.int16).cpu().numpy())
