@@ -93,9 +93,10 @@ struct RowSource {
   const float* const* scale_bias;  // fused from int8 rows only: per-row (scale, bias)
 };
 
-// Formats of the table rows the fused kernel reads, four columns per load:
-// fp32; bf16 (widened exactly); int8 with the row's scale s and bias z,
-// value (s * q) + z with two fp32 roundings (no fused multiply-add).
+// Formats of the table rows the fused kernel reads: fp32 (four columns per
+// 16-byte load); bf16 (widened exactly) and int8 with the row's scale s and
+// bias z, value (s * q) + z with two fp32 roundings (no fused multiply-add),
+// eight consecutive columns per load.
 struct FRowF32 {
   typedef float T;
   static constexpr bool kScaled = false;
@@ -103,25 +104,31 @@ struct FRowF32 {
 struct FRowBF16 {
   typedef uint16_t T;
   static constexpr bool kScaled = false;
-  __device__ static f4 load(const T* row, int kk, float2) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 u = *(const __attribute__((address_space(1))) u32x2*)(row + kk);
-    return f4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
-              __uint_as_float(u[1] & 0xffff0000u)};
+  // columns col .. col + 7 (16 bytes)
+  __device__ static void load8(const T* row, int col, float2, f4& lo, f4& hi) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 u = *(const __attribute__((address_space(1))) u32x4*)(row + col);
+    lo = f4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+            __uint_as_float(u[1] & 0xffff0000u)};
+    hi = f4{__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u), __uint_as_float(u[3] << 16),
+            __uint_as_float(u[3] & 0xffff0000u)};
   }
 };
 struct FRowI8 {
   typedef int8_t T;
   static constexpr bool kScaled = true;
-  __device__ static f4 load(const T* row, int kk, float2 sz) {
-    const uint32_t u = *(const __attribute__((address_space(1))) uint32_t*)(row + kk);
-    auto deq = [&](int sh) { return __fadd_rn(__fmul_rn(sz.x, (float)(int8_t)(u >> sh)), sz.y); };
-    return f4{deq(0), deq(8), deq(16), deq(24)};
+  // columns col .. col + 7 (8 bytes)
+  __device__ static void load8(const T* row, int col, float2 sz, f4& lo, f4& hi) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 u = *(const __attribute__((address_space(1))) u32x2*)(row + col);
+    auto deq = [&](uint32_t w, int sh) { return __fadd_rn(__fmul_rn(sz.x, (float)(int8_t)(w >> sh)), sz.y); };
+    lo = f4{deq(u[0], 0), deq(u[0], 8), deq(u[0], 16), deq(u[0], 24)};
+    hi = f4{deq(u[1], 0), deq(u[1], 8), deq(u[1], 16), deq(u[1], 24)};
   }
 };
 
 // Gram blocks of one sample held in registers (x[t][c]: rows t*16 + lane%16,
-// columns c*16 + 4*(lane/16) .. +3) into the sample's packed output row `ob`
+// columns col_of(c, lane/16) .. +3) into the sample's packed output row `ob`
 // (in LDS): dense vector first, then the strict lower triangle row by row,
 // then zeros up to pad_end.  The k loop is outermost so the MFMAs of all
 // blocks (J <= I) interleave as independent accumulation chains; a single
@@ -140,13 +147,22 @@ __device__ __forceinline__ const float* pick(bool c, const float* a, const float
   return reinterpret_cast<const float*>(c ? ua : ub);
 }
 
-template <int NT, int DC, typename OutT>
+// Column of register chunk c for lane group g: 16-wide chunks, four columns
+// each (WIDE = false), or 32-wide chunk pairs, eight consecutive columns each
+// (WIDE: one 16-byte load of a low-precision row).  Every row of a sample uses
+// the same mapping, so the Gram matrix sees one consistent k order.
+template <bool WIDE>
+__device__ __forceinline__ int col_of(int c, int g) {
+  return WIDE ? 32 * (c >> 1) + 8 * g + 4 * (c & 1) : c * 16 + 4 * g;
+}
+
+template <int NT, int DC, typename OutT, bool WIDE = false>
 __device__ __forceinline__ void gram_row(f4 (&x)[NT][DC], int n, int d, int pad_end, OutT* ob, int lane) {
   const int r16 = lane & 15, g = lane >> 4;
   if (r16 == 0) {  // row 0 lives in lanes 0, 16, 32, 48 of tile 0
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      const int kk = c * 16 + 4 * g;
+      const int kk = col_of<WIDE>(c, g);
       if (kk < d) put4(ob + kk, x[0][c]);
     }
   }
@@ -361,21 +377,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
           x[t][c] = ld4(rp + (kk < d ? kk : d - 4));
         }
       } else {
-        // table rows (row 0 of the table for lanes with no row: a valid
-        // address, masked below), and the dense row for the lanes of row 0
+        // table rows, eight columns per load (row 0 of the table for lanes
+        // with no row: a valid address, masked below), and the dense row for
+        // the lanes of row 0
         const int64_t rr = (row != 0 && len[t] > 0) ? r0[t] : 0;
         const TT* rp = tb[t] + rr * (int64_t)d;
         const float2 sz = R::kScaled ? sbt[t][rr] : make_float2(0.f, 0.f);
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const int kk = c * 16 + 4 * g;
-          x[t][c] = R::load(rp, kk < d ? kk : d - 4, sz);
+        for (int c = 0; c < DC; c += 2) {
+          const int col = col_of<true>(c, g);
+          R::load8(rp, col < d ? col : d - 8, sz, x[t][c], x[t][c + 1]);
         }
         if (t == 0) {
 #pragma unroll
           for (int c = 0; c < DC; ++c) {
-            const int kk = c * 16 + 4 * g;
-            const f4 xd = ld4(x0 + (kk < d ? kk : d - 4));
+            const int col = col_of<true>(c, g);
+            const f4 xd = ld4(x0 + (col < d ? col : d - 4));
             if (row == 0) x[0][c] = xd;
           }
         }
@@ -390,7 +407,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
       const int row = t * 16 + r16;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const bool live = c * 16 + 4 * g < d;
+        const bool live = col_of<!kF32>(c, g) < d;
         if (row == 0) {
           if (!live) x[t][c] = f4{0.f, 0.f, 0.f, 0.f};
         } else if (len[t] > 0 && live) {
@@ -429,20 +446,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
         // finished bag leaves it bit for bit unchanged
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+          if constexpr (kF32) {
 #pragma unroll
-          for (int c = 0; c < DC; ++c) {
-            const int kk = c * 16 + 4 * g;
-            const int kc = kk < d ? kk : d - 4;
-            f4 v;
-            if constexpr (kF32) v = ld4(rp[t] + kc);
-            else v = R::load(rq_row[t], kc, sz[t]);
-            x[t][c] = x[t][c] + ((q < len[t] && kk < d) ? v : f4{0.f, 0.f, 0.f, 0.f});
+            for (int c = 0; c < DC; ++c) {
+              const int kk = c * 16 + 4 * g;
+              const f4 v = ld4(rp[t] + (kk < d ? kk : d - 4));
+              x[t][c] = x[t][c] + ((q < len[t] && kk < d) ? v : f4{0.f, 0.f, 0.f, 0.f});
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < DC; c += 2) {
+              const int col = col_of<true>(c, g);
+              f4 lo, hi;
+              R::load8(rq_row[t], col < d ? col : d - 8, sz[t], lo, hi);
+              const bool on = q < len[t] && col < d;
+              x[t][c] = x[t][c] + (on ? lo : f4{0.f, 0.f, 0.f, 0.f});
+              x[t][c + 1] = x[t][c + 1] + (on ? hi : f4{0.f, 0.f, 0.f, 0.f});
+            }
           }
         }
       }
     }
     if constexpr (kPersist) take_meta(bn, o0n, o1n, pb, len, r0);  // next sample's first indices, in flight during the Gram matrix
-    gram_row<NT, DC, OutT>(x, n, d, pad_end, reinterpret_cast<OutT*>(rowb), lane);
+    gram_row<NT, DC, OutT, !kF32>(x, n, d, pad_end, reinterpret_cast<OutT*>(rowb), lane);
     row_out(rowb, reinterpret_cast<char*>(out + b * out_ld), pad_end * (int)sizeof(OutT), wide, lane);
     if (bn >= B) break;
     b = bn;
@@ -713,6 +739,7 @@ extern "C" int dlrm_embbag_interact_fwd_lp(const float* x_dense, int64_t xd_ld, 
   if (table_dtype != DLRM_BF16 && table_dtype != DLRM_I8) return DLRM_E_INVALID;
   if (table_dtype == DLRM_I8 && !scale_bias) return DLRM_E_INVALID;
   if (out_dtype != DLRM_BF16) return DLRM_E_UNSUPPORTED;  // low-precision rows feed a bf16 top MLP
+  if (d % 32 != 0) return DLRM_E_UNSUPPORTED;             // eight columns per lane load, 32-wide chunk pairs
   const int n = K + 1;
   const RowSource src{x_dense, xd_ld, reinterpret_cast<const float* const*>(tables), indices, offsets,
                       table_dtype == DLRM_I8 ? scale_bias : nullptr};

@@ -127,8 +127,11 @@ class DLRM:
         return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device="cuda")
 
     def use_fused(self, nnz: int) -> bool:
-        """Whether a batch of nnz lookups takes the fused lookup + interaction."""
+        """Whether a batch of nnz lookups takes the fused lookup + interaction
+        (from low-precision rows only for d a multiple of 32)."""
         if self.fused == "auto":
+            if self.table_dtype != "f32" and self.d % 32 != 0:
+                return False
             return nnz <= AUTO_FUSED_MAX_MEAN_BAG * self.K * self.B
         return bool(self.fused)
 

@@ -178,11 +178,16 @@ int dlrm_embbag_interact_fwd(const float* x_dense, int64_t xd_ld, const float* c
 /*
  * Fused pooled lookup and interaction from low-precision table rows: the
  * rows of dlrm_embbag_fwd_lp (bf16 widened exactly, or int8 with per-row
- * scale and bias, two fp32 roundings) pooled and interacted exactly as
- * dlrm_embbag_interact_fwd; bit-identical to dlrm_embbag_fwd_lp into X
- * followed by dlrm_interact_fwd.  table_dtype and scale_bias as
+ * scale and bias, two fp32 roundings) pooled as dlrm_embbag_fwd_lp (bit for
+ * bit, in registers) and interacted as dlrm_embbag_interact_fwd, with one
+ * difference: each lane feeds the Gram MFMAs eight consecutive columns of a
+ * row (one load of a low-precision row), so the pairs are summed in another
+ * order than by dlrm_interact_fwd and agree with it within the same
+ * dot-product bound, not bit for bit.  table_dtype and scale_bias as
  * dlrm_embbag_fwd_lp; other arguments as dlrm_embbag_interact_fwd.  The
- * output must be bf16 (the top MLP's input), DLRM_E_UNSUPPORTED otherwise.
+ * output must be bf16 (the top MLP's input) and d a multiple of 32 (each
+ * lane loads eight consecutive columns of a row), DLRM_E_UNSUPPORTED
+ * otherwise.
  */
 int dlrm_embbag_interact_fwd_lp(const float* x_dense, int64_t xd_ld, const void* const* tables, int32_t table_dtype,
                                 const float* const* scale_bias, int32_t K, int32_t d, const int64_t* indices,

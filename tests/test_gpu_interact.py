@@ -192,11 +192,16 @@ def test_interact_bwd_workload_shapes_full_batch():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "int8"])
-@pytest.mark.parametrize("K,d,bags", [(8, 16, "ragged"), (26, 128, "mostly_one"), (26, 128, "ragged"),
-                                      (100, 64, "ragged"), (3, 12, "mostly_one"), (31, 64, "mostly_one")])
+@pytest.mark.parametrize("K,d,bags", [(8, 32, "ragged"), (26, 128, "mostly_one"), (26, 128, "ragged"),
+                                      (100, 64, "ragged"), (3, 96, "mostly_one"), (31, 64, "mostly_one"),
+                                      (15, 160, "ragged")])
 def test_fused_gather_interaction_lp(dtype, K, d, bags):
-    """dlrm_embbag_interact_fwd_lp against dlrm_embbag_fwd_lp + dlrm_interact_fwd
-    (bit for bit) and against the oracle (bf16 row bound)."""
+    """dlrm_embbag_interact_fwd_lp against the oracle (dense part exact, pairs
+    within the bf16 row bound), and against dlrm_embbag_fwd_lp +
+    dlrm_interact_fwd: dense part bit for bit, pairs within the same bound
+    (the fused kernel feeds the MFMAs eight consecutive columns per lane, so
+    the pair sums run in another order); d = 160 leaves lane groups past the
+    row end in the last 32-column pair."""
     import deep_learning_recommendation_amd as D
 
     B, n = 203, K + 1
@@ -237,10 +242,27 @@ def test_fused_gather_interaction_lp(dtype, K, d, bags):
     one = torch.full((B, ld), 5.0, dtype=torch.bfloat16, device=DEV)
     D.dlrm_embbag_interact_fwd_lp(to_dev(x0), d, ptrs, code, sbp, K, d, to_dev(idx), to_dev(off), B, one, ld)
     torch.cuda.synchronize()
-    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
     E = oracle.embbag_fwd_lp(tabs, dtype, idx, off, B, scale_bias=sbs).reshape(B, K, d)
     Xr = np.concatenate([x0[:, None, :], E], axis=1)
     ref = oracle.interact_fwd(Xr)
+    tol = bf16_row_tolerance(Xr, ref)
     got = one.float().cpu().numpy()
-    assert np.all(np.abs(got[:, :width] - ref) <= bf16_row_tolerance(Xr, ref))
+    got2 = two.float().cpu().numpy()
+    assert torch.equal(one[:, :d].view(torch.int16), two[:, :d].view(torch.int16))
+    assert np.all(np.abs(got[:, :width] - ref) <= tol)
+    assert np.all(np.abs(got2[:, :width] - ref) <= tol)
     assert np.all(got[:, width:] == 0)
+
+
+def test_fused_lp_needs_32_column_multiple():
+    import deep_learning_recommendation_amd as D
+
+    banner("fused lp unsupported width")
+    K, d, B = 3, 16, 4
+    tdev = [torch.zeros((5, d), dtype=torch.int16, device=DEV) for _ in range(K)]
+    off = to_dev(np.arange(K * B + 1, dtype=np.int64))
+    idx = to_dev(np.zeros(K * B, dtype=np.int64))
+    x0 = torch.zeros((B, d), dtype=torch.float32, device=DEV)
+    out = torch.zeros((B, 32), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(D.DLRMError):
+        D.dlrm_embbag_interact_fwd_lp(x0, d, D.device_pointer_array(tdev), D.DLRM_BF16, None, K, d, idx, off, B, out, 32)
