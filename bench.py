@@ -12,7 +12,12 @@ Prints one JSON line: samples/s, the roofline of the dominant kernel (the
 fused pooled lookup + interaction kernel, or the gather alone in the
 gather microbench: algorithmic bytes per launch over its average launch
 time, measured with HIP events on its stream), and the CPU oracle timed on
-a bounded sample (about 10 s) of the same workload.
+a bounded sample (about 10 s) of the same workload.  An event record costs a
+few microseconds of GPU time, so the timed steps carry only the two events
+around the dominant kernel; the per-call breakdown (medians) comes from a
+short untimed pass after the timed region.  The defaults time 500 steps after 100 warm-up
+steps: far shorter runs report the clock's ramp as well (about 8% lower at
+20 steps of the forward workload).
 """
 from __future__ import annotations
 
@@ -68,8 +73,11 @@ def measured_traffic(key, kernel):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--breakdown-steps", type=int, default=20,
+                   help="untimed steps after the timed region with every call bracketed by events (the per-call "
+                        "breakdown; the timed steps carry only the dominant kernel's pair of events)")
     p.add_argument("--workload", default="forward", choices=["forward", "embbag", "interaction", "train", "tiny"])
     p.add_argument("--batches", type=int, default=2, help="distinct input batches rotated over the steps")
     p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
@@ -261,9 +269,15 @@ def main():
 
     stream = torch.cuda.current_stream()
     gather_t = Timer()
-    call_t = {}
+    call_t = {}   # per-call event pairs of the breakdown steps
+    dom_t = {}    # the dominant kernel's event pairs over the timed steps
+    DOMINANT = ("embbag", "embbag_interact")
 
-    def step(i, timed):
+    def step(i, mode):
+        """One step; mode None (warm-up), "timed" (events around the dominant
+        kernel only: each event record costs a few microseconds of GPU time)
+        or "breakdown" (events around every call)."""
+        timed = mode == "timed"
         dense, idx, off, G, y, nnz = dbatches[i % len(dbatches)]
         if model is None:
             e0 = gather_t.start(stream) if timed else None
@@ -278,11 +292,12 @@ def main():
         ev = {}
 
         def mark(name):
-            if timed:
+            # timed steps: the dominant kernel's mark and the next one (its end)
+            if mode == "breakdown" or (timed and (name in DOMINANT or len(ev) == 1)):
                 ev[name] = gather_t.start(stream)
 
         if args.chain:
-            return chain_step(model, dense, idx, off, y, nnz, mark, ev, timed)
+            return chain_step(model, dense, idx, off, y, nnz, mark, ev, mode)
         mark("bottom_mlp")
         D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
                        model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.x0, model.x0_ld, None,
@@ -320,15 +335,15 @@ def main():
             D.dlrm_embbag_bwd_sgd(model.table_ptrs, w.K, d, w.rows, idx, off, w.B, nnz, G, n * d, d, w.lr,
                                   model.ws_sparse)
         mark("end")
-        record(ev, timed)
+        record(ev, mode)
 
-    def record(ev, timed):
-        if timed:
+    def record(ev, mode):
+        if mode is not None:
             names = list(ev)
             for a, b in zip(names[:-1], names[1:]):
-                call_t.setdefault(a, []).append((ev[a], ev[b]))
+                (call_t if mode == "breakdown" else dom_t).setdefault(a, []).append((ev[a], ev[b]))
 
-    def chain_step(m, dense, idx, off, y, nnz, mark, ev, timed):
+    def chain_step(m, dense, idx, off, y, nnz, mark, ev, mode):
         """Forward with X materialised, then the backward from the loss."""
         n, d, B = m.n, m.d, w.B
         mark("bottom_mlp")
@@ -353,25 +368,34 @@ def main():
         mark("sparse_bwd_sgd")
         D.dlrm_embbag_bwd_sgd(m.table_ptrs, w.K, d, w.rows, idx, off, B, nnz, m.G, n * d, d, w.lr, m.ws_sparse)
         mark("end")
-        record(ev, timed)
+        record(ev, mode)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, True)
+        step(i, "timed")
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if model is not None and args.breakdown_steps > 0:
+        # two untimed steps first, so the host is ahead of the GPU again when
+        # the first bracketed call starts (else its interval holds host time)
+        for i in range(2):
+            step(args.steps + i, None)
+        for i in range(args.breakdown_steps):
+            step(args.steps + 2 + i, "breakdown")
+        torch.cuda.synchronize()
 
     ms_per_step = 1e3 * elapsed / args.steps
     value = w.B * args.steps / elapsed
-    breakdown = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in call_t.items()}
+    breakdown = {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in call_t.items()}
     nnz_mean = float(np.mean([b[5] for b in dbatches]))
-    if model is None or "embbag" in breakdown:
+    dom_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in dom_t.items()}
+    if model is None or "embbag" in dom_ms:
         kname, key = "embbag_fwd_kernel", None
         gbytes = gather_bytes(w.K, w.B, w.d, nnz_mean, lp)
-        g_ms = gather_t.mean_ms() if model is None else breakdown["embbag"]
+        g_ms = gather_t.mean_ms() if model is None else dom_ms["embbag"]
     else:
         # fused pooled lookup + interaction: every looked-up row, indices and
         # offsets, the dense rows it reads and the packed top-MLP rows it writes
@@ -379,7 +403,7 @@ def main():
         esz = model.top_in.element_size()
         gbytes = (gather_bytes(w.K, w.B, w.d, nnz_mean, lp) - 4 * w.K * w.B * w.d + 4 * w.B * w.d +
                   esz * w.B * model.top_ld)
-        g_ms = breakdown[key]
+        g_ms = dom_ms[key]
     achieved = gbytes / (g_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name + ("_uniform" if args.uniform else "") + ("_chain" if args.chain else "") +
                                ("" if lp == "f32" else "_" + lp), kname)
@@ -412,7 +436,8 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32+bf16" if w.mlp_dtype == "bf16" else "f32", "data": "synthetic",
            "config": cfg, "roofline": roofline, "cpu_baseline": cpu,
-           "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()}, "setup_s": round(t_setup, 1)}
+           "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
+           "breakdown_steps": args.breakdown_steps if model is not None else 0, "setup_s": round(t_setup, 1)}
     print(json.dumps(res), flush=True)
 
 
