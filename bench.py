@@ -268,6 +268,9 @@ def main():
     t_setup = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream()
+    # training: the index half of the sparse update (keys, sort, segments)
+    # runs on a second stream beside the forward and the dense backward
+    prep_stream = torch.cuda.Stream() if w.train else None
     gather_t = Timer()
     call_t = {}   # per-call event pairs of the breakdown steps
     dom_t = {}    # the dominant kernel's event pairs over the timed steps
@@ -296,8 +299,15 @@ def main():
             if mode == "breakdown" or (timed and (name in DOMINANT or len(ev) == 1)):
                 ev[name] = gather_t.start(stream)
 
+        def fork_prepare():
+            # after the lookup, so the sort overlaps the MLPs and the dense
+            # backward (MFMA-bound) rather than the HBM-bound lookup
+            prep_stream.wait_stream(stream)
+            with torch.cuda.stream(prep_stream):
+                D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx, off, w.B, nnz, model.ws_sparse)
+
         if args.chain:
-            return chain_step(model, dense, idx, off, y, nnz, mark, ev, mode)
+            return chain_step(model, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare)
         mark("bottom_mlp")
         D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
                        model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.x0, model.x0_ld, None,
@@ -310,6 +320,8 @@ def main():
             else:
                 D.dlrm_embbag_interact_fwd_lp(model.x0, model.x0_ld, model.table_ptrs, model.table_code, model.sb_ptrs,
                                               w.K, d, idx, off, w.B, model.top_in, model.top_ld)
+            if w.train:
+                fork_prepare()
         else:
             mark("embbag")
             if lp == "f32":
@@ -317,6 +329,8 @@ def main():
             else:
                 D.dlrm_embbag_fwd_lp(model.table_ptrs, model.table_code, model.sb_ptrs, w.K, d, idx, off, w.B, model.X,
                                      n * d, d, nnz=nnz)
+            if w.train:
+                fork_prepare()
             mark("interact")
             D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
         mark("top_mlp")
@@ -332,8 +346,9 @@ def main():
                            model.ws_bot, model.x0, model.x0_ld, G, n * d, model.dW_bot, model.db_bot, None, 0,
                            model.ws_bot_bwd)
             mark("sparse_bwd_sgd")
-            D.dlrm_embbag_bwd_sgd(model.table_ptrs, w.K, d, w.rows, idx, off, w.B, nnz, G, n * d, d, w.lr,
-                                  model.ws_sparse)
+            stream.wait_stream(prep_stream)
+            D.dlrm_embbag_bwd_sgd_apply(model.table_ptrs, w.K, d, w.rows, w.B, nnz, G, n * d, d, w.lr,
+                                        model.ws_sparse)
         mark("end")
         record(ev, mode)
 
@@ -343,7 +358,7 @@ def main():
             for a, b in zip(names[:-1], names[1:]):
                 (call_t if mode == "breakdown" else dom_t).setdefault(a, []).append((ev[a], ev[b]))
 
-    def chain_step(m, dense, idx, off, y, nnz, mark, ev, mode):
+    def chain_step(m, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare):
         """Forward with X materialised, then the backward from the loss."""
         n, d, B = m.n, m.d, w.B
         mark("bottom_mlp")
@@ -351,6 +366,7 @@ def main():
                        m.bottom.w_dtype, D.DLRM_ACT_RELU, m.x0, m.x0_ld, None, m.ws_bot, True)
         mark("embbag")
         D.dlrm_embbag_fwd(m.table_ptrs, w.K, d, idx, off, B, m.X, n * d, d, nnz=nnz)
+        fork_prepare()
         mark("interact")
         D.dlrm_interact_fwd(m.X, B, n, d, n * d, m.top_in, m.top_ld)
         mark("top_mlp")
@@ -366,7 +382,8 @@ def main():
         D.dlrm_mlp_bwd(B, m.bottom.dims, m.bottom.Ws, m.bottom.w_ld, D.DLRM_ACT_RELU, m.ws_bot, m.x0, m.x0_ld,
                        m.G, n * d, m.dW_bot, m.db_bot, None, 0, m.ws_bot_bwd)
         mark("sparse_bwd_sgd")
-        D.dlrm_embbag_bwd_sgd(m.table_ptrs, w.K, d, w.rows, idx, off, B, nnz, m.G, n * d, d, w.lr, m.ws_sparse)
+        stream.wait_stream(prep_stream)
+        D.dlrm_embbag_bwd_sgd_apply(m.table_ptrs, w.K, d, w.rows, B, nnz, m.G, n * d, d, w.lr, m.ws_sparse)
         mark("end")
         record(ev, mode)
 

@@ -8,7 +8,8 @@ entry point raises.
 from ._lib import (DLRM_ACT_NONE, DLRM_ACT_RELU, DLRM_BF16, DLRM_F32, DLRM_I8, DLRMError, EXPORTS,  # noqa: F401
                    LIB_PATH,
                    device_pointer_array, dlrm_abi_version, dlrm_bce_grad, dlrm_check_indices,
-                   dlrm_embbag_bwd_sgd, dlrm_embbag_bwd_sgd_workspace_size, dlrm_embbag_fwd, dlrm_embbag_fwd_lp,
+                   dlrm_embbag_bwd_sgd, dlrm_embbag_bwd_sgd_apply, dlrm_embbag_bwd_sgd_prepare,
+                   dlrm_embbag_bwd_sgd_workspace_size, dlrm_embbag_fwd, dlrm_embbag_fwd_lp,
                    dlrm_embbag_interact_fwd, dlrm_embbag_interact_fwd_lp,
                    dlrm_interact_bwd, dlrm_interact_fwd,
                    dlrm_mlp_bwd, dlrm_mlp_bwd_workspace_size, dlrm_mlp_fwd, dlrm_mlp_workspace_size, lib)

@@ -43,6 +43,9 @@ _SIGNATURES = {
     "dlrm_embbag_bwd_sgd_workspace_size": (_SZ, [_I32, _I64, _I64, _I32]),
     "dlrm_embbag_bwd_sgd": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _I64, _I64, _P, _I64, _I64, ctypes.c_float,
                                            _P, _SZ, _P]),
+    "dlrm_embbag_bwd_sgd_prepare": (ctypes.c_int, [_I32, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "dlrm_embbag_bwd_sgd_apply": (ctypes.c_int, [_P, _I32, _I32, _P, _I64, _I64, _P, _I64, _I64, ctypes.c_float, _P,
+                                                 _SZ, _P]),
     "dlrm_check_indices": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _P, _P]),
 }
 
@@ -207,6 +210,22 @@ def dlrm_embbag_bwd_sgd(table_ptrs, K: int, d: int, rows, indices, offsets, B: i
                                                              _ptr(offsets), B, nnz, _ptr(G), g_ld, g_col0,
                                                              ctypes.c_float(lr), _ptr(ws),
                                                              ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dlrm_embbag_bwd_sgd_prepare(K: int, rows, indices, offsets, B: int, nnz: int, ws, stream=None) -> None:
+    rows_h = (ctypes.c_int64 * K)(*[int(r) for r in rows])
+    _check("dlrm_embbag_bwd_sgd_prepare",
+           lib().dlrm_embbag_bwd_sgd_prepare(K, rows_h, _ptr(indices), _ptr(offsets), B, nnz, _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dlrm_embbag_bwd_sgd_apply(table_ptrs, K: int, d: int, rows, B: int, nnz: int, G, g_ld: int, g_col0: int,
+                              lr: float, ws, stream=None) -> None:
+    rows_h = (ctypes.c_int64 * K)(*[int(r) for r in rows])
+    _check("dlrm_embbag_bwd_sgd_apply",
+           lib().dlrm_embbag_bwd_sgd_apply(_ptr(table_ptrs), K, d, rows_h, B, nnz, _ptr(G), g_ld, g_col0,
+                                           ctypes.c_float(lr), _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream)))
 
 
 def dlrm_check_indices(indices, offsets, K: int, B: int, rows_dev, bad_count, stream=None) -> None:

@@ -708,75 +708,127 @@ extern "C" size_t dlrm_embbag_bwd_sgd_workspace_size(int32_t K, int64_t B, int64
   return L.bytes;
 }
 
-extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_t* rows,
-                                   const int64_t* indices, const int64_t* offsets, int64_t B, int64_t nnz,
-                                   const float* G, int64_t g_ld, int64_t g_col0, float lr, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
-  if (!tables || !rows || !indices || !offsets || !G) return DLRM_E_INVALID;
-  if (K < 1 || B < 1 || d < 4 || d > 1024 || (d % 4) != 0) return DLRM_E_INVALID;
-  if (nnz < 0 || nnz > 0x7fffffffLL || B > 0x7fffffffLL) return DLRM_E_INVALID;
-  if (g_col0 < 0 || g_ld < g_col0 + (int64_t)K * d || (g_ld % 4) != 0 || (g_col0 % 4) != 0 || !aligned16(G))
-    return DLRM_E_INVALID;
+namespace dlrm {
+namespace {
+// Checks shared by the three entry points; the key widths follow from the
+// table count and the largest table.
+int check_sparse(int32_t K, const int64_t* rows, int64_t B, int64_t nnz, int* row_bits, int* table_bits) {
+  if (!rows || K < 1 || B < 1 || B > 0x7fffffffLL || nnz < 0 || nnz > 0x7fffffffLL) return DLRM_E_INVALID;
   int64_t max_rows = 1;
   for (int k = 0; k < K; ++k) {
     if (rows[k] < 1) return DLRM_E_INVALID;
     max_rows = rows[k] > max_rows ? rows[k] : max_rows;
   }
-  const int row_bits = bits_for(max_rows - 1) > 0 ? bits_for(max_rows - 1) : 1;
-  const int table_bits = bits_for(K - 1);
-  if (row_bits + table_bits > 32) return DLRM_E_UNSUPPORTED;
-  if (nnz == 0) return DLRM_OK;
-  SparseLayout L;
-  sparse_layout(nnz, &L);
-  if (!ws || ws_bytes < L.bytes) return DLRM_E_WORKSPACE;
+  *row_bits = bits_for(max_rows - 1) > 0 ? bits_for(max_rows - 1) : 1;
+  *table_bits = bits_for(K - 1);
+  if (*row_bits + *table_bits > 32) return DLRM_E_UNSUPPORTED;
+  return DLRM_OK;
+}
+
+struct SparseBufs {
+  uint32_t* keys[2];
+  int32_t* vals[2];
+  uint32_t* hist;
+  uint32_t* bsum;
+  int32_t* seg;
+  uint32_t* seg_key;
+  uint32_t* counters;  // [0] segments, [1] hot segments, [2] next hot item, [3] next short-segment chunk
+  int32_t* hot;
+  int32_t* hot_ordered;
+};
+
+int sparse_bufs(int64_t nnz, void* ws, size_t ws_bytes, SparseLayout* L, SparseBufs* b) {
+  sparse_layout(nnz, L);
+  if (!ws || ws_bytes < L->bytes) return DLRM_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 255u) return DLRM_E_INVALID;
   char* w = static_cast<char*>(ws);
-  uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(w + L.keys[0]), reinterpret_cast<uint32_t*>(w + L.keys[1])};
-  int32_t* vals[2] = {reinterpret_cast<int32_t*>(w + L.vals[0]), reinterpret_cast<int32_t*>(w + L.vals[1])};
-  uint32_t* hist = reinterpret_cast<uint32_t*>(w + L.hist);
-  uint32_t* bsum = reinterpret_cast<uint32_t*>(w + L.bsum);
-  int32_t* seg = reinterpret_cast<int32_t*>(w + L.seg);
-  uint32_t* seg_key = reinterpret_cast<uint32_t*>(w + L.seg_key);
-  // counters: [0] segments, [1] hot segments, [2] next hot item, [3] next short-segment chunk
-  uint32_t* counters = reinterpret_cast<uint32_t*>(w + L.counters);
-  int32_t* hot = reinterpret_cast<int32_t*>(w + L.hot);
-  int32_t* hot_ordered = reinterpret_cast<int32_t*>(w + L.hot_ordered);
+  b->keys[0] = reinterpret_cast<uint32_t*>(w + L->keys[0]);
+  b->keys[1] = reinterpret_cast<uint32_t*>(w + L->keys[1]);
+  b->vals[0] = reinterpret_cast<int32_t*>(w + L->vals[0]);
+  b->vals[1] = reinterpret_cast<int32_t*>(w + L->vals[1]);
+  b->hist = reinterpret_cast<uint32_t*>(w + L->hist);
+  b->bsum = reinterpret_cast<uint32_t*>(w + L->bsum);
+  b->seg = reinterpret_cast<int32_t*>(w + L->seg);
+  b->seg_key = reinterpret_cast<uint32_t*>(w + L->seg_key);
+  b->counters = reinterpret_cast<uint32_t*>(w + L->counters);
+  b->hot = reinterpret_cast<int32_t*>(w + L->hot);
+  b->hot_ordered = reinterpret_cast<int32_t*>(w + L->hot_ordered);
+  return DLRM_OK;
+}
+
+// Sort passes for the key width: the sorted keys and bag ids end in buffer
+// passes % 2.
+int sort_passes(int row_bits, int table_bits) { return (row_bits + table_bits + 7) / 8; }
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const int64_t* indices,
+                                           const int64_t* offsets, int64_t B, int64_t nnz, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  if (!indices || !offsets) return DLRM_E_INVALID;
+  int row_bits = 0, table_bits = 0;
+  int rc = check_sparse(K, rows, B, nnz, &row_bits, &table_bits);
+  if (rc != DLRM_OK) return rc;
+  if (nnz == 0) return DLRM_OK;
+  SparseLayout L;
+  SparseBufs b;
+  if ((rc = sparse_bufs(nnz, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
   const int n = (int)nnz;
   const int64_t KB = (int64_t)K * B;
 
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, counters, 16);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters, 16);
   {
     int kg = 0;  // lanes per bag: the mean bag length rounded up to a power of two, at most 64
     while ((1LL << kg) * KB < nnz && kg < 6) ++kg;
     const int64_t kblocks = ceil_div(KB << kg, 256);
     if (kblocks > 0x7fffffffLL) return DLRM_E_UNSUPPORTED;
     hipLaunchKernelGGL(build_keys_kernel, dim3((unsigned)kblocks), dim3(256), 0, stream, indices, offsets, KB, B, kg,
-                       row_bits, keys[0], vals[0]);
+                       row_bits, b.keys[0], b.vals[0]);
   }
-  const int key_bits = row_bits + table_bits;
-  const int passes = (key_bits + 7) / 8;
+  const int passes = sort_passes(row_bits, table_bits);
   const int nblocks = (int)L.nblocks;
   int cur = 0;
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * 8;
-    hipLaunchKernelGGL(radix_hist_kernel, dim3(nblocks), dim3(RT), 0, stream, keys[cur], n, shift, hist, nblocks);
+    hipLaunchKernelGGL(radix_hist_kernel, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], n, shift, b.hist, nblocks);
     hipLaunchKernelGGL((scan_reduce_kernel<ArrayIn>), dim3((unsigned)L.scan_nb_hist), dim3(256), 0, stream,
-                       ArrayIn{hist}, L.hist_n, bsum);
-    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, bsum, (int)L.scan_nb_hist, nullptr);
-    hipLaunchKernelGGL(scan_apply_array_kernel, dim3((unsigned)L.scan_nb_hist), dim3(256), 0, stream, hist, L.hist_n,
-                       bsum, hist);
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nblocks), dim3(RT), 0, stream, keys[cur], vals[cur], keys[cur ^ 1],
-                       vals[cur ^ 1], n, shift, hist, nblocks);
+                       ArrayIn{b.hist}, L.hist_n, b.bsum);
+    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, b.bsum, (int)L.scan_nb_hist, nullptr);
+    hipLaunchKernelGGL(scan_apply_array_kernel, dim3((unsigned)L.scan_nb_hist), dim3(256), 0, stream, b.hist,
+                       L.hist_n, b.bsum, b.hist);
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], b.vals[cur],
+                       b.keys[cur ^ 1], b.vals[cur ^ 1], n, shift, b.hist, nblocks);
     cur ^= 1;
   }
   // run-length segmentation of the sorted keys
   hipLaunchKernelGGL((scan_reduce_kernel<HeadIn>), dim3((unsigned)L.scan_nb_keys), dim3(256), 0, stream,
-                     HeadIn{keys[cur]}, (int64_t)n, bsum);
-  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, bsum, (int)L.scan_nb_keys, &counters[0]);
-  hipLaunchKernelGGL(scan_apply_heads_kernel, dim3((unsigned)L.scan_nb_keys), dim3(256), 0, stream, keys[cur],
-                     (int64_t)n, bsum, seg, seg_key, &counters[0]);
-  hipLaunchKernelGGL(find_hot_kernel, dim3(1024), dim3(256), 0, stream, seg, &counters[0], hot, &counters[1]);
-  hipLaunchKernelGGL(order_hot_kernel, dim3(1), dim3(256), 0, stream, seg, hot, &counters[1], hot_ordered);
+                     HeadIn{b.keys[cur]}, (int64_t)n, b.bsum);
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, b.bsum, (int)L.scan_nb_keys, &b.counters[0]);
+  hipLaunchKernelGGL(scan_apply_heads_kernel, dim3((unsigned)L.scan_nb_keys), dim3(256), 0, stream, b.keys[cur],
+                     (int64_t)n, b.bsum, b.seg, b.seg_key, &b.counters[0]);
+  hipLaunchKernelGGL(find_hot_kernel, dim3(1024), dim3(256), 0, stream, b.seg, &b.counters[0], b.hot, &b.counters[1]);
+  hipLaunchKernelGGL(order_hot_kernel, dim3(1), dim3(256), 0, stream, b.seg, b.hot, &b.counters[1], b.hot_ordered);
+  return launch_status() != DLRM_OK ? DLRM_E_HIP : DLRM_OK;
+}
+
+extern "C" int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_t d, const int64_t* rows, int64_t B,
+                                         int64_t nnz, const float* G, int64_t g_ld, int64_t g_col0, float lr, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  if (!tables || !G) return DLRM_E_INVALID;
+  if (d < 4 || d > 1024 || (d % 4) != 0) return DLRM_E_INVALID;
+  if (g_col0 < 0 || g_ld < g_col0 + (int64_t)K * d || (g_ld % 4) != 0 || (g_col0 % 4) != 0 || !aligned16(G))
+    return DLRM_E_INVALID;
+  int row_bits = 0, table_bits = 0;
+  int rc = check_sparse(K, rows, B, nnz, &row_bits, &table_bits);
+  if (rc != DLRM_OK) return rc;
+  if (nnz == 0) return DLRM_OK;
+  SparseLayout L;
+  SparseBufs b;
+  if ((rc = sparse_bufs(nnz, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
+  const int cur = sort_passes(row_bits, table_bits) & 1;
+  // the work counters start from zero on every call, so one prepared
+  // workspace can be applied more than once
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters + 2, 2);
   if (launch_status() != DLRM_OK) return DLRM_E_HIP;
   // per-segment sums and the in-place update: the long segments on `stream`,
   // the short ones (disjoint rows) on the side stream at the same time, joined
@@ -788,16 +840,30 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
     (void)hipEventDestroy(fork);
     return DLRM_E_HIP;
   }
-  int rc = DLRM_OK;
   if (hipEventRecord(fork, stream) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess) rc = DLRM_E_HIP;
-  if (rc == DLRM_OK) rc = sgd_segments(tables, d, row_bits, seg_key, vals[cur], seg, hot_ordered, counters, G, g_ld,
-                                       g_col0, lr, stream, side);
+  if (rc == DLRM_OK)
+    rc = sgd_segments(tables, d, row_bits, b.seg_key, b.vals[cur], b.seg, b.hot_ordered, b.counters, G, g_ld, g_col0,
+                      lr, stream, side);
   // the join is recorded even after a failed launch, so `stream` never
   // waits on an event that was not recorded
   if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(stream, join, 0) != hipSuccess) rc = DLRM_E_HIP;
   (void)hipEventDestroy(fork);
   (void)hipEventDestroy(join);
   return rc;
+}
+
+extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_t* rows,
+                                   const int64_t* indices, const int64_t* offsets, int64_t B, int64_t nnz,
+                                   const float* G, int64_t g_ld, int64_t g_col0, float lr, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!tables || !rows || !indices || !offsets || !G) return DLRM_E_INVALID;
+  if (K < 1 || B < 1 || d < 4 || d > 1024 || (d % 4) != 0) return DLRM_E_INVALID;
+  if (nnz < 0 || nnz > 0x7fffffffLL || B > 0x7fffffffLL) return DLRM_E_INVALID;
+  if (g_col0 < 0 || g_ld < g_col0 + (int64_t)K * d || (g_ld % 4) != 0 || (g_col0 % 4) != 0 || !aligned16(G))
+    return DLRM_E_INVALID;
+  const int rc = dlrm_embbag_bwd_sgd_prepare(K, rows, indices, offsets, B, nnz, ws, ws_bytes, stream);
+  if (rc != DLRM_OK) return rc;
+  return dlrm_embbag_bwd_sgd_apply(tables, K, d, rows, B, nnz, G, g_ld, g_col0, lr, ws, ws_bytes, stream);
 }
 
 namespace dlrm {

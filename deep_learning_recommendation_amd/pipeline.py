@@ -17,7 +17,9 @@ the standalone lookup keeps more rows in flight (measured crossover below).
 Training step (sum-pooled tables, row-wise SGD):
   forward with saved activations, dlrm_bce_grad, dlrm_mlp_bwd(top),
   dlrm_mlp_bwd(bottom) seeded by the X row-0 gradient, and
-  dlrm_embbag_bwd_sgd with the X rows 1..K gradient.
+  dlrm_embbag_bwd_sgd with the X rows 1..K gradient (or its index half,
+  dlrm_embbag_bwd_sgd_prepare, on a second stream beside the forward and
+  dlrm_embbag_bwd_sgd_apply once the gradient exists).
 """
 from __future__ import annotations
 
@@ -167,19 +169,36 @@ class DLRM:
             self.ws_sparse = self._ws(need)
         return self.ws_sparse
 
-    def backward(self, labels, G, indices, offsets, nnz: int, lr: float, stream=None):
+    def sparse_prepare(self, indices, offsets, nnz: int, stream=None):
+        """The index half of the sparse update (keys, sort, segments): it
+        needs only this batch's indices, so it can run on a second stream
+        beside the forward and the dense backward; ``backward(...,
+        prepared=True)`` then applies it (the caller orders the two)."""
+        C.dlrm_embbag_bwd_sgd_prepare(self.K, self.rows, indices, offsets, self.B, nnz, self.sparse_workspace(nnz),
+                                      stream)
+
+    def _sparse_update(self, G, indices, offsets, nnz, lr, prepared, stream):
+        B, n, d = self.B, self.n, self.d
+        if prepared:
+            C.dlrm_embbag_bwd_sgd_apply(self.table_ptrs, self.K, d, self.rows, B, nnz, G, n * d, d, lr,
+                                        self.sparse_workspace(nnz), stream)
+        else:
+            C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, G, n * d, d, lr,
+                                  self.sparse_workspace(nnz), stream)
+
+    def backward(self, labels, G, indices, offsets, nnz: int, lr: float, stream=None, prepared: bool = False):
         """Dense gradients (top: from the BCE loss; bottom: from G[:, 0, :]) and
-        the sparse SGD update of the tables from G[:, 1..K, :]."""
+        the sparse SGD update of the tables from G[:, 1..K, :] (from a
+        ``sparse_prepare`` of this batch when ``prepared``)."""
         B, n, d = self.B, self.n, self.d
         C.dlrm_bce_grad(self.logit, 1, labels, B, self.dlogit, stream)
         C.dlrm_mlp_bwd(B, self.top.dims, self.top.Ws, self.top.w_ld, C.DLRM_ACT_NONE, self.ws_top, self.logit, 1,
                        self.dlogit, 1, self.dW_top, self.db_top, None, 0, self.ws_top_bwd, stream)
         C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.x0,
                        self.x0_ld, G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
-        C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, G, n * d, d, lr,
-                              self.sparse_workspace(nnz), stream)
+        self._sparse_update(G, indices, offsets, nnz, lr, prepared, stream)
 
-    def backward_chain(self, labels, indices, offsets, nnz: int, lr: float, stream=None):
+    def backward_chain(self, labels, indices, offsets, nnz: int, lr: float, stream=None, prepared: bool = False):
         """The whole training backward from the loss: BCE seed, top MLP (with
         the gradient of its input row), interaction backward to the gradient
         of X, then the bottom MLP from row 0 and the sparse SGD update from
@@ -196,5 +215,4 @@ class DLRM:
         C.dlrm_interact_bwd(self.X, B, n, d, n * d, self.g_top, self.top_w, self.G, n * d, stream)
         C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.x0,
                        self.x0_ld, self.G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
-        C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, self.G, n * d, d, lr,
-                              self.sparse_workspace(nnz), stream)
+        self._sparse_update(self.G, indices, offsets, nnz, lr, prepared, stream)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define DLRM_ABI_VERSION 2
+#define DLRM_ABI_VERSION 3
 
 enum {
   DLRM_OK = 0,
@@ -281,6 +281,30 @@ size_t dlrm_embbag_bwd_sgd_workspace_size(int32_t K, int64_t B, int64_t nnz, int
 int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_t* rows, const int64_t* indices,
                         const int64_t* offsets, int64_t B, int64_t nnz, const float* G, int64_t g_ld,
                         int64_t g_col0, float lr, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dlrm_embbag_bwd_sgd in two calls, for callers that overlap the index work
+ * with the forward and dense backward: the sort, segmentation and hot-row
+ * list depend on the indices only, not on the gradient.
+ *
+ * dlrm_embbag_bwd_sgd_prepare: the (table, row) keys, their stable radix
+ *   sort, the segments and the list of long segments, into ws.  Reads
+ *   indices and offsets only (K, rows, indices, offsets, B, nnz as for
+ *   dlrm_embbag_bwd_sgd).
+ * dlrm_embbag_bwd_sgd_apply: the per-row gradient sums and the update, from
+ *   a workspace that a prepare call with the same K, rows, B and nnz filled
+ *   and that nothing changed since (the caller orders the two calls, e.g.
+ *   by an event when they run on different streams).  The result is bit for
+ *   bit that of dlrm_embbag_bwd_sgd; the workspace stays prepared, so
+ *   applying it again updates the same rows again (a second SGD step with
+ *   the same indices).
+ * Same arguments, limits and error codes as dlrm_embbag_bwd_sgd.
+ */
+int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const int64_t* indices, const int64_t* offsets,
+                                int64_t B, int64_t nnz, void* ws, size_t ws_bytes, hipStream_t stream);
+int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_t d, const int64_t* rows, int64_t B, int64_t nnz,
+                              const float* G, int64_t g_ld, int64_t g_col0, float lr, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /*
  * Validate indices and offsets on the device.  rows_dev: device int64 [K].

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_strings(lib):
-    assert C.dlrm_abi_version() == 2
+    assert C.dlrm_abi_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert lib.dlrm_strerror(code)
     assert lib.dlrm_last_hip_error() == 0
@@ -120,3 +120,27 @@ def test_sparse_checks(lib):
              ctypes.c_void_p(0x100000), 1 << 30, NULL) == C.DLRM_E_UNSUPPORTED
     assert f(FAKE, 8, 128, rows, FAKE, FAKE, 8192, 100, FAKE, 9 * 128 - 4, 128, ctypes.c_float(0.01),
              ctypes.c_void_p(0x100000), 1 << 30, NULL) == C.DLRM_E_INVALID
+
+
+def test_sparse_prepare_apply_checks(lib):
+    """The two-call form rejects what the one-call form rejects, before
+    enqueueing any work."""
+    rows = (ctypes.c_int64 * 8)(*([50_000_000] * 8))
+    prep, apply = lib.dlrm_embbag_bwd_sgd_prepare, lib.dlrm_embbag_bwd_sgd_apply
+    lr = ctypes.c_float(0.01)
+    assert prep(8, rows, FAKE, FAKE, 8192, 6553600, ctypes.c_void_p(0x100000), 256, NULL) == C.DLRM_E_WORKSPACE
+    assert prep(8, rows, NULL, FAKE, 8192, 100, ctypes.c_void_p(0x100000), 1 << 30, NULL) == C.DLRM_E_INVALID
+    assert prep(8, rows, FAKE, FAKE, 8192, -1, ctypes.c_void_p(0x100000), 1 << 30, NULL) == C.DLRM_E_INVALID
+    big = (ctypes.c_int64 * 8)(*([1 << 31] * 8))
+    assert prep(8, big, FAKE, FAKE, 8192, 100, ctypes.c_void_p(0x100000), 1 << 30, NULL) == C.DLRM_E_UNSUPPORTED
+    assert prep(8, rows, FAKE, FAKE, 8192, 0, None, 0, NULL) == C.DLRM_OK  # nothing to sort
+    assert apply(FAKE, 8, 128, rows, 8192, 6553600, FAKE, 9 * 128, 128, lr, ctypes.c_void_p(0x100000), 256,
+                 NULL) == C.DLRM_E_WORKSPACE
+    assert apply(NULL, 8, 128, rows, 8192, 100, FAKE, 9 * 128, 128, lr, ctypes.c_void_p(0x100000), 1 << 30,
+                 NULL) == C.DLRM_E_INVALID
+    assert apply(FAKE, 8, 128, rows, 8192, 100, FAKE, 9 * 128 - 4, 128, lr, ctypes.c_void_p(0x100000), 1 << 30,
+                 NULL) == C.DLRM_E_INVALID
+    assert apply(FAKE, 8, 130, rows, 8192, 100, FAKE, 9 * 130, 130, lr, ctypes.c_void_p(0x100000), 1 << 30,
+                 NULL) == C.DLRM_E_INVALID
+    assert apply(FAKE, 8, 128, big, 8192, 100, FAKE, 9 * 128, 128, lr, ctypes.c_void_p(0x100000), 1 << 30,
+                 NULL) == C.DLRM_E_UNSUPPORTED

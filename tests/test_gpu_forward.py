@@ -87,18 +87,29 @@ def test_forward_full_size_sampled():
     assert np.max(np.abs(gl - logit)) <= 2e-2
 
 
-def test_train_step_scaled():
+@pytest.mark.parametrize("prepared", [False, True])
+def test_train_step_scaled(prepared):
+    """prepared: the sparse update's index half runs on a second stream
+    beside the forward (sparse_prepare), the update after the backward."""
     import deep_learning_recommendation_amd as D  # noqa: F401
 
     w = W.get("train").scaled(B=1024, rows=100_000)
-    banner("train step scaled")
+    banner(f"train step scaled prepared={prepared}")
     model, bottom, top = device_model(w, train=True)
     dense, idx, off = W.dense(w), *W.indices_offsets(w)
     G = W.upstream_grad(w)
     y = W.labels(w)
     idx_d, off_d = to_dev(idx), to_dev(off)
+    nnz = int(off[-1])
+    side = torch.cuda.Stream()
+    if prepared:
+        model.sparse_workspace(nnz)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            model.sparse_prepare(idx_d, off_d, nnz)
     model.forward(to_dev(dense), idx_d, off_d)
-    model.backward(to_dev(y), to_dev(G), idx_d, off_d, int(off[-1]), w.lr)
+    torch.cuda.current_stream().wait_stream(side)
+    model.backward(to_dev(y), to_dev(G), idx_d, off_d, nnz, w.lr, prepared=prepared)
     torch.cuda.synchronize()
     # sparse update: bit-exact on every touched row
     tabs, local, row_ids = W.compact_rows(w, idx, off)

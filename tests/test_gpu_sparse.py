@@ -154,3 +154,48 @@ def test_sparse_sgd_train_full_size():
         assert np.array_equal(bits(now), bits(R.table_rows(w.seed, k, w.rows[k], probe, w.d)))
     del tabs_dev
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d,K", [(128, 4), (64, 2), (132, 3)])
+def test_sparse_prepare_apply_two_calls(d, K):
+    """dlrm_embbag_bwd_sgd_prepare on a second stream (beside unrelated work
+    on the first), then dlrm_embbag_bwd_sgd_apply twice from the same
+    prepared workspace: two SGD steps, each bit-exact against the oracle."""
+    import deep_learning_recommendation_amd as D
+
+    B = 733
+    rows = [97, 1000, 5, 400][:K]
+    banner(f"sparse sgd prepare/apply d={d} K={K}")
+    g = np.random.default_rng(900 + d + K)
+    lens = g.integers(0, 40, size=K * B)
+    off = np.zeros(K * B + 1, dtype=np.int64)
+    np.cumsum(lens, out=off[1:])
+    idx = []
+    for k in range(K):
+        n = off[(k + 1) * B] - off[k * B]
+        idx.append(np.where(g.random(n) < 0.5, g.integers(0, 2, n), g.integers(0, rows[k], n)))
+    idx = np.concatenate(idx).astype(np.int64)
+    nnz = int(off[-1])
+    tabs = [g.standard_normal((rows[k], d)).astype(np.float32) for k in range(K)]
+    G = (g.standard_normal((B, (K + 1) * d)) * 0.01).astype(np.float32)
+    tabs_dev = [to_dev(t) for t in tabs]
+    ptrs = D.device_pointer_array(tabs_dev)
+    idx_d, off_d, G_d = to_dev(idx), to_dev(off), to_dev(G)
+    ws = torch.empty((D.dlrm_embbag_bwd_sgd_workspace_size(K, B, nnz, d),), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)  # whatever the workspace held before, prepare defines it
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    busy = torch.empty((1 << 26,), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(side):
+        D.dlrm_embbag_bwd_sgd_prepare(K, rows, idx_d, off_d, B, nnz, ws)
+    busy.fill_(1.0)  # unrelated work on the first stream meanwhile
+    torch.cuda.current_stream().wait_stream(side)
+    ref = [t.copy() for t in tabs]
+    for step in range(2):
+        D.dlrm_embbag_bwd_sgd_apply(ptrs, K, d, rows, B, nnz, G_d, G.shape[1], d, 0.01, ws)
+        torch.cuda.synchronize()
+        oracle.embbag_bwd_sgd(ref, idx, off, B, G, d, 0.01)
+        for k in range(K):
+            assert np.array_equal(bits(tabs_dev[k].cpu().numpy()), bits(ref[k])), (step, k)
+    counts = np.bincount(idx[off[0]:off[B]], minlength=rows[0])
+    assert counts.max() >= 128  # the hot-row path was exercised
