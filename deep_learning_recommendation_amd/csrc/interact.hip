@@ -132,8 +132,7 @@ struct FRowI8 {
 // (in LDS): dense vector first, then the strict lower triangle row by row,
 // then zeros up to pad_end.  The k loop is outermost so the MFMAs of all
 // blocks (J <= I) interleave as independent accumulation chains; a single
-// block is split into two partial chains.  Lanes whose (i, j) is not a kept
-// pair write to a dummy slot past the row, so the stores need no branches.
+// block is split into two partial chains.
 // 16-byte load through a global-address-space pointer (a plain pointer that
 // came out of memory would otherwise turn into a flat load)
 __device__ __forceinline__ f4 ld4(const float* p) { return *(const __attribute__((address_space(1))) f4*)(p); }
@@ -166,15 +165,26 @@ __device__ __forceinline__ void gram_row(f4 (&x)[NT][DC], int n, int d, int pad_
       if (kk < d) put4(ob + kk, x[0][c]);
     }
   }
-  const int dummy = pad_end;  // one spare element after the row
-  // D[i][j] of block (I, J): lane holds i = 4*(l/16) + r, j = l % 16
+  // D[i][j] of block (I, J): lane holds i = 16 I + a_r (a_r = 4 (l/16) + r)
+  // and j = 16 J + l % 16, whose packed position d + i (i - 1) / 2 + j is
+  // P_r + I Q_r + (128 I^2 - 8 I + 16 J) with the per-lane P_r = d +
+  // a_r (a_r - 1) / 2 + l % 16 and Q_r = 16 a_r, so each store costs one
+  // multiply-add; lanes off the strict lower triangle (or past row n) are
+  // masked off.
+  int P[4], Q[4];
+  bool below[4];  // j < i inside a diagonal block
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int a = 4 * g + r;
+    P[r] = d + a * (a - 1) / 2 + r16;
+    Q[r] = 16 * a;
+    below[r] = r16 < a;
+  }
   auto store_block = [&](int I, int J, f4 v) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = I * 16 + 4 * g + r;
-      const int j = J * 16 + r16;
-      const int at = (i < n && j < i) ? d + i * (i - 1) / 2 + j : dummy;
-      put(ob + at, v[r]);
+      const bool keep = I * 16 + 4 * g + r < n && (J < I || below[r]);
+      if (keep) put(ob + (P[r] + I * Q[r] + (128 * I * I - 8 * I + 16 * J)), v[r]);
     }
   };
   // chunk pairs (2p, 2p + 1); an odd last chunk pairs with zeros
@@ -513,8 +523,8 @@ struct FRowOf<3> { typedef FRowI8 type; };
 template <int NT, int DC, typename OutT, int MODE>
 void launch_mfma(const RowSource& src, int64_t B, int n, int d, OutT* out, int64_t out_ld, int pad_end,
                  hipStream_t s) {
-  // row buffer: pad_end elements plus one spare element for masked stores
-  const int row_bytes = (int)round_up((int64_t)(pad_end + 1) * (int64_t)sizeof(OutT), 16);
+  // row buffer: pad_end elements
+  const int row_bytes = (int)round_up((int64_t)pad_end * (int64_t)sizeof(OutT), 16);
   int spb = 65536 / row_bytes;  // samples (waves) per block within 64 KB of LDS
   spb = spb < 1 ? 1 : (spb > 4 ? 4 : spb);
   const int wide = ((out_ld * (int64_t)sizeof(OutT)) % 16) == 0;
