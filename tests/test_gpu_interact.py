@@ -41,7 +41,8 @@ def test_interact_fp32_within_dot_product_bound(n, d):
     assert np.all(got[:, width:pad_end] == 0)
 
 
-@pytest.mark.parametrize("n,d", [(9, 16), (27, 128), (101, 64), (101, 128), (128, 64)])
+@pytest.mark.parametrize("n,d", [(9, 16), (16, 64), (17, 16), (27, 128), (32, 32), (33, 128), (101, 64), (101, 128),
+                                 (128, 64)])
 def test_interact_integer_X_bitexact(n, d):
     # small integers: every product and partial sum is exact in fp32, so any
     # accumulation order (MFMA included) gives the oracle's value exactly;
@@ -52,6 +53,13 @@ def test_interact_integer_X_bitexact(n, d):
     got, width = _run(X)
     ref = oracle.interact_fwd(X)
     assert np.array_equal(bits(got[:, :width]), bits(ref))
+    # bf16 rows: the exact values rounded once to nearest even, at the same
+    # packed positions (the bf16 store path of the same kernel)
+    got_b, _ = _run(X, torch.bfloat16)
+    ref_b = torch.from_numpy(ref).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(bits(got_b[:, :width]), bits(ref_b))
+    # the row's padding up to the next multiple of 8 elements is zero
+    assert np.all(got[:, width:] == 0) and np.all(got_b[:, width:] == 0)
 
 
 def test_interact_bf16_output():
