@@ -269,7 +269,8 @@ def main():
 
     stream = torch.cuda.current_stream()
     # training: the index half of the sparse update (keys, sort, segments)
-    # runs on a second stream beside the forward and the dense backward
+    # runs on a second stream, forked after the lookup, beside the rest of
+    # the forward and the dense backward; the update waits for it
     prep_stream = torch.cuda.Stream() if w.train else None
     gather_t = Timer()
     call_t = {}   # per-call event pairs of the breakdown steps
