@@ -62,6 +62,19 @@ def make_mlp(dims, weights, biases, bf16: bool, device="cuda") -> MLPParams:
     return MLPParams(tuple(int(x) for x in dims), Ws, lds, bs, C.DLRM_BF16 if bf16 else C.DLRM_F32)
 
 
+def pad_first_layer(mlp: MLPParams, k_pad: int) -> MLPParams:
+    """The same MLP with its first layer's input widened to k_pad by zero
+    weight columns: the products of the zero columns add exact zeros, so
+    the outputs are unchanged, and a k that is a multiple of 64 takes the
+    GEMM's 64-wide k-tiles."""
+    W0 = mlp.Ws[0]
+    out_f = W0.shape[0]
+    Wp = torch.zeros((out_f, k_pad), dtype=W0.dtype, device=W0.device)
+    Wp[:, :W0.shape[1]] = W0
+    return MLPParams((k_pad,) + tuple(mlp.dims[1:]), [Wp] + list(mlp.Ws[1:]), [k_pad] + list(mlp.w_ld[1:]),
+                     mlp.biases, mlp.w_dtype)
+
+
 # Mean bag length up to which "auto" takes the fused lookup + interaction.
 AUTO_FUSED_MAX_MEAN_BAG = 2.0
 
@@ -103,7 +116,14 @@ class DLRM:
             self.x0_ld = n * d
         top_dtype = torch.bfloat16 if top.w_dtype == C.DLRM_BF16 else torch.float32
         self.top_ld = _round_up(self.top_w, 8) if top_dtype == torch.bfloat16 else _round_up(self.top_w, 4)
-        self.top_in = torch.empty((B, self.top_ld), dtype=top_dtype, device=dev)
+        if not train and top_dtype == torch.bfloat16 and self.top_w >= 256 and self.top_w % 64 != 0:
+            # forward only: the top MLP reads the interaction rows as K =
+            # top_w rounded up to 64 (zero columns, never written after
+            # the zero fill below), e.g. 512 for 479 (measured faster)
+            self.top_ld = _round_up(self.top_w, 64)
+            self.top = top = pad_first_layer(top, self.top_ld)
+        # zero-filled: columns past the interaction kernels' padding stay zero
+        self.top_in = torch.zeros((B, self.top_ld), dtype=top_dtype, device=dev)
         self.logit = torch.empty((B, 1), dtype=torch.float32, device=dev)
         self.prob = torch.empty((B,), dtype=torch.float32, device=dev)
         save = bool(train)
