@@ -419,8 +419,10 @@ def main():
         # offsets, the dense rows it reads and the packed top-MLP rows it writes
         kname, key = "fused_kernel", "embbag_interact"
         esz = model.top_in.element_size()
+        # the kernel writes d + P values and zeros up to the next multiple of 8
+        row_out = min((model.top_w + 7) // 8 * 8, model.top_ld)
         gbytes = (gather_bytes(w.K, w.B, w.d, nnz_mean, lp) - 4 * w.K * w.B * w.d + 4 * w.B * w.d +
-                  esz * w.B * model.top_ld)
+                  esz * w.B * row_out)
         g_ms = dom_ms[key]
     achieved = gbytes / (g_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name + ("_uniform" if args.uniform else "") + ("_chain" if args.chain else "") +
