@@ -85,7 +85,9 @@ class DLRM:
     def __init__(self, B: int, K: int, d: int, rows, tables, bottom: MLPParams, top: MLPParams, train: bool = False,
                  device="cuda", fused="auto", table_dtype: str = "f32", scale_bias=None):
         """table_dtype "f32", or "bf16" / "int8" rows (forward only) with, for
-        int8, ``scale_bias`` = K fp32 [m_k][2] tensors."""
+        int8, ``scale_bias`` = K fp32 [m_k][2] tensors.  A forward-only model
+        may widen the top MLP's first layer with zero columns (see
+        ``pad_first_layer``); ``self.top`` holds the layers the calls use."""
         self.B, self.K, self.d, self.n = B, K, d, K + 1
         self.rows = [int(r) for r in rows]
         self.tables = tables
