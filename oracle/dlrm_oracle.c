@@ -292,25 +292,35 @@ void oracle_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const float* cons
         const double gv = g[b * fo + o];
         delta[b * fo + o] = (relu && !(y[b * fo + o] > 0.0f)) ? 0.0 : gv;
       }
-#pragma omp parallel for schedule(static)
-    for (int32_t o = 0; o < fo; ++o) {
-      double sb = 0.0;
-      for (int64_t b = 0; b < B; ++b) sb += delta[b * fo + o];
-      db[l][o] = (float)sb;
-      for (int32_t i = 0; i < fi; ++i) {
-        double s = 0.0;
-        for (int64_t b = 0; b < B; ++b) s += delta[b * fo + o] * (double)x[b * fi + i];
-        dW[l][(int64_t)o * fi + i] = (float)s;
+    /* Every sum below runs over b (or o) in ascending order from 0.0; the
+     * loops over i are innermost only so that rows are read contiguously. */
+#pragma omp parallel
+    {
+      double* s = (double*)malloc(sizeof(double) * (size_t)fi);
+#pragma omp for schedule(static)
+      for (int32_t o = 0; o < fo; ++o) {
+        double sb = 0.0;
+        for (int32_t i = 0; i < fi; ++i) s[i] = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+          const double dv = delta[b * fo + o];
+          sb += dv;
+          for (int32_t i = 0; i < fi; ++i) s[i] += dv * (double)x[b * fi + i];
+        }
+        db[l][o] = (float)sb;
+        for (int32_t i = 0; i < fi; ++i) dW[l][(int64_t)o * fi + i] = (float)s[i];
       }
+      free(s);
     }
     if (l > 0 || dX) {
 #pragma omp parallel for schedule(static)
-      for (int64_t b = 0; b < B; ++b)
-        for (int32_t i = 0; i < fi; ++i) {
-          double s = 0.0;
-          for (int32_t o = 0; o < fo; ++o) s += delta[b * fo + o] * (double)W[l][(int64_t)o * fi + i];
-          g[b * fi + i] = s;
+      for (int64_t b = 0; b < B; ++b) {
+        double* gb = g + b * fi;
+        for (int32_t i = 0; i < fi; ++i) gb[i] = 0.0;
+        for (int32_t o = 0; o < fo; ++o) {
+          const double dv = delta[b * fo + o];
+          for (int32_t i = 0; i < fi; ++i) gb[i] += dv * (double)W[l][(int64_t)o * fi + i];
         }
+      }
     }
   }
   if (dX)
