@@ -11,5 +11,5 @@ from ._lib import (DLRM_ACT_NONE, DLRM_ACT_RELU, DLRM_BF16, DLRM_F32, DLRM_I8, D
                    dlrm_embbag_bwd_sgd, dlrm_embbag_bwd_sgd_apply, dlrm_embbag_bwd_sgd_prepare,
                    dlrm_embbag_bwd_sgd_workspace_size, dlrm_embbag_fwd, dlrm_embbag_fwd_lp,
                    dlrm_embbag_interact_fwd, dlrm_embbag_interact_fwd_lp,
-                   dlrm_interact_bwd, dlrm_interact_fwd,
+                   dlrm_interact_bwd, dlrm_interact_fwd, dlrm_linear_fwd,
                    dlrm_mlp_bwd, dlrm_mlp_bwd_workspace_size, dlrm_mlp_fwd, dlrm_mlp_workspace_size, lib)

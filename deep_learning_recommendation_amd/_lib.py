@@ -36,6 +36,7 @@ _SIGNATURES = {
     "dlrm_mlp_workspace_size": (_SZ, [_I64, _I32, _P, _I32, _I32]),
     "dlrm_mlp_fwd": (ctypes.c_int, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _SZ,
                                     _I32, _P]),
+    "dlrm_linear_fwd": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _P]),
     "dlrm_mlp_bwd_workspace_size": (_SZ, [_I64, _I32, _P]),
     "dlrm_mlp_bwd": (ctypes.c_int, [_I64, _I32, _P, _P, _P, _I32, _P, _P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _SZ,
                                     _P]),
@@ -45,7 +46,7 @@ _SIGNATURES = {
                                            _P, _SZ, _P]),
     "dlrm_embbag_bwd_sgd_prepare": (ctypes.c_int, [_I32, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "dlrm_embbag_bwd_sgd_apply": (ctypes.c_int, [_P, _I32, _I32, _P, _I64, _I64, _P, _I64, _I64, ctypes.c_float, _P,
-                                                 _SZ, _P]),
+                                                 _SZ, _P, _P]),
     "dlrm_check_indices": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _P, _P]),
 }
 
@@ -181,6 +182,13 @@ def dlrm_mlp_fwd(inp, in_ld: int, B: int, dims, Ws, w_ld, biases, w_dtype: int, 
                                                int(save_acts), _stream(stream)))
 
 
+def dlrm_linear_fwd(A, lda: int, W, ldw: int, bias, C, ldc: int, M: int, N: int, K: int, act: int,
+                    stream=None) -> None:
+    """One bf16 layer C = act(A W^T + b); C's dtype (fp32 or bf16) selects the output."""
+    _check("dlrm_linear_fwd", lib().dlrm_linear_fwd(_ptr(A), lda, _ptr(W), ldw, _ptr(bias), _ptr(C), _dtype_code(C),
+                                                     ldc, M, N, K, act, _stream(stream)))
+
+
 def dlrm_mlp_bwd_workspace_size(B: int, dims) -> int:
     return int(lib().dlrm_mlp_bwd_workspace_size(B, len(dims) - 1, _host_i32(dims)))
 
@@ -220,12 +228,16 @@ def dlrm_embbag_bwd_sgd_prepare(K: int, rows, indices, offsets, B: int, nnz: int
 
 
 def dlrm_embbag_bwd_sgd_apply(table_ptrs, K: int, d: int, rows, B: int, nnz: int, G, g_ld: int, g_col0: int,
-                              lr: float, ws, stream=None) -> None:
+                              lr: float, ws, stream=None, side=None) -> None:
+    """side: an optional second torch stream for the short segments; the
+    caller orders it (side.wait_stream(stream) before the call,
+    stream.wait_stream(side) after it)."""
     rows_h = (ctypes.c_int64 * K)(*[int(r) for r in rows])
+    side_h = ctypes.c_void_p(side.cuda_stream) if side is not None else None
     _check("dlrm_embbag_bwd_sgd_apply",
            lib().dlrm_embbag_bwd_sgd_apply(_ptr(table_ptrs), K, d, rows_h, B, nnz, _ptr(G), g_ld, g_col0,
                                            ctypes.c_float(lr), _ptr(ws), ws.numel() * ws.element_size(),
-                                           _stream(stream)))
+                                           _stream(stream), side_h))
 
 
 def dlrm_check_indices(indices, offsets, K: int, B: int, rows_dev, bad_count, stream=None) -> None:

@@ -68,11 +68,19 @@ __device__ __forceinline__ void lds_dma16_opaque(const void* src, const void* ld
 // Keeps the compiler from moving memory accesses across this point.
 __device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
 
+// Per-device caches (kernel attributes, occupancy, CU counts) are indexed
+// by the current device; devices past kMaxDevices share slot 0.
+constexpr int kMaxDevices = 64;
+inline int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  return dev;
+}
+
 // Compute units of the current device (queried once per device).
 inline int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  static int cached[kMaxDevices] = {0};
+  const int dev = current_device();
   if (cached[dev] == 0) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 1;

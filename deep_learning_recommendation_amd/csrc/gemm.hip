@@ -457,16 +457,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
   }
 }
 
-// Resident workgroups per CU of one fast-kernel instance (queried once).
+// Resident workgroups per CU of one fast-kernel instance (queried once per
+// device).
 template <typename Kern>
 int fast_occupancy(Kern kern, int threads) {
-  static int cached = 0;
-  if (cached == 0) {
+  static int cached[kMaxDevices] = {0};
+  const int dev = current_device();
+  if (cached[dev] == 0) {
     int v = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, 0) != hipSuccess || v < 1) v = 1;
-    cached = v;
+    cached[dev] = v;
   }
-  return cached;
+  return cached[dev];
 }
 
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2, bool PERSIST = false,
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 16);
   if (sub == 0 && row < M) {
-    float v = acc + bias[0];
+    float v = acc + (bias ? bias[0] : 0.f);
     if (relu) v = relu_f(v);
     out[(int64_t)row * ldo] = v;
     if (prob) prob[row] = 1.f / (1.f + expf(-v));

@@ -646,12 +646,13 @@ int launch_bwd(const float* X, int64_t B, int n, int d, int64_t x_ld, const floa
   spb = spb < 1 ? 1 : (spb > 4 ? 4 : spb);
   const size_t lds = (size_t)spb * wave_floats * 4;
   if (lds > 65536) {  // one large sample per block: allow the full LDS once
-    static bool raised = false;
-    if (!raised) {
+    static bool raised[kMaxDevices] = {false};
+    const int dev = current_device();
+    if (!raised[dev]) {
       if (hipFuncSetAttribute(reinterpret_cast<const void*>(interact_bwd_kernel<CT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLdsMax) != hipSuccess)
         return DLRM_E_HIP;
-      raised = true;
+      raised[dev] = true;
     }
   }
   hipLaunchKernelGGL((interact_bwd_kernel<CT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb), lds, s, X, B, n,

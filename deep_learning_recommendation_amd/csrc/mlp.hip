@@ -642,9 +642,8 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
     bool ok = true;
     for (int l = 0; l < 3; ++l) ok = ok && aligned16(W[l]) && aligned16(bias[l]) && (w_ld[l] % 8) == 0;
     if (ok) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-      static bool raised[64] = {false};
+      const int dev = current_device();
+      static bool raised[kMaxDevices] = {false};
       if (!raised[dev]) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(mlp3_fused_kernel),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kF3Lds) != hipSuccess)
@@ -697,6 +696,22 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
       rc = gemm_bf16(src, ld_src, w, wl, bias[l], dst, ld_dst, !last, M, fo, fi, relu, stream);
   }
   return rc;
+}
+
+extern "C" int dlrm_linear_fwd(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias, void* C,
+                               int32_t out_dtype, int64_t ldc, int64_t M, int32_t N, int32_t K, int32_t act,
+                               hipStream_t stream) {
+  if (!A || !W || !C) return DLRM_E_INVALID;
+  if (out_dtype != DLRM_F32 && out_dtype != DLRM_BF16) return DLRM_E_INVALID;
+  if (act != DLRM_ACT_NONE && act != DLRM_ACT_RELU) return DLRM_E_INVALID;
+  if (M < 1 || M > 0x7fffffffLL || N < 1 || K < 1 || lda < K || ldw < K || ldc < N) return DLRM_E_INVALID;
+  const uint16_t* a = static_cast<const uint16_t*>(A);
+  const uint16_t* w = static_cast<const uint16_t*>(W);
+  if (N == 1) {
+    if (out_dtype != DLRM_F32) return DLRM_E_INVALID;
+    return gemv_bf16(a, lda, w, bias, static_cast<float*>(C), ldc, nullptr, (int)M, K, act == DLRM_ACT_RELU, stream);
+  }
+  return gemm_bf16(a, lda, w, ldw, bias, C, ldc, out_dtype == DLRM_BF16, (int)M, N, K, act == DLRM_ACT_RELU, stream);
 }
 
 extern "C" size_t dlrm_mlp_bwd_workspace_size(int64_t B, int32_t L, const int32_t* dims) {

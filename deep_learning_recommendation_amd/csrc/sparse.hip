@@ -14,15 +14,15 @@
 //   4. one fused kernel: each segment's gradient sum over its occurrences in
 //      sorted order (fp32, from +0) and the update T <- T - lr * g.
 // Hot rows (Zipf heads with 10^5 occurrences) make step 4's longest serial
-// chain the latency floor.  Segments of at least kHot occurrences go to a
-// producer/consumer kernel: per (segment, 64-column slice) one wave adds, one
-// column per lane, from an LDS ring that seven other waves keep filled with
-// direct global-to-LDS loads, so the serial adds never wait on memory.  Hot
-// items are handed out longest first.  The remaining (short) segments take
-// one lane group each.
+// chain the latency floor.  Step 4 is one persistent launch with one block
+// per CU.  Segments of at least kHot occurrences come first, as
+// producer/consumer items: per (segment, 64-column slice) one wave adds, one
+// column per lane, from an LDS ring that six other waves keep filled, so the
+// serial adds never wait on memory.  Hot items are handed out longest first;
+// a block that finds none left turns its seven waves to the short segments
+// (one lane group each, chunks taken from a second counter), so the CUs that
+// the few longest chains leave free take the rest of the work meanwhile.
 #include "common.hpp"
-
-#include <mutex>
 
 namespace dlrm {
 namespace {
@@ -33,13 +33,13 @@ constexpr int RTILE = RT * RITEMS;     // 4096 keys per tile
 constexpr int SCAN_ITEMS = 8;
 constexpr int SCAN_TILE = 256 * SCAN_ITEMS;
 constexpr int kHot = 128;              // occurrences from which a segment is "hot"
-constexpr int kHotBlocks = 256;        // persistent blocks of the hot kernel (one per CU)
 constexpr int kHB = 64;                // occurrences per LDS ring slot
 constexpr int kSlots = 8;              // ring slots
 constexpr int kRS = kHB + 4;           // floats per column row of a slot (padded: conflict-free 16-byte reads)
 constexpr int kLoaders = 6;            // loader waves per hot block (plus one adder)
 constexpr int kAdder = 3;              // the adder's wave index: alone on its SIMD when waves go round-robin
-constexpr int kLightBlocks = 2048;
+constexpr int kApplyThreads = 64 * (kLoaders + 1);
+constexpr int kLightBlocks = 2048;     // persistent blocks of the standalone short-segment kernel
 
 // ------------------------------------------------------------------ keys
 
@@ -336,8 +336,8 @@ __device__ __forceinline__ void lds_store(int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Hot segments.  A block (7 waves) takes (segment, 64-column slice) items
-// from a global counter.  Wave kAdder is the adder (the only wave on its
+// Hot segments (first phase of the apply kernel).  A block (7 waves) takes
+// (segment, 64-column slice) items from a global counter until none is left.  Wave kAdder is the adder (the only wave on its
 // SIMD when the waves are placed round-robin): lane j owns column j of the
 // slice and adds the occurrences in sorted order, reading them from LDS.
 // The other six waves are loaders: block t of the segment (occurrences
@@ -350,18 +350,23 @@ __device__ __forceinline__ void lds_store(int32_t* p, int32_t v) {
 // waits until the adder has finished the slot's previous block
 // ("consumed"), writes, and publishes the running block number in
 // ready[slot].
-__global__ __launch_bounds__(64 * (kLoaders + 1)) void hot_sgd_kernel(float* const* __restrict__ tables, int d, int row_bits,
-                                                      const uint32_t* __restrict__ seg_key,
-                                                      const int32_t* __restrict__ bags,
-                                                      const int32_t* __restrict__ seg_start,
-                                                      const int32_t* __restrict__ hot,
-                                                      const uint32_t* __restrict__ nhot,
-                                                      const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
-                                                      float lr, uint32_t* __restrict__ next_item) {
-  __shared__ __attribute__((aligned(16))) float ring[kSlots][64 * kRS];
-  __shared__ int32_t ready[kSlots];
-  __shared__ int32_t consumed;
-  __shared__ uint32_t s_item;
+struct HotLds {
+  float ring[kSlots][64 * kRS];
+  int32_t ready[kSlots];
+  int32_t consumed;
+  uint32_t s_item;
+};
+
+__device__ __forceinline__ void hot_phase(HotLds& sm, float* const* __restrict__ tables, int d, int row_bits,
+                                          const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ bags,
+                                          const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
+                                          const uint32_t* __restrict__ nhot, const float* __restrict__ G,
+                                          int64_t g_ld, int64_t g_col0, float lr,
+                                          uint32_t* __restrict__ next_item) {
+  auto& ring = sm.ring;
+  auto& ready = sm.ready;
+  auto& consumed = sm.consumed;
+  auto& s_item = sm.s_item;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < kSlots) ready[tid] = -1;
   if (tid == 0) consumed = 0;
@@ -530,22 +535,19 @@ __global__ __launch_bounds__(64 * (kLoaders + 1)) void hot_sgd_kernel(float* con
   }
 }
 
-// Short segments: a group of 2^g_log2 lanes (V float4 each) per segment.
-// The group loads up to one bag id per lane at once, then walks the bags in
-// order with U gradient rows in flight, broadcasting each bag id from its lane.
-// Waves take chunks of kLightChunk segments per group from a shared counter,
-// so the blocks that become resident early (beside the hot kernel) and late
-// (after its short items end) share the work as they come.
+// Short segments (per wave): a group of 2^g_log2 lanes (V float4 each) per
+// segment.  The group loads up to one bag id per lane at once, then walks
+// the bags in order with U gradient rows in flight, broadcasting each bag id
+// from its lane.  Waves take chunks of kLightChunk segments per group from a
+// shared counter, so waves that start early and late share the work as they
+// come.
 constexpr int kLightChunk = 16;
-template <int V>
-__global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict__ tables, int d, int g_log2,
-                                                        int row_bits, const uint32_t* __restrict__ seg_key,
-                                                        const int32_t* __restrict__ bags,
-                                                        const int32_t* __restrict__ seg_start,
-                                                        const uint32_t* __restrict__ nseg,
-                                                        const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
-                                                        float lr, uint32_t* __restrict__ next) {
-  constexpr int U = 8 / V;
+template <int V, int U>
+__device__ __forceinline__ void light_phase(float* const* __restrict__ tables, int d, int g_log2, int row_bits,
+                                            const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ bags,
+                                            const int32_t* __restrict__ seg_start,
+                                            const uint32_t* __restrict__ nseg, const float* __restrict__ G,
+                                            int64_t g_ld, int64_t g_col0, float lr, uint32_t* __restrict__ next) {
   const int lane = threadIdx.x & 63;
   const uint32_t row_mask = (row_bits >= 32) ? 0xffffffffu : ((1u << row_bits) - 1u);
   const int GL = 1 << g_log2;  // lanes per group
@@ -625,6 +627,45 @@ __global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict
   }
 }
 
+// The hot segments alone (the two-stream form: the short ones run beside it
+// on the caller's second stream).
+__global__ __launch_bounds__(kApplyThreads) void hot_sgd_kernel(
+    float* const* __restrict__ tables, int d, int row_bits, const uint32_t* __restrict__ seg_key,
+    const int32_t* __restrict__ bags, const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
+    const uint32_t* __restrict__ nhot, const float* __restrict__ G, int64_t g_ld, int64_t g_col0, float lr,
+    uint32_t* __restrict__ next_item) {
+  __shared__ __attribute__((aligned(16))) HotLds sm;
+  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, nhot, G, g_ld, g_col0, lr, next_item);
+}
+
+// The short segments alone (many small persistent blocks; the two-stream
+// form).
+template <int V>
+__global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict__ tables, int d, int g_log2,
+                                                        int row_bits, const uint32_t* __restrict__ seg_key,
+                                                        const int32_t* __restrict__ bags,
+                                                        const int32_t* __restrict__ seg_start,
+                                                        const uint32_t* __restrict__ nseg,
+                                                        const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
+                                                        float lr, uint32_t* __restrict__ next) {
+  light_phase<V, 8 / V>(tables, d, g_log2, row_bits, seg_key, bags, seg_start, nseg, G, g_ld, g_col0, lr, next);
+}
+
+// The segment sums and the in-place update: hot items first, then the
+// short segments, in one launch (one block per CU).
+template <int V>
+__global__ __launch_bounds__(kApplyThreads) void sgd_apply_kernel(
+    float* const* __restrict__ tables, int d, int g_log2, int row_bits, const uint32_t* __restrict__ seg_key,
+    const int32_t* __restrict__ bags, const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
+    const uint32_t* __restrict__ counters, const float* __restrict__ G, int64_t g_ld, int64_t g_col0, float lr,
+    uint32_t* __restrict__ next) {
+  __shared__ __attribute__((aligned(16))) HotLds sm;
+  // counters: [0] segments, [1] hot segments; next: [0] hot item, [1] short-segment chunk
+  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, &counters[1], G, g_ld, g_col0, lr, &next[0]);
+  light_phase<V, 16 / V>(tables, d, g_log2, row_bits, seg_key, bags, seg_start, &counters[0], G, g_ld, g_col0, lr,
+                         &next[1]);
+}
+
 int bits_for(int64_t x) {  // bits needed to hold 0..x
   int b = 0;
   while (b < 63 && (x >> b) != 0) ++b;
@@ -662,23 +703,6 @@ void sparse_layout(int64_t nnz, SparseLayout* L) {
   L->hot = take(4 * (size_t)(n / kHot + 1));
   L->hot_ordered = take(4 * (size_t)(n / kHot + 1));
   L->bytes = cv.bytes();
-}
-
-// A second stream per device (default priority) for the short segments,
-// which run beside the hot-segment kernel: that kernel's critical path is a
-// few serial chains on a few CUs while the rest of the chip would idle.
-hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev]) {
-    hipStream_t s = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    streams[dev] = s;
-  }
-  return streams[dev];
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
@@ -813,7 +837,7 @@ extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const
 
 extern "C" int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_t d, const int64_t* rows, int64_t B,
                                          int64_t nnz, const float* G, int64_t g_ld, int64_t g_col0, float lr, void* ws,
-                                         size_t ws_bytes, hipStream_t stream) {
+                                         size_t ws_bytes, hipStream_t stream, hipStream_t side) {
   if (!tables || !G) return DLRM_E_INVALID;
   if (d < 4 || d > 1024 || (d % 4) != 0) return DLRM_E_INVALID;
   if (g_col0 < 0 || g_ld < g_col0 + (int64_t)K * d || (g_ld % 4) != 0 || (g_col0 % 4) != 0 || !aligned16(G))
@@ -827,29 +851,17 @@ extern "C" int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_
   if ((rc = sparse_bufs(nnz, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
   const int cur = sort_passes(row_bits, table_bits) & 1;
   // the work counters start from zero on every call, so one prepared
-  // workspace can be applied more than once
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters + 2, 2);
-  if (launch_status() != DLRM_OK) return DLRM_E_HIP;
-  // per-segment sums and the in-place update: the long segments on `stream`,
-  // the short ones (disjoint rows) on the side stream at the same time, joined
-  // back into `stream` before returning
-  hipStream_t side = side_stream();
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (!side || hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return DLRM_E_HIP;
-  if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
-    (void)hipEventDestroy(fork);
-    return DLRM_E_HIP;
+  // workspace can be applied more than once; each stream clears the counter
+  // its own kernel takes work from
+  if (side) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters + 2, 1);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, side, b.counters + 3, 1);
+  } else {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters + 2, 2);
   }
-  if (hipEventRecord(fork, stream) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess) rc = DLRM_E_HIP;
-  if (rc == DLRM_OK)
-    rc = sgd_segments(tables, d, row_bits, b.seg_key, b.vals[cur], b.seg, b.hot_ordered, b.counters, G, g_ld, g_col0,
+  if (launch_status() != DLRM_OK) return DLRM_E_HIP;
+  return sgd_segments(tables, d, row_bits, b.seg_key, b.vals[cur], b.seg, b.hot_ordered, b.counters, G, g_ld, g_col0,
                       lr, stream, side);
-  // the join is recorded even after a failed launch, so `stream` never
-  // waits on an event that was not recorded
-  if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(stream, join, 0) != hipSuccess) rc = DLRM_E_HIP;
-  (void)hipEventDestroy(fork);
-  (void)hipEventDestroy(join);
-  return rc;
 }
 
 extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_t* rows,
@@ -863,7 +875,7 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
     return DLRM_E_INVALID;
   const int rc = dlrm_embbag_bwd_sgd_prepare(K, rows, indices, offsets, B, nnz, ws, ws_bytes, stream);
   if (rc != DLRM_OK) return rc;
-  return dlrm_embbag_bwd_sgd_apply(tables, K, d, rows, B, nnz, G, g_ld, g_col0, lr, ws, ws_bytes, stream);
+  return dlrm_embbag_bwd_sgd_apply(tables, K, d, rows, B, nnz, G, g_ld, g_col0, lr, ws, ws_bytes, stream, nullptr);
 }
 
 namespace dlrm {
@@ -871,9 +883,6 @@ namespace {
 int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_key, const int32_t* vals,
                  const int32_t* seg, const int32_t* hot_ordered, uint32_t* counters, const float* G, int64_t g_ld,
                  int64_t g_col0, float lr, hipStream_t stream, hipStream_t side) {
-  hipLaunchKernelGGL(hot_sgd_kernel, dim3(kHotBlocks), dim3(64 * (kLoaders + 1)), 0, stream, tables, d, row_bits, seg_key,
-                     vals, seg, hot_ordered, &counters[1], G, g_ld, g_col0, lr, &counters[2]);
-  if (launch_status() != DLRM_OK) return DLRM_E_HIP;
   // short segments: half as many lanes as float4 columns (two float4 per
   // lane), at most 64
   const int d4 = d / 4;
@@ -881,16 +890,29 @@ int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_
   while ((1 << l2) < d4) ++l2;
   const int g_log2 = l2 > 0 ? (l2 - 1 < 6 ? l2 - 1 : 6) : 0;
   const int V = (d4 + (1 << g_log2) - 1) >> g_log2;
-  const dim3 grid(kLightBlocks), block(256);
-  if (V == 1)
-    hipLaunchKernelGGL((light_sgd_kernel<1>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg,
-                       &counters[0], G, g_ld, g_col0, lr, &counters[3]);
-  else if (V == 2)
-    hipLaunchKernelGGL((light_sgd_kernel<2>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg,
-                       &counters[0], G, g_ld, g_col0, lr, &counters[3]);
-  else
-    hipLaunchKernelGGL((light_sgd_kernel<4>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg,
-                       &counters[0], G, g_ld, g_col0, lr, &counters[3]);
+  const dim3 cus((unsigned)device_cu_count()), apply_block(kApplyThreads);
+  if (side) {
+    // long segments on `stream`, short ones on `side` at the same time
+    hipLaunchKernelGGL(hot_sgd_kernel, cus, apply_block, 0, stream, tables, d, row_bits, seg_key, vals, seg,
+                       hot_ordered, counters + 1, G, g_ld, g_col0, lr, counters + 2);
+    if (launch_status() != DLRM_OK) return DLRM_E_HIP;
+    const dim3 grid(kLightBlocks), block(256);
+#define DLRM_LIGHT(VV)                                                                                            \
+  hipLaunchKernelGGL((light_sgd_kernel<VV>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg, \
+                     counters, G, g_ld, g_col0, lr, counters + 3)
+    if (V == 1) DLRM_LIGHT(1);
+    else if (V == 2) DLRM_LIGHT(2);
+    else DLRM_LIGHT(4);
+#undef DLRM_LIGHT
+    return launch_status();
+  }
+#define DLRM_APPLY(VV)                                                                                          \
+  hipLaunchKernelGGL((sgd_apply_kernel<VV>), cus, apply_block, 0, stream, tables, d, g_log2, row_bits, seg_key, \
+                     vals, seg, hot_ordered, counters, G, g_ld, g_col0, lr, counters + 2)
+  if (V == 1) DLRM_APPLY(1);
+  else if (V == 2) DLRM_APPLY(2);
+  else DLRM_APPLY(4);
+#undef DLRM_APPLY
   return launch_status();
 }
 }  // namespace

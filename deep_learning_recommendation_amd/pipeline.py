@@ -83,11 +83,12 @@ class DLRM:
     """Device state and call sequence for one batch size."""
 
     def __init__(self, B: int, K: int, d: int, rows, tables, bottom: MLPParams, top: MLPParams, train: bool = False,
-                 device="cuda", fused="auto", table_dtype: str = "f32", scale_bias=None):
+                 device="cuda", fused="auto", table_dtype: str = "f32", scale_bias=None, pad_top: bool = True):
         """table_dtype "f32", or "bf16" / "int8" rows (forward only) with, for
         int8, ``scale_bias`` = K fp32 [m_k][2] tensors.  A forward-only model
-        may widen the top MLP's first layer with zero columns (see
-        ``pad_first_layer``); ``self.top`` holds the layers the calls use."""
+        widens the top MLP's first layer with zero columns unless ``pad_top``
+        is False (see ``pad_first_layer``); ``self.top`` holds the layers the
+        calls use."""
         self.B, self.K, self.d, self.n = B, K, d, K + 1
         self.rows = [int(r) for r in rows]
         self.tables = tables
@@ -118,13 +119,16 @@ class DLRM:
             self.x0_ld = n * d
         top_dtype = torch.bfloat16 if top.w_dtype == C.DLRM_BF16 else torch.float32
         self.top_ld = _round_up(self.top_w, 8) if top_dtype == torch.bfloat16 else _round_up(self.top_w, 4)
-        if not train and top_dtype == torch.bfloat16 and self.top_w >= 256 and self.top_w % 64 != 0:
+        if pad_top and not train and top_dtype == torch.bfloat16 and self.top_w >= 256 and self.top_w % 64 != 0:
             # forward only: the top MLP reads the interaction rows as K =
-            # top_w rounded up to 64 (zero columns, never written after
-            # the zero fill below), e.g. 512 for 479 (measured faster)
+            # top_w rounded up to 64 (zero columns), e.g. 512 for 479
+            # (measured faster)
             self.top_ld = _round_up(self.top_w, 64)
             self.top = top = pad_first_layer(top, self.top_ld)
-        # zero-filled: columns past the interaction kernels' padding stay zero
+        # zero-filled once: the interaction calls write columns below
+        # round_up(top_w, 8) only (zeros from top_w on), so the columns up to
+        # top_ld stay zero and meet zero weight columns
+        self.top_written = min(_round_up(self.top_w, 8), self.top_ld)
         self.top_in = torch.zeros((B, self.top_ld), dtype=top_dtype, device=dev)
         self.logit = torch.empty((B, 1), dtype=torch.float32, device=dev)
         self.prob = torch.empty((B,), dtype=torch.float32, device=dev)
@@ -199,26 +203,35 @@ class DLRM:
         C.dlrm_embbag_bwd_sgd_prepare(self.K, self.rows, indices, offsets, self.B, nnz, self.sparse_workspace(nnz),
                                       stream)
 
-    def _sparse_update(self, G, indices, offsets, nnz, lr, prepared, stream):
+    def _sparse_update(self, G, indices, offsets, nnz, lr, prepared, stream, side=None):
         B, n, d = self.B, self.n, self.d
         if prepared:
             C.dlrm_embbag_bwd_sgd_apply(self.table_ptrs, self.K, d, self.rows, B, nnz, G, n * d, d, lr,
-                                        self.sparse_workspace(nnz), stream)
+                                        self.sparse_workspace(nnz), stream, side)
         else:
             C.dlrm_embbag_bwd_sgd(self.table_ptrs, self.K, d, self.rows, indices, offsets, B, nnz, G, n * d, d, lr,
                                   self.sparse_workspace(nnz), stream)
 
-    def backward(self, labels, G, indices, offsets, nnz: int, lr: float, stream=None, prepared: bool = False):
+    def backward(self, labels, G, indices, offsets, nnz: int, lr: float, stream=None, prepared: bool = False,
+                 side=None):
         """Dense gradients (top: from the BCE loss; bottom: from G[:, 0, :]) and
         the sparse SGD update of the tables from G[:, 1..K, :] (from a
-        ``sparse_prepare`` of this batch when ``prepared``)."""
+        ``sparse_prepare`` of this batch when ``prepared``; then ``side``, a
+        second torch stream, may take the update's short segments, forked
+        from and joined back into the update's stream here)."""
         B, n, d = self.B, self.n, self.d
         C.dlrm_bce_grad(self.logit, 1, labels, B, self.dlogit, stream)
         C.dlrm_mlp_bwd(B, self.top.dims, self.top.Ws, self.top.w_ld, C.DLRM_ACT_NONE, self.ws_top, self.logit, 1,
                        self.dlogit, 1, self.dW_top, self.db_top, None, 0, self.ws_top_bwd, stream)
         C.dlrm_mlp_bwd(B, self.bottom.dims, self.bottom.Ws, self.bottom.w_ld, C.DLRM_ACT_RELU, self.ws_bot, self.x0,
                        self.x0_ld, G, n * d, self.dW_bot, self.db_bot, None, 0, self.ws_bot_bwd, stream)
-        self._sparse_update(G, indices, offsets, nnz, lr, prepared, stream)
+        if prepared and side is not None:
+            cur = stream if stream is not None else torch.cuda.current_stream()
+            side.wait_stream(cur)
+            self._sparse_update(G, indices, offsets, nnz, lr, prepared, stream, side)
+            cur.wait_stream(side)
+        else:
+            self._sparse_update(G, indices, offsets, nnz, lr, prepared, stream)
 
     def backward_chain(self, labels, indices, offsets, nnz: int, lr: float, stream=None, prepared: bool = False):
         """The whole training backward from the loss: BCE seed, top MLP (with

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define DLRM_ABI_VERSION 3
+#define DLRM_ABI_VERSION 4
 
 enum {
   DLRM_OK = 0,
@@ -92,9 +92,10 @@ int dlrm_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const int6
 /*
  * Embedding lookup with sum pooling from low-precision table rows.
  * Quantised tables are what a bandwidth-bound recommendation model gains
- * from (the explainer's citations in Evaluation & Benchmarks: a survey of
- * quantisation notes it pays where the problem is bandwidth-bound, as in
- * recommendation systems).  Each value read is first turned into fp32, then
+ * from ([ML1] "Deep Learning Recommendation Model for Personalization and
+ * Recommendation Systems", mlsanity summary, Citations in the corpus: a
+ * survey of quantisation methods cites the model as a bandwidth-bound
+ * problem where quantisation pays).  Each value read is first turned into fp32, then
  * pooled exactly as dlrm_embbag_fwd (fp32, bag order, from +0.0):
  *   DLRM_BF16  T_k is bf16 [m_k][d] (2 bytes per value): widened exactly.
  *   DLRM_I8    T_k is int8 [m_k][d] (1 byte per value) and scale_bias[k] is
@@ -124,7 +125,13 @@ int dlrm_embbag_fwd_lp(const void* const* tables, int32_t table_dtype, const flo
  *            out[d + i(i-1)/2 + j] = sum_c X_b[i][c] X_b[j][c] for j < i < n.
  *            out_ld >= d + n(n-1)/2.  Columns beyond that (up to out_ld) are
  *            written with zeros up to the next multiple of 8.
- *   Accuracy: fp32 products, fp32 accumulation (|err| <= d u sum|x_i x_j|).
+ *   Accuracy: every fp32 value is split exactly into three bf16 parts
+ *            (x = h + m + l) and the six products hh, hm, mh, hl, mm, lh are
+ *            summed in fp32 by bf16 MFMAs; the dropped terms (ml, lm, ll)
+ *            are below 2^-20 |x_ic x_jc| each, so
+ *            |err| <= (2^-20 d + 2^-24 (d + 24)) sum_c |x_ic x_jc|, below
+ *            1e-5 sum_c |x_ic x_jc| for d <= 256.  Small integers (and other
+ *            values with at most 8 significant bits) give exact results.
  *   Limits:  2 <= n <= 128, d % 4 == 0, 4 <= d <= 256.
  */
 int dlrm_interact_fwd(const float* X, int64_t B, int32_t n, int32_t d, int64_t x_ld, void* out,
@@ -224,6 +231,27 @@ int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int64_t B, int
                  int32_t save_acts, hipStream_t stream);
 
 /*
+ * One fully connected bf16 layer, the building block of the bf16 MLPs above
+ * (dlrm_mlp_fwd runs each of its bf16 layers with the same kernels):
+ *     C = act(A W^T + b)
+ * ([EXPL] Key Method Details, "Bottom MLP" / "Top MLP": FC layers with ReLU.)
+ *   A        bf16 [M][lda] (lda >= K), the layer input.
+ *   W        bf16 [N][ldw] (ldw >= K), one K-contiguous row per output.
+ *   bias     nullable fp32 [N] (NULL: zero).
+ *   C        out_dtype DLRM_F32 or DLRM_BF16 (bf16: rounded to nearest
+ *            even after bias and activation), [M][ldc], ldc >= N.
+ *   act      DLRM_ACT_NONE or DLRM_ACT_RELU.
+ *   Products of bf16 values are exact; they are summed in fp32 (MFMA),
+ *   starting from the bias.  N == 1 takes a dot-product kernel (fp32 output
+ *   only; DLRM_E_INVALID for bf16) that adds the bias last.  16-byte aligned A and W with lda, ldw
+ *   multiples of 8 take the fast MFMA kernel, anything else a generic one.
+ *   Limits: M >= 1, N >= 1, K >= 1, M, N, K < 2^31.
+ */
+int dlrm_linear_fwd(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias, void* C,
+                    int32_t out_dtype, int64_t ldc, int64_t M, int32_t N, int32_t K, int32_t act,
+                    hipStream_t stream);
+
+/*
  * Multilayer perceptron, backward (bf16 networks).
  * Training minimises binary cross-entropy ([EXPL] Key Method Details,
  * "Loss"); the caller passes dY = dLoss/d(out) (for BCE on the logit,
@@ -298,13 +326,21 @@ int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_
  *   bit that of dlrm_embbag_bwd_sgd; the workspace stays prepared, so
  *   applying it again updates the same rows again (a second SGD step with
  *   the same indices).
+ *   side (nullable): a second stream of the caller.  NULL: everything runs
+ *   on `stream` in one launch.  Otherwise the long segments (Zipf heads,
+ *   whose serial sums occupy a few CUs for the whole call) run on `stream`
+ *   and the short ones on `side` at the same time; the two touch disjoint
+ *   rows.  The caller orders `side` after everything the call depends on
+ *   (e.g. hipStreamWaitEvent(side, e) on an event e recorded on `stream`
+ *   just before the call) and its later work after both streams (the same
+ *   in reverse).  The library creates no stream and no event.
  * Same arguments, limits and error codes as dlrm_embbag_bwd_sgd.
  */
 int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const int64_t* indices, const int64_t* offsets,
                                 int64_t B, int64_t nnz, void* ws, size_t ws_bytes, hipStream_t stream);
 int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_t d, const int64_t* rows, int64_t B, int64_t nnz,
                               const float* G, int64_t g_ld, int64_t g_col0, float lr, void* ws, size_t ws_bytes,
-                              hipStream_t stream);
+                              hipStream_t stream, hipStream_t side);
 
 /*
  * Validate indices and offsets on the device.  rows_dev: device int64 [K].

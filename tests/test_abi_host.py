@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_strings(lib):
-    assert C.dlrm_abi_version() == 3
+    assert C.dlrm_abi_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert lib.dlrm_strerror(code)
     assert lib.dlrm_last_hip_error() == 0
@@ -135,12 +135,39 @@ def test_sparse_prepare_apply_checks(lib):
     assert prep(8, big, FAKE, FAKE, 8192, 100, ctypes.c_void_p(0x100000), 1 << 30, NULL) == C.DLRM_E_UNSUPPORTED
     assert prep(8, rows, FAKE, FAKE, 8192, 0, None, 0, NULL) == C.DLRM_OK  # nothing to sort
     assert apply(FAKE, 8, 128, rows, 8192, 6553600, FAKE, 9 * 128, 128, lr, ctypes.c_void_p(0x100000), 256,
-                 NULL) == C.DLRM_E_WORKSPACE
+                 NULL, NULL) == C.DLRM_E_WORKSPACE
     assert apply(NULL, 8, 128, rows, 8192, 100, FAKE, 9 * 128, 128, lr, ctypes.c_void_p(0x100000), 1 << 30,
-                 NULL) == C.DLRM_E_INVALID
+                 NULL, NULL) == C.DLRM_E_INVALID
     assert apply(FAKE, 8, 128, rows, 8192, 100, FAKE, 9 * 128 - 4, 128, lr, ctypes.c_void_p(0x100000), 1 << 30,
-                 NULL) == C.DLRM_E_INVALID
+                 NULL, NULL) == C.DLRM_E_INVALID
     assert apply(FAKE, 8, 130, rows, 8192, 100, FAKE, 9 * 130, 130, lr, ctypes.c_void_p(0x100000), 1 << 30,
-                 NULL) == C.DLRM_E_INVALID
+                 NULL, NULL) == C.DLRM_E_INVALID
     assert apply(FAKE, 8, 128, big, 8192, 100, FAKE, 9 * 128, 128, lr, ctypes.c_void_p(0x100000), 1 << 30,
-                 NULL) == C.DLRM_E_UNSUPPORTED
+                 NULL, NULL) == C.DLRM_E_UNSUPPORTED
+
+
+def test_linear_argument_checks(lib):
+    f = lib.dlrm_linear_fwd
+    act = C.DLRM_ACT_RELU
+    assert f(NULL, 64, FAKE, 64, NULL, FAKE, C.DLRM_BF16, 128, 100, 128, 64, act, NULL) == C.DLRM_E_INVALID
+    assert f(FAKE, 63, FAKE, 64, NULL, FAKE, C.DLRM_BF16, 128, 100, 128, 64, act, NULL) == C.DLRM_E_INVALID  # lda < K
+    assert f(FAKE, 64, FAKE, 64, NULL, FAKE, C.DLRM_BF16, 127, 100, 128, 64, act, NULL) == C.DLRM_E_INVALID  # ldc < N
+    assert f(FAKE, 64, FAKE, 64, NULL, FAKE, 7, 128, 100, 128, 64, act, NULL) == C.DLRM_E_INVALID            # dtype
+    assert f(FAKE, 64, FAKE, 64, NULL, FAKE, C.DLRM_BF16, 128, 100, 128, 64, 5, NULL) == C.DLRM_E_INVALID    # act
+    assert f(FAKE, 64, FAKE, 64, NULL, FAKE, C.DLRM_BF16, 1, 100, 1, 64, act, NULL) == C.DLRM_E_INVALID      # N=1 bf16
+    assert f(FAKE, 64, FAKE, 64, NULL, FAKE, C.DLRM_F32, 128, 0, 128, 64, act, NULL) == C.DLRM_E_INVALID     # M = 0
+
+
+def test_library_creates_no_streams_or_events():
+    """The library enqueues on the caller's stream only: no source creates a
+    stream or an event, or synchronises the device."""
+    import glob
+    import re
+
+    srcs = glob.glob(os.path.join(os.path.dirname(C.LIB_PATH), "csrc", "*"))
+    assert srcs
+    pat = re.compile(r"hip(StreamCreate\w*|EventCreate\w*|DeviceSynchronize|StreamSynchronize|Malloc\w*|Free)\s*\(")
+    for p in srcs:
+        with open(p) as f:
+            text = f.read()
+        assert not pat.search(text), (p, pat.search(text).group(0))

@@ -133,16 +133,32 @@ def test_sparse_sgd_train_scaled():
         assert np.array_equal(bits(got), bits(tabs[k]))
 
 
-def test_sparse_sgd_train_full_size():
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_sparse_sgd_train_full_size(two_streams):
     """The training workload at full size (8 x 5e7 x 128 tables, 6.5M
     lookups with Zipf(1.2) hot rows): every touched row bit-exact, 1e5
-    random untouched rows unchanged."""
+    random untouched rows unchanged.  two_streams: prepare, then apply with
+    the short segments on a second stream."""
+    import deep_learning_recommendation_amd as D
+
     w = W.get("train")
-    banner(f"sparse sgd train full size: {w.K} x {w.rows[0]} x {w.d}")
+    banner(f"sparse sgd train full size: {w.K} x {w.rows[0]} x {w.d} two_streams={two_streams}")
     idx, off = W.indices_offsets(w)
     tabs_dev = SD.make_tables(w)
     G = W.upstream_grad(w).reshape(w.B, -1)
-    _run_sgd(tabs_dev, w.rows, idx, off, w.B, w.d, G, w.d, w.lr)
+    if two_streams:
+        nnz = int(off[-1])
+        ws = torch.empty((D.dlrm_embbag_bwd_sgd_workspace_size(w.K, w.B, nnz, w.d),), dtype=torch.uint8, device=DEV)
+        ptrs = D.device_pointer_array(tabs_dev)
+        idx_d, off_d, G_d = to_dev(idx), to_dev(off), to_dev(G)
+        D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx_d, off_d, w.B, nnz, ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        D.dlrm_embbag_bwd_sgd_apply(ptrs, w.K, w.d, w.rows, w.B, nnz, G_d, G.shape[1], w.d, w.lr, ws, side=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+    else:
+        _run_sgd(tabs_dev, w.rows, idx, off, w.B, w.d, G, w.d, w.lr)
     tabs, local, row_ids = W.compact_rows(w, idx, off)
     oracle.embbag_bwd_sgd(tabs, local, off, w.B, G, w.d, w.lr)
     g = np.random.default_rng(5)
@@ -156,11 +172,14 @@ def test_sparse_sgd_train_full_size():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("two_streams", [False, True])
 @pytest.mark.parametrize("d,K", [(128, 4), (64, 2), (132, 3)])
-def test_sparse_prepare_apply_two_calls(d, K):
+def test_sparse_prepare_apply_two_calls(d, K, two_streams):
     """dlrm_embbag_bwd_sgd_prepare on a second stream (beside unrelated work
     on the first), then dlrm_embbag_bwd_sgd_apply twice from the same
-    prepared workspace: two SGD steps, each bit-exact against the oracle."""
+    prepared workspace: two SGD steps, each bit-exact against the oracle.
+    two_streams: the apply's short segments run on a second stream of the
+    caller (forked from and joined back into the first)."""
     import deep_learning_recommendation_amd as D
 
     B = 733
@@ -191,8 +210,14 @@ def test_sparse_prepare_apply_two_calls(d, K):
     busy.fill_(1.0)  # unrelated work on the first stream meanwhile
     torch.cuda.current_stream().wait_stream(side)
     ref = [t.copy() for t in tabs]
+    cur = torch.cuda.current_stream()
     for step in range(2):
-        D.dlrm_embbag_bwd_sgd_apply(ptrs, K, d, rows, B, nnz, G_d, G.shape[1], d, 0.01, ws)
+        if two_streams:
+            side.wait_stream(cur)
+            D.dlrm_embbag_bwd_sgd_apply(ptrs, K, d, rows, B, nnz, G_d, G.shape[1], d, 0.01, ws, side=side)
+            cur.wait_stream(side)
+        else:
+            D.dlrm_embbag_bwd_sgd_apply(ptrs, K, d, rows, B, nnz, G_d, G.shape[1], d, 0.01, ws)
         torch.cuda.synchronize()
         oracle.embbag_bwd_sgd(ref, idx, off, B, G, d, 0.01)
         for k in range(K):
