@@ -11,13 +11,18 @@ top MLP with sigmoid); inputs are resident in HBM before timing starts.
 Prints one JSON line: samples/s, the roofline of the dominant kernel (the
 fused pooled lookup + interaction kernel, or the gather alone in the
 gather microbench: algorithmic bytes per launch over its average launch
-time, measured with HIP events on its stream), and the CPU oracle timed on
-a bounded sample (about 10 s) of the same workload.  An event record costs a
-few microseconds of GPU time, so the timed steps carry only the two events
-around the dominant kernel; the per-call breakdown (medians) comes from a
-short untimed pass after the timed region.  The defaults time 500 steps after 100 warm-up
-steps: far shorter runs report the clock's ramp as well (about 8% lower at
-20 steps of the forward workload).
+time, measured with HIP events on its stream), the matrix-core fraction of
+every MLP layer (algorithmic 2*M*N*K flops over its HIP-event time over the
+2.5 PFLOP/s bf16 peak), and the CPU oracle timed on a bounded sample (about
+10 s) of the same workload, with all threads and with one.
+
+An event record costs a few microseconds of GPU time, so the timed steps
+carry only the two events around the dominant kernel.  The per-call
+breakdown (medians; the forward top MLP layer by layer through
+dlrm_linear_fwd, the same kernels dlrm_mlp_fwd launches) comes from an
+untimed pass of at least --breakdown-seconds that runs before the warm-up
+and timed steps; it also brings the GPU to its steady clock, which a few
+warm-up steps alone do not (20 steps from a cold start read about 10% low).
 """
 from __future__ import annotations
 
@@ -76,8 +81,10 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--breakdown-steps", type=int, default=20,
-                   help="untimed steps after the timed region with every call bracketed by events (the per-call "
-                        "breakdown; the timed steps carry only the dominant kernel's pair of events)")
+                   help="least number of untimed steps before the warm-up with every call bracketed by events (the "
+                        "per-call breakdown; the timed steps carry only the dominant kernel's pair of events)")
+    p.add_argument("--breakdown-seconds", type=float, default=1.0,
+                   help="the breakdown pass runs at least this long (0 with --breakdown-steps 0 skips it)")
     p.add_argument("--workload", default="forward", choices=["forward", "embbag", "interaction", "train", "tiny"])
     p.add_argument("--batches", type=int, default=2, help="distinct input batches rotated over the steps")
     p.add_argument("--uniform", action="store_true", help="uniform indices instead of Zipf (control run)")
@@ -193,6 +200,30 @@ def cpu_baseline(w, batches, bottom, top, n_samples, chain=False, min_seconds=10
     return S * passes, dt, oracle.num_threads(), passes
 
 
+def cpu_baseline_single(w, batches, bottom, top, n_samples, chain=False, min_seconds=4.0, table_dtype="f32"):
+    """The same oracle pass with one thread on a smaller sample."""
+    import oracle
+
+    threads = oracle.num_threads()
+    oracle.set_threads(1)
+    try:
+        return cpu_baseline(w, batches, bottom, top, n_samples, chain=chain, min_seconds=min_seconds,
+                            table_dtype=table_dtype)
+    finally:
+        oracle.set_threads(threads)
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def mlp_layer_flops(B, dims):
+    return [2.0 * B * i * o for i, o in zip(dims[:-1], dims[1:])]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -268,10 +299,16 @@ def main():
     t_setup = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream()
-    # training: the index half of the sparse update (keys, sort, segments)
-    # runs on a second stream, forked after the lookup, beside the rest of
-    # the forward and the dense backward; the update waits for it
+    # training: the sparse update runs on a second stream, forked after the
+    # lookup (it reads only the indices, the synthetic gradient and the
+    # tables the lookup has finished reading): the index half (keys, sort,
+    # segments), then the sums and the update, whose short segments take a
+    # third stream; the interaction, top MLP and dense backward run on the
+    # first stream meanwhile, and the step ends when all three are done.
+    # (The per-call breakdown runs the calls one after another on the first
+    # stream instead, so that each interval holds one call.)
     prep_stream = torch.cuda.Stream() if w.train else None
+    light_stream = torch.cuda.Stream() if w.train else None
     gather_t = Timer()
     call_t = {}   # per-call event pairs of the breakdown steps
     dom_t = {}    # the dominant kernel's event pairs over the timed steps
@@ -294,6 +331,7 @@ def main():
             return
         n, d = model.n, model.d
         ev = {}
+        overlap = w.train and mode != "breakdown"
 
         def mark(name):
             # timed steps: the dominant kernel's mark and the next one (its end)
@@ -307,8 +345,19 @@ def main():
             with torch.cuda.stream(prep_stream):
                 D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx, off, w.B, nnz, model.ws_sparse)
 
+        def sparse_apply(Gs, on_side):
+            """The sums and the update: long segments on the stream that ran
+            the prepare (or the first one), short ones on the third stream."""
+            s0 = prep_stream if on_side else stream
+            if not on_side:
+                stream.wait_stream(prep_stream)
+            light_stream.wait_stream(s0)
+            D.dlrm_embbag_bwd_sgd_apply(model.table_ptrs, w.K, d, w.rows, w.B, nnz, Gs, n * d, d, w.lr,
+                                        model.ws_sparse, stream=s0, side=light_stream)
+            s0.wait_stream(light_stream)
+
         if args.chain:
-            return chain_step(model, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare)
+            return chain_step(model, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare, sparse_apply, overlap)
         mark("bottom_mlp")
         D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
                        model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.x0, model.x0_ld, None,
@@ -334,11 +383,16 @@ def main():
                 fork_prepare()
             mark("interact")
             D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
-        mark("top_mlp")
-        D.dlrm_mlp_fwd(model.top_in, model.top_ld, w.B, model.top.dims, model.top.Ws, model.top.w_ld,
-                       model.top.biases, model.top.w_dtype, D.DLRM_ACT_NONE, model.logit, 1, model.prob,
-                       model.ws_top, w.train)
+        if mode == "breakdown" and not w.train and bf16:
+            top_layers(model, mark)
+        else:
+            mark("top_mlp")
+            D.dlrm_mlp_fwd(model.top_in, model.top_ld, w.B, model.top.dims, model.top.Ws, model.top.w_ld,
+                           model.top.biases, model.top.w_dtype, D.DLRM_ACT_NONE, model.logit, 1, model.prob,
+                           model.ws_top, w.train)
         if w.train:
+            if overlap:
+                sparse_apply(G, True)  # needs only the prepared segments and G
             mark("dense_bwd")
             D.dlrm_bce_grad(model.logit, 1, y, w.B, model.dlogit)
             D.dlrm_mlp_bwd(w.B, model.top.dims, model.top.Ws, model.top.w_ld, D.DLRM_ACT_NONE, model.ws_top,
@@ -346,12 +400,32 @@ def main():
             D.dlrm_mlp_bwd(w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld, D.DLRM_ACT_RELU,
                            model.ws_bot, model.x0, model.x0_ld, G, n * d, model.dW_bot, model.db_bot, None, 0,
                            model.ws_bot_bwd)
-            mark("sparse_bwd_sgd")
-            stream.wait_stream(prep_stream)
-            D.dlrm_embbag_bwd_sgd_apply(model.table_ptrs, w.K, d, w.rows, w.B, nnz, G, n * d, d, w.lr,
-                                        model.ws_sparse)
+            if not overlap:
+                mark("sparse_bwd_sgd")
+                sparse_apply(G, False)
+            else:
+                stream.wait_stream(prep_stream)
         mark("end")
         record(ev, mode)
+
+    layer_bufs = {}
+
+    def top_layers(m, mark):
+        """The forward top MLP one layer at a time (dlrm_linear_fwd: the
+        kernels dlrm_mlp_fwd launches for it), each layer between two marks."""
+        dims = m.top.dims
+        if not layer_bufs:
+            for l in range(1, len(dims) - 1):
+                ld = (dims[l] + 7) // 8 * 8
+                layer_bufs[l] = (torch.empty((w.B, ld), dtype=torch.bfloat16, device=dev), ld)
+        src, ld_src = m.top_in, m.top_ld
+        for l in range(len(dims) - 1):
+            mark(f"top_l{l}")
+            last = l == len(dims) - 2
+            dst, ld_dst = (m.logit, 1) if last else layer_bufs[l + 1]
+            D.dlrm_linear_fwd(src, ld_src, m.top.Ws[l], m.top.w_ld[l], m.top.biases[l], dst, ld_dst, w.B,
+                              dims[l + 1], dims[l], D.DLRM_ACT_NONE if last else D.DLRM_ACT_RELU)
+            src, ld_src = dst, ld_dst
 
     def record(ev, mode):
         if mode is not None:
@@ -359,8 +433,10 @@ def main():
             for a, b in zip(names[:-1], names[1:]):
                 (call_t if mode == "breakdown" else dom_t).setdefault(a, []).append((ev[a], ev[b]))
 
-    def chain_step(m, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare):
-        """Forward with X materialised, then the backward from the loss."""
+    def chain_step(m, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare, sparse_apply, overlap):
+        """Forward with X materialised, then the backward from the loss (the
+        sparse update, once the X gradient exists, beside the bottom MLP's
+        backward)."""
         n, d, B = m.n, m.d, w.B
         mark("bottom_mlp")
         D.dlrm_mlp_fwd(dense, dense.shape[1], B, m.bottom.dims, m.bottom.Ws, m.bottom.w_ld, m.bottom.biases,
@@ -379,15 +455,33 @@ def main():
                        m.dW_top, m.db_top, m.g_top, m.top_w, m.ws_top_bwd)
         mark("interact_bwd")
         D.dlrm_interact_bwd(m.X, B, n, d, n * d, m.g_top, m.top_w, m.G, n * d)
+        if overlap:
+            prep_stream.wait_stream(stream)  # the X gradient
+            sparse_apply(m.G, True)
         mark("bottom_bwd")
         D.dlrm_mlp_bwd(B, m.bottom.dims, m.bottom.Ws, m.bottom.w_ld, D.DLRM_ACT_RELU, m.ws_bot, m.x0, m.x0_ld,
                        m.G, n * d, m.dW_bot, m.db_bot, None, 0, m.ws_bot_bwd)
-        mark("sparse_bwd_sgd")
-        stream.wait_stream(prep_stream)
-        D.dlrm_embbag_bwd_sgd_apply(m.table_ptrs, w.K, d, w.rows, B, nnz, m.G, n * d, d, w.lr, m.ws_sparse)
+        if overlap:
+            stream.wait_stream(prep_stream)
+        else:
+            mark("sparse_bwd_sgd")
+            sparse_apply(m.G, False)
         mark("end")
         record(ev, mode)
 
+    breakdown_done = 0
+    if model is not None and args.breakdown_steps > 0:
+        # the per-call breakdown pass (untimed): two plain steps first, so
+        # the host is ahead of the GPU when the first bracketed call starts
+        for i in range(2):
+            step(i, None)
+        tb = time.perf_counter()
+        while breakdown_done < args.breakdown_steps or time.perf_counter() - tb < args.breakdown_seconds:
+            step(2 + breakdown_done, "breakdown")
+            breakdown_done += 1
+            if breakdown_done % 50 == 0:
+                torch.cuda.synchronize()  # keep the host within 50 steps of the GPU
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i, None)
     torch.cuda.synchronize()
@@ -396,14 +490,6 @@ def main():
         step(i, "timed")
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    if model is not None and args.breakdown_steps > 0:
-        # two untimed steps first, so the host is ahead of the GPU again when
-        # the first bracketed call starts (else its interval holds host time)
-        for i in range(2):
-            step(args.steps + i, None)
-        for i in range(args.breakdown_steps):
-            step(args.steps + 2 + i, "breakdown")
-        torch.cuda.synchronize()
 
     ms_per_step = 1e3 * elapsed / args.steps
     value = w.B * args.steps / elapsed
@@ -430,12 +516,46 @@ def main():
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(gbytes), "avg_launch_ms": round(g_ms, 4)}
+    if traffic is not None:
+        # the bytes HBM really moved (Zipf rows repeat and hit in cache)
+        roofline["hbm_measured_GBs"] = round(traffic / (g_ms * 1e-3) / 1e9, 1)
+        roofline["hbm_measured_frac"] = round(traffic / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    # matrix cores: algorithmic MLP flops over the HIP-event time of the calls
+    mfma = None
+    if model is not None and w.mlp_dtype == "bf16":
+        def frac(flops, ms):
+            tf = flops / (ms * 1e-3) / 1e12
+            return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        mfma = {"peak_tflops": BF16_PEAK_TFLOPS}
+        bflops = mlp_layer_flops(w.B, w.bottom)
+        if "bottom_mlp" in breakdown:
+            mfma["bottom_mlp"] = dict(frac(sum(bflops), breakdown["bottom_mlp"]), dims="-".join(map(str, w.bottom)))
+        tdims = model.top.dims
+        tflops = mlp_layer_flops(w.B, w.top)  # the model's own widths (a padded first layer's zero columns excluded)
+        layers = []
+        for l in range(len(tdims) - 1):
+            if f"top_l{l}" in breakdown:
+                layers.append(dict(frac(tflops[l], breakdown[f"top_l{l}"]), layer=f"{w.top[l]}->{w.top[l + 1]}",
+                                   k_run=tdims[l]))
+        if layers:
+            mfma["top_layers"] = layers
+            tot = sum(breakdown[f"top_l{l}"] for l in range(len(tdims) - 1))
+            mfma["top_mlp"] = frac(sum(tflops), tot)
+        elif "top_mlp" in breakdown:
+            mfma["top_mlp"] = frac(sum(tflops), breakdown["top_mlp"])
+        if "dense_bwd" in breakdown:
+            # weight gradients of every layer, input gradients of every layer but the first of each MLP
+            fl = 2 * sum(bflops) - bflops[0] + 2 * sum(tflops) - tflops[0]
+            mfma["dense_bwd"] = frac(fl, breakdown["dense_bwd"])
 
     cpu = None
     if not args.no_cpu_baseline:
         ns = args.cpu_samples or {"forward": 16384, "embbag": 16384, "interaction": 512, "train": 1024,
                                   "tiny": 128}[w.name]
         S, dt, thr, passes = cpu_baseline(w, batches, bottom, top, ns, chain=args.chain, table_dtype=lp)
+        S1, dt1, _, passes1 = cpu_baseline_single(w, batches, bottom, top, max(1, ns // max(thr, 1)),
+                                                  chain=args.chain, table_dtype=lp)
         what = {"forward": "forward pass", "embbag": "pooled lookups", "interaction": "forward pass",
                 "train": "forward pass and sparse SGD update", "tiny": "forward pass"}[w.name]
         if args.chain:
@@ -444,7 +564,11 @@ def main():
             what += f" from {lp} rows"
         cpu = {"value": round(S / dt, 2), "unit": "samples/s", "cores": thr, "kind": "oracle",
                "sample": f"{what} of the first {S // passes} samples of batch 0, repeated {passes} times "
-                         f"({dt:.1f} s; tables regenerated for the touched rows only, outside the timed region)"}
+                         f"({dt:.1f} s; tables regenerated for the touched rows only, outside the timed region)",
+               "threads": thr, "host_cores": host_cores(),
+               "single_thread": {"value": round(S1 / dt1, 2), "unit": "samples/s",
+                                 "sample": f"the first {S1 // passes1} samples, repeated {passes1} times "
+                                           f"({dt1:.1f} s, one thread)"}}
 
     cfg = {"workload": w.name, "batch": w.B, "tables": w.K, "d": w.d, "rows_total": int(sum(w.rows)),
            "bag": f"{w.bag}:{w.bag_len}", "index": f"{w.index_dist}" + (f"({w.alpha})" if w.index_dist == "zipf" else ""),
@@ -455,9 +579,9 @@ def main():
     res = {"metric": METRIC, "value": round(value, 1), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32+bf16" if w.mlp_dtype == "bf16" else "f32", "data": "synthetic",
-           "config": cfg, "roofline": roofline, "cpu_baseline": cpu,
+           "config": cfg, "roofline": roofline, "mfma": mfma, "cpu_baseline": cpu,
            "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
-           "breakdown_steps": args.breakdown_steps if model is not None else 0, "setup_s": round(t_setup, 1)}
+           "breakdown_steps": breakdown_done, "setup_s": round(t_setup, 1)}
     print(json.dumps(res), flush=True)
 
 
