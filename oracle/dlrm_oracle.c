@@ -96,10 +96,11 @@ void oracle_embbag_fwd(const float* const* tables, int32_t K, int32_t d, const i
 
 /*
  * Embedding lookup with sum pooling from low-precision table rows.
- * The explainer's citation list (Evaluation & Benchmarks) carries the note
- * that quantisation pays where a problem is bandwidth-bound, as
- * recommendation is; the pages fix no format, so two plain ones are read
- * here.  Every stored value is first turned into an fp32 number v, then the
+ * The page "Deep Learning Recommendation Model for Personalization and
+ * Recommendation Systems" (mlsanity summary), Citations in the corpus,
+ * carries a quantisation survey's note that quantisation pays where a
+ * problem is bandwidth-bound, as recommendation is; the pages fix no
+ * format, so two plain ones are read here.  Every stored value is first turned into an fp32 number v, then the
  * bag is pooled exactly as oracle_embbag_fwd (fp32, ascending position,
  * from +0.0f):
  *   dtype 1 (bf16):  v = the bf16 value widened to fp32 (exact: the 16 bits
