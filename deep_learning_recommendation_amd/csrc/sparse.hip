@@ -24,6 +24,8 @@
 // the few longest chains leave free take the rest of the work meanwhile.
 #include "common.hpp"
 
+#include <mutex>
+
 namespace dlrm {
 namespace {
 
@@ -862,6 +864,56 @@ extern "C" int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_
   if (launch_status() != DLRM_OK) return DLRM_E_HIP;
   return sgd_segments(tables, d, row_bits, b.seg_key, b.vals[cur], b.seg, b.hot_ordered, b.counters, G, g_ld, g_col0,
                       lr, stream, side);
+}
+
+// ------------------------------------------------------------------ no-allocation form
+//
+// dlrm_embbag_bwd_sgd_noalloc keeps the workspace of dlrm_embbag_bwd_sgd in
+// a file-scope device array instead of a caller buffer.  Every GPU that runs
+// the library holds its own copy of the array from the moment the library's
+// code object is loaded on it until the process ends.  In host code the
+// array's name is only a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current
+// (on the entry point's first call there) and kept per device.
+constexpr size_t kNoallocScratchBytes = (size_t)DLRM_NOALLOC_SCRATCH_MB << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kNoallocScratchBytes];
+
+namespace dlrm {
+namespace {
+void* noalloc_scratch() {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip_error = (int)e;
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+}  // namespace
+}  // namespace dlrm
+
+extern "C" int dlrm_embbag_bwd_sgd_noalloc(float* const* tables, int32_t K, int32_t d, const int64_t* rows,
+                                           const int64_t* indices, const int64_t* offsets, int64_t B, int64_t nnz,
+                                           const float* G, int64_t g_ld, int64_t g_col0, float lr,
+                                           hipStream_t stream) {
+  if (nnz < 0 || nnz > 0x7fffffffLL) return DLRM_E_INVALID;
+  SparseLayout L;
+  sparse_layout(nnz, &L);
+  if (L.bytes > kNoallocScratchBytes) return DLRM_E_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return DLRM_E_HIP;
+  // the same kernels as dlrm_embbag_bwd_sgd on the static scratch (its
+  // counters are cleared by a kernel at the start of each call)
+  return dlrm_embbag_bwd_sgd(tables, K, d, rows, indices, offsets, B, nnz, G, g_ld, g_col0, lr, ws,
+                             kNoallocScratchBytes, stream);
 }
 
 extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_t* rows,

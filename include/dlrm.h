@@ -343,6 +343,25 @@ int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_t d, const 
                               hipStream_t stream, hipStream_t side);
 
 /*
+ * dlrm_embbag_bwd_sgd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid allocation).  The workspace lives
+ * in a static device array of DLRM_NOALLOC_SCRATCH_MB MiB inside the
+ * library: each GPU the library runs on holds one until the process ends.
+ * The call allocates nothing (no hipMalloc, no hipFree).  Arguments, limits
+ * and results as dlrm_embbag_bwd_sgd (bit for bit the same table rows);
+ * nnz needing more scratch than the array holds (about 11 million lookups)
+ * returns DLRM_E_WORKSPACE before anything is enqueued.  Every call on one
+ * GPU shares that GPU's array and leaves its contents behind: calls that
+ * overlap on one GPU (on different streams, or from different threads
+ * without ordering) race and are not allowed.
+ */
+#define DLRM_NOALLOC_SCRATCH_MB 256
+int dlrm_embbag_bwd_sgd_noalloc(float* const* tables, int32_t K, int32_t d, const int64_t* rows,
+                                const int64_t* indices, const int64_t* offsets, int64_t B, int64_t nnz,
+                                const float* G, int64_t g_ld, int64_t g_col0, float lr, hipStream_t stream);
+
+/*
  * Validate indices and offsets on the device.  rows_dev: device int64 [K].
  * Adds to *bad_count (device int64, caller zeroes it) the number of indices
  * outside [0, rows[k]) plus the number of decreasing offset steps, plus one
