@@ -8,8 +8,10 @@
 // path is:
 //   1. keys: one (table, row) key and one bag id per index position
 //      (position order = table-major bag order);
-//   2. a stable least-significant-digit radix sort on the keys, 8 bits per
-//      pass; stability keeps equal keys in position order;
+//   2. a stable least-significant-digit radix sort over the row bits of the
+//      keys (8 or 9 bits per pass); stability keeps equal keys in position
+//      order, and since positions are table-major, equal rows of different
+//      tables stay in table order, so every (table, row) key forms one run;
 //   3. run-length segmentation (head flags, device-wide exclusive scan);
 //   4. one fused kernel: each segment's gradient sum over its occurrences in
 //      sorted order (fp32, from +0) and the update T <- T - lr * g.
@@ -32,6 +34,7 @@ namespace {
 constexpr int RT = 256;                // threads per sort block
 constexpr int RITEMS = 16;             // keys per thread per tile
 constexpr int RTILE = RT * RITEMS;     // 4096 keys per tile
+constexpr int kMaxBuckets = 512;       // radix digits of at most 9 bits
 constexpr int SCAN_ITEMS = 8;
 constexpr int SCAN_TILE = 256 * SCAN_ITEMS;
 constexpr int kHot = 128;              // occurrences from which a segment is "hot"
@@ -69,15 +72,18 @@ __global__ __launch_bounds__(256) void build_keys_kernel(const int64_t* __restri
 
 // ------------------------------------------------------------------ radix sort
 
+template <int DB>  // digit bits (8 or 9): 2^DB buckets
 __global__ __launch_bounds__(RT) void radix_hist_kernel(const uint32_t* __restrict__ keys, int n, int shift,
                                                         uint32_t* __restrict__ hist, int nblocks) {
-  __shared__ uint32_t cnt[256];
-  cnt[threadIdx.x] = 0;
+  constexpr int NB = 1 << DB, PER = NB / RT;  // buckets, buckets per thread
+  __shared__ uint32_t cnt[NB];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) cnt[threadIdx.x + q * RT] = 0;
   __syncthreads();
   const int base = blockIdx.x * RTILE;
   const int lane = threadIdx.x & 63;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // lanes with equal digits found by eight ballots; the lowest of them adds
+  // lanes with equal digits found by DB ballots; the lowest of them adds
   // the group's count (Zipf keys share digits, so one atomic per group
   // instead of one per key)
   uint32_t kv[RITEMS];
@@ -90,10 +96,10 @@ __global__ __launch_bounds__(RT) void radix_hist_kernel(const uint32_t* __restri
   for (int i = 0; i < RITEMS; ++i) {
     const int p = base + i * RT + threadIdx.x;
     const bool valid = p < n;
-    const uint32_t digit = (kv[i] >> shift) & 255u;
+    const uint32_t digit = (kv[i] >> shift) & (uint32_t)(NB - 1);
     uint64_t peers = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < DB; ++b) {
       const bool bit = (digit >> b) & 1u;
       const uint64_t m = __ballot(bit);
       peers &= bit ? m : ~m;
@@ -101,25 +107,35 @@ __global__ __launch_bounds__(RT) void radix_hist_kernel(const uint32_t* __restri
     if (valid && (peers & lt) == 0ull) atomicAdd(&cnt[digit], (uint32_t)__popcll(peers));
   }
   __syncthreads();
-  hist[(int64_t)threadIdx.x * nblocks + blockIdx.x] = cnt[threadIdx.x];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int d = threadIdx.x + q * RT;
+    hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
+  }
 }
 
 // Stable scatter: the tile is taken in RITEMS rounds of 256 consecutive keys;
 // inside a round a key's rank is (keys of its digit in earlier rounds) +
 // (in earlier waves of this round) + (in lower lanes of its wave), the last
-// term found by matching the 8 digit bits with wave ballots.
+// term found by matching the DB digit bits with wave ballots.
+template <int DB>
 __global__ __launch_bounds__(RT) void radix_scatter_kernel(const uint32_t* __restrict__ kin,
                                                            const int32_t* __restrict__ vin,
                                                            uint32_t* __restrict__ kout, int32_t* __restrict__ vout,
                                                            int n, int shift, const uint32_t* __restrict__ offs,
                                                            int nblocks) {
-  __shared__ uint32_t run[256];
-  __shared__ uint32_t wcnt[4][256];
-  __shared__ uint32_t woff[4][256];
+  constexpr int NB = 1 << DB, PER = NB / RT;
+  __shared__ uint32_t run[NB];
+  __shared__ uint32_t wcnt[4][NB];
+  __shared__ uint32_t woff[4][NB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  run[tid] = offs[(int64_t)tid * nblocks + blockIdx.x];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+  for (int q = 0; q < PER; ++q) {
+    const int d = tid + q * RT;
+    run[d] = offs[(int64_t)d * nblocks + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w][d] = 0;
+  }
   __syncthreads();
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < RITEMS; ++r) {
@@ -127,10 +143,10 @@ __global__ __launch_bounds__(RT) void radix_scatter_kernel(const uint32_t* __res
     const bool valid = p < n;
     const uint32_t key = valid ? kin[p] : 0u;
     const int32_t val = valid ? vin[p] : 0;
-    const uint32_t digit = (key >> shift) & 255u;
+    const uint32_t digit = (key >> shift) & (uint32_t)(NB - 1);
     uint64_t peers = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < DB; ++b) {
       const bool bit = (digit >> b) & 1u;
       const uint64_t m = __ballot(bit);
       peers &= bit ? m : ~m;
@@ -138,15 +154,17 @@ __global__ __launch_bounds__(RT) void radix_scatter_kernel(const uint32_t* __res
     const uint32_t rank = (uint32_t)__popcll(peers & lt);
     if (valid && (peers & lt) == 0ull) wcnt[wave][digit] = (uint32_t)__popcll(peers);
     __syncthreads();
-    {
-      uint32_t acc = run[tid];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int d = tid + q * RT;
+      uint32_t acc = run[d];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        woff[w][tid] = acc;
-        acc += wcnt[w][tid];
-        wcnt[w][tid] = 0;
+        woff[w][d] = acc;
+        acc += wcnt[w][d];
+        wcnt[w][d] = 0;
       }
-      run[tid] = acc;
+      run[d] = acc;
     }
     __syncthreads();
     if (valid) {
@@ -689,7 +707,7 @@ void sparse_layout(int64_t nnz, SparseLayout* L) {
   };
   const int64_t n = nnz > 0 ? nnz : 1;
   L->nblocks = ceil_div(n, RTILE);
-  L->hist_n = 256 * L->nblocks;
+  L->hist_n = (int64_t)kMaxBuckets * L->nblocks;
   L->scan_nb_hist = ceil_div(L->hist_n, SCAN_TILE);
   L->scan_nb_keys = ceil_div(n, SCAN_TILE);
   L->keys[0] = take(4 * (size_t)n);
@@ -782,9 +800,19 @@ int sparse_bufs(int64_t nnz, void* ws, size_t ws_bytes, SparseLayout* L, SparseB
   return DLRM_OK;
 }
 
-// Sort passes for the key width: the sorted keys and bag ids end in buffer
-// passes % 2.
-int sort_passes(int row_bits, int table_bits) { return (row_bits + table_bits + 7) / 8; }
+// The sort runs over the row bits only: positions are table-major (the
+// bags of table k come before those of table k + 1), so a stable sort by
+// row leaves equal rows in table order and every (table, row) key in one
+// run.  Digits of 8 bits, or 9 where that saves a pass (26 row bits: three
+// passes of 9 instead of four of 8).  The sorted keys and bag ids end in
+// buffer passes % 2.
+struct SortPlan {
+  int passes, digit_bits;
+};
+SortPlan sort_plan(int row_bits) {
+  const int p8 = (row_bits + 7) / 8, p9 = (row_bits + 8) / 9;
+  return p9 < p8 ? SortPlan{p9, 9} : SortPlan{p8, 8};
+}
 }  // namespace
 }  // namespace dlrm
 
@@ -811,19 +839,29 @@ extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const
     hipLaunchKernelGGL(build_keys_kernel, dim3((unsigned)kblocks), dim3(256), 0, stream, indices, offsets, KB, B, kg,
                        row_bits, b.keys[0], b.vals[0]);
   }
-  const int passes = sort_passes(row_bits, table_bits);
+  const SortPlan plan = sort_plan(row_bits);
   const int nblocks = (int)L.nblocks;
+  const int64_t hist_n = ((int64_t)1 << plan.digit_bits) * nblocks;  // digit-major counts
+  const unsigned scan_nb = (unsigned)ceil_div(hist_n, SCAN_TILE);
   int cur = 0;
-  for (int pass = 0; pass < passes; ++pass) {
-    const int shift = pass * 8;
-    hipLaunchKernelGGL(radix_hist_kernel, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], n, shift, b.hist, nblocks);
-    hipLaunchKernelGGL((scan_reduce_kernel<ArrayIn>), dim3((unsigned)L.scan_nb_hist), dim3(256), 0, stream,
-                       ArrayIn{b.hist}, L.hist_n, b.bsum);
-    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, b.bsum, (int)L.scan_nb_hist, nullptr);
-    hipLaunchKernelGGL(scan_apply_array_kernel, dim3((unsigned)L.scan_nb_hist), dim3(256), 0, stream, b.hist,
-                       L.hist_n, b.bsum, b.hist);
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], b.vals[cur],
-                       b.keys[cur ^ 1], b.vals[cur ^ 1], n, shift, b.hist, nblocks);
+  for (int pass = 0; pass < plan.passes; ++pass) {
+    const int shift = pass * plan.digit_bits;
+    if (plan.digit_bits == 9)
+      hipLaunchKernelGGL(radix_hist_kernel<9>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], n, shift, b.hist,
+                         nblocks);
+    else
+      hipLaunchKernelGGL(radix_hist_kernel<8>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], n, shift, b.hist,
+                         nblocks);
+    hipLaunchKernelGGL((scan_reduce_kernel<ArrayIn>), dim3(scan_nb), dim3(256), 0, stream, ArrayIn{b.hist}, hist_n,
+                       b.bsum);
+    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, b.bsum, (int)scan_nb, nullptr);
+    hipLaunchKernelGGL(scan_apply_array_kernel, dim3(scan_nb), dim3(256), 0, stream, b.hist, hist_n, b.bsum, b.hist);
+    if (plan.digit_bits == 9)
+      hipLaunchKernelGGL(radix_scatter_kernel<9>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], b.vals[cur],
+                         b.keys[cur ^ 1], b.vals[cur ^ 1], n, shift, b.hist, nblocks);
+    else
+      hipLaunchKernelGGL(radix_scatter_kernel<8>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], b.vals[cur],
+                         b.keys[cur ^ 1], b.vals[cur ^ 1], n, shift, b.hist, nblocks);
     cur ^= 1;
   }
   // run-length segmentation of the sorted keys
@@ -851,7 +889,7 @@ extern "C" int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_
   SparseLayout L;
   SparseBufs b;
   if ((rc = sparse_bufs(nnz, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
-  const int cur = sort_passes(row_bits, table_bits) & 1;
+  const int cur = sort_plan(row_bits).passes & 1;
   // the work counters start from zero on every call, so one prepared
   // workspace can be applied more than once; each stream clears the counter
   // its own kernel takes work from
