@@ -25,6 +25,13 @@ __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 __device__ __forceinline__ float relu_f(float v) { return v > 0.f ? v : 0.f; }
 
+// bf16 pair with each half kept where the matching half of y is a positive
+// bf16 value and zeroed elsewhere
+__device__ __forceinline__ uint32_t mask_pair(uint32_t v, uint32_t y) {
+  const bool lo = bf16_to_f32((uint16_t)(y & 0xffffu)) > 0.f, hi = bf16_to_f32((uint16_t)(y >> 16)) > 0.f;
+  return (lo ? (v & 0xffffu) : 0u) | (hi ? (v & 0xffff0000u) : 0u);
+}
+
 // 8 consecutive bf16 (row, k..k+7); zero outside rows x [0, kend).
 template <bool VEC>
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, int64_t ld, int row, int rows, int k,
@@ -77,11 +84,12 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
 // 256 accumulators and run one wave per SIMD, smaller ones two.
 constexpr int fast_waves_per_eu(int WM, int WN) { return WM * WN > 128 * 64 ? 1 : 2; }
 
-template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S, bool PERSIST, int ILV>
+template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S, bool PERSIST, int ILV,
+          bool DELTA = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(fast_waves_per_eu(WM, WN)))) void gemm_bf16_fast_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, OutT* __restrict__ C, int64_t ldc, int M, int N, int K, int relu, int tiles_n,
-    int tiles, int k_per_split, int vec_out) {
+    int tiles, int k_per_split, int vec_out, DeltaOut dout) {
   static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
   constexpr int RB = BK * 2;                      // bytes per tile row
   constexpr int CPR = BK / 8;                     // 16-byte chunks per row
@@ -371,6 +379,103 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
     }
 
     const bool full = m0 + BM <= M && n0 + BN <= N && vec_out;
+    if constexpr (DELTA) {
+      // Input gradient of a ReLU layer: g = this tile, masked by the layer
+      // input y > 0, rounded to bf16 and written row-major to C; the tile then
+      // goes through LDS column-major (the stages are free: every wave is past
+      // its last operand read) and leaves transposed into dT, each thread
+      // summing eight rows of one column for the bias-gradient partials.
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      uint16_t* lt = reinterpret_cast<uint16_t*>(smem);  // [BN][BM]
+      const bool yvec = (dout.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(dout.y) & 15u) == 0;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          uint32_t pk[4][2];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) pk[g][h] = pack_bf16x2(acc[tm][tn][4 * g + 2 * h], acc[tm][tn][4 * g + 2 * h + 1]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const auto s01 = __builtin_amdgcn_permlane32_swap(pk[0][h], pk[1][h], false, false);
+            const auto s23 = __builtin_amdgcn_permlane32_swap(pk[2][h], pk[3][h], false, false);
+            pk[0][h] = s01[0];
+            pk[1][h] = s01[1];
+            pk[2][h] = s23[0];
+            pk[3][h] = s23[1];
+          }
+          // this lane: tile row rl, columns c0 .. c0+7 (lo) and c0+16 .. c0+23 (hi)
+          const int rl = wm * WM + tm * 32 + r32, i = m0 + rl;
+          const int c0 = wn * WN + tn * 32 + 8 * half;
+          uint32_t v[2][4] = {{pk[0][0], pk[0][1], pk[1][0], pk[1][1]}, {pk[2][0], pk[2][1], pk[3][0], pk[3][1]}};
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int j = n0 + c0 + 16 * p;
+            uint32_t y[4] = {0u, 0u, 0u, 0u};  // columns past N or rows past M: masked to zero
+            if (i < M) {
+              const uint16_t* yr = dout.y + (int64_t)i * dout.ldy + j;
+              if (yvec && j + 8 <= N) {
+                const uint4 yv = *reinterpret_cast<const uint4*>(yr);
+                y[0] = yv.x, y[1] = yv.y, y[2] = yv.z, y[3] = yv.w;
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  if (j + e < N) y[e >> 1] |= (uint32_t)yr[e] << (16 * (e & 1));
+              }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[p][q] = mask_pair(v[p][q], y[q]);
+            if (i < M) {
+              uint16_t* cr = reinterpret_cast<uint16_t*>(C) + (int64_t)i * ldc + j;
+              if (vec_out && j + 8 <= N) {
+                *reinterpret_cast<uint4*>(cr) = make_uint4(v[p][0], v[p][1], v[p][2], v[p][3]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  if (j + e < N) cr[e] = (uint16_t)(v[p][e >> 1] >> (16 * (e & 1)));
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lt[(c0 + 16 * p + e) * BM + rl] = (uint16_t)(v[p][e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      // transposed rows: item (column jl, row group q), q fastest, so that
+      // BM / 8 consecutive lanes write one column's BM rows contiguously
+      constexpr int QG = BM / 8, NT = NWAVES * 64;
+      const bool tvec = (dout.ldt % 8) == 0 && (reinterpret_cast<uintptr_t>(dout.dT) & 15u) == 0;
+#pragma unroll
+      for (int it = 0; it < BN * QG / NT; ++it) {
+        const int item = it * NT + tid;
+        const int q = item % QG, jl = item / QG;
+        const uint4 w4 = *reinterpret_cast<const uint4*>(lt + jl * BM + 8 * q);
+        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum = sum + bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+        for (int o = 1; o < QG; o <<= 1) sum = sum + __shfl_xor(sum, o, QG);
+        const int j = n0 + jl, i0 = m0 + 8 * q;
+        if (j < N) {
+          if (q == 0) dout.dbp[(int64_t)(m0 / BM) * N + j] = sum;
+          uint16_t* tr = dout.dT + (int64_t)j * dout.ldt + i0;
+          if (tvec && i0 + 8 <= M) {
+            *reinterpret_cast<uint4*>(tr) = w4;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (i0 + e < M) tr[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+      goto tile_done;
+    }
     if constexpr (sizeof(OutT) == 2 && !PARTIAL) {
       if (full) {
 #pragma unroll
@@ -472,13 +577,14 @@ int fast_occupancy(Kern kern, int threads) {
 }
 
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2, bool PERSIST = false,
-          int ILV = 0>
+          int ILV = 0, bool DELTA = false>
 void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
-                 int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s) {
+                 int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s,
+                 DeltaOut dout = DeltaOut{}) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int tiles = tm * tn;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S, PERSIST, ILV>;
+  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S, PERSIST, ILV, DELTA>;
   int grid = tiles;
   if constexpr (PERSIST) {
     const int slots = fast_occupancy(kern, threads) * device_cu_count();
@@ -489,7 +595,7 @@ void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw,
   constexpr int VW = 16 / (int)sizeof(OutT);
   const int vec_out = (ldc % VW) == 0 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
   hipLaunchKernelGGL(kern, dim3(grid, 1, splits), dim3(threads), 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu,
-                     tn, tiles, k_per_split, vec_out);
+                     tn, tiles, k_per_split, vec_out, dout);
 }
 
 // Tile choice: the largest block tile that still gives every CU a tile
@@ -793,6 +899,30 @@ int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, co
     auto* c = static_cast<float*>(C);
     if (fast) pick_fast<float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
     else launch_generic<float, false>(A, lda, W, ldw, bias, c, ldc, M, N, K, relu, 1, kps, s);
+  }
+  return launch_status();
+}
+
+int gemm_bf16_delta(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, int M, int N, int K,
+                    uint16_t* dlt, int64_t ldd, const DeltaOut& dout, int* tile_rows, hipStream_t s) {
+  if (M <= 0 || N <= 0) return DLRM_OK;
+  const bool fast = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0 && lda >= K && ldw >= K &&
+                    (int64_t)256 * lda < ((int64_t)1 << 31) && (int64_t)256 * ldw < ((int64_t)1 << 31);
+  if (!fast) return DLRM_E_UNSUPPORTED;
+  const int kps = (int)round_up(K > 0 ? K : 1, 64);
+  // the largest block tile that still gives every CU a tile (as pick_fast)
+  if (ceil_div(M, 256) * ceil_div(N, 256) >= 256) {
+    *tile_rows = 256;
+    if ((K % 64) == 0 && K >= 512)
+      launch_fast<256, 256, 128, 64, uint16_t, false, 64, 2, false, 2, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K,
+                                                                            0, 1, kps, s, dout);
+    else
+      launch_fast<256, 256, 128, 64, uint16_t, false, 32, 4, false, 1, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K,
+                                                                            0, 1, kps, s, dout);
+  } else {
+    *tile_rows = 128;
+    launch_fast<128, 128, 64, 64, uint16_t, false, 64, 2, false, 2, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K, 0,
+                                                                         1, kps, s, dout);
   }
   return launch_status();
 }

@@ -10,11 +10,13 @@
 // fused, everything else the bf16 MFMA GEMM with bias + ReLU + convert fused
 // in its epilogue.
 //
-// Backward (bf16 networks): per layer, delta = g * 1[y > 0] (bf16 for the
-// MFMA operands), db by a deterministic two-stage column sum, dW = delta^T x
-// as a split-K MFMA GEMM over the batch (partials summed in a fixed order),
-// and g_prev = delta W.  Transposed copies make every GEMM the K-contiguous
-// form the MFMA kernel reads.
+// Backward (bf16 networks): per layer, dW = delta^T x as a split-K MFMA GEMM
+// over the batch (partials summed in a fixed order) and delta W, whose
+// epilogue applies the ReLU mask of the layer below, rounds to bf16 and
+// writes that layer's delta in both layouts with its bias-gradient partials
+// (a deterministic two-stage column sum); only the last layer's delta, from
+// the caller's fp32 dY, takes a separate pass.  Transposed copies make every
+// GEMM the K-contiguous form the MFMA kernel reads.
 #include "gemm.hpp"
 
 namespace dlrm {
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__
 }
 
 struct BwdLayout {
-  size_t g[2], dlt, dltT, xT, wT, part, dbp, bytes;
+  size_t dlt[2], dltT[2], xT, wT, part, dbp, bytes;
   int64_t ld_dlt, ld_B, splits_max;
 };
 
@@ -568,10 +570,10 @@ bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
     cv.used += bytes;
     return at;
   };
-  lay->g[0] = take(4 * (size_t)(B * wmax));
-  lay->g[1] = take(4 * (size_t)(B * wmax));
-  lay->dlt = take(2 * (size_t)(B * lay->ld_dlt));
-  lay->dltT = take(2 * (size_t)(wfo * lay->ld_B));
+  for (int i = 0; i < 2; ++i) {
+    lay->dlt[i] = take(2 * (size_t)(B * lay->ld_dlt));
+    lay->dltT[i] = take(2 * (size_t)(wfo * lay->ld_B));
+  }
   lay->xT = take(2 * (size_t)(wmax * lay->ld_B));
   lay->wT = take(2 * (size_t)(wmax * lay->ld_dlt));
   lay->part = take(4 * (size_t)(kMaxSplits * prod));
@@ -742,43 +744,37 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
 
   const char* fws = static_cast<const char*>(fwd_ws);
   char* w = static_cast<char*>(ws);
-  float* gbuf[2] = {reinterpret_cast<float*>(w + bl.g[0]), reinterpret_cast<float*>(w + bl.g[1])};
-  uint16_t* dlt = reinterpret_cast<uint16_t*>(w + bl.dlt);
-  uint16_t* dltT = reinterpret_cast<uint16_t*>(w + bl.dltT);
+  uint16_t* dlt[2] = {reinterpret_cast<uint16_t*>(w + bl.dlt[0]), reinterpret_cast<uint16_t*>(w + bl.dlt[1])};
+  uint16_t* dltT[2] = {reinterpret_cast<uint16_t*>(w + bl.dltT[0]), reinterpret_cast<uint16_t*>(w + bl.dltT[1])};
   uint16_t* xT = reinterpret_cast<uint16_t*>(w + bl.xT);
   uint16_t* wT = reinterpret_cast<uint16_t*>(w + bl.wT);
   float* part = reinterpret_cast<float*>(w + bl.part);
   float* dbp = reinterpret_cast<float*>(w + bl.dbp);
   const int M = (int)B;
-  const int chunks = (int)ceil_div(B, kDRows);
-
-  const float* g = dY;
-  int64_t ldg = dy_ld;
+  const dim3 b1(256);
   int rc = DLRM_OK;
-  for (int l = L - 1; l >= 0 && rc == DLRM_OK; --l) {
-    const int fi = dims[l], fo = dims[l + 1];
-    const bool relu = (l < L - 1) || last_act == DLRM_ACT_RELU;
-    const dim3 b1(256), gd((unsigned)ceil_div(fo, kDCols), (unsigned)chunks);
-    // 1. delta (bf16, both layouts) and the bias-gradient partials
-    // vector accesses: g 16-byte, delta 8-byte and y (16-byte fp32 / 8-byte bf16) aligned rows
+
+  // 1. the last layer's delta from dY (fp32), both layouts, and its bias
+  //    gradient; every earlier layer's delta comes out of the input-gradient
+  //    GEMM of the layer above it
+  {
+    const int fo = dims[L];
+    const bool relu = last_act == DLRM_ACT_RELU;
+    const float* y = relu ? out : dY;  // mask source unused when relu == 0
+    const int64_t ldy = relu ? out_ld : dy_ld;
     auto al = [](const void* p, int64_t ld, int esz, int bytes) {
       return (reinterpret_cast<uintptr_t>(p) % bytes) == 0 && ((ld * esz) % bytes) == 0;
     };
-    const bool vg = al(g, ldg, 4, 16) && al(dlt, bl.ld_dlt, 2, 8);
-    if (l == L - 1) {
-      const float* y = relu ? out : g;  // mask source unused when relu == 0
-      const int64_t ldy = relu ? out_ld : ldg;
-      const int vec = vg && al(y, ldy, 4, 16);
-      hipLaunchKernelGGL((delta_db_kernel<float>), gd, b1, 0, stream, g, ldg, y, ldy, (int)relu, dlt, bl.ld_dlt, dltT,
-                         bl.ld_B, dbp, M, fo, vec);
-    } else {
-      const uint16_t* y = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l + 1]);
-      const int vec = vg && al(y, fl.act_ld[l + 1], 2, 8);
-      hipLaunchKernelGGL((delta_db_kernel<uint16_t>), gd, b1, 0, stream, g, ldg, y, fl.act_ld[l + 1], (int)relu, dlt,
-                         bl.ld_dlt, dltT, bl.ld_B, dbp, M, fo, vec);
-    }
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 64)), b1, 0, stream, dbp, chunks, fo, db[l]);
-    if ((rc = launch_status()) != DLRM_OK) break;
+    const int vec = al(dY, dy_ld, 4, 16) && al(dlt[0], bl.ld_dlt, 2, 8) && al(y, ldy, 4, 16);
+    const int chunks = (int)ceil_div(B, kDRows);
+    hipLaunchKernelGGL((delta_db_kernel<float>), dim3((unsigned)ceil_div(fo, kDCols), (unsigned)chunks), b1, 0, stream,
+                       dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, dltT[0], bl.ld_B, dbp, M, fo, vec);
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 64)), b1, 0, stream, dbp, chunks, fo, db[L - 1]);
+    rc = launch_status();
+  }
+  int cur = 0;
+  for (int l = L - 1; l >= 0 && rc == DLRM_OK; --l) {
+    const int fi = dims[l], fo = dims[l + 1];
     // 2. dW = delta^T x  (M = fo, N = fi, K = B), split over the batch
     const uint16_t* x = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l]);
     if ((rc = transpose_bf16(x, fl.act_ld[l], xT, bl.ld_B, M, fi, stream)) != DLRM_OK) break;
@@ -787,18 +783,33 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     if (splits > kMaxSplits) splits = kMaxSplits;
     if (splits > (int)ceil_div(M, 256)) splits = (int)ceil_div(M, 256);
     if (splits < 1) splits = 1;
-    if ((rc = gemm_bf16_splitk(dltT, bl.ld_B, xT, bl.ld_B, part, fo, fi, M, splits, stream)) != DLRM_OK) break;
+    if ((rc = gemm_bf16_splitk(dltT[cur], bl.ld_B, xT, bl.ld_B, part, fo, fi, M, splits, stream)) != DLRM_OK) break;
     if ((rc = reduce_splits(part, splits, fo, fi, nullptr, dW[l], fi, false, stream)) != DLRM_OK) break;
-    // 3. g_prev = delta W  (M = B, N = fi, K = fo)
-    if (l > 0 || dX) {
-      const int64_t wl = w_ld ? w_ld[l] : fi;
-      if ((rc = transpose_bf16(static_cast<const uint16_t*>(W[l]), wl, wT, bl.ld_dlt, fo, fi, stream)) != DLRM_OK) break;
-      float* gp = (l == 0) ? dX : gbuf[l & 1];
-      const int64_t ldp = (l == 0) ? dx_ld : fi;
-      rc = gemm_bf16(dlt, bl.ld_dlt, wT, bl.ld_dlt, nullptr, gp, ldp, false, M, fi, fo, false, stream);
-      g = gp;
-      ldg = ldp;
+    if (l == 0 && !dX) break;
+    // 3. the input gradient delta W  (M = B, N = fi, K = fo)
+    const int64_t wl = w_ld ? w_ld[l] : fi;
+    if ((rc = transpose_bf16(static_cast<const uint16_t*>(W[l]), wl, wT, bl.ld_dlt, fo, fi, stream)) != DLRM_OK) break;
+    if (l == 0) {  // the MLP input's gradient, fp32
+      rc = gemm_bf16(dlt[cur], bl.ld_dlt, wT, bl.ld_dlt, nullptr, dX, dx_ld, false, M, fi, fo, false, stream);
+      break;
     }
+    // layer l-1 is a ReLU layer whose output is layer l's input x: its delta
+    // (masked by x > 0, bf16, both layouts) and bias-gradient partials come
+    // straight out of the GEMM
+    DeltaOut dout;
+    dout.y = x;
+    dout.ldy = fl.act_ld[l];
+    dout.dT = dltT[cur ^ 1];
+    dout.ldt = bl.ld_B;
+    dout.dbp = dbp;
+    int tile_rows = 128;
+    if ((rc = gemm_bf16_delta(dlt[cur], bl.ld_dlt, wT, bl.ld_dlt, M, fi, fo, dlt[cur ^ 1], bl.ld_dlt, dout, &tile_rows,
+                              stream)) != DLRM_OK)
+      break;
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fi, 64)), b1, 0, stream, dbp,
+                       (int)ceil_div(B, tile_rows), fi, db[l - 1]);
+    if ((rc = launch_status()) != DLRM_OK) break;
+    cur ^= 1;
   }
   return rc;
 }

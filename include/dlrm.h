@@ -267,6 +267,8 @@ int dlrm_linear_fwd(const void* A, int64_t lda, const void* W, int64_t ldw, cons
  *   dX       nullable fp32 [B][dx_ld], gradient w.r.t. the MLP input.
  *   delta_l = g_l * 1[y_l > 0] on ReLU layers; g_{l-1} = delta_l W_l.  The
  *   GEMMs take bf16 operands (delta rounded to bf16) with fp32 sums.
+ *   db_l sums delta_l over the batch in fp32: the fp32 delta of the last
+ *   layer, the bf16-rounded delta (the GEMM operand) of the others.
  *   ws       dlrm_mlp_bwd_workspace_size() bytes.
  */
 size_t dlrm_mlp_bwd_workspace_size(int64_t B, int32_t L, const int32_t* dims);
