@@ -340,7 +340,13 @@ def main():
 
         def fork_prepare():
             # after the lookup, so the sort overlaps the MLPs and the dense
-            # backward (MFMA-bound) rather than the HBM-bound lookup
+            # backward (MFMA-bound) rather than the HBM-bound lookup; the
+            # breakdown pass runs it alone on the first stream instead
+            if mode == "breakdown":
+                mark("sparse_prepare")
+                D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx, off, w.B, nnz, model.ws_sparse)
+                prep_stream.wait_stream(stream)
+                return
             prep_stream.wait_stream(stream)
             with torch.cuda.stream(prep_stream):
                 D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx, off, w.B, nnz, model.ws_sparse)
