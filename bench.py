@@ -299,12 +299,13 @@ def main():
     t_setup = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream()
-    # training: the sparse update runs on a second stream, forked after the
-    # lookup (it reads only the indices, the synthetic gradient and the
-    # tables the lookup has finished reading): the index half (keys, sort,
-    # segments), then the sums and the update, whose short segments take a
-    # third stream; the interaction, top MLP and dense backward run on the
-    # first stream meanwhile, and the step ends when all three are done.
+    # training: the sparse update runs on a second stream: the index half
+    # (keys, sort, segments) from the start of the step (it reads only the
+    # indices), then, once the lookup has finished reading the tables, the
+    # sums and the update (the synthetic gradient is an input), whose short
+    # segments take a third stream; the interaction, top MLP and dense
+    # backward run on the first stream meanwhile, and the step ends when all
+    # three are done.
     # (The per-call breakdown runs the calls one after another on the first
     # stream instead, so that each interval holds one call.)
     prep_stream = torch.cuda.Stream() if w.train else None
@@ -339,17 +340,22 @@ def main():
                 ev[name] = gather_t.start(stream)
 
         def fork_prepare():
-            # after the lookup, so the sort overlaps the MLPs and the dense
-            # backward (MFMA-bound) rather than the HBM-bound lookup; the
-            # breakdown pass runs it alone on the first stream instead
+            # the index half reads only the indices: it starts with the step,
+            # beside the bottom MLP and the lookup (the sort is on the path to
+            # the update, the lookup is not); the breakdown pass runs it alone
+            # on the first stream after the lookup instead
             if mode == "breakdown":
-                mark("sparse_prepare")
-                D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx, off, w.B, nnz, model.ws_sparse)
-                prep_stream.wait_stream(stream)
                 return
             prep_stream.wait_stream(stream)
             with torch.cuda.stream(prep_stream):
                 D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx, off, w.B, nnz, model.ws_sparse)
+
+        def after_lookup():
+            # the update writes rows the lookup reads: it waits for the lookup
+            if mode == "breakdown":
+                mark("sparse_prepare")
+                D.dlrm_embbag_bwd_sgd_prepare(w.K, w.rows, idx, off, w.B, nnz, model.ws_sparse)
+            prep_stream.wait_stream(stream)
 
         def sparse_apply(Gs, on_side):
             """The sums and the update: long segments on the stream that ran
@@ -362,8 +368,10 @@ def main():
                                         model.ws_sparse, stream=s0, side=light_stream)
             s0.wait_stream(light_stream)
 
+        if w.train:
+            fork_prepare()
         if args.chain:
-            return chain_step(model, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare, sparse_apply, overlap)
+            return chain_step(model, dense, idx, off, y, nnz, mark, ev, mode, after_lookup, sparse_apply, overlap)
         mark("bottom_mlp")
         D.dlrm_mlp_fwd(dense, dense.shape[1], w.B, model.bottom.dims, model.bottom.Ws, model.bottom.w_ld,
                        model.bottom.biases, model.bottom.w_dtype, D.DLRM_ACT_RELU, model.x0, model.x0_ld, None,
@@ -377,7 +385,7 @@ def main():
                 D.dlrm_embbag_interact_fwd_lp(model.x0, model.x0_ld, model.table_ptrs, model.table_code, model.sb_ptrs,
                                               w.K, d, idx, off, w.B, model.top_in, model.top_ld)
             if w.train:
-                fork_prepare()
+                after_lookup()
         else:
             mark("embbag")
             if lp == "f32":
@@ -386,7 +394,7 @@ def main():
                 D.dlrm_embbag_fwd_lp(model.table_ptrs, model.table_code, model.sb_ptrs, w.K, d, idx, off, w.B, model.X,
                                      n * d, d, nnz=nnz)
             if w.train:
-                fork_prepare()
+                after_lookup()
             mark("interact")
             D.dlrm_interact_fwd(model.X, w.B, n, d, n * d, model.top_in, model.top_ld)
         if mode == "breakdown" and not w.train and bf16:
@@ -445,7 +453,7 @@ def main():
             for a, b in zip(names[:-1], names[1:]):
                 (call_t if mode == "breakdown" else dom_t).setdefault(a, []).append((ev[a], ev[b]))
 
-    def chain_step(m, dense, idx, off, y, nnz, mark, ev, mode, fork_prepare, sparse_apply, overlap):
+    def chain_step(m, dense, idx, off, y, nnz, mark, ev, mode, after_lookup, sparse_apply, overlap):
         """Forward with X materialised, then the backward from the loss (the
         sparse update, once the X gradient exists, beside the bottom MLP's
         backward)."""
@@ -455,7 +463,7 @@ def main():
                        m.bottom.w_dtype, D.DLRM_ACT_RELU, m.x0, m.x0_ld, None, m.ws_bot, True)
         mark("embbag")
         D.dlrm_embbag_fwd(m.table_ptrs, w.K, d, idx, off, B, m.X, n * d, d, nnz=nnz)
-        fork_prepare()
+        after_lookup()
         mark("interact")
         D.dlrm_interact_fwd(m.X, B, n, d, n * d, m.top_in, m.top_ld)
         mark("top_mlp")

@@ -356,6 +356,140 @@ __device__ __forceinline__ void lds_store(int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// The adder's loop over the full blocks of an item, scheduled by hand.  Every
+// instruction between two dependent adds lengthens the chain (measured on
+// gfx950: a dependent fp32 add issues every 4.4 cycles; a 16-byte LDS read
+// placed between two adds adds about 15 cycles, four of them back to back
+// about 6 cycles each; a satisfied wait about 4), so a block runs as four
+// steps of [four 16-byte reads, one wait, sixteen adds], the reads for the
+// step after next, the waits counted exactly (one wave's LDS accesses complete
+// in order).  Step buffers live in v192..v255 (A, B: steps 0 and 1, reloaded
+// from the next block during steps 2 and 3; C, D: steps 2 and 3).  The slot
+// is released (consumed = block + 1) right after its last reads are issued:
+// they are performed before any later access of this wave, so before the
+// loader can see the release.  The next block's flag is read before its first
+// reads; if it was not yet up, those reads are dropped and issued again once
+// it is.
+#define HOT_RD(v0, v3, op, off) "ds_read_b128 v[" #v0 ":" #v3 "], %[" #op "] offset:" #off "\n\t"
+#define HOT_RD_A(op) HOT_RD(192, 195, op, 0) HOT_RD(196, 199, op, 16) HOT_RD(200, 203, op, 32) HOT_RD(204, 207, op, 48)
+#define HOT_RD_B(op) HOT_RD(208, 211, op, 64) HOT_RD(212, 215, op, 80) HOT_RD(216, 219, op, 96) HOT_RD(220, 223, op, 112)
+#define HOT_RD_C(op) HOT_RD(224, 227, op, 128) HOT_RD(228, 231, op, 144) HOT_RD(232, 235, op, 160) HOT_RD(236, 239, op, 176)
+#define HOT_RD_D(op) HOT_RD(240, 243, op, 192) HOT_RD(244, 247, op, 208) HOT_RD(248, 251, op, 224) HOT_RD(252, 255, op, 240)
+#define HOT_ADD(v) "v_add_f32 %[acc], %[acc], v" #v "\n\t"
+#define HOT_ADD4(a, b, c, e) HOT_ADD(a) HOT_ADD(b) HOT_ADD(c) HOT_ADD(e)
+#define HOT_ADDS_A HOT_ADD4(192, 193, 194, 195) HOT_ADD4(196, 197, 198, 199) HOT_ADD4(200, 201, 202, 203) HOT_ADD4(204, 205, 206, 207)
+#define HOT_ADDS_B HOT_ADD4(208, 209, 210, 211) HOT_ADD4(212, 213, 214, 215) HOT_ADD4(216, 217, 218, 219) HOT_ADD4(220, 221, 222, 223)
+#define HOT_ADDS_C HOT_ADD4(224, 225, 226, 227) HOT_ADD4(228, 229, 230, 231) HOT_ADD4(232, 233, 234, 235) HOT_ADD4(236, 237, 238, 239)
+#define HOT_ADDS_D HOT_ADD4(240, 241, 242, 243) HOT_ADD4(244, 245, 246, 247) HOT_ADD4(248, 249, 250, 251) HOT_ADD4(252, 253, 254, 255)
+static_assert(kHB == 64 && kSlots == 8, "the adder loop takes 64-occurrence blocks in an 8-slot ring");
+static_assert(64 * kRS * sizeof(float) == 0x4400, "the adder loop's slot stride");
+__device__ __forceinline__ void hot_adder_full_blocks(float& acc, int32_t base, int32_t nfull, const float* lane_col,
+                                                      const int32_t* ready, int32_t* consumed) {
+  const uint32_t col = (uint32_t)reinterpret_cast<uintptr_t>(lane_col);  // LDS byte addresses
+  const uint32_t rdy = (uint32_t)reinterpret_cast<uintptr_t>(ready);
+  const uint32_t cons = (uint32_t)reinterpret_cast<uintptr_t>(consumed);
+  uint32_t s_t, s_tn, s_exp, s_slot, s_off, s_fa, s_fl, s_c, v_cur, v_nxt, v_fa, v_fl, v_tmp;
+  uint64_t s_ex;
+  __asm__ volatile(
+      // block 0: wait for its flag, then issue steps 0 and 1
+      "s_mov_b32 %[t], 0\n\t"
+      "s_mov_b32 %[exp], %[base]\n\t"
+      "s_and_b32 %[slot], %[exp], 7\n\t"
+      "s_lshl_b32 %[fa], %[slot], 2\n\t"
+      "s_add_u32 %[fa], %[fa], %[rdy]\n\t"
+      "v_mov_b32 %[vfa], %[fa]\n"
+      "HOT_W0_%=:\n\t"
+      "ds_read_b32 %[vfl], %[vfa]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_readfirstlane_b32 %[fl], %[vfl]\n\t"
+      "s_cmp_eq_u32 %[fl], %[exp]\n\t"
+      "s_cbranch_scc1 HOT_R0_%=\n\t"
+      "s_sleep 1\n\t"
+      "s_branch HOT_W0_%=\n"
+      "HOT_R0_%=:\n\t"
+      "s_mul_i32 %[off], %[slot], 0x4400\n\t"
+      "v_add_u32 %[cur], %[off], %[col]\n\t"
+      HOT_RD_A(cur) HOT_RD_B(cur)
+      "HOT_L_%=:\n\t"
+      // the next block (after the last one, this block again: those reads are dropped)
+      "s_add_u32 %[tn], %[t], 1\n\t"
+      "s_cmp_lt_u32 %[tn], %[nfull]\n\t"
+      "s_cselect_b32 %[tn], %[tn], %[t]\n\t"
+      "s_add_u32 %[exp], %[base], %[tn]\n\t"
+      "s_and_b32 %[slot], %[exp], 7\n\t"
+      "s_mul_i32 %[off], %[slot], 0x4400\n\t"
+      "v_add_u32 %[nxt], %[off], %[col]\n\t"
+      "s_lshl_b32 %[fa], %[slot], 2\n\t"
+      "s_add_u32 %[fa], %[fa], %[rdy]\n\t"
+      "v_mov_b32 %[vfa], %[fa]\n\t"
+      // step 0: A in flight or done, B, C younger
+      HOT_RD_C(cur)
+      "s_waitcnt lgkmcnt(8)\n\t"
+      HOT_ADDS_A
+      // step 1: this block's last reads, then its release
+      HOT_RD_D(cur)
+      "s_add_u32 %[c], %[base], %[t]\n\t"
+      "s_add_u32 %[c], %[c], 1\n\t"
+      "v_mov_b32 %[tmp], %[c]\n\t"
+      "s_mov_b64 %[ex], exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "ds_write_b32 %[cons], %[tmp]\n\t"
+      "s_mov_b64 exec, %[ex]\n\t"
+      "s_waitcnt lgkmcnt(9)\n\t"
+      HOT_ADDS_B
+      // step 2: the next block's flag and its step 0
+      "ds_read_b32 %[vfl], %[vfa]\n\t"
+      HOT_RD_A(nxt)
+      "s_waitcnt lgkmcnt(10)\n\t"
+      HOT_ADDS_C
+      // step 3: the next block's step 1
+      HOT_RD_B(nxt)
+      "s_waitcnt lgkmcnt(10)\n\t"
+      HOT_ADDS_D
+      "s_add_u32 %[t], %[t], 1\n\t"
+      "s_cmp_ge_u32 %[t], %[nfull]\n\t"
+      "s_cbranch_scc1 HOT_D_%=\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_readfirstlane_b32 %[fl], %[vfl]\n\t"
+      "v_mov_b32 %[cur], %[nxt]\n\t"
+      "s_cmp_eq_u32 %[fl], %[exp]\n\t"
+      "s_cbranch_scc1 HOT_L_%=\n\t"
+      // the flag was not up when read: drop those reads, wait, read again
+      "s_waitcnt lgkmcnt(0)\n"
+      "HOT_S_%=:\n\t"
+      "s_sleep 1\n\t"
+      "ds_read_b32 %[vfl], %[vfa]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_readfirstlane_b32 %[fl], %[vfl]\n\t"
+      "s_cmp_eq_u32 %[fl], %[exp]\n\t"
+      "s_cbranch_scc0 HOT_S_%=\n\t"
+      HOT_RD_A(cur) HOT_RD_B(cur)
+      "s_branch HOT_L_%=\n"
+      "HOT_D_%=:\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [acc] "+v"(acc), [t] "=&s"(s_t), [tn] "=&s"(s_tn), [exp] "=&s"(s_exp), [slot] "=&s"(s_slot),
+        [off] "=&s"(s_off), [fa] "=&s"(s_fa), [fl] "=&s"(s_fl), [c] "=&s"(s_c), [ex] "=&s"(s_ex),
+        [cur] "=&v"(v_cur), [nxt] "=&v"(v_nxt), [vfa] "=&v"(v_fa), [vfl] "=&v"(v_fl), [tmp] "=&v"(v_tmp)
+      : [base] "s"(base), [nfull] "s"(nfull), [rdy] "s"(rdy), [col] "v"(col), [cons] "v"(cons)
+      : "memory", "scc",
+        "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204",
+        "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217",
+        "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230",
+        "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243",
+        "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
+}
+#undef HOT_RD
+#undef HOT_RD_A
+#undef HOT_RD_B
+#undef HOT_RD_C
+#undef HOT_RD_D
+#undef HOT_ADD
+#undef HOT_ADD4
+#undef HOT_ADDS_A
+#undef HOT_ADDS_B
+#undef HOT_ADDS_C
+#undef HOT_ADDS_D
+
 // Hot segments (first phase of the apply kernel).  A block (7 waves) takes
 // (segment, 64-column slice) items from a global counter until none is left.  Wave kAdder is the adder (the only wave on its
 // SIMD when the waves are placed round-robin): lane j owns column j of the
@@ -409,81 +543,14 @@ __device__ __forceinline__ void hot_phase(HotLds& sm, float* const* __restrict__
     const int64_t r = (int64_t)(key & row_mask);
     const int32_t nblk = (end - beg + kHB - 1) / kHB;
     if (wave == kAdder) {
-      // The adds run as one stream over the full blocks, 16 values (four
-      // 16-byte LDS reads) per step, with the reads issued three steps
-      // ahead: twelve reads in flight (lgkmcnt counts up to 15).  Measured
-      // on one wave, wider steps keep the adder closest to its add rate.
-      constexpr int kStep = 16, kAhead = 3, kSteps = kHB / kStep, kBufs = 4, kReads = kStep / 4;
       const int32_t len = end - beg;
       const int32_t nfull = len / kHB;
       float acc = 0.f;
-      float v[kBufs][kStep];
-      // occurrences kStep * st .. + kStep - 1 of this lane's column
-      auto step_load = [&](int32_t t, int st, float* dst) {
-        const float* p = &ring[(base + t) & (kSlots - 1)][lane * kRS + st * kStep];
-#pragma unroll
-        for (int q = 0; q < kStep; q += 4) {
-          const float4 a = *reinterpret_cast<const float4*>(p + q);
-          dst[q] = a.x;
-          dst[q + 1] = a.y;
-          dst[q + 2] = a.z;
-          dst[q + 3] = a.w;
-        }
-      };
-      auto wait_ready = [&](int32_t t) {
-        while (lds_load(&ready[(base + t) & (kSlots - 1)]) != base + t) __builtin_amdgcn_s_sleep(1);
-        compiler_fence();
-      };
-      // The next block's flag is read with a plain LDS load just before its
-      // first data reads and checked at the end of this block.  One wave's
-      // LDS accesses execute in order and a loader writes its flag only
-      // after its data writes have completed, so a flag that shows the block
-      // proves the data reads after it saw the data; otherwise (rare) those
-      // reads are repeated once the flag is up.  Plain accesses keep the
-      // compiler's waits exact (an atomic or a loop-carried use would drain
-      // every read in flight).
-      auto flag = [&](int32_t t) { return ready[(base + t) & (kSlots - 1)]; };
-      if (nfull > 0) {
-        wait_ready(0);
-#pragma unroll
-        for (int st = 0; st < kAhead; ++st) step_load(0, st, v[st]);
-      }
-      for (int32_t t = 0; t < nfull; ++t) {
-        const bool more = t + 1 < nfull;
-        const int32_t tn = more ? t + 1 : t;
-        int32_t fl = base + tn;
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-          // reads kAhead steps ahead, then this step's adds; the scheduling
-          // barrier keeps the compiler from hoisting every read to the top
-          if (st + kAhead == kSteps) {
-            compiler_fence();
-            fl = flag(tn);
-            compiler_fence();
-          }
-          if (st + kAhead < kSteps)
-            step_load(t, st + kAhead, v[(st + kAhead) & (kBufs - 1)]);
-          else
-            step_load(tn, st + kAhead - kSteps, v[(st + kAhead) & (kBufs - 1)]);
-          // this step's values were read kAhead steps ago: the kAhead * kReads
-          // younger reads (and at most one flag access) may still be in flight
-          __builtin_amdgcn_s_waitcnt(0xc07f & ~0x0f00 | ((kAhead * kReads) << 8));
-#pragma unroll
-          for (int o = 0; o < kStep; ++o) acc = acc + v[st & (kBufs - 1)][o];
-          __asm__ volatile("" : "+v"(acc));  // this step's adds stay in this step
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        compiler_fence();
-        if (lane == 0) consumed = base + t + 1;
-        if (more && fl != base + t + 1) {  // the next block's first reads came too early
-          wait_ready(t + 1);
-#pragma unroll
-          for (int st = 0; st < kAhead; ++st) step_load(t + 1, st, v[st]);
-        }
-      }
+      if (nfull > 0) hot_adder_full_blocks(acc, base, nfull, &ring[0][lane * kRS], ready, &consumed);
       if (nfull * kHB < len) {  // the last, partial block
         const int32_t t = nfull;
-        wait_ready(t);
+        while (lds_load(&ready[(base + t) & (kSlots - 1)]) != base + t) __builtin_amdgcn_s_sleep(1);
+        compiler_fence();
         const float* col = &ring[(base + t) & (kSlots - 1)][lane * kRS];
         for (int o = 0; o < len - nfull * kHB; ++o) acc = acc + col[o];
         compiler_fence();
