@@ -32,11 +32,9 @@ namespace dlrm {
 namespace {
 
 constexpr int RT = 256;                // threads per sort block
-constexpr int RITEMS = 16;             // keys per thread per tile
-constexpr int RTILE = RT * RITEMS;     // 4096 keys per tile
-constexpr int kMaxBuckets = 512;       // radix digits of at most 9 bits
-constexpr int SCAN_ITEMS = 8;
-constexpr int SCAN_TILE = 256 * SCAN_ITEMS;
+constexpr int ITEMS = 16;              // keys per thread per tile
+constexpr int TILE = RT * ITEMS;       // 4096 positions per tile
+constexpr int kMaxDigits = 512;        // buckets of a digit of at most 9 bits
 constexpr int kHot = 128;              // occurrences from which a segment is "hot"
 constexpr int kHB = 64;                // occurrences per LDS ring slot
 constexpr int kSlots = 8;              // ring slots
@@ -71,111 +69,17 @@ __global__ __launch_bounds__(256) void build_keys_kernel(const int64_t* __restri
 }
 
 // ------------------------------------------------------------------ radix sort
-
-template <int DB>  // digit bits (8 or 9): 2^DB buckets
-__global__ __launch_bounds__(RT) void radix_hist_kernel(const uint32_t* __restrict__ keys, int n, int shift,
-                                                        uint32_t* __restrict__ hist, int nblocks) {
-  constexpr int NB = 1 << DB, PER = NB / RT;  // buckets, buckets per thread
-  __shared__ uint32_t cnt[NB];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) cnt[threadIdx.x + q * RT] = 0;
-  __syncthreads();
-  const int base = blockIdx.x * RTILE;
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // lanes with equal digits found by DB ballots; the lowest of them adds
-  // the group's count (Zipf keys share digits, so one atomic per group
-  // instead of one per key)
-  uint32_t kv[RITEMS];
-#pragma unroll
-  for (int i = 0; i < RITEMS; ++i) {
-    const int p = base + i * RT + threadIdx.x;
-    kv[i] = p < n ? keys[p] : 0u;
-  }
-#pragma unroll
-  for (int i = 0; i < RITEMS; ++i) {
-    const int p = base + i * RT + threadIdx.x;
-    const bool valid = p < n;
-    const uint32_t digit = (kv[i] >> shift) & (uint32_t)(NB - 1);
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const bool bit = (digit >> b) & 1u;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
-    }
-    if (valid && (peers & lt) == 0ull) atomicAdd(&cnt[digit], (uint32_t)__popcll(peers));
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int d = threadIdx.x + q * RT;
-    hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
-  }
-}
-
-// Stable scatter: the tile is taken in RITEMS rounds of 256 consecutive keys;
-// inside a round a key's rank is (keys of its digit in earlier rounds) +
-// (in earlier waves of this round) + (in lower lanes of its wave), the last
-// term found by matching the DB digit bits with wave ballots.
-template <int DB>
-__global__ __launch_bounds__(RT) void radix_scatter_kernel(const uint32_t* __restrict__ kin,
-                                                           const int32_t* __restrict__ vin,
-                                                           uint32_t* __restrict__ kout, int32_t* __restrict__ vout,
-                                                           int n, int shift, const uint32_t* __restrict__ offs,
-                                                           int nblocks) {
-  constexpr int NB = 1 << DB, PER = NB / RT;
-  __shared__ uint32_t run[NB];
-  __shared__ uint32_t wcnt[4][NB];
-  __shared__ uint32_t woff[4][NB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int d = tid + q * RT;
-    run[d] = offs[(int64_t)d * nblocks + blockIdx.x];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) wcnt[w][d] = 0;
-  }
-  __syncthreads();
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = 0; r < RITEMS; ++r) {
-    const int p = blockIdx.x * RTILE + r * RT + tid;
-    const bool valid = p < n;
-    const uint32_t key = valid ? kin[p] : 0u;
-    const int32_t val = valid ? vin[p] : 0;
-    const uint32_t digit = (key >> shift) & (uint32_t)(NB - 1);
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const bool bit = (digit >> b) & 1u;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
-    }
-    const uint32_t rank = (uint32_t)__popcll(peers & lt);
-    if (valid && (peers & lt) == 0ull) wcnt[wave][digit] = (uint32_t)__popcll(peers);
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int d = tid + q * RT;
-      uint32_t acc = run[d];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        woff[w][d] = acc;
-        acc += wcnt[w][d];
-        wcnt[w][d] = 0;
-      }
-      run[d] = acc;
-    }
-    __syncthreads();
-    if (valid) {
-      const uint32_t pos = woff[wave][digit] + rank;
-      kout[pos] = key;
-      vout[pos] = val;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ scans
+//
+// A pass is four kernels without any waiting between blocks: the per-tile
+// digit counts (tile_hist_kernel, counts[tile][digit]); their sums over
+// chunks of 64 tiles (chunk_sum_kernel); the offsets, each (tile, digit)'s
+// first position = the digit's start (the totals of the digits below it) +
+// the digit's count in earlier chunks + in earlier tiles of its chunk
+// (tile_offset_kernel); and the stable scatter of each tile
+// (scatter_kernel), which ranks its keys with wave ballots and writes them
+// through LDS in digit order, so each digit's keys of a tile leave as one
+// contiguous span.
+constexpr int kChunk = 64;  // tiles per chunk of the offset scan
 
 // block-wide exclusive scan of one value per thread (256 threads); returns
 // the exclusive prefix and writes the block total to *total
@@ -201,147 +105,346 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + x - v;
 }
 
-// input views for the generic scan
-struct ArrayIn {
-  const uint32_t* a;
-  __device__ uint32_t operator()(int64_t i) const { return a[i]; }
-};
-struct HeadIn {  // 1 where a new run of equal keys starts
-  const uint32_t* k;
-  __device__ uint32_t operator()(int64_t i) const { return (i == 0 || k[i] != k[i - 1]) ? 1u : 0u; }
-};
+// Tile t's keys: wave w holds positions w * 1024 + 64 i + lane of the tile
+// (item i), the layout the scatter ranks in.
+__device__ __forceinline__ int tile_pos(int wave, int i, int lane) { return wave * (TILE / 4) + 64 * i + lane; }
 
-template <class In>
-__global__ __launch_bounds__(256) void scan_reduce_kernel(In in, int64_t n, uint32_t* __restrict__ bsum) {
-  __shared__ uint32_t s_wave[4];
-  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+// counts[tile][digit] of one pass (per-wave LDS counters).
+template <int DB>
+__global__ __launch_bounds__(RT) void tile_hist_kernel(const uint32_t* __restrict__ keys, int n, int shift,
+                                                       uint32_t* __restrict__ counts, int tiles) {
+  constexpr int NB = 1 << DB;
+  __shared__ uint32_t cnt[4][NB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4 * NB; i += RT) (&cnt[0][0])[i] = 0u;
+  __syncthreads();
+  const int64_t t0 = (int64_t)blockIdx.x * TILE;
+  const int cnt_n = (int)(n - t0 < TILE ? n - t0 : TILE);
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int q = tile_pos(wave, i, lane);
+    key[i] = q < cnt_n ? keys[t0 + q] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i)
+    if (tile_pos(wave, i, lane) < cnt_n) atomicAdd(&cnt[wave][(key[i] >> shift) & (uint32_t)(NB - 1)], 1u);
+  __syncthreads();
+  for (int dg = tid; dg < NB; dg += RT)
+    counts[(int64_t)blockIdx.x * NB + dg] = cnt[0][dg] + cnt[1][dg] + cnt[2][dg] + cnt[3][dg];
+}
+
+// sums[chunk][digit] = the digit's count over the chunk's tiles: block
+// (chunk, 64-digit group), lane = digit, wave w takes 16 of the 64 tiles.
+template <int DB>
+__global__ __launch_bounds__(RT) void chunk_sum_kernel(const uint32_t* __restrict__ counts, int tiles,
+                                                       uint32_t* __restrict__ sums) {
+  constexpr int NB = 1 << DB;
+  __shared__ uint32_t part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int dg = blockIdx.y * 64 + lane;
+  const int t0 = blockIdx.x * kChunk + wave * (kChunk / 4);
+  uint32_t v[kChunk / 4];
+#pragma unroll
+  for (int i = 0; i < kChunk / 4; ++i) v[i] = t0 + i < tiles ? counts[(int64_t)(t0 + i) * NB + dg] : 0u;
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i)
-    if (base + i < n) s += in(base + i);
-  uint32_t total;
-  block_exclusive_scan(s, s_wave, &total);
-  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
-}
-
-// single block: exclusive scan of bsum[0..nb) in place, total to *total_out
-__global__ __launch_bounds__(256) void scan_top_kernel(uint32_t* __restrict__ bsum, int nb,
-                                                       uint32_t* __restrict__ total_out) {
-  __shared__ uint32_t s_wave[4];
-  __shared__ uint32_t carry;
-  if (threadIdx.x == 0) carry = 0;
+  for (int i = 0; i < kChunk / 4; ++i) s += v[i];
+  part[wave][lane] = s;
   __syncthreads();
-  for (int base = 0; base < nb; base += 256) {
-    const int i = base + threadIdx.x;
-    const uint32_t v = i < nb ? bsum[i] : 0u;
-    uint32_t total;
-    const uint32_t ex = block_exclusive_scan(v, s_wave, &total);
-    const uint32_t c = carry;
-    if (i < nb) bsum[i] = c + ex;
-    __syncthreads();
-    if (threadIdx.x == 0) carry = c + total;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0 && total_out) *total_out = carry;
+  if (wave == 0) sums[(int64_t)blockIdx.x * NB + dg] = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
 }
 
-// out[i] = exclusive prefix (array mode)
-__global__ __launch_bounds__(256) void scan_apply_array_kernel(const uint32_t* __restrict__ in, int64_t n,
-                                                               const uint32_t* __restrict__ bsum,
-                                                               uint32_t* __restrict__ out) {
-  __shared__ uint32_t s_wave[4];
-  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
-  uint32_t v[SCAN_ITEMS], s = 0;
+// sum of col[0], col[stride], ..., col[(rows - 1) stride], eight loads in flight
+__device__ __forceinline__ uint32_t column_sum(const uint32_t* __restrict__ col, int64_t stride, int rows) {
+  uint32_t t = 0;
+  for (int r0 = 0; r0 < rows; r0 += 8) {
+    uint32_t v[8];
 #pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    v[i] = (base + i < n) ? in[base + i] : 0u;
-    s += v[i];
+    for (int u = 0; u < 8; ++u) v[u] = r0 + u < rows ? col[(int64_t)(r0 + u) * stride] : 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t += v[u];
+  }
+  return t;
+}
+
+// offsets[tile][digit] for the tiles of chunk blockIdx.x and the digits of
+// group blockIdx.y: the digit totals (all chunk sums: every block redoes
+// the sums and their exclusive scan over digits), the digit's count in
+// earlier chunks, then in earlier tiles of the chunk (wave w: tiles
+// 16 w .. 16 w + 15, after the three waves before it).
+template <int DB>
+__global__ __launch_bounds__(RT) void tile_offset_kernel(const uint32_t* __restrict__ counts,
+                                                         const uint32_t* __restrict__ sums, int tiles,
+                                                         uint32_t* __restrict__ offsets) {
+  constexpr int NB = 1 << DB, DPT = NB / RT;
+  __shared__ uint32_t s_wave[4];
+  __shared__ uint32_t dstart[NB];
+  __shared__ uint32_t part[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunks = (tiles + kChunk - 1) / kChunk;
+  const int chunk = blockIdx.x;
+  // digit totals and starts (thread: digits DPT tid .. DPT tid + DPT - 1)
+  uint32_t tot[DPT];
+  uint32_t tsum = 0;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    tot[j] = column_sum(sums + tid * DPT + j, NB, chunks);
+    tsum += tot[j];
   }
   uint32_t total;
-  uint32_t run = bsum[blockIdx.x] + block_exclusive_scan(s, s_wave, &total);
+  uint32_t run = block_exclusive_scan(tsum, s_wave, &total);
 #pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    if (base + i < n) out[base + i] = run;
-    run += v[i];
+  for (int j = 0; j < DPT; ++j) {
+    dstart[tid * DPT + j] = run;
+    run += tot[j];
+  }
+  __syncthreads();
+  const int dg = blockIdx.y * 64 + lane;
+  uint32_t base = dstart[dg] + column_sum(sums + dg, NB, chunk);
+  const int t0 = chunk * kChunk + wave * (kChunk / 4);
+  uint32_t v[kChunk / 4];
+#pragma unroll
+  for (int i = 0; i < kChunk / 4; ++i) v[i] = t0 + i < tiles ? counts[(int64_t)(t0 + i) * NB + dg] : 0u;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kChunk / 4; ++i) s += v[i];
+  part[wave][lane] = s;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) base += part[w][lane];
+#pragma unroll
+  for (int i = 0; i < kChunk / 4; ++i) {
+    if (t0 + i < tiles) offsets[(int64_t)(t0 + i) * NB + dg] = base;
+    base += v[i];
   }
 }
 
-// seg_start[run id] = position of each run head; seg_start[U] = n
-__global__ __launch_bounds__(256) void scan_apply_heads_kernel(const uint32_t* __restrict__ keys, int64_t n,
-                                                               const uint32_t* __restrict__ bsum,
-                                                               int32_t* __restrict__ seg_start,
-                                                               uint32_t* __restrict__ seg_key,
-                                                               const uint32_t* __restrict__ nseg) {
+// One pass: stable scatter of tile blockIdx.x by the digit at `shift`.  The
+// rank of a key is (its digit's count in earlier waves) + (in earlier items
+// of its wave) + (in lower lanes of its item), the last from DB ballots.
+template <int DB>
+__global__ __launch_bounds__(RT) void scatter_kernel(const uint32_t* __restrict__ kin, const int32_t* __restrict__ vin,
+                                                     uint32_t* __restrict__ kout, int32_t* __restrict__ vout, int n,
+                                                     int shift, const uint32_t* __restrict__ offsets, int tiles) {
+  constexpr int NB = 1 << DB, DPT = NB / RT;  // digits per thread (contiguous)
+  __shared__ uint32_t wcnt[4][NB];           // per-wave counts, then per-wave offsets
+  __shared__ uint32_t lstart[NB];            // tile-local start of each digit
+  __shared__ uint32_t gbase[NB];             // global position of a digit's span minus its tile-local start
+  __shared__ uint32_t lkeys[TILE];
+  __shared__ int32_t lvals[TILE];
   __shared__ uint32_t s_wave[4];
-  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
-  HeadIn h{keys};
-  uint32_t v[SCAN_ITEMS], s = 0;
-#pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    v[i] = (base + i < n) ? h(base + i) : 0u;
-    s += v[i];
-  }
-  uint32_t total;
-  uint32_t run = bsum[blockIdx.x] + block_exclusive_scan(s, s_wave, &total);
-#pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    if (v[i]) {
-      seg_start[run] = (int32_t)(base + i);
-      seg_key[run] = keys[base + i];
-    }
-    run += v[i];
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) seg_start[*nseg] = (int32_t)n;
-}
-
-__global__ __launch_bounds__(256) void find_hot_kernel(const int32_t* __restrict__ seg_start,
-                                                       const uint32_t* __restrict__ nseg, int32_t* __restrict__ hot,
-                                                       uint32_t* __restrict__ nhot) {
-  const uint32_t U = *nseg;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x;
+  for (int i = tid; i < 4 * NB; i += RT) (&wcnt[0][0])[i] = 0u;
+  __syncthreads();
+  const int64_t t0 = (int64_t)tile * TILE;
+  const int cnt = (int)(n - t0 < TILE ? n - t0 : TILE);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const uint32_t stride = gridDim.x * blockDim.x;
-  // every lane of a wave runs the same number of iterations (ballots below)
-  for (uint32_t s0 = blockIdx.x * blockDim.x; s0 < U; s0 += stride) {
-    const uint32_t s = s0 + threadIdx.x;
-    const bool is_hot = s < U && seg_start[s + 1] - seg_start[s] >= kHot;
-    const uint64_t m = __ballot(is_hot);
-    if (m == 0ull) continue;
-    uint32_t at = 0;
-    if (lane == __ffsll((long long)m) - 1) at = atomicAdd(nhot, (uint32_t)__popcll(m));
-    at = __shfl(at, __ffsll((long long)m) - 1, 64);
-    if (is_hot) hot[at + __popcll(m & below)] = (int32_t)s;
+  uint32_t key[ITEMS];
+  int32_t val[ITEMS];
+  uint32_t rank[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int q = tile_pos(wave, i, lane);
+    key[i] = q < cnt ? kin[t0 + q] : 0u;
+    val[i] = q < cnt ? vin[t0 + q] : 0;
   }
-}
-
-// One block: hot segments regrouped by floor(log2(length)), longest group
-// first, so the longest serial chains start first (order inside a group is
-// arbitrary; every segment's result is independent of it).
-__global__ __launch_bounds__(256) void order_hot_kernel(const int32_t* __restrict__ seg_start,
-                                                        const int32_t* __restrict__ hot,
-                                                        const uint32_t* __restrict__ nhot,
-                                                        int32_t* __restrict__ ordered) {
-  __shared__ uint32_t cnt[32];
-  const uint32_t n = *nhot;
-  if (threadIdx.x < 32) cnt[threadIdx.x] = 0;
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const int32_t h = hot[i];
-    atomicAdd(&cnt[31 - __clz(seg_start[h + 1] - seg_start[h])], 1u);
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const bool valid = tile_pos(wave, i, lane) < cnt;
+    const uint32_t dg = (key[i] >> shift) & (uint32_t)(NB - 1);
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const bool bit = (dg >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    // every lane reads the count before its group's lowest lane adds to it
+    const uint32_t before = valid ? wcnt[wave][dg] : 0u;
+    rank[i] = before + (uint32_t)__popcll(peers & below);
+    if (valid && (peers & below) == 0ull) wcnt[wave][dg] = before + (uint32_t)__popcll(peers);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  uint32_t tc[DPT];
+  uint32_t tsum = 0;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int dg = tid * DPT + j;
     uint32_t run = 0;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t c = cnt[b];
-      cnt[b] = run;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t c = wcnt[w][dg];
+      wcnt[w][dg] = run;
       run += c;
     }
+    tc[j] = run;
+    tsum += run;
+  }
+  uint32_t total;
+  uint32_t lrun = block_exclusive_scan(tsum, s_wave, &total);
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int dg = tid * DPT + j;
+    lstart[dg] = lrun;
+    gbase[dg] = offsets[(int64_t)tile * NB + dg] - lrun;
+    lrun += tc[j];
   }
   __syncthreads();
-  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const int32_t h = hot[i];
-    ordered[atomicAdd(&cnt[31 - __clz(seg_start[h + 1] - seg_start[h])], 1u)] = h;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    if (tile_pos(wave, i, lane) < cnt) {
+      const uint32_t dg = (key[i] >> shift) & (uint32_t)(NB - 1);
+      const uint32_t lp = lstart[dg] + wcnt[wave][dg] + rank[i];
+      lkeys[lp] = key[i];
+      lvals[lp] = val[i];
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int j = tid; j < cnt; j += RT) {
+    const uint32_t k = lkeys[j];
+    const uint32_t pos = gbase[(k >> shift) & (uint32_t)(NB - 1)] + (uint32_t)j;
+    kout[pos] = k;
+    vout[pos] = lvals[j];
+  }
+}
+
+// ------------------------------------------------------------------ segments
+//
+// Run-length segmentation of the sorted keys, the same three steps: run
+// heads per tile (heads_count_kernel), their exclusive scan over tiles
+// (heads_scan_kernel: the run count to counters[0], seg_start[runs] = n),
+// and seg_start[run] / seg_key[run] at every head (heads_write_kernel).  A
+// head whose key is still there kHot - 1 positions later starts a hot run;
+// its length class floor(log2(length)) follows from probes at 2^j - 1
+// positions after the head (the run is contiguous), and the run joins the
+// list of its class.  The update takes hot runs class by class, longest
+// class first, so the longest serial chains start first.
+constexpr int kHotClassMin = 7;   // 2^7 = kHot
+constexpr int kHotClassMax = 30;  // runs shorter than 2^31
+static_assert((1 << kHotClassMin) == kHot, "hot runs start at class kHotClassMin");
+constexpr int kHotCountBase = 16;  // counters[kHotCountBase + class]: hot runs of each class
+
+// first slot of class c's list: the classes below it hold at most
+// n >> c' + 1 runs each
+__host__ __device__ inline int64_t hot_class_base(int64_t n, int c) {
+  int64_t b = 0;
+  for (int q = kHotClassMin; q < c; ++q) b += (n >> q) + 1;
+  return b;
+}
+
+// head ballots of a tile: item i of wave w is position w * 1024 + 64 i + lane;
+// the key before a position comes from the lane below (lane 0: from lane 63
+// of the item before, or memory for the wave's first position)
+__device__ __forceinline__ void tile_heads(const uint32_t* __restrict__ keys, int n, int64_t t0, int cnt,
+                                           uint32_t (&key)[ITEMS], uint64_t (&head)[ITEMS]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int q = tile_pos(wave, i, lane);
+    key[i] = q < cnt ? keys[t0 + q] : 0u;
+  }
+  const int64_t p0 = t0 + tile_pos(wave, 0, 0);
+  const uint32_t first_prev = (lane == 0 && p0 > 0 && p0 - t0 < cnt) ? keys[p0 - 1] : 0u;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int q = tile_pos(wave, i, lane);
+    const uint32_t up = (uint32_t)__shfl_up((int)key[i], 1, 64);
+    const uint32_t wrap = i > 0 ? (uint32_t)__shfl((int)key[i > 0 ? i - 1 : 0], 63, 64) : first_prev;
+    const uint32_t prev = lane > 0 ? up : wrap;
+    const bool h = q < cnt && (t0 + q == 0 || prev != key[i]);
+    head[i] = __ballot(h);
+  }
+}
+
+__global__ __launch_bounds__(RT) void heads_count_kernel(const uint32_t* __restrict__ keys, int n,
+                                                         uint32_t* __restrict__ tile_runs) {
+  __shared__ uint32_t s_wcnt[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * TILE;
+  const int cnt = (int)(n - t0 < TILE ? n - t0 : TILE);
+  uint32_t key[ITEMS];
+  uint64_t head[ITEMS];
+  tile_heads(keys, n, t0, cnt, key, head);
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) c += (uint32_t)__popcll(head[i]);
+  if (lane == 0) s_wcnt[wave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) tile_runs[blockIdx.x] = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+}
+
+// one block: exclusive scan of the tiles' run counts in place
+__global__ __launch_bounds__(RT) void heads_scan_kernel(uint32_t* __restrict__ tile_runs, int tiles, int n,
+                                                        int32_t* __restrict__ seg_start,
+                                                        uint32_t* __restrict__ counters) {
+  __shared__ uint32_t s_wave[4];
+  uint32_t carry = 0;
+  for (int base = 0; base < tiles; base += RT) {
+    const int i = base + threadIdx.x;
+    const uint32_t v = i < tiles ? tile_runs[i] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_exclusive_scan(v, s_wave, &total);
+    if (i < tiles) tile_runs[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) {
+    counters[0] = carry;
+    seg_start[carry] = n;
+  }
+}
+
+__global__ __launch_bounds__(RT) void heads_write_kernel(const uint32_t* __restrict__ keys, int n,
+                                                         const uint32_t* __restrict__ tile_runs,
+                                                         int32_t* __restrict__ seg_start,
+                                                         uint32_t* __restrict__ seg_key, int32_t* __restrict__ hot,
+                                                         uint32_t* __restrict__ counters) {
+  __shared__ uint32_t s_wcnt[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * TILE;
+  const int cnt = (int)(n - t0 < TILE ? n - t0 : TILE);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t key[ITEMS];
+  uint64_t head[ITEMS];
+  tile_heads(keys, n, t0, cnt, key, head);
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) c += (uint32_t)__popcll(head[i]);
+  if (lane == 0) s_wcnt[wave] = c;
+  __syncthreads();
+  uint32_t run = tile_runs[blockIdx.x];
+  for (int w = 0; w < wave; ++w) run += s_wcnt[w];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int64_t p = t0 + tile_pos(wave, i, lane);
+    const bool h = (head[i] >> lane) & 1ull;
+    const uint32_t r = run + (uint32_t)__popcll(head[i] & below);
+    run += (uint32_t)__popcll(head[i]);
+    bool is_hot = false;
+    if (h) {
+      seg_start[r] = (int32_t)p;
+      seg_key[r] = key[i];
+      is_hot = p + kHot - 1 < n && keys[p + kHot - 1] == key[i];
+    }
+    // each hot run's class: len >= 2^j exactly for j <= floor(log2 len), so
+    // the class is kHotClassMin plus the number of matching probes 2^j - 1
+    // positions on (lane j - kHotClassMin - 1 probes j, all at once)
+    uint64_t hm = __ballot(is_hot);
+    while (hm) {
+      const int src = __ffsll((long long)hm) - 1;
+      hm &= hm - 1;
+      const int64_t hp = t0 + tile_pos(wave, i, src);
+      const uint32_t hk = (uint32_t)__shfl((int)key[i], src, 64);
+      const int j = kHotClassMin + 1 + lane;
+      const int64_t q = hp + (1ll << (j < 62 ? j : 62)) - 1;
+      const bool match = j <= kHotClassMax && q < n && keys[q] == hk;
+      const int cls = kHotClassMin + (int)__popcll(__ballot(match));
+      if (lane == src) {
+        const uint32_t at = atomicAdd(&counters[kHotCountBase + cls], 1u);
+        hot[hot_class_base(n, cls) + at] = (int32_t)r;
+      }
+    }
   }
 }
 
@@ -509,12 +612,18 @@ struct HotLds {
   int32_t ready[kSlots];
   int32_t consumed;
   uint32_t s_item;
+  int32_t s_seg;
+  uint32_t cls_first[kHotClassMax + 1];  // first hot run number of each class (classes longest first)
+  uint32_t cls_end[kHotClassMax + 1];
+  uint32_t cls_base[kHotClassMax + 1];   // its list's first slot
+  uint32_t s_items;
 };
 
 __device__ __forceinline__ void hot_phase(HotLds& sm, float* const* __restrict__ tables, int d, int row_bits,
                                           const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ bags,
                                           const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
-                                          const uint32_t* __restrict__ nhot, const float* __restrict__ G,
+                                          const uint32_t* __restrict__ counters, int64_t n,
+                                          const float* __restrict__ G,
                                           int64_t g_ld, int64_t g_col0, float lr,
                                           uint32_t* __restrict__ next_item) {
   auto& ring = sm.ring;
@@ -526,15 +635,36 @@ __device__ __forceinline__ void hot_phase(HotLds& sm, float* const* __restrict__
   if (tid == 0) consumed = 0;
   const uint32_t row_mask = (row_bits >= 32) ? 0xffffffffu : ((1u << row_bits) - 1u);
   const int slices = (d + 63) >> 6;
-  const uint32_t items = *nhot * (uint32_t)slices;
+  // the class table, once per block (the item loop resolves a run number
+  // from LDS)
+  if (tid == 0) {
+    uint32_t first = 0;
+    for (int c = kHotClassMax; c >= kHotClassMin; --c) {
+      const uint32_t k = counters[kHotCountBase + c];
+      sm.cls_first[c] = first;
+      sm.cls_end[c] = first + k;
+      sm.cls_base[c] = (uint32_t)hot_class_base(n, c);
+      first += k;
+    }
+    sm.s_items = first * (uint32_t)slices;
+  }
   int32_t base = 0;  // running block number of this block's first ring use in the current item
   for (;;) {
     __syncthreads();
-    if (tid == 0) s_item = atomicAdd(next_item, 1u);
+    if (tid == 0) {
+      const uint32_t it = atomicAdd(next_item, 1u);
+      s_item = it;
+      if (it < sm.s_items) {
+        const uint32_t run = it / (uint32_t)slices;
+        int c = kHotClassMax;
+        while (c > kHotClassMin && run >= sm.cls_end[c]) --c;
+        sm.s_seg = hot[sm.cls_base[c] + run - sm.cls_first[c]];
+      }
+    }
     __syncthreads();
     const uint32_t item = s_item;
-    if (item >= items) break;
-    const int32_t s = hot[item / slices];
+    if (item >= sm.s_items) break;
+    const int32_t s = sm.s_seg;
     const int col0 = (int)(item % slices) * 64;
     const int cols = min(64, d - col0);
     const int32_t beg = seg_start[s], end = seg_start[s + 1];
@@ -719,10 +849,11 @@ __device__ __forceinline__ void light_phase(float* const* __restrict__ tables, i
 __global__ __launch_bounds__(kApplyThreads) void hot_sgd_kernel(
     float* const* __restrict__ tables, int d, int row_bits, const uint32_t* __restrict__ seg_key,
     const int32_t* __restrict__ bags, const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
-    const uint32_t* __restrict__ nhot, const float* __restrict__ G, int64_t g_ld, int64_t g_col0, float lr,
+    const uint32_t* __restrict__ counters, int64_t n, const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
+    float lr,
     uint32_t* __restrict__ next_item) {
   __shared__ __attribute__((aligned(16))) HotLds sm;
-  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, nhot, G, g_ld, g_col0, lr, next_item);
+  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, counters, n, G, g_ld, g_col0, lr, next_item);
 }
 
 // The short segments alone (many small persistent blocks; the two-stream
@@ -744,11 +875,11 @@ template <int V>
 __global__ __launch_bounds__(kApplyThreads) void sgd_apply_kernel(
     float* const* __restrict__ tables, int d, int g_log2, int row_bits, const uint32_t* __restrict__ seg_key,
     const int32_t* __restrict__ bags, const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
-    const uint32_t* __restrict__ counters, const float* __restrict__ G, int64_t g_ld, int64_t g_col0, float lr,
-    uint32_t* __restrict__ next) {
+    const uint32_t* __restrict__ counters, int64_t n, const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
+    float lr, uint32_t* __restrict__ next) {
   __shared__ __attribute__((aligned(16))) HotLds sm;
-  // counters: [0] segments, [1] hot segments; next: [0] hot item, [1] short-segment chunk
-  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, &counters[1], G, g_ld, g_col0, lr, &next[0]);
+  // counters: [0] segments, hot runs per class; next: [0] hot item, [1] short-segment chunk
+  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, counters, n, G, g_ld, g_col0, lr, &next[0]);
   light_phase<V, 16 / V>(tables, d, g_log2, row_bits, seg_key, bags, seg_start, &counters[0], G, g_ld, g_col0, lr,
                          &next[1]);
 }
@@ -760,9 +891,14 @@ int bits_for(int64_t x) {  // bits needed to hold 0..x
 }
 
 struct SparseLayout {
-  size_t keys[2], vals[2], hist, bsum, seg, seg_key, counters, hot, hot_ordered, bytes;
-  int64_t nblocks, hist_n, scan_nb_hist, scan_nb_keys;
+  size_t keys[2], vals[2], counts, sums, offsets, seg, seg_key, counters, hot, bytes;
+  int64_t tiles;
 };
+
+// counters: [0] segments, [2] next hot item, [3] next short-segment chunk,
+// [kHotCountBase + c] hot runs of class c (cleared on every prepare)
+constexpr int kCounters = 48;
+static_assert(kHotCountBase + kHotClassMax < kCounters, "hot class counters");
 
 void sparse_layout(int64_t nnz, SparseLayout* L) {
   Carver cv(nullptr);
@@ -773,27 +909,23 @@ void sparse_layout(int64_t nnz, SparseLayout* L) {
     return at;
   };
   const int64_t n = nnz > 0 ? nnz : 1;
-  L->nblocks = ceil_div(n, RTILE);
-  L->hist_n = (int64_t)kMaxBuckets * L->nblocks;
-  L->scan_nb_hist = ceil_div(L->hist_n, SCAN_TILE);
-  L->scan_nb_keys = ceil_div(n, SCAN_TILE);
+  L->tiles = ceil_div(n, TILE);
   L->keys[0] = take(4 * (size_t)n);
   L->keys[1] = take(4 * (size_t)n);
   L->vals[0] = take(4 * (size_t)n);
   L->vals[1] = take(4 * (size_t)n);
-  L->hist = take(4 * (size_t)L->hist_n);
-  const int64_t nb = L->scan_nb_hist > L->scan_nb_keys ? L->scan_nb_hist : L->scan_nb_keys;
-  L->bsum = take(4 * (size_t)nb);
+  L->counts = take(4 * (size_t)kMaxDigits * L->tiles);
+  L->sums = take(4 * (size_t)kMaxDigits * ceil_div(L->tiles, kChunk));
+  L->offsets = take(4 * (size_t)kMaxDigits * L->tiles);
   L->seg = take(4 * (size_t)(n + 1));
   L->seg_key = take(4 * (size_t)n);
-  L->counters = take(4 * 16);
-  L->hot = take(4 * (size_t)(n / kHot + 1));
-  L->hot_ordered = take(4 * (size_t)(n / kHot + 1));
+  L->counters = take(4 * (size_t)kCounters);
+  L->hot = take(4 * (size_t)hot_class_base(n, kHotClassMax + 1));
   L->bytes = cv.bytes();
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 }  // namespace
@@ -802,8 +934,8 @@ __global__ void zero_u32_kernel(uint32_t* p, int n) {
 namespace dlrm {
 namespace {
 int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_key, const int32_t* vals,
-                 const int32_t* seg, const int32_t* hot_ordered, uint32_t* counters, const float* G, int64_t g_ld,
-                 int64_t g_col0, float lr, hipStream_t stream, hipStream_t side);
+                 const int32_t* seg, const int32_t* hot, uint32_t* counters, int64_t n, const float* G,
+                 int64_t g_ld, int64_t g_col0, float lr, hipStream_t stream, hipStream_t side);
 }  // namespace
 }  // namespace dlrm
 
@@ -839,13 +971,13 @@ int check_sparse(int32_t K, const int64_t* rows, int64_t B, int64_t nnz, int* ro
 struct SparseBufs {
   uint32_t* keys[2];
   int32_t* vals[2];
-  uint32_t* hist;
-  uint32_t* bsum;
+  uint32_t* counts;
+  uint32_t* sums;
+  uint32_t* offsets;
   int32_t* seg;
   uint32_t* seg_key;
-  uint32_t* counters;  // [0] segments, [1] hot segments, [2] next hot item, [3] next short-segment chunk
+  uint32_t* counters;
   int32_t* hot;
-  int32_t* hot_ordered;
 };
 
 int sparse_bufs(int64_t nnz, void* ws, size_t ws_bytes, SparseLayout* L, SparseBufs* b) {
@@ -857,13 +989,13 @@ int sparse_bufs(int64_t nnz, void* ws, size_t ws_bytes, SparseLayout* L, SparseB
   b->keys[1] = reinterpret_cast<uint32_t*>(w + L->keys[1]);
   b->vals[0] = reinterpret_cast<int32_t*>(w + L->vals[0]);
   b->vals[1] = reinterpret_cast<int32_t*>(w + L->vals[1]);
-  b->hist = reinterpret_cast<uint32_t*>(w + L->hist);
-  b->bsum = reinterpret_cast<uint32_t*>(w + L->bsum);
+  b->counts = reinterpret_cast<uint32_t*>(w + L->counts);
+  b->sums = reinterpret_cast<uint32_t*>(w + L->sums);
+  b->offsets = reinterpret_cast<uint32_t*>(w + L->offsets);
   b->seg = reinterpret_cast<int32_t*>(w + L->seg);
   b->seg_key = reinterpret_cast<uint32_t*>(w + L->seg_key);
   b->counters = reinterpret_cast<uint32_t*>(w + L->counters);
   b->hot = reinterpret_cast<int32_t*>(w + L->hot);
-  b->hot_ordered = reinterpret_cast<int32_t*>(w + L->hot_ordered);
   return DLRM_OK;
 }
 
@@ -897,7 +1029,7 @@ extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const
   const int n = (int)nnz;
   const int64_t KB = (int64_t)K * B;
 
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters, 16);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters, kCounters);
   {
     int kg = 0;  // lanes per bag: the mean bag length rounded up to a power of two, at most 64
     while ((1LL << kg) * KB < nnz && kg < 6) ++kg;
@@ -907,38 +1039,24 @@ extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const
                        row_bits, b.keys[0], b.vals[0]);
   }
   const SortPlan plan = sort_plan(row_bits);
-  const int nblocks = (int)L.nblocks;
-  const int64_t hist_n = ((int64_t)1 << plan.digit_bits) * nblocks;  // digit-major counts
-  const unsigned scan_nb = (unsigned)ceil_div(hist_n, SCAN_TILE);
+  const unsigned tiles = (unsigned)L.tiles;
+  const dim3 chunk_grid((unsigned)ceil_div(L.tiles, kChunk), (unsigned)((1 << plan.digit_bits) / 64));
   int cur = 0;
   for (int pass = 0; pass < plan.passes; ++pass) {
     const int shift = pass * plan.digit_bits;
-    if (plan.digit_bits == 9)
-      hipLaunchKernelGGL(radix_hist_kernel<9>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], n, shift, b.hist,
-                         nblocks);
-    else
-      hipLaunchKernelGGL(radix_hist_kernel<8>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], n, shift, b.hist,
-                         nblocks);
-    hipLaunchKernelGGL((scan_reduce_kernel<ArrayIn>), dim3(scan_nb), dim3(256), 0, stream, ArrayIn{b.hist}, hist_n,
-                       b.bsum);
-    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, b.bsum, (int)scan_nb, nullptr);
-    hipLaunchKernelGGL(scan_apply_array_kernel, dim3(scan_nb), dim3(256), 0, stream, b.hist, hist_n, b.bsum, b.hist);
-    if (plan.digit_bits == 9)
-      hipLaunchKernelGGL(radix_scatter_kernel<9>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], b.vals[cur],
-                         b.keys[cur ^ 1], b.vals[cur ^ 1], n, shift, b.hist, nblocks);
-    else
-      hipLaunchKernelGGL(radix_scatter_kernel<8>, dim3(nblocks), dim3(RT), 0, stream, b.keys[cur], b.vals[cur],
-                         b.keys[cur ^ 1], b.vals[cur ^ 1], n, shift, b.hist, nblocks);
+#define DLRM_PASS(DB)                                                                                                hipLaunchKernelGGL(tile_hist_kernel<DB>, dim3(tiles), dim3(RT), 0, stream, b.keys[cur], n, shift, b.counts,                          (int)tiles);                                                                                    hipLaunchKernelGGL(chunk_sum_kernel<DB>, chunk_grid, dim3(RT), 0, stream, b.counts, (int)tiles, b.sums);           hipLaunchKernelGGL(tile_offset_kernel<DB>, chunk_grid, dim3(RT), 0, stream, b.counts, b.sums, (int)tiles,                             b.offsets);                                                                                     hipLaunchKernelGGL(scatter_kernel<DB>, dim3(tiles), dim3(RT), 0, stream, b.keys[cur], b.vals[cur],                                   b.keys[cur ^ 1], b.vals[cur ^ 1], n, shift, b.offsets, (int)tiles)
+    if (plan.digit_bits == 9) {
+      DLRM_PASS(9);
+    } else {
+      DLRM_PASS(8);
+    }
+#undef DLRM_PASS
     cur ^= 1;
   }
-  // run-length segmentation of the sorted keys
-  hipLaunchKernelGGL((scan_reduce_kernel<HeadIn>), dim3((unsigned)L.scan_nb_keys), dim3(256), 0, stream,
-                     HeadIn{b.keys[cur]}, (int64_t)n, b.bsum);
-  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, stream, b.bsum, (int)L.scan_nb_keys, &b.counters[0]);
-  hipLaunchKernelGGL(scan_apply_heads_kernel, dim3((unsigned)L.scan_nb_keys), dim3(256), 0, stream, b.keys[cur],
-                     (int64_t)n, b.bsum, b.seg, b.seg_key, &b.counters[0]);
-  hipLaunchKernelGGL(find_hot_kernel, dim3(1024), dim3(256), 0, stream, b.seg, &b.counters[0], b.hot, &b.counters[1]);
-  hipLaunchKernelGGL(order_hot_kernel, dim3(1), dim3(256), 0, stream, b.seg, b.hot, &b.counters[1], b.hot_ordered);
+  hipLaunchKernelGGL(heads_count_kernel, dim3(tiles), dim3(RT), 0, stream, b.keys[cur], n, b.counts);
+  hipLaunchKernelGGL(heads_scan_kernel, dim3(1), dim3(RT), 0, stream, b.counts, (int)tiles, n, b.seg, b.counters);
+  hipLaunchKernelGGL(heads_write_kernel, dim3(tiles), dim3(RT), 0, stream, b.keys[cur], n, b.counts, b.seg,
+                     b.seg_key, b.hot, b.counters);
   return launch_status() != DLRM_OK ? DLRM_E_HIP : DLRM_OK;
 }
 
@@ -967,7 +1085,7 @@ extern "C" int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters + 2, 2);
   }
   if (launch_status() != DLRM_OK) return DLRM_E_HIP;
-  return sgd_segments(tables, d, row_bits, b.seg_key, b.vals[cur], b.seg, b.hot_ordered, b.counters, G, g_ld, g_col0,
+  return sgd_segments(tables, d, row_bits, b.seg_key, b.vals[cur], b.seg, b.hot, b.counters, nnz, G, g_ld, g_col0,
                       lr, stream, side);
 }
 
@@ -1038,8 +1156,8 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
 namespace dlrm {
 namespace {
 int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_key, const int32_t* vals,
-                 const int32_t* seg, const int32_t* hot_ordered, uint32_t* counters, const float* G, int64_t g_ld,
-                 int64_t g_col0, float lr, hipStream_t stream, hipStream_t side) {
+                 const int32_t* seg, const int32_t* hot, uint32_t* counters, int64_t n, const float* G,
+                 int64_t g_ld, int64_t g_col0, float lr, hipStream_t stream, hipStream_t side) {
   // short segments: half as many lanes as float4 columns (two float4 per
   // lane), at most 64
   const int d4 = d / 4;
@@ -1051,7 +1169,7 @@ int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_
   if (side) {
     // long segments on `stream`, short ones on `side` at the same time
     hipLaunchKernelGGL(hot_sgd_kernel, cus, apply_block, 0, stream, tables, d, row_bits, seg_key, vals, seg,
-                       hot_ordered, counters + 1, G, g_ld, g_col0, lr, counters + 2);
+                       hot, counters, n, G, g_ld, g_col0, lr, counters + 2);
     if (launch_status() != DLRM_OK) return DLRM_E_HIP;
     const dim3 grid(kLightBlocks), block(256);
 #define DLRM_LIGHT(VV)                                                                                            \
@@ -1065,7 +1183,7 @@ int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_
   }
 #define DLRM_APPLY(VV)                                                                                          \
   hipLaunchKernelGGL((sgd_apply_kernel<VV>), cus, apply_block, 0, stream, tables, d, g_log2, row_bits, seg_key, \
-                     vals, seg, hot_ordered, counters, G, g_ld, g_col0, lr, counters + 2)
+                     vals, seg, hot, counters, n, G, g_ld, g_col0, lr, counters + 2)
   if (V == 1) DLRM_APPLY(1);
   else if (V == 2) DLRM_APPLY(2);
   else DLRM_APPLY(4);

@@ -352,7 +352,7 @@ int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_t d, const 
  * library: each GPU the library runs on holds one until the process ends.
  * The call allocates nothing (no hipMalloc, no hipFree).  Arguments, limits
  * and results as dlrm_embbag_bwd_sgd (bit for bit the same table rows);
- * nnz needing more scratch than the array holds (about 11 million lookups)
+ * nnz needing more scratch than the array holds (about 10.7 million lookups)
  * returns DLRM_E_WORKSPACE before anything is enqueued.  Every call on one
  * GPU shares that GPU's array and leaves its contents behind: calls that
  * overlap on one GPU (on different streams, or from different threads
