@@ -752,13 +752,19 @@ __device__ __forceinline__ void hot_phase(HotLds& sm, float* const* __restrict__
   }
 }
 
-// Short segments (per wave): a group of 2^g_log2 lanes (V float4 each) per
-// segment.  The group loads up to one bag id per lane at once, then walks
-// the bags in order with U gradient rows in flight, broadcasting each bag id
-// from its lane.  Waves take chunks of kLightChunk segments per group from a
-// shared counter, so waves that start early and late share the work as they
-// come.
-constexpr int kLightChunk = 16;
+// Short segments (per wave).  A wave takes 64 consecutive segments from a
+// shared counter (waves that start early and late share the work as they
+// come) and loads what every one of them needs first at once, one segment
+// per lane: its start, end and key, then the bag of its first occurrence.
+// A group of 2^g_log2 lanes (V float4 of a row each) then takes its share
+// of the 64 segments kLightBatch at a time: the table rows and the first
+// gradient rows of the batch are in flight together (most short segments
+// have one occurrence: that is all they need), then each segment's further
+// occurrences follow in order, up to one bag id per lane loaded at once and
+// U gradient rows in flight, each bag id broadcast from its lane.  (Batches
+// of 2 and 4 segments measured slower on the training workload: the
+// registers they hold cut the waves per SIMD from 7 to 3.)
+constexpr int kLightBatch = 1;
 template <int V, int U>
 __device__ __forceinline__ void light_phase(float* const* __restrict__ tables, int d, int g_log2, int row_bits,
                                             const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ bags,
@@ -771,73 +777,104 @@ __device__ __forceinline__ void light_phase(float* const* __restrict__ tables, i
   const int gl = lane & (GL - 1);
   const int wgroups = 64 >> g_log2;  // groups per wave
   const int grp = lane >> g_log2;
+  const int per_group = 64 / wgroups;  // segments of a chunk per group
   const int d4 = d >> 2;
   const uint32_t nsegs = *nseg;
-  const uint32_t per_wave = (uint32_t)(wgroups * kLightChunk);
   for (;;) {
     uint32_t c0 = 0;
-    if (lane == 0) c0 = atomicAdd(next, per_wave);
+    if (lane == 0) c0 = atomicAdd(next, 64u);
     c0 = (uint32_t)__shfl((int)c0, 0, 64);
     if (c0 >= nsegs) break;  // whole wave
-    for (int i = 0; i < kLightChunk; ++i) {
-      const uint32_t s = c0 + (uint32_t)(i * wgroups + grp);
-      if (s >= nsegs) break;  // whole group (later segments of the chunk are past the end too)
-      const int32_t beg = seg_start[s], end = seg_start[s + 1];
-      const uint32_t key = seg_key[s];
-      if (end - beg >= kHot) continue;
-      const int k = (int)(key >> row_bits);
-      const int64_t r = (int64_t)(key & row_mask);
-      float4* trow = reinterpret_cast<float4*>(tables[k] + r * d);
-      float4 tv[V];
+    // lane i: segment c0 + i
+    const uint32_t ms = c0 + (uint32_t)lane;
+    const bool mvalid = ms < nsegs;
+    const int32_t mbeg = mvalid ? seg_start[ms] : 0;
+    const int32_t mend = mvalid ? seg_start[ms + 1] : 0;
+    const uint32_t mkey = mvalid ? seg_key[ms] : 0u;
+    const bool mlight = mvalid && mend - mbeg < kHot;
+    const int32_t mbag0 = mlight ? bags[mbeg] : 0;
+    for (int r0 = 0; r0 < per_group; r0 += kLightBatch) {
+      // the batch: segments grp + (r0 + j) * wgroups of the chunk
+      int32_t beg[kLightBatch], len[kLightBatch];
+      float4* trow[kLightBatch];
+      const float* gbase[kLightBatch];
+      float4 tv[kLightBatch][V], g0[kLightBatch][V];
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const int c4 = gl + j * GL;
-        tv[j] = c4 < d4 ? trow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < kLightBatch; ++j) {
+        const int src = grp + (r0 + j) * wgroups;
+        const bool in = r0 + j < per_group;
+        const int sl = in ? src : 0;
+        beg[j] = __shfl(mbeg, sl, 64);
+        const int32_t e = __shfl(mend, sl, 64);
+        const uint32_t key = (uint32_t)__shfl((int)mkey, sl, 64);
+        const bool light = in && __shfl((int)mlight, sl, 64) != 0;
+        const int32_t bag0 = __shfl(mbag0, sl, 64);
+        len[j] = light ? e - beg[j] : 0;
+        const int k = (int)(key >> row_bits);
+        const int64_t r = (int64_t)(key & row_mask);
+        trow[j] = reinterpret_cast<float4*>(tables[light ? k : 0] + r * d);
+        gbase[j] = G + g_col0 + (int64_t)k * d;
+        const float4* grow = reinterpret_cast<const float4*>(gbase[j] + (int64_t)bag0 * g_ld);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int c4 = gl + v * GL;
+          const bool ok = light && c4 < d4;
+          tv[j][v] = ok ? trow[j][c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          g0[j][v] = ok ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
-      const float* gbase = G + g_col0 + (int64_t)k * d;
-      float4 acc[V];
 #pragma unroll
-      for (int j = 0; j < V; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int32_t q0 = beg; q0 < end; q0 += GL) {
-        const int m = min(GL, end - q0);
-        const int32_t my_bag = gl < m ? bags[q0 + gl] : 0;
-        for (int u0 = 0; u0 < m; u0 += U) {
-          float4 v[U][V];
+      for (int j = 0; j < kLightBatch; ++j) {
+        if (len[j] == 0) continue;  // whole group
+        float4 acc[V];
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const bool ok = u0 + u < m;
-            const int64_t bag = __shfl(my_bag, ok ? u0 + u : 0, GL);
-            const float4* grow = reinterpret_cast<const float4*>(gbase + bag * g_ld);
+        for (int v = 0; v < V; ++v) {  // the sum starts from +0
+          acc[v].x = 0.f + g0[j][v].x;
+          acc[v].y = 0.f + g0[j][v].y;
+          acc[v].z = 0.f + g0[j][v].z;
+          acc[v].w = 0.f + g0[j][v].w;
+        }
+        for (int32_t q0 = beg[j] + 1; q0 < beg[j] + len[j]; q0 += GL) {
+          const int m = min(GL, beg[j] + len[j] - q0);
+          const int32_t my_bag = gl < m ? bags[q0 + gl] : 0;
+          for (int u0 = 0; u0 < m; u0 += U) {
+            float4 vv[U][V];
 #pragma unroll
-            for (int j = 0; j < V; ++j) {
-              const int c4 = gl + j * GL;
-              v[u][j] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int u = 0; u < U; ++u) {
+              const bool ok = u0 + u < m;
+              const int64_t bag = __shfl(my_bag, ok ? u0 + u : 0, GL);
+              const float4* grow = reinterpret_cast<const float4*>(gbase[j] + bag * g_ld);
+#pragma unroll
+              for (int v = 0; v < V; ++v) {
+                const int c4 = gl + v * GL;
+                vv[u][v] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+              }
             }
-          }
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            if (u0 + u < m) {
+            for (int u = 0; u < U; ++u) {
+              if (u0 + u < m) {
 #pragma unroll
-              for (int j = 0; j < V; ++j) {
-                acc[j].x = acc[j].x + v[u][j].x;
-                acc[j].y = acc[j].y + v[u][j].y;
-                acc[j].z = acc[j].z + v[u][j].z;
-                acc[j].w = acc[j].w + v[u][j].w;
+                for (int v = 0; v < V; ++v) {
+                  acc[v].x = acc[v].x + vv[u][v].x;
+                  acc[v].y = acc[v].y + vv[u][v].y;
+                  acc[v].z = acc[v].z + vv[u][v].z;
+                  acc[v].w = acc[v].w + vv[u][v].w;
+                }
               }
             }
           }
         }
-      }
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const int c4 = gl + j * GL;
-        if (c4 < d4) {
-          float4 o;
-          o.x = __fsub_rn(tv[j].x, __fmul_rn(lr, acc[j].x));
-          o.y = __fsub_rn(tv[j].y, __fmul_rn(lr, acc[j].y));
-          o.z = __fsub_rn(tv[j].z, __fmul_rn(lr, acc[j].z));
-          o.w = __fsub_rn(tv[j].w, __fmul_rn(lr, acc[j].w));
-          trow[c4] = o;
+        for (int v = 0; v < V; ++v) {
+          const int c4 = gl + v * GL;
+          if (c4 < d4) {
+            float4 o;
+            o.x = __fsub_rn(tv[j][v].x, __fmul_rn(lr, acc[v].x));
+            o.y = __fsub_rn(tv[j][v].y, __fmul_rn(lr, acc[v].y));
+            o.z = __fsub_rn(tv[j][v].z, __fmul_rn(lr, acc[v].z));
+            o.w = __fsub_rn(tv[j][v].w, __fmul_rn(lr, acc[v].w));
+            trow[j][c4] = o;
+          }
         }
       }
     }
