@@ -85,26 +85,35 @@ __global__ __launch_bounds__(256) void copy_bf16_kernel(const uint16_t* __restri
 //
 // A three-layer bf16 network K0 (<= 16) -> 512 -> 256 -> 128 with ReLU after
 // the hidden layers (the bottom-MLP shape 13-512-256-128) in one kernel.  A
-// workgroup of four waves (one per SIMD) owns 128 rows, each wave 32 of
-// them, and every activation of a wave's rows stays in its registers: with
-// the W fragment as the first MFMA operand, a lane holds one row and groups
-// of four consecutive output columns, and after bias, ReLU, bf16 rounding
-// and one cross-half lane swap (v_permlane32_swap) each lane holds eight
-// consecutive columns -- exactly the operand layout of the next layer's
-// MFMA (row l % 32, k = 8 * (l / 32) .. +7 of each 16-wide k-step).  The
-// rounding points are those of the layer-by-layer path (input, hidden
-// activations in bf16; fp32 accumulation; fp32 output).
+// workgroup of eight waves (two per SIMD) owns 128 rows: waves w and w + 4
+// share rows 32 w .. 32 w + 31 and split the columns of layers 2 and 3 in
+// halves, so each SIMD runs two independent MFMA chains.  Every activation
+// of a wave's rows stays in registers: with the W fragment as the first
+// MFMA operand, a lane holds one row and groups of four consecutive output
+// columns, and after bias, ReLU, bf16 rounding and one cross-half lane swap
+// (v_permlane32_swap) each lane holds eight consecutive columns -- exactly
+// the operand layout of the next layer's MFMA (row l % 32, k = 8 * (l / 32)
+// .. +7 of each 16-wide k-step).  The rounding points are those of the
+// layer-by-layer path (input, hidden activations in bf16; fp32
+// accumulation; fp32 output).
 //
-// The weights of layers 2 and 3 stream through a ring of four 32 KB LDS
-// stages, loaded straight from global memory (global_load_lds_dwordx4,
-// coalesced rows): ten chunks, eight of W2 (64 k x 256 rows) and two of W3
-// (128 k x 128 rows), three in flight ahead of the one being used.  Layer
-// 1's weights (512 x K0) are read as fragments from global memory.  The
-// output rows are written in fp32; for training the bf16 input and hidden
-// activations the backward pass reads are written as well.
+// Layer 1 (K0 -> 512, one k-step) is computed by both waves of a pair, two
+// output blocks (64 columns) at a time, just before the layer-2 k-steps that
+// take them as operands (its weights sit in LDS as MFMA fragments, 16 KB,
+// columns at or past K0 zeroed).  The weights of layers 2 and 3 stream through a
+// ring of four 32 KB LDS stages, loaded straight from global memory
+// (global_load_lds_dwordx4, coalesced rows): ten chunks, eight of W2 (64 k x
+// 256 rows) and two of W3 (128 k x 128 rows), three in flight ahead of the
+// one being used.  The two halves of layer 2's output meet in the two
+// stages layer 2 leaves free (16 KB per 32 rows), so that each wave has all
+// 256 k of layer 3.  The output rows are written in fp32; for training the
+// bf16 input and hidden activations the backward pass reads are written as
+// well.
 constexpr int kF3Rows = 128, kF3D1 = 512, kF3D2 = 256, kF3D3 = 128, kF3K0 = 16;
+constexpr int kF3Waves = 8;
 constexpr int kF3Stage = 32768, kF3Ring = 4 * kF3Stage;
-constexpr int kF3Lds = kF3Ring + 4096;  // the ring, then the three bias vectors (2 KB, 1 KB, 512 B)
+constexpr int kF3W1Lds = kF3Ring + 4096;        // W1 fragments (16 KB) after the bias vectors
+constexpr int kF3Lds = kF3W1Lds + kF3D1 * 32;  // the ring, the three bias vectors (2 KB, 1 KB, 512 B), W1
 constexpr int kF3Chunks = 10;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -162,7 +171,7 @@ __device__ __forceinline__ void f3_bias(f32x16_t& acc, const char* b, int col0, 
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mlp3_fused_kernel(
+__global__ __launch_bounds__(64 * kF3Waves) __attribute__((amdgpu_waves_per_eu(2, 2))) void mlp3_fused_kernel(
     const float* __restrict__ in, int64_t in_ld, int K0, int M, const uint16_t* __restrict__ W1, int64_t w1_ld,
     const float* __restrict__ b1, const uint16_t* __restrict__ W2, int64_t w2_ld, const float* __restrict__ b2,
     const uint16_t* __restrict__ W3, int64_t w3_ld, const float* __restrict__ b3, int relu3, float* __restrict__ out,
@@ -170,12 +179,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint16_t* __restrict__ act2) {
   extern __shared__ __attribute__((aligned(1024))) char f3_smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = wave & 3, ch = wave >> 2;  // row group, column half
   const int r32 = lane & 31, half = lane >> 5;
-  const int row = blockIdx.x * kF3Rows + wave * 32 + r32;  // this lane's row (all layers)
+  const int row = blockIdx.x * kF3Rows + rg * 32 + r32;  // this lane's row (all layers)
   const bool row_ok = row < M;
 
   // chunk c of the weight ring into stage c % 4: 32 instructions of 1 KB,
-  // eight per wave; instruction j of wave w fills rows (8w + j) * (64 / cpr) ..
+  // four per wave; instruction j of wave w fills rows (4w + j) * (64 / cpr) ..
   auto issue = [&](int c) {
     char* st = f3_smem + (c & 3) * kF3Stage;
     const int cpr = f3_cpr(c), rpi = 64 / cpr;
@@ -184,9 +194,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int k0 = c < 8 ? c * 64 : (c - 8) * 128;
     const int lrow = lane / cpr, lpc = lane % cpr;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = (wave * 8 + j) * rpi + lrow;
-      lds_dma16_opaque(base + (int64_t)n * ld + k0 + (lpc ^ f3_swz(n, cpr)) * 8, st + (wave * 8 + j) * 1024);
+    for (int j = 0; j < 4; ++j) {
+      const int n = (wave * 4 + j) * rpi + lrow;
+      lds_dma16_opaque(base + (int64_t)n * ld + k0 + (lpc ^ f3_swz(n, cpr)) * 8, st + (wave * 4 + j) * 1024);
     }
   };
   // the B fragments of k-step ks of chunk c for output blocks tn0 .. tn0+TN-1
@@ -200,28 +210,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       fb[t] = *reinterpret_cast<const bf16x8_t*>(st + n * cpr * 16 + (((2 * ks + half) ^ f3_swz(n, cpr)) * 16));
     }
   };
-  // wait until at most `younger` chunks issued after the awaited one are still in flight
+  // wait until at most `younger` chunks issued after the awaited one are
+  // still in flight (four instructions per chunk per wave)
   auto wait_younger = [&](int younger) {
-    if (younger >= 4) wait_vmcnt<32>();
-    else if (younger == 3) wait_vmcnt<24>();
-    else if (younger == 2) wait_vmcnt<16>();
-    else if (younger == 1) wait_vmcnt<8>();
+    if (younger >= 4) wait_vmcnt<16>();
+    else if (younger == 3) wait_vmcnt<12>();
+    else if (younger == 2) wait_vmcnt<8>();
+    else if (younger == 1) wait_vmcnt<4>();
     else wait_vmcnt<0>();
   };
 
-  // bias vectors into LDS first (one 1 KB instruction per wave; lanes past
-  // the end of b3 re-read its start into the padding)
-  {
+  // bias vectors into LDS first (one 1 KB instruction for each of waves 0-3;
+  // lanes past the end of b3 re-read its start into the padding)
+  if (wave < 4) {
     char* ba = f3_smem + kF3Ring;
     const int off = wave * 1024 + lane * 16;
     const float* src = off < 2048 ? b1 + off / 4 : off < 3072 ? b2 + (off - 2048) / 4 : off < 3584 ? b3 + (off - 3072) / 4 : b3;
     lds_dma16_opaque(src, ba + wave * 1024);
   }
-  // ---- operands of layer 1 in registers: this lane's input row (k = 8*(l/32)
-  // .. +7, bf16) and the W1 fragments of the 16 output blocks (rows 32b + l%32,
-  // the same k; columns at or past K0 read as zero).  Branch-free, so that
-  // every load is in flight at once: out-of-range positions re-read an
-  // in-range one and are masked afterwards.
+  // ---- layer 1's operands: this lane's input row (k = 8*(l/32) .. +7, bf16,
+  // in registers) and the W1 fragments of the 16 output blocks in LDS
+  // (fragment (b, h, r): row 32 b + r, k = 8 h .. 8 h + 7; columns at or past
+  // K0 zeroed).  Branch-free, so that every load is in flight at once:
+  // out-of-range positions re-read an in-range one and are masked afterwards.
   float x[8];
   {
     const float* src = in + (int64_t)(row_ok ? row : M - 1) * in_ld;
@@ -231,11 +242,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       x[q] = src[k < K0 ? k : K0 - 1];
     }
   }
-  uint4 w1f[kF3D1 / 32];
-  const int w1k = half * 8 < K0 ? half * 8 : 0;  // an in-range start for lanes whose k is all masked
+  uint4 w1p[2];
 #pragma unroll
-  for (int b = 0; b < kF3D1 / 32; ++b)
-    w1f[b] = *reinterpret_cast<const uint4*>(W1 + (int64_t)(b * 32 + r32) * w1_ld + w1k);
+  for (int i = 0; i < 2; ++i) {
+    const int p = threadIdx.x + i * 64 * kF3Waves;  // fragment: row p / 2, k-half p % 2
+    const int kh = p & 1;
+    w1p[i] = *reinterpret_cast<const uint4*>(W1 + (int64_t)(p >> 1) * w1_ld + (kh * 8 < K0 ? kh * 8 : 0));
+  }
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
   uint32_t win[4];
 #pragma unroll
@@ -245,19 +258,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t hi = k + 1 < K0 ? (uint32_t)f32_to_bf16(x[2 * q + 1]) : 0u;
     win[q] = lo | (hi << 16);
   }
+  uint4* w1s = reinterpret_cast<uint4*>(f3_smem + kF3W1Lds);
 #pragma unroll
-  for (int b = 0; b < kF3D1 / 32; ++b) {
-    uint32_t x[4] = {w1f[b].x, w1f[b].y, w1f[b].z, w1f[b].w};
+  for (int i = 0; i < 2; ++i) {
+    const int p = threadIdx.x + i * 64 * kF3Waves;
+    const int n = p >> 1, kh = p & 1;
+    uint32_t v[4] = {w1p[i].x, w1p[i].y, w1p[i].z, w1p[i].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int k = half * 8 + 2 * q;
-      x[q] = k >= K0 ? 0u : (k + 1 >= K0 ? (x[q] & 0xffffu) : x[q]);
+      const int k = kh * 8 + 2 * q;
+      v[q] = k >= K0 ? 0u : (k + 1 >= K0 ? (v[q] & 0xffffu) : v[q]);
     }
-    w1f[b] = make_uint4(x[0], x[1], x[2], x[3]);
+    w1s[((n >> 5) * 2 + kh) * 32 + (n & 31)] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   // the plain loads and the bias vectors have landed before any chunk is
-  // issued, so no later wait of the compiler's covers a chunk
+  // issued, so no later wait of the compiler's covers a chunk; the W1
+  // fragments are in LDS for every wave after the barrier
   wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   compiler_fence();
   issue(0);
@@ -267,52 +285,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const char* bias1 = f3_smem + kF3Ring;
   const char* bias2 = bias1 + 2048;
   const char* bias3 = bias1 + 3072;
+  const uint4 ua = make_uint4(win[0], win[1], win[2], win[3]);
+  if (ch == 0 && act0 != nullptr && row_ok && half * 8 < ld0)
+    *reinterpret_cast<uint4*>(act0 + (int64_t)row * ld0 + half * 8) = ua;
+  const bf16x8_t a1 = as_bf16x8(ua);
 
-  // ---- layer 1: K0 -> 512, 16 output blocks of 32 columns, one k-step
-  uint4 h1[32];  // bf16 layer-1 activations in layer-2 operand order (k-step s = h1[s])
-  {
-    const uint4 ua = make_uint4(win[0], win[1], win[2], win[3]);
-    if (act0 != nullptr && row_ok && half * 8 < ld0) *reinterpret_cast<uint4*>(act0 + (int64_t)row * ld0 + half * 8) = ua;
-    const bf16x8_t a1 = as_bf16x8(ua);
-    // four blocks at a time, so that four independent MFMA and packing
-    // chains interleave
+  // ---- layers 1 and 2: chunk c (k-steps 4c .. 4c+3 of layer 2) takes layer
+  // 1's output blocks 2c and 2c+1; this wave's four output blocks of layer 2
+  // are 4 ch .. 4 ch + 3
+  uint4 h1[4];
+  auto layer1 = [&](int c) {
+    f32x16_t acc[2];
 #pragma unroll
-    for (int b0 = 0; b0 < kF3D1 / 32; b0 += 4) {
-      f32x16_t acc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f3_bias(acc[j], bias1, (b0 + j) * 32, half);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w1f[b0 + j]), a1, acc[j], 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f3_pack(acc[j], true, h1[2 * (b0 + j)], h1[2 * (b0 + j) + 1]);
+    for (int j = 0; j < 2; ++j) {
+      f3_bias(acc[j], bias1, (2 * c + j) * 32, half);
+      const uint4 w = w1s[((2 * c + j) * 2 + half) * 32 + r32];
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), a1, acc[j], 0, 0, 0);
     }
-    if (act1 != nullptr && row_ok) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f3_pack(acc[j], true, h1[2 * j], h1[2 * j + 1]);
+    if (ch == 0 && act1 != nullptr && row_ok) {
       uint16_t* g = act1 + (int64_t)row * kF3D1 + 8 * half;
 #pragma unroll
-      for (int b = 0; b < kF3D1 / 32; ++b) {
-        *reinterpret_cast<uint4*>(g + b * 32) = h1[2 * b];
-        *reinterpret_cast<uint4*>(g + b * 32 + 16) = h1[2 * b + 1];
+      for (int j = 0; j < 2; ++j) {
+        *reinterpret_cast<uint4*>(g + (2 * c + j) * 32) = h1[2 * j];
+        *reinterpret_cast<uint4*>(g + (2 * c + j) * 32 + 16) = h1[2 * j + 1];
       }
     }
-  }
-
-  // ---- layer 2: 512 -> 256 (chunks 0 .. 7, four k-steps each, 8 output blocks)
-  f32x16_t acc2[8];
+  };
+  f32x16_t acc2[4];
 #pragma unroll
-  for (int tn = 0; tn < 8; ++tn) f3_bias(acc2[tn], bias2, tn * 32, half);
-  bf16x8_t fb[2][8];
+  for (int t = 0; t < 4; ++t) f3_bias(acc2[t], bias2, (4 * ch + t) * 32, half);
+  bf16x8_t fb[2][4];
   wait_younger(3);  // chunk 0
   __builtin_amdgcn_s_barrier();
   compiler_fence();
-  read_b(0, 0, fb[0], 0, 8);
+  read_b(0, 0, fb[0], 4 * ch, 4);
+  layer1(0);
   int buf = 0;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks < 3) {
-        read_b(c, ks + 1, fb[buf ^ 1], 0, 8);
+        read_b(c, ks + 1, fb[buf ^ 1], 4 * ch, 4);
       } else {
         // hand-over to chunk c+1: after the barrier every wave's reads of
         // chunk c are done, so chunk c+4 can load into its stage.  Layer 3
@@ -322,70 +338,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __builtin_amdgcn_s_barrier();
         compiler_fence();
         if (c + 4 < kF3Chunks) issue(c + 4);
-        if (c < 7) read_b(c + 1, 0, fb[buf ^ 1], 0, 8);
-        else read_b(8, 0, fb[buf ^ 1], 0, 2);
+        if (c < 7) read_b(c + 1, 0, fb[buf ^ 1], 4 * ch, 4);
+        else read_b(8, 0, fb[buf ^ 1], 2 * ch, 2);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8_t a = as_bf16x8(h1[c * 4 + ks]);
+      const bf16x8_t a = as_bf16x8(h1[ks]);
 #pragma unroll
-      for (int tn = 0; tn < 8; ++tn) acc2[tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][tn], a, acc2[tn], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) acc2[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][t], a, acc2[t], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       buf ^= 1;
     }
+    if (c < 7) layer1(c + 1);
   }
-  // layer 2's activations become layer 3's operands
-  uint4 h2[16];
+  // layer 2's activations become layer 3's operands: this wave's k-steps
+  // 8 ch .. 8 ch + 7, the partner's through LDS stages 2 and 3 (free: the
+  // last hand-over barrier came after every read of chunks 6 and 7)
+  uint4 mine[8], other[8];  // k-steps 8 ch .. 8 ch + 7, and the partner's
 #pragma unroll
-  for (int tn = 0; tn < 8; ++tn) f3_pack(acc2[tn], true, h2[2 * tn], h2[2 * tn + 1]);
+  for (int t = 0; t < 4; ++t) f3_pack(acc2[t], true, mine[2 * t], mine[2 * t + 1]);
+  {
+    uint4* xch = reinterpret_cast<uint4*>(f3_smem + 2 * kF3Stage) + rg * 16 * 64;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xch[(8 * ch + q) * 64 + lane] = mine[q];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) other[q] = xch[(8 * (1 - ch) + q) * 64 + lane];
+  }
   if (act2 != nullptr && row_ok) {
     uint16_t* g = act2 + (int64_t)row * kF3D2 + 8 * half;
 #pragma unroll
-    for (int tn = 0; tn < 8; ++tn) {
-      *reinterpret_cast<uint4*>(g + tn * 32) = h2[2 * tn];
-      *reinterpret_cast<uint4*>(g + tn * 32 + 16) = h2[2 * tn + 1];
+    for (int t = 0; t < 4; ++t) {
+      *reinterpret_cast<uint4*>(g + (4 * ch + t) * 32) = mine[2 * t];
+      *reinterpret_cast<uint4*>(g + (4 * ch + t) * 32 + 16) = mine[2 * t + 1];
     }
   }
 
-  // ---- layer 3: 256 -> 128 in two halves of 64 columns (chunks 8 and 9
-  // hold k 0-127 and 128-255); each half's fp32 rows are stored while the
-  // next half computes
+  // ---- layer 3: 256 -> 128, this wave's 64 columns (output blocks 2 ch and
+  // 2 ch + 1; chunks 8 and 9 hold k 0-127 and 128-255)
+  f32x16_t acc3[2];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    f32x16_t acc3[2];
+  for (int j = 0; j < 2; ++j) f3_bias(acc3[j], bias3, (2 * ch + j) * 32, half);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) f3_bias(acc3[j], bias3, (2 * hf + j) * 32, half);
+  for (int ks = 0; ks < 16; ++ks) {
+    if (ks < 15) read_b(8 + ((ks + 1) >> 3), (ks + 1) & 7, fb[buf ^ 1], 2 * ch, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8_t a = as_bf16x8((ks < 8) == (ch == 0) ? mine[ks & 7] : other[ks & 7]);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (ks < 15) read_b(8 + ((ks + 1) >> 3), (ks + 1) & 7, fb[buf ^ 1], 2 * hf, 2);
-      else if (hf == 0) read_b(8, 0, fb[buf ^ 1], 2, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8_t a = as_bf16x8(h2[ks]);
+    for (int j = 0; j < 2; ++j) acc3[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], a, acc3[j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    buf ^= 1;
+  }
+  if (row_ok) {
+    float* o = out + (int64_t)row * out_ld + 4 * half;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc3[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], a, acc3[j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      buf ^= 1;
-    }
-    if (row_ok) {
-      float* o = out + (int64_t)row * out_ld + 4 * half;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] = acc3[j][4 * g + q];
-            if (relu3) v[q] = v[q] > 0.f ? v[q] : 0.f;
-          }
-          float* d = o + (2 * hf + j) * 32 + 8 * g;
-          if (vec_out) {
-            *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) d[q] = v[q];
-          }
+        for (int q = 0; q < 4; ++q) {
+          v[q] = acc3[j][4 * g + q];
+          if (relu3) v[q] = v[q] > 0.f ? v[q] : 0.f;
         }
-    }
+        float* d = o + (2 * ch + j) * 32 + 8 * g;
+        if (vec_out) {
+          *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[q] = v[q];
+        }
+      }
   }
 }
 
@@ -656,7 +680,7 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
       uint16_t* a0 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[0]) : nullptr;
       uint16_t* a1 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[1]) : nullptr;
       uint16_t* a2 = save_acts ? reinterpret_cast<uint16_t*>(wsb + lay.act_off[2]) : nullptr;
-      hipLaunchKernelGGL(mlp3_fused_kernel, dim3((unsigned)ceil_div(B, kF3Rows)), dim3(256), kF3Lds, stream,
+      hipLaunchKernelGGL(mlp3_fused_kernel, dim3((unsigned)ceil_div(B, kF3Rows)), dim3(64 * kF3Waves), kF3Lds, stream,
                          static_cast<const float*>(in), in_ld, dims[0], M, static_cast<const uint16_t*>(W[0]),
                          (int64_t)w_ld[0], bias[0], static_cast<const uint16_t*>(W[1]), (int64_t)w_ld[1], bias[1],
                          static_cast<const uint16_t*>(W[2]), (int64_t)w_ld[2], bias[2],
