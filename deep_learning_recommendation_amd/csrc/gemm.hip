@@ -85,7 +85,7 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
 constexpr int fast_waves_per_eu(int WM, int WN) { return WM * WN > 128 * 64 ? 1 : 2; }
 
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S, bool PERSIST, int ILV,
-          bool DELTA = false>
+          bool DELTA = false, bool KA = false, bool KW = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(fast_waves_per_eu(WM, WN)))) void gemm_bf16_fast_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, OutT* __restrict__ C, int64_t ldc, int M, int N, int K, int relu, int tiles_n,
@@ -104,6 +104,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
   // one logical chunk; XOR-ing the chunk with row bits above the rows that
   // share a bank group spreads them over all 64 banks
   auto swz = [](int row) { return CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
+  // k-major operands (KA: A stored [K][M]; KW: W stored [K][N]).  A tile is
+  // then BK rows of k, each BM (BN) values long, loaded as it lies in memory,
+  // and the MFMA fragments (eight consecutive k of one row of C's operand)
+  // come out of LDS through transposing reads: ds_read_b64_tr_b16 gives lane
+  // j of each 16-lane group element j of the 16-wide segment that the group's
+  // lanes address, from the four k-rows they point at (lane s: k-row s / 4,
+  // elements 4 (s % 4) .. +3).  The 16-byte chunks of a k-row are
+  // XOR-swizzled so that the four k-rows of one read fall on distinct banks.
+  constexpr int CPKA = BM / 8, CPKW = BN / 8;       // 16-byte chunks per k-row
+  constexpr int RPKA = 64 / CPKA, RPKW = 64 / CPKW;  // k-rows per 1 KB load instruction
+  auto swzk = [](int krow, int cpk) { return cpk >= 16 ? 4 * (krow & 3) : (cpk == 8 ? 4 * ((krow >> 1) & 1) : 0); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave - (wave / WAVES_N) * WAVES_N;
@@ -124,36 +135,64 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
   if (tile >= end) return;
 
   // this lane's DMA rows: instruction j of wave w fills rows (w*INS + j)*RPI + lane/CPR
+  // (k-major: instruction j fills k-rows (w*INS + j)*RPK + lane/CPK, and
+  // a_c / b_c is the column of the lane's chunk within the tile)
   const int lrow = lane / CPR, lpc = lane % CPR;
   int a_r[A_INS], b_r[B_INS], a_c[A_INS], b_c[B_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
-    a_r[j] = (wave * A_INS + j) * RPI + lrow;
-    a_c[j] = (lpc ^ swz(a_r[j])) * 8;
+    if constexpr (KA) {
+      a_r[j] = (wave * A_INS + j) * RPKA + lane / CPKA;
+      a_c[j] = ((lane % CPKA) ^ swzk(a_r[j], CPKA)) * 8;
+    } else {
+      a_r[j] = (wave * A_INS + j) * RPI + lrow;
+      a_c[j] = (lpc ^ swz(a_r[j])) * 8;
+    }
   }
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
-    b_r[j] = (wave * B_INS + j) * RPI + lrow;
-    b_c[j] = (lpc ^ swz(b_r[j])) * 8;
+    if constexpr (KW) {
+      b_r[j] = (wave * B_INS + j) * RPKW + lane / CPKW;
+      b_c[j] = ((lane % CPKW) ^ swzk(b_r[j], CPKW)) * 8;
+    } else {
+      b_r[j] = (wave * B_INS + j) * RPI + lrow;
+      b_c[j] = (lpc ^ swz(b_r[j])) * 8;
+    }
   }
+  // k-major: columns past M (N) read the last whole chunk of the row (their
+  // results are never stored); k-rows past the end re-read the last one and
+  // are zeroed in LDS
+  const int mlast = ((M + 7) & ~7) - 8, nlast = ((N + 7) & ~7) - 8;
   const uint16_t* a_row[A_INS];
   const uint16_t* b_row[B_INS];
   auto rows_of = [&](int t, const uint16_t** ar, const uint16_t** br) {
     const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) ar[j] = A + (int64_t)min(tm * BM + a_r[j], M - 1) * lda;
+    for (int j = 0; j < A_INS; ++j) {
+      if constexpr (KA) ar[j] = A + min(tm * BM + a_c[j], mlast);
+      else ar[j] = A + (int64_t)min(tm * BM + a_r[j], M - 1) * lda;
+    }
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) br[j] = W + (int64_t)min(tn * BN + b_r[j], N - 1) * ldw;
+    for (int j = 0; j < B_INS; ++j) {
+      if constexpr (KW) br[j] = W + min(tn * BN + b_c[j], nlast);
+      else br[j] = W + (int64_t)min(tn * BN + b_r[j], N - 1) * ldw;
+    }
+  };
+  auto a_src = [&](int k0, int j) -> const uint16_t* {
+    if constexpr (KA) return a_row[j] + (int64_t)min(k0 + a_r[j], kend - 1) * lda;
+    else return a_row[j] + min(k0 + a_c[j], kpad - 8);
+  };
+  auto b_src = [&](int k0, int j) -> const uint16_t* {
+    if constexpr (KW) return b_row[j] + (int64_t)min(k0 + b_r[j], kend - 1) * ldw;
+    else return b_row[j] + min(k0 + b_c[j], kpad - 8);
   };
   auto issue = [&](int kt) {
     char* st = smem + (kt % S) * STAGE;
     const int k0 = kbeg + kt * BK;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j)
-      lds_dma16_opaque(a_row[j] + min(k0 + a_c[j], kpad - 8), st + (wave * A_INS + j) * 1024);
+    for (int j = 0; j < A_INS; ++j) lds_dma16_opaque(a_src(k0, j), st + (wave * A_INS + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j)
-      lds_dma16_opaque(b_row[j] + min(k0 + b_c[j], kpad - 8), st + BM * RB + (wave * B_INS + j) * 1024);
+    for (int j = 0; j < B_INS; ++j) lds_dma16_opaque(b_src(k0, j), st + BM * RB + (wave * B_INS + j) * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -164,50 +203,83 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
     const int valid = kend - (kbeg + kt * BK);
     if (valid >= BK) return;
     char* wst = smem + (kt % S) * STAGE;
-    for (int e = tid; e < (BM + BN) * CPR; e += NWAVES * 64) {
-      const int row = e / CPR, c = e % CPR;
-      if (c * 8 + 8 > valid) {
-        uint16_t* p = reinterpret_cast<uint16_t*>(wst + row * RB + ((c ^ swz(row)) * 16));
+    // k-major operand: whole k-rows valid .. BK-1; otherwise columns
+    // valid .. BK-1 of every row
+    auto zero_rows = [&](char* base, int width) {
+      for (int e = valid * width / 8 + tid; e < BK * width / 8; e += NWAVES * 64)
+        reinterpret_cast<uint4*>(base)[e] = make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto zero_cols = [&](char* base, int rows) {
+      for (int e = tid; e < rows * CPR; e += NWAVES * 64) {
+        const int row = e / CPR, c = e % CPR;
+        if (c * 8 + 8 > valid) {
+          uint16_t* p = reinterpret_cast<uint16_t*>(base + row * RB + ((c ^ swz(row)) * 16));
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          if (c * 8 + x >= valid) p[x] = 0;
+          for (int x = 0; x < 8; ++x)
+            if (c * 8 + x >= valid) p[x] = 0;
+        }
       }
-    }
+    };
+    if constexpr (KA) zero_rows(wst, BM);
+    else zero_cols(wst, BM);
+    if constexpr (KW) zero_rows(wst + BM * RB, BN);
+    else zero_cols(wst + BM * RB, BN);
     __syncthreads();
   };
   // MFMA operands of k-step ks of the tile in stage st, double-buffered in
   // registers: the reads of step ks+1 are in flight during the MFMAs of ks
+  // fragment of rows mb .. mb+31 of a k-major operand (width values per
+  // k-row), k-step ks: two transposing reads of four k-rows each
+  auto frag_tr = [&](const char* base, int width, int cpk, int ks, int mb) -> bf16x8 {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int m = mb + 16 * (grp & 1) + 4 * (sl & 3);
+    const int kr = ks * 16 + 8 * (grp >> 1) + (sl >> 2);
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    v4s v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int krow = kr + 4 * h;
+      const int off = krow * width * 2 + (((m >> 3) ^ swzk(krow, cpk)) * 16) + (m & 7) * 2;
+      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)((__attribute__((address_space(3))) char*)base + off));
+    }
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s r = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
+  };
+  auto frag_a = [&](const char* st, int ks, int i) -> bf16x8 {
+    if constexpr (KA) {
+      return frag_tr(st, BM, CPKA, ks, wm * WM + i * 32);
+    } else {
+      const int c = 2 * ks + half, row = wm * WM + i * 32 + r32;
+      return *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ swz(row)) * 16));
+    }
+  };
+  auto frag_w = [&](const char* st, int ks, int j) -> bf16x8 {
+    if constexpr (KW) {
+      return frag_tr(st + BM * RB, BN, CPKW, ks, wn * WN + j * 32);
+    } else {
+      const int c = 2 * ks + half, row = wn * WN + j * 32 + r32;
+      return *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ swz(row)) * 16));
+    }
+  };
   auto load_frags = [&](const char* st, int ks, int buf) {
-    const int c = 2 * ks + half;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WM + i * 32 + r32;
-      fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ swz(row)) * 16));
-    }
+    for (int i = 0; i < TM; ++i) fa[buf][i] = frag_a(st, ks, i);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wn * WN + j * 32 + r32;
-      fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ swz(row)) * 16));
-    }
+    for (int j = 0; j < TN; ++j) fb[buf][j] = frag_w(st, ks, j);
   };
   auto issue_one = [&](int kt, int j) {
     char* st = smem + (kt % S) * STAGE;
     const int k0 = kbeg + kt * BK;
     if (j < A_INS)
-      lds_dma16_opaque(a_row[j] + min(k0 + a_c[j], kpad - 8), st + (wave * A_INS + j) * 1024);
+      lds_dma16_opaque(a_src(k0, j), st + (wave * A_INS + j) * 1024);
     else
-      lds_dma16_opaque(b_row[j - A_INS] + min(k0 + b_c[j - A_INS], kpad - 8),
-                       st + BM * RB + (wave * B_INS + j - A_INS) * 1024);
+      lds_dma16_opaque(b_src(k0, j - A_INS), st + BM * RB + (wave * B_INS + j - A_INS) * 1024);
   };
   auto load_one = [&](const char* st, int ks, int buf, int f) {
-    const int c = 2 * ks + half;
-    if (f < TM) {
-      const int row = wm * WM + f * 32 + r32;
-      fa[buf][f] = *reinterpret_cast<const bf16x8*>(st + row * RB + ((c ^ swz(row)) * 16));
-    } else {
-      const int row = wn * WN + (f - TM) * 32 + r32;
-      fb[buf][f - TM] = *reinterpret_cast<const bf16x8*>(st + BM * RB + row * RB + ((c ^ swz(row)) * 16));
-    }
+    if (f < TM) fa[buf][f] = frag_a(st, ks, f);
+    else fb[buf][f - TM] = frag_w(st, ks, f - TM);
   };
   auto mfma_one = [&](int buf, int q) {
     const int i = q / TN, j = q % TN;
@@ -465,7 +537,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
         if (j < N) {
           if (q == 0) dout.dbp[(int64_t)(m0 / BM) * N + j] = sum;
           uint16_t* tr = dout.dT + (int64_t)j * dout.ldt + i0;
-          if (tvec && i0 + 8 <= M) {
+          if (!dout.dT) {
+          } else if (tvec && i0 + 8 <= M) {
             *reinterpret_cast<uint4*>(tr) = w4;
           } else {
 #pragma unroll
@@ -577,14 +650,14 @@ int fast_occupancy(Kern kern, int threads) {
 }
 
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2, bool PERSIST = false,
-          int ILV = 0, bool DELTA = false>
+          int ILV = 0, bool DELTA = false, bool KA = false, bool KW = false>
 void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
                  int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s,
                  DeltaOut dout = DeltaOut{}) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int tiles = tm * tn;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S, PERSIST, ILV, DELTA>;
+  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S, PERSIST, ILV, DELTA, KA, KW>;
   int grid = tiles;
   if constexpr (PERSIST) {
     const int slots = fast_occupancy(kern, threads) * device_cu_count();
@@ -903,26 +976,54 @@ int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, co
   return launch_status();
 }
 
-int gemm_bf16_delta(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, int M, int N, int K,
-                    uint16_t* dlt, int64_t ldd, const DeltaOut& dout, int* tile_rows, hipStream_t s) {
+namespace {
+// The fast kernel's operand conditions: 16-byte aligned rows whose pitch is
+// a multiple of 8 values and holds a whole row (K values, or M / N values
+// for a k-major operand).
+bool fast_operand(const uint16_t* p, int64_t ld, int64_t need) {
+  return aligned16(p) && (ld % 8) == 0 && ld >= need && (int64_t)256 * ld < ((int64_t)1 << 31);
+}
+}  // namespace
+
+int gemm_bf16_ex(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* W, int64_t ldw, bool w_kmajor,
+                 void* C, int64_t ldc, bool out_bf16, int M, int N, int K, hipStream_t s) {
+  if (!a_kmajor && !w_kmajor) return gemm_bf16(A, lda, W, ldw, nullptr, C, ldc, out_bf16, M, N, K, false, s);
   if (M <= 0 || N <= 0) return DLRM_OK;
-  const bool fast = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0 && lda >= K && ldw >= K &&
-                    (int64_t)256 * lda < ((int64_t)1 << 31) && (int64_t)256 * ldw < ((int64_t)1 << 31);
-  if (!fast) return DLRM_E_UNSUPPORTED;
+  if (a_kmajor || out_bf16 || !fast_operand(A, lda, K) || !fast_operand(W, ldw, N)) return DLRM_E_UNSUPPORTED;
+  const int kps = (int)round_up(K > 0 ? K : 1, 64);
+  launch_fast<128, 128, 64, 64, float, false, 64, 2, false, 2, false, false, true>(
+      A, lda, W, ldw, nullptr, static_cast<float*>(C), ldc, M, N, K, 0, 1, kps, s);
+  return launch_status();
+}
+
+int gemm_bf16_delta(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, bool w_kmajor, int M, int N,
+                    int K, uint16_t* dlt, int64_t ldd, const DeltaOut& dout, int* tile_rows, hipStream_t s) {
+  if (M <= 0 || N <= 0) return DLRM_OK;
+  if (!fast_operand(A, lda, K) || !fast_operand(W, ldw, w_kmajor ? N : K)) return DLRM_E_UNSUPPORTED;
   const int kps = (int)round_up(K > 0 ? K : 1, 64);
   // the largest block tile that still gives every CU a tile (as pick_fast)
-  if (ceil_div(M, 256) * ceil_div(N, 256) >= 256) {
-    *tile_rows = 256;
-    if ((K % 64) == 0 && K >= 512)
+  const bool big = ceil_div(M, 256) * ceil_div(N, 256) >= 256, deep = (K % 64) == 0 && K >= 512;
+  *tile_rows = big ? 256 : 128;
+  if (w_kmajor) {
+    if (big && deep)
+      launch_fast<256, 256, 128, 64, uint16_t, false, 64, 2, false, 2, true, false, true>(
+          A, lda, W, ldw, nullptr, dlt, ldd, M, N, K, 0, 1, kps, s, dout);
+    else if (big)
+      launch_fast<256, 256, 128, 64, uint16_t, false, 32, 4, false, 1, true, false, true>(
+          A, lda, W, ldw, nullptr, dlt, ldd, M, N, K, 0, 1, kps, s, dout);
+    else
+      launch_fast<128, 128, 64, 64, uint16_t, false, 64, 2, false, 2, true, false, true>(
+          A, lda, W, ldw, nullptr, dlt, ldd, M, N, K, 0, 1, kps, s, dout);
+  } else {
+    if (big && deep)
       launch_fast<256, 256, 128, 64, uint16_t, false, 64, 2, false, 2, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K,
                                                                             0, 1, kps, s, dout);
-    else
+    else if (big)
       launch_fast<256, 256, 128, 64, uint16_t, false, 32, 4, false, 1, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K,
                                                                             0, 1, kps, s, dout);
-  } else {
-    *tile_rows = 128;
-    launch_fast<128, 128, 64, 64, uint16_t, false, 64, 2, false, 2, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K, 0,
-                                                                         1, kps, s, dout);
+    else
+      launch_fast<128, 128, 64, 64, uint16_t, false, 64, 2, false, 2, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K,
+                                                                           0, 1, kps, s, dout);
   }
   return launch_status();
 }
@@ -935,6 +1036,16 @@ int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t 
   const int kps = (int)round_up(ceil_div(K > 0 ? K : 1, splits), 64);
   if (fast) pick_fast<float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
   else launch_generic<float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
+  return launch_status();
+}
+
+int gemm_bf16_splitk_kmajor(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M,
+                            int N, int K, int splits, hipStream_t s) {
+  if (M <= 0 || N <= 0) return DLRM_OK;
+  if (!fast_operand(A, lda, M) || !fast_operand(W, ldw, N)) return DLRM_E_UNSUPPORTED;
+  const int kps = (int)round_up(ceil_div(K > 0 ? K : 1, splits), 64);
+  launch_fast<128, 128, 64, 64, float, true, 64, 2, false, 2, false, true, true>(A, lda, W, ldw, nullptr, part, N, M,
+                                                                                N, K, 0, splits, kps, s);
   return launch_status();
 }
 

@@ -11,10 +11,18 @@ namespace dlrm {
 // part[z][M][N] (no bias or activation) and reduce_splits() finishes.
 int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, void* C,
               int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s);
-// Input gradient of a ReLU layer, fused: g = A W^T (no bias), then
-// delta = bf16(g) where y > 0 and 0 elsewhere, written row-major to dlt
-// [M][ldd] and transposed to dout.dT [N][ldt], and per block of *tile_rows
-// rows the fp32 column sums of delta to dout.dbp[(row / *tile_rows)][N].
+// As gemm_bf16 without bias or activation, with operands that may be stored
+// k-major: a_kmajor, A is [K][M] (lda its pitch) instead of [M][K];
+// w_kmajor, W is [K][N] instead of [N][K].  The k-major forms need 16-byte
+// aligned rows with a pitch that is a multiple of 8 and fp32 output
+// (DLRM_E_UNSUPPORTED otherwise).
+int gemm_bf16_ex(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* W, int64_t ldw, bool w_kmajor,
+                 void* C, int64_t ldc, bool out_bf16, int M, int N, int K, hipStream_t s);
+// Input gradient of a ReLU layer, fused: g = A W^T (no bias; W k-major,
+// i.e. stored [K][N], with w_kmajor), then delta = bf16(g) where y > 0 and
+// 0 elsewhere, written row-major to dlt [M][ldd] and, when dout.dT is set,
+// transposed to dout.dT [N][ldt], and per block of *tile_rows rows the fp32
+// column sums of delta to dout.dbp[(row / *tile_rows)][N].
 struct DeltaOut {
   const uint16_t* y = nullptr;  // bf16 [M][ldy], the mask source
   int64_t ldy = 0;
@@ -22,10 +30,15 @@ struct DeltaOut {
   int64_t ldt = 0;
   float* dbp = nullptr;
 };
-int gemm_bf16_delta(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, int M, int N, int K,
-                    uint16_t* dlt, int64_t ldd, const DeltaOut& dout, int* tile_rows, hipStream_t s);
+int gemm_bf16_delta(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, bool w_kmajor, int M, int N,
+                    int K, uint16_t* dlt, int64_t ldd, const DeltaOut& dout, int* tile_rows, hipStream_t s);
 int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M, int N,
                      int K, int splits, hipStream_t s);
+// Split-K partials with both operands k-major: part[z][M][N] = the sum over
+// slice z of k of A[k][m] W[k][n] (A [K][M], W [K][N]), e.g. a weight
+// gradient delta^T x straight from the row-major delta and activations.
+int gemm_bf16_splitk_kmajor(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M,
+                            int N, int K, int splits, hipStream_t s);
 int reduce_splits(const float* part, int splits, int M, int N, const float* bias, float* C, int64_t ldc,
                   bool relu, hipStream_t s);
 

@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__
   {
     const int cc = threadIdx.x, col = c0 + cc;
     if (col < N) part[(int64_t)blockIdx.y * N + col] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
-    if (col < N) {
+    if (col < N && dltT) {
       // column cc of the tile is row col of delta^T: 64 rows, 8 per 16-byte store
       uint16_t* dst = dltT + (int64_t)col * ldt + r0;
 #pragma unroll
@@ -566,8 +566,8 @@ __global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__
 }
 
 struct BwdLayout {
-  size_t dlt[2], dltT[2], xT, wT, part, dbp, bytes;
-  int64_t ld_dlt, ld_B, splits_max;
+  size_t dlt[2], wT, part, dbp, bytes;
+  int64_t ld_dlt, splits_max;
 };
 
 constexpr int kMaxSplits = 16;
@@ -586,7 +586,6 @@ bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
   }
   Carver cv(nullptr);
   lay->ld_dlt = round_up(wfo, 8);
-  lay->ld_B = round_up(B, 8);
   lay->splits_max = kMaxSplits;
   auto take = [&](size_t bytes) {
     cv.used = (size_t)round_up((int64_t)cv.used, 256);
@@ -594,11 +593,7 @@ bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
     cv.used += bytes;
     return at;
   };
-  for (int i = 0; i < 2; ++i) {
-    lay->dlt[i] = take(2 * (size_t)(B * lay->ld_dlt));
-    lay->dltT[i] = take(2 * (size_t)(wfo * lay->ld_B));
-  }
-  lay->xT = take(2 * (size_t)(wmax * lay->ld_B));
+  for (int i = 0; i < 2; ++i) lay->dlt[i] = take(2 * (size_t)(B * lay->ld_dlt));
   lay->wT = take(2 * (size_t)(wmax * lay->ld_dlt));
   lay->part = take(4 * (size_t)(kMaxSplits * prod));
   lay->dbp = take(4 * (size_t)(ceil_div(B, kDRows) * wfo));
@@ -769,8 +764,6 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
   const char* fws = static_cast<const char*>(fwd_ws);
   char* w = static_cast<char*>(ws);
   uint16_t* dlt[2] = {reinterpret_cast<uint16_t*>(w + bl.dlt[0]), reinterpret_cast<uint16_t*>(w + bl.dlt[1])};
-  uint16_t* dltT[2] = {reinterpret_cast<uint16_t*>(w + bl.dltT[0]), reinterpret_cast<uint16_t*>(w + bl.dltT[1])};
-  uint16_t* xT = reinterpret_cast<uint16_t*>(w + bl.xT);
   uint16_t* wT = reinterpret_cast<uint16_t*>(w + bl.wT);
   float* part = reinterpret_cast<float*>(w + bl.part);
   float* dbp = reinterpret_cast<float*>(w + bl.dbp);
@@ -778,9 +771,11 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
   const dim3 b1(256);
   int rc = DLRM_OK;
 
-  // 1. the last layer's delta from dY (fp32), both layouts, and its bias
-  //    gradient; every earlier layer's delta comes out of the input-gradient
-  //    GEMM of the layer above it
+  // 1. the last layer's delta from dY (fp32) and its bias gradient; every
+  //    earlier layer's delta comes out of the input-gradient GEMM of the
+  //    layer above it.  The weight-gradient GEMMs read the row-major delta
+  //    and activations k-major (transposing reads from LDS), so no
+  //    transposed copies are made.
   {
     const int fo = dims[L];
     const bool relu = last_act == DLRM_ACT_RELU;
@@ -792,43 +787,48 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     const int vec = al(dY, dy_ld, 4, 16) && al(dlt[0], bl.ld_dlt, 2, 8) && al(y, ldy, 4, 16);
     const int chunks = (int)ceil_div(B, kDRows);
     hipLaunchKernelGGL((delta_db_kernel<float>), dim3((unsigned)ceil_div(fo, kDCols), (unsigned)chunks), b1, 0, stream,
-                       dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, dltT[0], bl.ld_B, dbp, M, fo, vec);
+                       dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, nullptr, 0, dbp, M, fo, vec);
     hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 64)), b1, 0, stream, dbp, chunks, fo, db[L - 1]);
     rc = launch_status();
   }
   int cur = 0;
   for (int l = L - 1; l >= 0 && rc == DLRM_OK; --l) {
     const int fi = dims[l], fo = dims[l + 1];
-    // 2. dW = delta^T x  (M = fo, N = fi, K = B), split over the batch
+    // 2. dW = delta^T x  (M = fo, N = fi, K = B), split over the batch;
+    //    delta [B][fo] and x [B][fi] are both read k-major
     const uint16_t* x = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l]);
-    if ((rc = transpose_bf16(x, fl.act_ld[l], xT, bl.ld_B, M, fi, stream)) != DLRM_OK) break;
     const int64_t tiles = ceil_div(fo, 128) * ceil_div(fi, 128);
     int splits = (int)ceil_div(512, tiles);
     if (splits > kMaxSplits) splits = kMaxSplits;
     if (splits > (int)ceil_div(M, 256)) splits = (int)ceil_div(M, 256);
     if (splits < 1) splits = 1;
-    if ((rc = gemm_bf16_splitk(dltT[cur], bl.ld_B, xT, bl.ld_B, part, fo, fi, M, splits, stream)) != DLRM_OK) break;
+    if ((rc = gemm_bf16_splitk_kmajor(dlt[cur], bl.ld_dlt, x, fl.act_ld[l], part, fo, fi, M, splits, stream)) !=
+        DLRM_OK)
+      break;
     if ((rc = reduce_splits(part, splits, fo, fi, nullptr, dW[l], fi, false, stream)) != DLRM_OK) break;
     if (l == 0 && !dX) break;
-    // 3. the input gradient delta W  (M = B, N = fi, K = fo)
+    // 3. the input gradient delta W  (M = B, N = fi, K = fo): W [fo][fi] is
+    //    read k-major where its rows allow, else through a transposed copy
     const int64_t wl = w_ld ? w_ld[l] : fi;
-    if ((rc = transpose_bf16(static_cast<const uint16_t*>(W[l]), wl, wT, bl.ld_dlt, fo, fi, stream)) != DLRM_OK) break;
+    const uint16_t* Wl = static_cast<const uint16_t*>(W[l]);
+    const bool wk = aligned16(Wl) && (wl % 8) == 0;
+    if (!wk && (rc = transpose_bf16(Wl, wl, wT, bl.ld_dlt, fo, fi, stream)) != DLRM_OK) break;
+    const uint16_t* wop = wk ? Wl : wT;
+    const int64_t wop_ld = wk ? wl : bl.ld_dlt;
     if (l == 0) {  // the MLP input's gradient, fp32
-      rc = gemm_bf16(dlt[cur], bl.ld_dlt, wT, bl.ld_dlt, nullptr, dX, dx_ld, false, M, fi, fo, false, stream);
+      rc = gemm_bf16_ex(dlt[cur], bl.ld_dlt, false, wop, wop_ld, wk, dX, dx_ld, false, M, fi, fo, stream);
       break;
     }
     // layer l-1 is a ReLU layer whose output is layer l's input x: its delta
-    // (masked by x > 0, bf16, both layouts) and bias-gradient partials come
+    // (masked by x > 0, bf16, row-major) and bias-gradient partials come
     // straight out of the GEMM
     DeltaOut dout;
     dout.y = x;
     dout.ldy = fl.act_ld[l];
-    dout.dT = dltT[cur ^ 1];
-    dout.ldt = bl.ld_B;
     dout.dbp = dbp;
     int tile_rows = 128;
-    if ((rc = gemm_bf16_delta(dlt[cur], bl.ld_dlt, wT, bl.ld_dlt, M, fi, fo, dlt[cur ^ 1], bl.ld_dlt, dout, &tile_rows,
-                              stream)) != DLRM_OK)
+    if ((rc = gemm_bf16_delta(dlt[cur], bl.ld_dlt, wop, wop_ld, wk, M, fi, fo, dlt[cur ^ 1], bl.ld_dlt, dout,
+                              &tile_rows, stream)) != DLRM_OK)
       break;
     hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fi, 64)), b1, 0, stream, dbp,
                        (int)ceil_div(B, tile_rows), fi, db[l - 1]);

@@ -185,6 +185,73 @@ def test_mlp_bf16_backward(which, B):
     assert rel(dX.cpu().numpy(), rX) <= 2e-2
 
 
+def _int_params(dims, seed, density):
+    """Weights in {-1, 0, 1} (nonzero with probability `density`) and biases
+    in {-2, .., 2}: every value exact in bf16."""
+    g = np.random.default_rng(seed)
+    out = []
+    for fi, fo in zip(dims[:-1], dims[1:]):
+        Wf = g.integers(-1, 2, size=(fo, fi)) * (g.random((fo, fi)) < density)
+        b = g.integers(-2, 3, size=fo)
+        out.append((Wf.astype(np.float32), None, b.astype(np.float32)))
+    return out
+
+
+@pytest.mark.parametrize("dims,B,padded", [((64, 256, 128, 64), 8192, True), ((64, 256, 128, 64), 1000, True),
+                                           ((20, 136, 72, 8), 8191, True), ((20, 132, 72, 8), 777, False)])
+def test_mlp_bf16_backward_integer_exact(dims, B, padded):
+    """Integer inputs, weights, biases and upstream gradients, small enough
+    that every sum the forward and the backward form is an integer below
+    2^23 in magnitude (checked on the oracle's sums of magnitudes): each
+    fp32 sum is then exact in any order and each bf16 rounding sees the same
+    value on both sides, so dW, db and dX equal the oracle's bit for bit.
+    This pins the weight-gradient GEMM that reads delta and the activations
+    k-major (transposing LDS reads; ragged batch tails at 1000, 8191 and 777
+    rows; outputs of 72 and 8 columns) and the input-gradient GEMM that reads
+    W k-major, or, with weight rows of 20 and 132 values (no 16-byte pitch),
+    through a transposed copy."""
+    import deep_learning_recommendation_amd as D
+    from deep_learning_recommendation_amd import pipeline as PL
+
+    banner(f"mlp backward integer-exact dims={dims} B={B} padded={padded}")
+    params = _int_params(dims, 5 + B, 0.25)
+    g = np.random.default_rng(B)
+    x = g.integers(-1, 2, size=(B, dims[0])).astype(np.float32)
+    dY = g.integers(-1, 2, size=(B, dims[-1])).astype(np.float32)
+    Ws = [p[0] for p in params]
+    bs = [p[2] for p in params]
+    # sums of magnitudes: the same network on |x|, |W|, |b| (forward) and on
+    # |W|, |dY| (backward) bounds every partial sum
+    _, _, acts_abs = oracle.mlp_fwd(np.abs(x), [np.abs(w) for w in Ws], [np.abs(b) for b in bs], False, True,
+                                    save_acts=True)
+    mW, mb, mX = oracle.mlp_bwd([np.abs(w) for w in Ws], acts_abs, np.abs(dY), True, want_dx=True)
+    assert max(float(np.max(a)) for a in acts_abs[1:]) < 2.0 ** 23
+    assert max(float(np.max(m)) for m in list(mW) + list(mb) + [mX]) < 2.0 ** 23
+
+    if padded:
+        mp = _mlp_dev(dims, params, True)
+    else:  # weight rows of exactly fi values
+        Wd = [torch.as_tensor(w).to(device=DEV, dtype=torch.bfloat16).contiguous() for w in Ws]
+        mp = PL.MLPParams(tuple(dims), Wd, [int(w.shape[1]) for w in Ws],
+                          [torch.as_tensor(b).to(DEV).contiguous() for b in bs], D.DLRM_BF16)
+    out, _, ws = _fwd(mp, x, True, save=True)
+    dY_dev = to_dev(dY)
+    dWs = [torch.empty((o, i), dtype=torch.float32, device=DEV) for i, o in zip(dims[:-1], dims[1:])]
+    dbs = [torch.empty((o,), dtype=torch.float32, device=DEV) for o in dims[1:]]
+    dX = torch.empty((B, dims[0]), dtype=torch.float32, device=DEV)
+    wsb = torch.empty((D.dlrm_mlp_bwd_workspace_size(B, dims),), dtype=torch.uint8, device=DEV)
+    D.dlrm_mlp_bwd(B, dims, mp.Ws, mp.w_ld, D.DLRM_ACT_RELU, ws, out, dims[-1], dY_dev, dims[-1], dWs, dbs, dX,
+                   dims[0], wsb)
+    torch.cuda.synchronize()
+    ref_out, _, acts = oracle.mlp_fwd(x, Ws, bs, True, True, save_acts=True)
+    assert np.array_equal(out.cpu().numpy(), ref_out.astype(np.float32))
+    rW, rb, rX = oracle.mlp_bwd(Ws, acts, dY, True, want_dx=True)
+    for l in range(len(dims) - 1):
+        assert np.array_equal(dWs[l].cpu().numpy(), rW[l].astype(np.float32)), l
+        assert np.array_equal(dbs[l].cpu().numpy(), rb[l].astype(np.float32)), l
+    assert np.array_equal(dX.cpu().numpy(), rX.astype(np.float32))
+
+
 def _bf16_params(dims, seed):
     """Glorot-normal weights stored as bf16 (their fp32 values), U(+-1/sqrt(fan_in)) biases."""
     g = np.random.default_rng(seed)
