@@ -535,26 +535,47 @@ __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__
   }
 }
 
-// db[o] = sum of the per-chunk partials: 64 columns per block, wave w sums
-// chunks w, w+4, ... and the four wave sums are added in wave order.
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int chunks, int N,
-                                                           float* __restrict__ db) {
+// One launch finishes a layer's gradients: blocks [0, rblocks) add the
+// split-K partials of dW in split order (eight loads in flight); each other
+// block sums the per-chunk partials of 64 entries of db, wave w taking
+// chunks w, w + 4, ... in order and the four wave sums added in wave order.
+__global__ __launch_bounds__(256) void grad_finalize_kernel(const float* __restrict__ part, int splits, int M,
+                                                            int N, float* __restrict__ dW, int64_t ldw, int rblocks,
+                                                            const float* __restrict__ dbp, int chunks,
+                                                            float* __restrict__ db) {
+  if ((int)blockIdx.x < rblocks) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t MN = (int64_t)M * N;
+    if (t >= MN) return;
+    const int i = (int)(t / N), j = (int)(t - (int64_t)i * N);
+    float v = 0.f;
+    for (int z0 = 0; z0 < splits; z0 += 8) {
+      float p[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) p[q] = (z0 + q < splits) ? part[(z0 + q) * MN + t] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (z0 + q < splits) v = v + p[q];
+    }
+    dW[(int64_t)i * ldw + j] = v;
+    return;
+  }
   __shared__ float red[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int o = blockIdx.x * 64 + lane;
+  const int o = ((int)blockIdx.x - rblocks) * 64 + lane;
   float s = 0.f;
-  if (o < N)
-    for (int c0 = wave; c0 < chunks; c0 += 32) {  // eight loads in flight, added in chunk order
+  if (o < M)
+    for (int c0 = wave; c0 < chunks; c0 += 32) {
       float v[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = (c0 + 4 * t < chunks) ? part[(int64_t)(c0 + 4 * t) * N + o] : 0.f;
+      for (int t = 0; t < 8; ++t) v[t] = (c0 + 4 * t < chunks) ? dbp[(int64_t)(c0 + 4 * t) * M + o] : 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
         if (c0 + 4 * t < chunks) s = s + v[t];
     }
   red[wave][lane] = s;
   __syncthreads();
-  if (wave == 0 && o < N) db[o] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  if (wave == 0 && o < M) db[o] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 __global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__ logit, int64_t ld,
@@ -770,6 +791,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
   const int M = (int)B;
   const dim3 b1(256);
   int rc = DLRM_OK;
+  int db_chunks = 0;  // row chunks of the bias-gradient partials in dbp
 
   // 1. the last layer's delta from dY (fp32) and its bias gradient; every
   //    earlier layer's delta comes out of the input-gradient GEMM of the
@@ -788,7 +810,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     const int chunks = (int)ceil_div(B, kDRows);
     hipLaunchKernelGGL((delta_db_kernel<float>), dim3((unsigned)ceil_div(fo, kDCols), (unsigned)chunks), b1, 0, stream,
                        dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, nullptr, 0, dbp, M, fo, vec);
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fo, 64)), b1, 0, stream, dbp, chunks, fo, db[L - 1]);
+    db_chunks = chunks;
     rc = launch_status();
   }
   int cur = 0;
@@ -797,15 +819,24 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     // 2. dW = delta^T x  (M = fo, N = fi, K = B), split over the batch;
     //    delta [B][fo] and x [B][fi] are both read k-major
     const uint16_t* x = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l]);
+    // about one 128 x 128 tile per CU: fewer slices were as fast and write
+    // fewer partials (measured: slices for 256 tiles 0.290 ms per dense
+    // backward, 512 0.297, 1024 0.309)
     const int64_t tiles = ceil_div(fo, 128) * ceil_div(fi, 128);
-    int splits = (int)ceil_div(512, tiles);
+    int splits = (int)ceil_div(256, tiles);
     if (splits > kMaxSplits) splits = kMaxSplits;
     if (splits > (int)ceil_div(M, 256)) splits = (int)ceil_div(M, 256);
     if (splits < 1) splits = 1;
     if ((rc = gemm_bf16_splitk_kmajor(dlt[cur], bl.ld_dlt, x, fl.act_ld[l], part, fo, fi, M, splits, stream)) !=
         DLRM_OK)
       break;
-    if ((rc = reduce_splits(part, splits, fo, fi, nullptr, dW[l], fi, false, stream)) != DLRM_OK) break;
+    // dW from the partials and db from the partials the layer's delta left
+    {
+      const int rblocks = (int)ceil_div((int64_t)fo * fi, 256);
+      hipLaunchKernelGGL(grad_finalize_kernel, dim3((unsigned)(rblocks + ceil_div(fo, 64))), b1, 0, stream, part,
+                         splits, fo, fi, dW[l], (int64_t)fi, rblocks, dbp, db_chunks, db[l]);
+      if ((rc = launch_status()) != DLRM_OK) break;
+    }
     if (l == 0 && !dX) break;
     // 3. the input gradient delta W  (M = B, N = fi, K = fo): W [fo][fi] is
     //    read k-major where its rows allow, else through a transposed copy
@@ -830,9 +861,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     if ((rc = gemm_bf16_delta(dlt[cur], bl.ld_dlt, wop, wop_ld, wk, M, fi, fo, dlt[cur ^ 1], bl.ld_dlt, dout,
                               &tile_rows, stream)) != DLRM_OK)
       break;
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)ceil_div(fi, 64)), b1, 0, stream, dbp,
-                       (int)ceil_div(B, tile_rows), fi, db[l - 1]);
-    if ((rc = launch_status()) != DLRM_OK) break;
+    db_chunks = (int)ceil_div(B, tile_rows);
     cur ^= 1;
   }
   return rc;
