@@ -578,6 +578,133 @@ __global__ __launch_bounds__(256) void grad_finalize_kernel(const float* __restr
   if (wave == 0 && o < M) db[o] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
+// Layers with a single output (the top MLP's logit layer) as two plain
+// kernels instead of degenerate GEMMs.  A block covers kR1Rows rows and 256
+// columns: thread t takes eight consecutive columns (16-byte loads; a row
+// pitch that is a multiple of 8 keeps the last chunk inside the row) and the
+// rows t / 32, t / 32 + 8, ... of the chunk, all its loads in flight at
+// once; the eight row groups' sums are then added in group order.
+constexpr int kR1Rows = 128, kR1Per = kR1Rows / 8;
+
+__device__ __forceinline__ void unpack8(const uint4 q, float (&f)[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+}
+
+// Adds the eight row groups' column sums of this block in group order; the
+// threads of group 0 return the totals.
+__device__ __forceinline__ void r1_group_sum(float (&acc)[8], float (*red)[256]) {
+  const int t = threadIdx.x, rg = t >> 5, cg = t & 31;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = acc[e];
+  __syncthreads();
+  if (rg == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = red[0][cg * 8 + e];
+#pragma unroll
+      for (int g = 1; g < 8; ++g) v = v + red[g][cg * 8 + e];
+      acc[e] = v;
+    }
+  }
+}
+
+// Weight gradient: part[z][i] = the fp32 sum over the rows of chunk z of
+// delta[b] x[b][i] (each product of two bf16 values is exact), added up
+// across chunks by grad_finalize_kernel like split-K partials.
+__global__ __launch_bounds__(256) void rank1_wgrad_kernel(const uint16_t* __restrict__ dlt, int64_t ldd,
+                                                          const uint16_t* __restrict__ x, int64_t ldx, int B, int fi,
+                                                          float* __restrict__ part) {
+  __shared__ float red[8][256];
+  const int t = threadIdx.x, rg = t >> 5, z = blockIdx.y;
+  const int c = blockIdx.x * 256 + (t & 31) * 8;
+  const int cl = c < fi ? c : 0;  // lanes past the row read its first chunk (results dropped)
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  uint4 q[kR1Per];
+  float dv[kR1Per];
+#pragma unroll
+  for (int r = 0; r < kR1Per; ++r) {
+    const int b = z * kR1Rows + rg + 8 * r, bb = b < B ? b : B - 1;
+    q[r] = *reinterpret_cast<const uint4*>(x + (int64_t)bb * ldx + cl);
+    dv[r] = b < B ? bf16_to_f32(dlt[(int64_t)bb * ldd]) : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < kR1Per; ++r) {
+    float f[8];
+    unpack8(q[r], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + dv[r] * f[e];
+  }
+  r1_group_sum(acc, red);
+  if (rg == 0)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c + e < fi) part[(int64_t)z * fi + c + e] = acc[e];
+}
+
+// Delta of the ReLU layer below a single-output layer, as the GEMM epilogue
+// forms it: bf16(+0 + delta[b] w[i]) where y[b][i] > 0, else +0 (columns
+// past fi written as 0), and per chunk the fp32 column sums of the rounded
+// values.
+__global__ __launch_bounds__(256) void rank1_delta_kernel(const uint16_t* __restrict__ dlt, int64_t ldd,
+                                                          const uint16_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ y, int64_t ldy, int B, int fi,
+                                                          uint16_t* __restrict__ out, int64_t ldo,
+                                                          float* __restrict__ dbp) {
+  __shared__ float red[8][256];
+  const int t = threadIdx.x, rg = t >> 5, z = blockIdx.y;
+  const int c = blockIdx.x * 256 + (t & 31) * 8;
+  const bool live = c < fi;
+  const int cl = live ? c : 0;
+  float wv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) wv[e] = (c + e < fi) ? bf16_to_f32(w[c + e]) : 0.f;
+  uint4 q[kR1Per];
+  float dv[kR1Per];
+#pragma unroll
+  for (int r = 0; r < kR1Per; ++r) {
+    const int b = z * kR1Rows + rg + 8 * r, bb = b < B ? b : B - 1;
+    q[r] = *reinterpret_cast<const uint4*>(y + (int64_t)bb * ldy + cl);
+    dv[r] = bf16_to_f32(dlt[(int64_t)bb * ldd]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < kR1Per; ++r) {
+    const int b = z * kR1Rows + rg + 8 * r;
+    float f[8];
+    unpack8(q[r], f);
+    uint32_t h[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t v = (c + e < fi && f[e] > 0.f) ? f32_to_bf16(0.f + dv[r] * wv[e]) : (uint16_t)0;
+      h[e >> 1] |= (uint32_t)v << (16 * (e & 1));
+      if (b < B) acc[e] = acc[e] + bf16_to_f32(v);
+    }
+    if (b < B && live) *reinterpret_cast<uint4*>(out + (int64_t)b * ldo + c) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+  r1_group_sum(acc, red);
+  if (rg == 0)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c + e < fi) dbp[(int64_t)z * fi + c + e] = acc[e];
+}
+
+// Batch slices of a layer's weight-gradient GEMM: about 256 tiles of 128 x
+// 128 in all (fewer slices were as fast and write fewer partials; measured
+// with slices for 256 tiles 0.290 ms per dense backward, 512 0.297, 1024
+// 0.309), each slice at least 128 rows of the batch.  Single-output layers
+// take one slice per kR1Rows rows.
+constexpr int kMaxSplits = 64;
+int wgrad_splits(int64_t B, int fo, int fi) {
+  if (fo == 1) return (int)ceil_div(B, kR1Rows);
+  const int64_t tiles = ceil_div(fo, 128) * ceil_div(fi, 128);
+  int64_t s = ceil_div(256, tiles);
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > ceil_div(B, 128)) s = ceil_div(B, 128);
+  return s < 1 ? 1 : (int)s;
+}
+
 __global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__ logit, int64_t ld,
                                                        const float* __restrict__ y, int64_t B, float* __restrict__ dY) {
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -588,10 +715,8 @@ __global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__
 
 struct BwdLayout {
   size_t dlt[2], wT, part, dbp, bytes;
-  int64_t ld_dlt, splits_max;
+  int64_t ld_dlt;
 };
-
-constexpr int kMaxSplits = 16;
 
 bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
   if (L < 1 || L > 64 || B < 1) return false;
@@ -602,12 +727,11 @@ bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
   }
   for (int l = 0; l < L; ++l) {
     wfo = dims[l + 1] > wfo ? dims[l + 1] : wfo;
-    const int64_t p = (int64_t)dims[l] * dims[l + 1];
+    const int64_t p = (int64_t)wgrad_splits(B, dims[l + 1], dims[l]) * dims[l] * dims[l + 1];
     prod = p > prod ? p : prod;
   }
   Carver cv(nullptr);
   lay->ld_dlt = round_up(wfo, 8);
-  lay->splits_max = kMaxSplits;
   auto take = [&](size_t bytes) {
     cv.used = (size_t)round_up((int64_t)cv.used, 256);
     const size_t at = cv.used;
@@ -616,7 +740,7 @@ bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
   };
   for (int i = 0; i < 2; ++i) lay->dlt[i] = take(2 * (size_t)(B * lay->ld_dlt));
   lay->wT = take(2 * (size_t)(wmax * lay->ld_dlt));
-  lay->part = take(4 * (size_t)(kMaxSplits * prod));
+  lay->part = take(4 * (size_t)prod);
   lay->dbp = take(4 * (size_t)(ceil_div(B, kDRows) * wfo));
   lay->bytes = cv.bytes();
   return true;
@@ -819,17 +943,15 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     // 2. dW = delta^T x  (M = fo, N = fi, K = B), split over the batch;
     //    delta [B][fo] and x [B][fi] are both read k-major
     const uint16_t* x = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l]);
-    // about one 128 x 128 tile per CU: fewer slices were as fast and write
-    // fewer partials (measured: slices for 256 tiles 0.290 ms per dense
-    // backward, 512 0.297, 1024 0.309)
-    const int64_t tiles = ceil_div(fo, 128) * ceil_div(fi, 128);
-    int splits = (int)ceil_div(256, tiles);
-    if (splits > kMaxSplits) splits = kMaxSplits;
-    if (splits > (int)ceil_div(M, 256)) splits = (int)ceil_div(M, 256);
-    if (splits < 1) splits = 1;
-    if ((rc = gemm_bf16_splitk_kmajor(dlt[cur], bl.ld_dlt, x, fl.act_ld[l], part, fo, fi, M, splits, stream)) !=
-        DLRM_OK)
-      break;
+    const int splits = wgrad_splits(B, fo, fi);
+    if (fo == 1) {
+      hipLaunchKernelGGL(rank1_wgrad_kernel, dim3((unsigned)ceil_div(fi, 256), (unsigned)splits), b1, 0, stream,
+                         dlt[cur], bl.ld_dlt, x, fl.act_ld[l], M, fi, part);
+      rc = launch_status();
+    } else {
+      rc = gemm_bf16_splitk_kmajor(dlt[cur], bl.ld_dlt, x, fl.act_ld[l], part, fo, fi, M, splits, stream);
+    }
+    if (rc != DLRM_OK) break;
     // dW from the partials and db from the partials the layer's delta left
     {
       const int rblocks = (int)ceil_div((int64_t)fo * fi, 256);
@@ -842,6 +964,14 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     //    read k-major where its rows allow, else through a transposed copy
     const int64_t wl = w_ld ? w_ld[l] : fi;
     const uint16_t* Wl = static_cast<const uint16_t*>(W[l]);
+    if (fo == 1 && l > 0) {  // a single-output layer above a ReLU layer
+      hipLaunchKernelGGL(rank1_delta_kernel, dim3((unsigned)ceil_div(fi, 256), (unsigned)ceil_div(B, kR1Rows)), b1, 0,
+                         stream, dlt[cur], bl.ld_dlt, Wl, x, fl.act_ld[l], M, fi, dlt[cur ^ 1], bl.ld_dlt, dbp);
+      if ((rc = launch_status()) != DLRM_OK) break;
+      db_chunks = (int)ceil_div(B, kR1Rows);
+      cur ^= 1;
+      continue;
+    }
     const bool wk = aligned16(Wl) && (wl % 8) == 0;
     if (!wk && (rc = transpose_bf16(Wl, wl, wT, bl.ld_dlt, fo, fi, stream)) != DLRM_OK) break;
     const uint16_t* wop = wk ? Wl : wT;

@@ -198,7 +198,8 @@ def _int_params(dims, seed, density):
 
 
 @pytest.mark.parametrize("dims,B,padded", [((64, 256, 128, 64), 8192, True), ((64, 256, 128, 64), 1000, True),
-                                           ((20, 136, 72, 8), 8191, True), ((20, 132, 72, 8), 777, False)])
+                                           ((20, 136, 72, 8), 8191, True), ((20, 132, 72, 8), 777, False),
+                                           ((24, 136, 64, 1), 8192, True), ((24, 136, 64, 1), 333, True)])
 def test_mlp_bf16_backward_integer_exact(dims, B, padded):
     """Integer inputs, weights, biases and upstream gradients, small enough
     that every sum the forward and the backward form is an integer below
@@ -209,7 +210,8 @@ def test_mlp_bf16_backward_integer_exact(dims, B, padded):
     k-major (transposing LDS reads; ragged batch tails at 1000, 8191 and 777
     rows; outputs of 72 and 8 columns) and the input-gradient GEMM that reads
     W k-major, or, with weight rows of 20 and 132 values (no 16-byte pitch),
-    through a transposed copy."""
+    through a transposed copy; a last layer of one output takes the
+    single-output kernels."""
     import deep_learning_recommendation_amd as D
     from deep_learning_recommendation_amd import pipeline as PL
 
