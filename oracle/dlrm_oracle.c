@@ -15,7 +15,9 @@
  *
  * Precision: floating point is fp64 except where the contract fixes fp32:
  * pooled embeddings and SGD-updated rows are defined bit-exactly as fp32
- * sums in bag order, so those two functions compute in fp32 in that order.
+ * sums in a fixed order (bag order; for the SGD rows, blocks of 128
+ * occurrences in position order), so those two functions compute in fp32 in
+ * that order.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp (no fast-math).  OpenMP splits
  * only independent outputs, so results do not depend on the thread count.
@@ -334,19 +336,28 @@ void oracle_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const float* cons
  * Sparse embedding backward with row-wise SGD, in place.
  * Sum pooling sends the gradient of bag (k, b) unchanged to every row it
  * looked up, once per occurrence.  For each row r of table k that the batch
- * touches:
- *   g[c] = sum over occurrences p of r in table k's bags, p ascending, of
- *          G[b(p)*g_ld + g_col0 + k*d + c]     (fp32, from +0.0f)
+ * touches, with its occurrences p_0 < p_1 < ... in table k's bags (position
+ * order) and x_i = G[b(p_i)*g_ld + g_col0 + k*d + c]:
+ *   S_j  = the sum of the block x_{128j} .. x_{128j+127} (or to the last
+ *          occurrence), in order, fp32 from +0.0f
+ *   g[c] = the sum of S_0, S_1, ... in order, fp32 from +0.0f
  *   T_k[r][c] = T_k[r][c] - (lr * g[c])        (two fp32 roundings, no FMA)
+ * The pages define the row's gradient as the plain sum of its occurrences'
+ * gradients and fix no order for it; this order (blocks of SGD_BLOCK in
+ * position order) is one a parallel machine reaches, and for at most
+ * SGD_BLOCK + 1 occurrences it is the plain left-to-right sum.
  * Rows the batch does not touch are left as they are.  rows[k] is the row
  * count of table k.
  */
+#define SGD_BLOCK 128
 void oracle_embbag_bwd_sgd(float* const* tables, const int64_t* rows, int32_t K, int32_t d, const int64_t* idx,
                            const int64_t* off, int64_t B, const float* G, int64_t g_ld, int64_t g_col0,
                            float lr) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int32_t k = 0; k < K; ++k) {
-    float* acc = (float*)calloc((size_t)rows[k] * (size_t)d, sizeof(float));
+    float* acc = (float*)calloc((size_t)rows[k] * (size_t)d, sizeof(float)); /* sum of finished blocks */
+    float* blk = (float*)calloc((size_t)rows[k] * (size_t)d, sizeof(float)); /* the open block's sum */
+    int64_t* count = (int64_t*)calloc((size_t)rows[k], sizeof(int64_t));     /* occurrences so far */
     unsigned char* touched = (unsigned char*)calloc((size_t)rows[k], 1);
     for (int64_t b = 0; b < B; ++b) {
       const float* gb = G + b * g_ld + g_col0 + (int64_t)k * d;
@@ -354,18 +365,28 @@ void oracle_embbag_bwd_sgd(float* const* tables, const int64_t* rows, int32_t K,
         const int64_t r = idx[p];
         touched[r] = 1;
         float* a = acc + r * (int64_t)d;
-        for (int32_t c = 0; c < d; ++c) a[c] = a[c] + gb[c];
+        float* bs = blk + r * (int64_t)d;
+        if (count[r] > 0 && count[r] % SGD_BLOCK == 0) /* a block is full: it joins the total */
+          for (int32_t c = 0; c < d; ++c) {
+            a[c] = a[c] + bs[c];
+            bs[c] = 0.0f;
+          }
+        for (int32_t c = 0; c < d; ++c) bs[c] = bs[c] + gb[c];
+        count[r] += 1;
       }
     }
     float* T = tables[k];
     for (int64_t r = 0; r < rows[k]; ++r) {
       if (!touched[r]) continue;
       for (int32_t c = 0; c < d; ++c) {
-        const float step = lr * acc[r * (int64_t)d + c];
+        const float g = acc[r * (int64_t)d + c] + blk[r * (int64_t)d + c]; /* the last block */
+        const float step = lr * g;
         T[r * (int64_t)d + c] = T[r * (int64_t)d + c] - step;
       }
     }
     free(acc);
+    free(blk);
+    free(count);
     free(touched);
   }
 }

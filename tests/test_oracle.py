@@ -461,9 +461,11 @@ def test_mlp_bwd_finite_differences(orc):
 
 # --------------------------------------------------------------------------- sparse backward + SGD
 
-def _sort_based_sgd(tabs, idx, off, B, G, g_col0, lr):
+def _sort_based_sgd(tabs, idx, off, B, G, g_col0, lr, block=128):
     """Second formulation: stable sort of (table, row) keys, then segmented
-    fp32 sums over the sorted occurrences and one update per unique row."""
+    fp32 sums over the sorted occurrences (in blocks of `block` occurrences,
+    each summed from +0, the block sums added from +0) and one update per
+    unique row."""
     K, d = len(tabs), tabs[0].shape[1]
     out = [t.copy() for t in tabs]
     bag = np.repeat(np.arange(K * B), np.diff(off))
@@ -476,9 +478,13 @@ def _sort_based_sgd(tabs, idx, off, B, G, g_col0, lr):
     for h, e in zip(heads, ends):
         k, r = int(sk[h] >> 40), int(sk[h] & ((1 << 40) - 1))
         gsum = np.zeros(d, np.float32)
-        for q in order[h:e]:
-            b = bag[q] % B
-            gsum = (gsum + G[b, g_col0 + k * d: g_col0 + (k + 1) * d]).astype(np.float32)
+        occ = order[h:e]
+        for j0 in range(0, len(occ), block):
+            part = np.zeros(d, np.float32)
+            for q in occ[j0:j0 + block]:
+                b = bag[q] % B
+                part = (part + G[b, g_col0 + k * d: g_col0 + (k + 1) * d]).astype(np.float32)
+            gsum = (gsum + part).astype(np.float32)
         out[k][r] = (out[k][r] - (np.float32(lr) * gsum).astype(np.float32)).astype(np.float32)
     return out
 
@@ -494,6 +500,35 @@ def test_sparse_sgd_matches_sort_based_formulation(orc):
     orc.embbag_bwd_sgd(got, idx, off, B, G, d, 0.01)
     for a, b in zip(got, ref):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_sparse_sgd_long_rows_sum_in_blocks_of_128(orc):
+    """Rows with up to several hundred occurrences: the update follows the blocked order
+    (blocks of 128 in position order, block sums added in order); up to 129
+    occurrences that is the plain left-to-right sum, and on the long rows the
+    two orders give different bits (so the order is really pinned)."""
+    g = np.random.default_rng(18)
+    K, B, d = 2, 600, 8
+    rows = [6, 40]
+    lens = g.integers(0, 5, size=K * B)
+    off = np.zeros(K * B + 1, dtype=np.int64)
+    np.cumsum(lens, out=off[1:])
+    idx = np.concatenate([np.minimum(g.zipf(1.3, size=off[(k + 1) * B] - off[k * B]) - 1, rows[k] - 1)
+                          for k in range(K)]).astype(np.int64)
+    tabs = [g.standard_normal((m, d)).astype(np.float32) for m in rows]
+    # gradients of mixed magnitude, so that the summation order shows in the bits
+    G = (g.standard_normal((B, K * d)) * np.exp2(g.integers(-12, 12, size=(B, K * d)))).astype(np.float32)
+    got = [t.copy() for t in tabs]
+    orc.embbag_bwd_sgd(got, idx, off, B, G, 0, 0.01)
+    blocked = _sort_based_sgd(tabs, idx, off, B, G, 0, 0.01, block=128)
+    plain = _sort_based_sgd(tabs, idx, off, B, G, 0, 0.01, block=1 << 30)
+    for k in range(K):
+        assert np.array_equal(got[k].view(np.uint32), blocked[k].view(np.uint32))
+        cnt = np.bincount(idx[off[k * B]:off[(k + 1) * B]], minlength=rows[k])
+        short = cnt <= 129
+        assert np.array_equal(blocked[k][short].view(np.uint32), plain[k][short].view(np.uint32))
+    assert max(np.bincount(idx[off[k * B]:off[(k + 1) * B]]).max() for k in range(K)) > 400
+    assert any(not np.array_equal(blocked[k].view(np.uint32), plain[k].view(np.uint32)) for k in range(K))
 
 
 def test_sparse_sgd_single_occurrence_and_untouched(orc):

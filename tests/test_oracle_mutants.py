@@ -60,6 +60,12 @@ MUTANTS = {
                        ["test_sparse_sgd_single_occurrence_and_untouched", "test_sparse_sgd_dyadic_exact"]),
     "sgd_ignores_table_slot": ("G + b * g_ld + g_col0 + (int64_t)k * d", "G + b * g_ld + g_col0",
                                ["test_sparse_sgd_matches_sort_based_formulation", "test_sparse_sgd_dyadic_exact"]),
+    "sgd_plain_order": ("count[r] > 0 && count[r] % SGD_BLOCK == 0", "0",
+                        ["test_sparse_sgd_long_rows_sum_in_blocks_of_128"]),
+    "sgd_block_of_64": ("count[r] % SGD_BLOCK == 0", "count[r] % 64 == 0",
+                        ["test_sparse_sgd_long_rows_sum_in_blocks_of_128"]),
+    "sgd_drops_last_block": ("acc[r * (int64_t)d + c] + blk[r * (int64_t)d + c]", "acc[r * (int64_t)d + c]",
+                             ["test_sparse_sgd_single_occurrence_and_untouched", "test_sparse_sgd_dyadic_exact"]),
     "sgd_never_marks_touched": ("touched[r] = 1;", "",
                                    ["test_sparse_sgd_single_occurrence_and_untouched", "test_sparse_sgd_matches_sort_based_formulation"]),
 }
