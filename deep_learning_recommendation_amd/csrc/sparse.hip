@@ -3,27 +3,25 @@
 // Sum pooling hands each bag's gradient unchanged to every row the bag
 // looked up, once per occurrence (the lookup of "Deep Learning
 // Recommendation Model (DLRM)" explainer, Key Method Details, Embedding
-// tables; training by binary cross-entropy, Key Method Details, Loss).  The
-// per-row gradient must be one serial fp32 sum in position order, so the
-// path is:
+// tables; training by binary cross-entropy, Key Method Details, Loss).  A
+// row's gradient is the fp32 sum of its occurrences' gradients in a fixed
+// order: position order, in blocks of kHot = 128 occurrences (each block
+// summed from +0, then the block sums in order; up to 129 occurrences that
+// is the plain left-to-right sum).  The path:
 //   1. keys: one (table, row) key and one bag id per index position
 //      (position order = table-major bag order);
 //   2. a stable least-significant-digit radix sort over the row bits of the
 //      keys (8 or 9 bits per pass); stability keeps equal keys in position
 //      order, and since positions are table-major, equal rows of different
 //      tables stay in table order, so every (table, row) key forms one run;
-//   3. run-length segmentation (head flags, device-wide exclusive scan);
-//   4. one fused kernel: each segment's gradient sum over its occurrences in
-//      sorted order (fp32, from +0) and the update T <- T - lr * g.
-// Hot rows (Zipf heads with 10^5 occurrences) make step 4's longest serial
-// chain the latency floor.  Step 4 is one persistent launch with one block
-// per CU.  Segments of at least kHot occurrences come first, as
-// producer/consumer items: per (segment, 64-column slice) one wave adds, one
-// column per lane, from an LDS ring that six other waves keep filled, so the
-// serial adds never wait on memory.  Hot items are handed out longest first;
-// a block that finds none left turns its seven waves to the short segments
-// (one lane group each, chunks taken from a second counter), so the CUs that
-// the few longest chains leave free take the rest of the work meanwhile.
+//   3. run-length segmentation (head flags, device-wide exclusive scan); runs
+//      of at least kHot occurrences ("hot", the Zipf heads with up to 10^5
+//      occurrences) are listed apart;
+//   4. the sums and the update T <- T - lr * g: short runs one lane group
+//      each, in sorted order; hot runs in three steps, their blocks' sums in
+//      parallel (one lane group per block), then per run the block sums in
+//      order and the update.  The blocked order keeps a 10^5-occurrence row
+//      from being one serial chain of 10^5 dependent adds.
 #include "common.hpp"
 
 #include <mutex>
@@ -35,14 +33,9 @@ constexpr int RT = 256;                // threads per sort block
 constexpr int ITEMS = 16;              // keys per thread per tile
 constexpr int TILE = RT * ITEMS;       // 4096 positions per tile
 constexpr int kMaxDigits = 512;        // buckets of a digit of at most 9 bits
-constexpr int kHot = 128;              // occurrences from which a segment is "hot"
-constexpr int kHB = 64;                // occurrences per LDS ring slot
-constexpr int kSlots = 8;              // ring slots
-constexpr int kRS = kHB + 4;           // floats per column row of a slot (padded: conflict-free 16-byte reads)
-constexpr int kLoaders = 6;            // loader waves per hot block (plus one adder)
-constexpr int kAdder = 3;              // the adder's wave index: alone on its SIMD when waves go round-robin
-constexpr int kApplyThreads = 64 * (kLoaders + 1);
-constexpr int kLightBlocks = 2048;     // persistent blocks of the standalone short-segment kernel
+constexpr int kHot = 128;              // occurrences from which a segment is "hot", and its block size
+constexpr int kLightBlocks = 2048;     // persistent blocks of the short-segment kernel
+constexpr int kHotBlocks = 1024;       // persistent blocks of the hot-run kernels
 
 // ------------------------------------------------------------------ keys
 
@@ -450,308 +443,6 @@ __global__ __launch_bounds__(RT) void heads_write_kernel(const uint32_t* __restr
 
 // ------------------------------------------------------------------ reduce + SGD
 
-// Hand-over flags in LDS, read and written as workgroup-scope atomics so
-// that every access really goes to LDS and stays in program order.
-__device__ __forceinline__ int32_t lds_load(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_store(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// The adder's loop over the full blocks of an item, scheduled by hand.  Every
-// instruction between two dependent adds lengthens the chain (measured on
-// gfx950: a dependent fp32 add issues every 4.4 cycles; a 16-byte LDS read
-// placed between two adds adds about 15 cycles, four of them back to back
-// about 6 cycles each; a satisfied wait about 4), so a block runs as four
-// steps of [four 16-byte reads, one wait, sixteen adds], the reads for the
-// step after next, the waits counted exactly (one wave's LDS accesses complete
-// in order).  Step buffers live in v192..v255 (A, B: steps 0 and 1, reloaded
-// from the next block during steps 2 and 3; C, D: steps 2 and 3).  The slot
-// is released (consumed = block + 1) right after its last reads are issued:
-// they are performed before any later access of this wave, so before the
-// loader can see the release.  The next block's flag is read before its first
-// reads; if it was not yet up, those reads are dropped and issued again once
-// it is.
-#define HOT_RD(v0, v3, op, off) "ds_read_b128 v[" #v0 ":" #v3 "], %[" #op "] offset:" #off "\n\t"
-#define HOT_RD_A(op) HOT_RD(192, 195, op, 0) HOT_RD(196, 199, op, 16) HOT_RD(200, 203, op, 32) HOT_RD(204, 207, op, 48)
-#define HOT_RD_B(op) HOT_RD(208, 211, op, 64) HOT_RD(212, 215, op, 80) HOT_RD(216, 219, op, 96) HOT_RD(220, 223, op, 112)
-#define HOT_RD_C(op) HOT_RD(224, 227, op, 128) HOT_RD(228, 231, op, 144) HOT_RD(232, 235, op, 160) HOT_RD(236, 239, op, 176)
-#define HOT_RD_D(op) HOT_RD(240, 243, op, 192) HOT_RD(244, 247, op, 208) HOT_RD(248, 251, op, 224) HOT_RD(252, 255, op, 240)
-#define HOT_ADD(v) "v_add_f32 %[acc], %[acc], v" #v "\n\t"
-#define HOT_ADD4(a, b, c, e) HOT_ADD(a) HOT_ADD(b) HOT_ADD(c) HOT_ADD(e)
-#define HOT_ADDS_A HOT_ADD4(192, 193, 194, 195) HOT_ADD4(196, 197, 198, 199) HOT_ADD4(200, 201, 202, 203) HOT_ADD4(204, 205, 206, 207)
-#define HOT_ADDS_B HOT_ADD4(208, 209, 210, 211) HOT_ADD4(212, 213, 214, 215) HOT_ADD4(216, 217, 218, 219) HOT_ADD4(220, 221, 222, 223)
-#define HOT_ADDS_C HOT_ADD4(224, 225, 226, 227) HOT_ADD4(228, 229, 230, 231) HOT_ADD4(232, 233, 234, 235) HOT_ADD4(236, 237, 238, 239)
-#define HOT_ADDS_D HOT_ADD4(240, 241, 242, 243) HOT_ADD4(244, 245, 246, 247) HOT_ADD4(248, 249, 250, 251) HOT_ADD4(252, 253, 254, 255)
-static_assert(kHB == 64 && kSlots == 8, "the adder loop takes 64-occurrence blocks in an 8-slot ring");
-static_assert(64 * kRS * sizeof(float) == 0x4400, "the adder loop's slot stride");
-__device__ __forceinline__ void hot_adder_full_blocks(float& acc, int32_t base, int32_t nfull, const float* lane_col,
-                                                      const int32_t* ready, int32_t* consumed) {
-  const uint32_t col = (uint32_t)reinterpret_cast<uintptr_t>(lane_col);  // LDS byte addresses
-  const uint32_t rdy = (uint32_t)reinterpret_cast<uintptr_t>(ready);
-  const uint32_t cons = (uint32_t)reinterpret_cast<uintptr_t>(consumed);
-  uint32_t s_t, s_tn, s_exp, s_slot, s_off, s_fa, s_fl, s_c, v_cur, v_nxt, v_fa, v_fl, v_tmp;
-  uint64_t s_ex;
-  __asm__ volatile(
-      // block 0: wait for its flag, then issue steps 0 and 1
-      "s_mov_b32 %[t], 0\n\t"
-      "s_mov_b32 %[exp], %[base]\n\t"
-      "s_and_b32 %[slot], %[exp], 7\n\t"
-      "s_lshl_b32 %[fa], %[slot], 2\n\t"
-      "s_add_u32 %[fa], %[fa], %[rdy]\n\t"
-      "v_mov_b32 %[vfa], %[fa]\n"
-      "HOT_W0_%=:\n\t"
-      "ds_read_b32 %[vfl], %[vfa]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_readfirstlane_b32 %[fl], %[vfl]\n\t"
-      "s_cmp_eq_u32 %[fl], %[exp]\n\t"
-      "s_cbranch_scc1 HOT_R0_%=\n\t"
-      "s_sleep 1\n\t"
-      "s_branch HOT_W0_%=\n"
-      "HOT_R0_%=:\n\t"
-      "s_mul_i32 %[off], %[slot], 0x4400\n\t"
-      "v_add_u32 %[cur], %[off], %[col]\n\t"
-      HOT_RD_A(cur) HOT_RD_B(cur)
-      "HOT_L_%=:\n\t"
-      // the next block (after the last one, this block again: those reads are dropped)
-      "s_add_u32 %[tn], %[t], 1\n\t"
-      "s_cmp_lt_u32 %[tn], %[nfull]\n\t"
-      "s_cselect_b32 %[tn], %[tn], %[t]\n\t"
-      "s_add_u32 %[exp], %[base], %[tn]\n\t"
-      "s_and_b32 %[slot], %[exp], 7\n\t"
-      "s_mul_i32 %[off], %[slot], 0x4400\n\t"
-      "v_add_u32 %[nxt], %[off], %[col]\n\t"
-      "s_lshl_b32 %[fa], %[slot], 2\n\t"
-      "s_add_u32 %[fa], %[fa], %[rdy]\n\t"
-      "v_mov_b32 %[vfa], %[fa]\n\t"
-      // step 0: A in flight or done, B, C younger
-      HOT_RD_C(cur)
-      "s_waitcnt lgkmcnt(8)\n\t"
-      HOT_ADDS_A
-      // step 1: this block's last reads, then its release
-      HOT_RD_D(cur)
-      "s_add_u32 %[c], %[base], %[t]\n\t"
-      "s_add_u32 %[c], %[c], 1\n\t"
-      "v_mov_b32 %[tmp], %[c]\n\t"
-      "s_mov_b64 %[ex], exec\n\t"
-      "s_mov_b64 exec, 1\n\t"
-      "ds_write_b32 %[cons], %[tmp]\n\t"
-      "s_mov_b64 exec, %[ex]\n\t"
-      "s_waitcnt lgkmcnt(9)\n\t"
-      HOT_ADDS_B
-      // step 2: the next block's flag and its step 0
-      "ds_read_b32 %[vfl], %[vfa]\n\t"
-      HOT_RD_A(nxt)
-      "s_waitcnt lgkmcnt(10)\n\t"
-      HOT_ADDS_C
-      // step 3: the next block's step 1
-      HOT_RD_B(nxt)
-      "s_waitcnt lgkmcnt(10)\n\t"
-      HOT_ADDS_D
-      "s_add_u32 %[t], %[t], 1\n\t"
-      "s_cmp_ge_u32 %[t], %[nfull]\n\t"
-      "s_cbranch_scc1 HOT_D_%=\n\t"
-      "s_waitcnt lgkmcnt(8)\n\t"
-      "v_readfirstlane_b32 %[fl], %[vfl]\n\t"
-      "v_mov_b32 %[cur], %[nxt]\n\t"
-      "s_cmp_eq_u32 %[fl], %[exp]\n\t"
-      "s_cbranch_scc1 HOT_L_%=\n\t"
-      // the flag was not up when read: drop those reads, wait, read again
-      "s_waitcnt lgkmcnt(0)\n"
-      "HOT_S_%=:\n\t"
-      "s_sleep 1\n\t"
-      "ds_read_b32 %[vfl], %[vfa]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_readfirstlane_b32 %[fl], %[vfl]\n\t"
-      "s_cmp_eq_u32 %[fl], %[exp]\n\t"
-      "s_cbranch_scc0 HOT_S_%=\n\t"
-      HOT_RD_A(cur) HOT_RD_B(cur)
-      "s_branch HOT_L_%=\n"
-      "HOT_D_%=:\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      : [acc] "+v"(acc), [t] "=&s"(s_t), [tn] "=&s"(s_tn), [exp] "=&s"(s_exp), [slot] "=&s"(s_slot),
-        [off] "=&s"(s_off), [fa] "=&s"(s_fa), [fl] "=&s"(s_fl), [c] "=&s"(s_c), [ex] "=&s"(s_ex),
-        [cur] "=&v"(v_cur), [nxt] "=&v"(v_nxt), [vfa] "=&v"(v_fa), [vfl] "=&v"(v_fl), [tmp] "=&v"(v_tmp)
-      : [base] "s"(base), [nfull] "s"(nfull), [rdy] "s"(rdy), [col] "v"(col), [cons] "v"(cons)
-      : "memory", "scc",
-        "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204",
-        "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217",
-        "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230",
-        "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243",
-        "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
-}
-#undef HOT_RD
-#undef HOT_RD_A
-#undef HOT_RD_B
-#undef HOT_RD_C
-#undef HOT_RD_D
-#undef HOT_ADD
-#undef HOT_ADD4
-#undef HOT_ADDS_A
-#undef HOT_ADDS_B
-#undef HOT_ADDS_C
-#undef HOT_ADDS_D
-
-// Hot segments (first phase of the apply kernel).  A block (7 waves) takes
-// (segment, 64-column slice) items from a global counter until none is left.  Wave kAdder is the adder (the only wave on its
-// SIMD when the waves are placed round-robin): lane j owns column j of the
-// slice and adds the occurrences in sorted order, reading them from LDS.
-// The other six waves are loaders: block t of the segment (occurrences
-// 64t..64t+63) goes to ring slot (running block number) mod kSlots, loaded
-// by loader t mod 6.  A slot is column-major (column c's 64 occurrences are
-// contiguous, rows padded to kRS floats), so the adder reads four
-// consecutive occurrences of its column with one 16-byte LDS read.  A loader lane loads a 4 x 4 piece
-// (4 occurrences x 4 columns) of the block into registers, transposes it
-// and writes four 16-byte column pieces.  Hand-over per slot: the loader
-// waits until the adder has finished the slot's previous block
-// ("consumed"), writes, and publishes the running block number in
-// ready[slot].
-struct HotLds {
-  float ring[kSlots][64 * kRS];
-  int32_t ready[kSlots];
-  int32_t consumed;
-  uint32_t s_item;
-  int32_t s_seg;
-  uint32_t cls_first[kHotClassMax + 1];  // first hot run number of each class (classes longest first)
-  uint32_t cls_end[kHotClassMax + 1];
-  uint32_t cls_base[kHotClassMax + 1];   // its list's first slot
-  uint32_t s_items;
-};
-
-__device__ __forceinline__ void hot_phase(HotLds& sm, float* const* __restrict__ tables, int d, int row_bits,
-                                          const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ bags,
-                                          const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
-                                          const uint32_t* __restrict__ counters, int64_t n,
-                                          const float* __restrict__ G,
-                                          int64_t g_ld, int64_t g_col0, float lr,
-                                          uint32_t* __restrict__ next_item) {
-  auto& ring = sm.ring;
-  auto& ready = sm.ready;
-  auto& consumed = sm.consumed;
-  auto& s_item = sm.s_item;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kSlots) ready[tid] = -1;
-  if (tid == 0) consumed = 0;
-  const uint32_t row_mask = (row_bits >= 32) ? 0xffffffffu : ((1u << row_bits) - 1u);
-  const int slices = (d + 63) >> 6;
-  // the class table, once per block (the item loop resolves a run number
-  // from LDS)
-  if (tid == 0) {
-    uint32_t first = 0;
-    for (int c = kHotClassMax; c >= kHotClassMin; --c) {
-      const uint32_t k = counters[kHotCountBase + c];
-      sm.cls_first[c] = first;
-      sm.cls_end[c] = first + k;
-      sm.cls_base[c] = (uint32_t)hot_class_base(n, c);
-      first += k;
-    }
-    sm.s_items = first * (uint32_t)slices;
-  }
-  int32_t base = 0;  // running block number of this block's first ring use in the current item
-  for (;;) {
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t it = atomicAdd(next_item, 1u);
-      s_item = it;
-      if (it < sm.s_items) {
-        const uint32_t run = it / (uint32_t)slices;
-        int c = kHotClassMax;
-        while (c > kHotClassMin && run >= sm.cls_end[c]) --c;
-        sm.s_seg = hot[sm.cls_base[c] + run - sm.cls_first[c]];
-      }
-    }
-    __syncthreads();
-    const uint32_t item = s_item;
-    if (item >= sm.s_items) break;
-    const int32_t s = sm.s_seg;
-    const int col0 = (int)(item % slices) * 64;
-    const int cols = min(64, d - col0);
-    const int32_t beg = seg_start[s], end = seg_start[s + 1];
-    const uint32_t key = seg_key[s];
-    const int k = (int)(key >> row_bits);
-    const int64_t r = (int64_t)(key & row_mask);
-    const int32_t nblk = (end - beg + kHB - 1) / kHB;
-    if (wave == kAdder) {
-      const int32_t len = end - beg;
-      const int32_t nfull = len / kHB;
-      float acc = 0.f;
-      if (nfull > 0) hot_adder_full_blocks(acc, base, nfull, &ring[0][lane * kRS], ready, &consumed);
-      if (nfull * kHB < len) {  // the last, partial block
-        const int32_t t = nfull;
-        while (lds_load(&ready[(base + t) & (kSlots - 1)]) != base + t) __builtin_amdgcn_s_sleep(1);
-        compiler_fence();
-        const float* col = &ring[(base + t) & (kSlots - 1)][lane * kRS];
-        for (int o = 0; o < len - nfull * kHB; ++o) acc = acc + col[o];
-        compiler_fence();
-        if (lane == 0) consumed = base + t + 1;
-      }
-      if (lane < cols) {
-        float* t = tables[k] + r * d + col0 + lane;
-        *t = __fsub_rn(*t, __fmul_rn(lr, acc));
-      }
-    } else {
-      // Loader: lane (c4, sub) = (lane / 4, lane % 4) brings columns
-      // 4 c4 .. 4 c4 + 3 of occurrences 4 (sub + 4 m) + r (m, r = 0..3): 16
-      // global loads of 16 bytes, each 4 x 4 piece transposed in registers
-      // and written as four 16-byte column pieces.  Three blocks of the
-      // wave are in flight: while block t is written to its slot, the rows
-      // of its next block (t + kLoaders) are loading and the bag ids of the
-      // one after.
-      const int c4 = min(lane >> 2, cols / 4 - 1);
-      const int sub = lane & 3;
-      const float* gsrc = G + g_col0 + (int64_t)k * d + col0 + 4 * c4;
-      auto occ = [&](int i) { return 4 * (sub + 4 * (i >> 2)) + (i & 3); };
-      auto load_bags = [&](int32_t t, int32_t (&bag)[16]) {
-        const int32_t q0 = beg + t * kHB, last = end - 1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bag[i] = bags[min(q0 + occ(i), last)];
-      };
-      // rows of a partial block past its end re-read its last row (bag ids
-      // were clamped); the adder never reads them
-      auto load_rows = [&](const int32_t (&bag)[16], float4 (&v)[16]) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const float4*>(gsrc + (int64_t)bag[i] * g_ld);
-      };
-      int32_t t = wave < kAdder ? wave : wave - 1;
-      int32_t bag[16];
-      float4 v[16];
-      if (t < nblk) {
-        load_bags(t, bag);
-        load_rows(bag, v);
-        if (t + kLoaders < nblk) load_bags(t + kLoaders, bag);
-      }
-      for (; t < nblk; t += kLoaders) {
-        const int32_t g = base + t;
-        const int slot = g & (kSlots - 1);
-        float4 vn[16];
-        if (t + kLoaders < nblk) {
-          load_rows(bag, vn);
-          if (t + 2 * kLoaders < nblk) load_bags(t + 2 * kLoaders, bag);
-        }
-        while (lds_load(&consumed) < g - kSlots + 1) __builtin_amdgcn_s_sleep(1);
-        compiler_fence();
-        float* dst = &ring[slot][0];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float4 a = v[4 * m], b = v[4 * m + 1], c = v[4 * m + 2], e = v[4 * m + 3];
-          float* p = dst + (4 * c4) * kRS + 4 * (sub + 4 * m);
-          *reinterpret_cast<float4*>(p) = make_float4(a.x, b.x, c.x, e.x);
-          *reinterpret_cast<float4*>(p + kRS) = make_float4(a.y, b.y, c.y, e.y);
-          *reinterpret_cast<float4*>(p + 2 * kRS) = make_float4(a.z, b.z, c.z, e.z);
-          *reinterpret_cast<float4*>(p + 3 * kRS) = make_float4(a.w, b.w, c.w, e.w);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slot is written before its flag
-        compiler_fence();
-        if (lane == 0) lds_store(&ready[slot], g);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = vn[i];
-      }
-    }
-    base += nblk;
-  }
-}
-
 // Short segments (per wave).  A wave takes 64 consecutive segments from a
 // shared counter (waves that start early and late share the work as they
 // come) and loads what every one of them needs first at once, one segment
@@ -881,20 +572,7 @@ __device__ __forceinline__ void light_phase(float* const* __restrict__ tables, i
   }
 }
 
-// The hot segments alone (the two-stream form: the short ones run beside it
-// on the caller's second stream).
-__global__ __launch_bounds__(kApplyThreads) void hot_sgd_kernel(
-    float* const* __restrict__ tables, int d, int row_bits, const uint32_t* __restrict__ seg_key,
-    const int32_t* __restrict__ bags, const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
-    const uint32_t* __restrict__ counters, int64_t n, const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
-    float lr,
-    uint32_t* __restrict__ next_item) {
-  __shared__ __attribute__((aligned(16))) HotLds sm;
-  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, counters, n, G, g_ld, g_col0, lr, next_item);
-}
-
-// The short segments alone (many small persistent blocks; the two-stream
-// form).
+// The short segments (many small persistent blocks).
 template <int V>
 __global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict__ tables, int d, int g_log2,
                                                         int row_bits, const uint32_t* __restrict__ seg_key,
@@ -906,19 +584,222 @@ __global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict
   light_phase<V, 8 / V>(tables, d, g_log2, row_bits, seg_key, bags, seg_start, nseg, G, g_ld, g_col0, lr, next);
 }
 
-// The segment sums and the in-place update: hot items first, then the
-// short segments, in one launch (one block per CU).
-template <int V>
-__global__ __launch_bounds__(kApplyThreads) void sgd_apply_kernel(
-    float* const* __restrict__ tables, int d, int g_log2, int row_bits, const uint32_t* __restrict__ seg_key,
-    const int32_t* __restrict__ bags, const int32_t* __restrict__ seg_start, const int32_t* __restrict__ hot,
-    const uint32_t* __restrict__ counters, int64_t n, const float* __restrict__ G, int64_t g_ld, int64_t g_col0,
-    float lr, uint32_t* __restrict__ next) {
-  __shared__ __attribute__((aligned(16))) HotLds sm;
-  // counters: [0] segments, hot runs per class; next: [0] hot item, [1] short-segment chunk
-  hot_phase(sm, tables, d, row_bits, seg_key, bags, seg_start, hot, counters, n, G, g_ld, g_col0, lr, &next[0]);
-  light_phase<V, 16 / V>(tables, d, g_log2, row_bits, seg_key, bags, seg_start, &counters[0], G, g_ld, g_col0, lr,
-                         &next[1]);
+// Hot runs.  Run number u counts the runs class by class, longest class
+// first, in list order; hot_scan_kernel gives run u its segment (hseg[u])
+// and its first block number (hoff[u], an exclusive scan of the block
+// counts ceil(length / kHot)); hot_map_kernel describes every block
+// (occurrences [beg, end), key); hot_part_kernel sums each block's gradient
+// rows in sorted order from +0 into hpart[block]; hot_final_kernel adds a
+// run's block sums in order from +0 and updates the row.
+struct HotBlock {
+  int32_t beg, end;
+  uint32_t key;
+  int32_t pad;
+};
+constexpr int kHotRunsAt = 4, kHotBlocksAt = 5;  // counters[]: hot runs, hot blocks
+
+// one block of RT threads
+__global__ __launch_bounds__(RT) void hot_scan_kernel(const int32_t* __restrict__ seg_start,
+                                                      const int32_t* __restrict__ hot,
+                                                      uint32_t* __restrict__ counters, int64_t n,
+                                                      int32_t* __restrict__ hseg, int32_t* __restrict__ hoff) {
+  __shared__ uint32_t cls_first[kHotClassMax + 1], cls_end[kHotClassMax + 1], s_wave[4];
+  if (threadIdx.x == 0) {
+    uint32_t first = 0;
+    for (int c = kHotClassMax; c >= kHotClassMin; --c) {
+      cls_first[c] = first;
+      first += counters[kHotCountBase + c];
+      cls_end[c] = first;
+    }
+  }
+  __syncthreads();
+  const uint32_t total = cls_end[kHotClassMin];
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < total; base += RT) {
+    const uint32_t u = base + threadIdx.x;
+    uint32_t nb = 0;
+    if (u < total) {
+      int c = kHotClassMax;
+      while (c > kHotClassMin && u >= cls_end[c]) --c;
+      const int32_t sg = hot[hot_class_base(n, c) + (u - cls_first[c])];
+      hseg[u] = sg;
+      nb = (uint32_t)((seg_start[sg + 1] - seg_start[sg] + kHot - 1) / kHot);
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan(nb, s_wave, &tot);
+    if (u < total) hoff[u] = (int32_t)(carry + ex);
+    carry += tot;
+  }
+  if (threadIdx.x == 0) {
+    hoff[total] = (int32_t)carry;
+    counters[kHotRunsAt] = total;
+    counters[kHotBlocksAt] = carry;
+  }
+}
+
+// one wave per run (grid-stride), lanes over its blocks
+__global__ __launch_bounds__(256) void hot_map_kernel(const int32_t* __restrict__ seg_start,
+                                                      const uint32_t* __restrict__ seg_key,
+                                                      const uint32_t* __restrict__ counters,
+                                                      const int32_t* __restrict__ hseg,
+                                                      const int32_t* __restrict__ hoff,
+                                                      HotBlock* __restrict__ blocks) {
+  const uint32_t total = counters[kHotRunsAt];
+  const int lane = threadIdx.x & 63;
+  const uint32_t waves = gridDim.x * (blockDim.x >> 6);
+  for (uint32_t u = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); u < total; u += waves) {
+    const int32_t sg = hseg[u], q0 = hoff[u], nb = hoff[u + 1] - q0;
+    const int32_t beg = seg_start[sg], end = seg_start[sg + 1];
+    const uint32_t key = seg_key[sg];
+    for (int32_t j = lane; j < nb; j += 64) {
+      HotBlock hb;
+      hb.beg = beg + j * kHot;
+      hb.end = min(end, hb.beg + kHot);
+      hb.key = key;
+      hb.pad = 0;
+      blocks[q0 + j] = hb;
+    }
+  }
+}
+
+// A group of 2^g_log2 lanes per item (V float4 of a row per lane, the
+// columns of a slice); the groups of a wave walk the items with the grid's
+// stride.
+struct Groups {
+  int gl, grp, per_wave, GL;
+  __device__ Groups(int g_log2) {
+    const int lane = threadIdx.x & 63;
+    GL = 1 << g_log2;
+    gl = lane & (GL - 1);
+    grp = lane >> g_log2;
+    per_wave = 64 >> g_log2;
+  }
+  __device__ uint32_t first() const {
+    return (uint32_t)((blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * per_wave + grp);
+  }
+  __device__ uint32_t stride() const { return (uint32_t)(gridDim.x * (blockDim.x >> 6) * per_wave); }
+};
+
+template <int V, int U>
+__global__ __launch_bounds__(256) void hot_part_kernel(int d, int g_log2, int row_bits,
+                                                       const HotBlock* __restrict__ blocks,
+                                                       const uint32_t* __restrict__ counters,
+                                                       const int32_t* __restrict__ bags, const float* __restrict__ G,
+                                                       int64_t g_ld, int64_t g_col0, float* __restrict__ hpart) {
+  const Groups gp(g_log2);
+  const int d4 = d >> 2, cols4 = gp.GL * V;  // float4 columns per slice
+  const int slices = (d4 + cols4 - 1) / cols4;
+  const uint32_t items = counters[kHotBlocksAt] * (uint32_t)slices;
+  for (uint32_t it = gp.first(); it < items; it += gp.stride()) {
+    const uint32_t q = it / (uint32_t)slices;
+    const int c40 = (int)(it - q * (uint32_t)slices) * cols4;
+    const HotBlock hb = blocks[q];
+    const int k = (int)(hb.key >> row_bits);
+    const float* gbase = G + g_col0 + (int64_t)k * d;
+    float4 acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int32_t p0 = hb.beg; p0 < hb.end; p0 += gp.GL) {
+      const int m = min(gp.GL, hb.end - p0);
+      const int32_t my_bag = gp.gl < m ? bags[p0 + gp.gl] : 0;
+      for (int u0 = 0; u0 < m; u0 += U) {
+        float4 vv[U][V];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = u0 + u < m;
+          const int64_t bag = __shfl(my_bag, ok ? u0 + u : 0, gp.GL);
+          const float4* grow = reinterpret_cast<const float4*>(gbase + bag * g_ld);
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            const int c4 = c40 + gp.gl + v * gp.GL;
+            vv[u][v] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (u0 + u < m) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+              acc[v].x = acc[v].x + vv[u][v].x;
+              acc[v].y = acc[v].y + vv[u][v].y;
+              acc[v].z = acc[v].z + vv[u][v].z;
+              acc[v].w = acc[v].w + vv[u][v].w;
+            }
+          }
+        }
+      }
+    }
+    float4* dst = reinterpret_cast<float4*>(hpart + (int64_t)q * d);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int c4 = c40 + gp.gl + v * gp.GL;
+      if (c4 < d4) dst[c4] = acc[v];
+    }
+  }
+}
+
+template <int V, int U>
+__global__ __launch_bounds__(256) void hot_final_kernel(float* const* __restrict__ tables, int d, int g_log2,
+                                                        int row_bits, const uint32_t* __restrict__ counters,
+                                                        const int32_t* __restrict__ hseg,
+                                                        const int32_t* __restrict__ hoff,
+                                                        const uint32_t* __restrict__ seg_key,
+                                                        const float* __restrict__ hpart, float lr) {
+  const Groups gp(g_log2);
+  const uint32_t row_mask = (row_bits >= 32) ? 0xffffffffu : ((1u << row_bits) - 1u);
+  const int d4 = d >> 2, cols4 = gp.GL * V;
+  const int slices = (d4 + cols4 - 1) / cols4;
+  const uint32_t items = counters[kHotRunsAt] * (uint32_t)slices;
+  for (uint32_t it = gp.first(); it < items; it += gp.stride()) {
+    const uint32_t u = it / (uint32_t)slices;
+    const int c40 = (int)(it - u * (uint32_t)slices) * cols4;
+    const int32_t q0 = hoff[u], q1 = hoff[u + 1];
+    const uint32_t key = seg_key[hseg[u]];
+    const int k = (int)(key >> row_bits);
+    const int64_t r = (int64_t)(key & row_mask);
+    float4 acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int32_t q = q0; q < q1; q += U) {
+      float4 vv[U][V];
+#pragma unroll
+      for (int u2 = 0; u2 < U; ++u2) {
+        const int32_t qq = q + u2 < q1 ? q + u2 : q1 - 1;
+        const float4* src = reinterpret_cast<const float4*>(hpart + (int64_t)qq * d);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int c4 = c40 + gp.gl + v * gp.GL;
+          vv[u2][v] = c4 < d4 ? src[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u2 = 0; u2 < U; ++u2) {
+        if (q + u2 < q1) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            acc[v].x = acc[v].x + vv[u2][v].x;
+            acc[v].y = acc[v].y + vv[u2][v].y;
+            acc[v].z = acc[v].z + vv[u2][v].z;
+            acc[v].w = acc[v].w + vv[u2][v].w;
+          }
+        }
+      }
+    }
+    float4* trow = reinterpret_cast<float4*>(tables[k] + r * d);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int c4 = c40 + gp.gl + v * gp.GL;
+      if (c4 < d4) {
+        const float4 t = trow[c4];
+        float4 o;
+        o.x = __fsub_rn(t.x, __fmul_rn(lr, acc[v].x));
+        o.y = __fsub_rn(t.y, __fmul_rn(lr, acc[v].y));
+        o.z = __fsub_rn(t.z, __fmul_rn(lr, acc[v].z));
+        o.w = __fsub_rn(t.w, __fmul_rn(lr, acc[v].w));
+        trow[c4] = o;
+      }
+    }
+  }
 }
 
 int bits_for(int64_t x) {  // bits needed to hold 0..x
@@ -928,16 +809,20 @@ int bits_for(int64_t x) {  // bits needed to hold 0..x
 }
 
 struct SparseLayout {
-  size_t keys[2], vals[2], counts, sums, offsets, seg, seg_key, counters, hot, bytes;
+  size_t keys[2], vals[2], counts, sums, offsets, seg, seg_key, counters, hot, hseg, hoff, hblocks, hpart, bytes;
   int64_t tiles;
 };
 
-// counters: [0] segments, [2] next hot item, [3] next short-segment chunk,
-// [kHotCountBase + c] hot runs of class c (cleared on every prepare)
+// counters: [0] segments, [3] next short-segment chunk, [kHotRunsAt] hot
+// runs, [kHotBlocksAt] their blocks, [kHotCountBase + c] hot runs of class
+// c (cleared on every prepare)
 constexpr int kCounters = 48;
 static_assert(kHotCountBase + kHotClassMax < kCounters, "hot class counters");
 
-void sparse_layout(int64_t nnz, SparseLayout* L) {
+// Everything up to the hot-run buffers is what the prepare step needs; the
+// block sums (n / 64 blocks at most: a run of L >= kHot occurrences has
+// ceil(L / kHot) < 2 L / kHot blocks) take d floats each and come last.
+void sparse_layout(int64_t nnz, int d, SparseLayout* L) {
   Carver cv(nullptr);
   auto take = [&](size_t bytes) {
     cv.used = (size_t)round_up((int64_t)cv.used, 256);
@@ -958,6 +843,11 @@ void sparse_layout(int64_t nnz, SparseLayout* L) {
   L->seg_key = take(4 * (size_t)n);
   L->counters = take(4 * (size_t)kCounters);
   L->hot = take(4 * (size_t)hot_class_base(n, kHotClassMax + 1));
+  const int64_t max_runs = n / kHot + 1, max_blocks = n / (kHot / 2) + 1;
+  L->hseg = take(4 * (size_t)max_runs);
+  L->hoff = take(4 * (size_t)(max_runs + 1));
+  L->hblocks = take(sizeof(HotBlock) * (size_t)max_blocks);
+  L->hpart = take(4 * (size_t)max_blocks * (size_t)(d > 0 ? d : 0));
   L->bytes = cv.bytes();
 }
 
@@ -970,9 +860,9 @@ __global__ void zero_u32_kernel(uint32_t* p, int n) {
 
 namespace dlrm {
 namespace {
-int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_key, const int32_t* vals,
-                 const int32_t* seg, const int32_t* hot, uint32_t* counters, int64_t n, const float* G,
-                 int64_t g_ld, int64_t g_col0, float lr, hipStream_t stream, hipStream_t side);
+struct SparseBufs;
+int sgd_segments(float* const* tables, int d, int row_bits, int cur, const SparseBufs& b, int64_t n,
+                 const float* G, int64_t g_ld, int64_t g_col0, float lr, hipStream_t stream, hipStream_t side);
 }  // namespace
 }  // namespace dlrm
 
@@ -981,10 +871,9 @@ using namespace dlrm;
 extern "C" size_t dlrm_embbag_bwd_sgd_workspace_size(int32_t K, int64_t B, int64_t nnz, int32_t d) {
   (void)K;
   (void)B;
-  (void)d;
-  if (nnz < 0) return 0;
+  if (nnz < 0 || d < 0) return 0;
   SparseLayout L;
-  sparse_layout(nnz, &L);
+  sparse_layout(nnz, d, &L);
   return L.bytes;
 }
 
@@ -1015,10 +904,15 @@ struct SparseBufs {
   uint32_t* seg_key;
   uint32_t* counters;
   int32_t* hot;
+  int32_t* hseg;
+  int32_t* hoff;
+  HotBlock* hblocks;
+  float* hpart;
 };
 
-int sparse_bufs(int64_t nnz, void* ws, size_t ws_bytes, SparseLayout* L, SparseBufs* b) {
-  sparse_layout(nnz, L);
+// d = 0: the prepare step's view (no block sums)
+int sparse_bufs(int64_t nnz, int d, void* ws, size_t ws_bytes, SparseLayout* L, SparseBufs* b) {
+  sparse_layout(nnz, d, L);
   if (!ws || ws_bytes < L->bytes) return DLRM_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 255u) return DLRM_E_INVALID;
   char* w = static_cast<char*>(ws);
@@ -1033,6 +927,10 @@ int sparse_bufs(int64_t nnz, void* ws, size_t ws_bytes, SparseLayout* L, SparseB
   b->seg_key = reinterpret_cast<uint32_t*>(w + L->seg_key);
   b->counters = reinterpret_cast<uint32_t*>(w + L->counters);
   b->hot = reinterpret_cast<int32_t*>(w + L->hot);
+  b->hseg = reinterpret_cast<int32_t*>(w + L->hseg);
+  b->hoff = reinterpret_cast<int32_t*>(w + L->hoff);
+  b->hblocks = reinterpret_cast<HotBlock*>(w + L->hblocks);
+  b->hpart = reinterpret_cast<float*>(w + L->hpart);
   return DLRM_OK;
 }
 
@@ -1062,7 +960,7 @@ extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const
   if (nnz == 0) return DLRM_OK;
   SparseLayout L;
   SparseBufs b;
-  if ((rc = sparse_bufs(nnz, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
+  if ((rc = sparse_bufs(nnz, 0, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
   const int n = (int)nnz;
   const int64_t KB = (int64_t)K * B;
 
@@ -1110,20 +1008,14 @@ extern "C" int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_
   if (nnz == 0) return DLRM_OK;
   SparseLayout L;
   SparseBufs b;
-  if ((rc = sparse_bufs(nnz, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
+  if ((rc = sparse_bufs(nnz, d, ws, ws_bytes, &L, &b)) != DLRM_OK) return rc;
   const int cur = sort_plan(row_bits).passes & 1;
-  // the work counters start from zero on every call, so one prepared
-  // workspace can be applied more than once; each stream clears the counter
-  // its own kernel takes work from
-  if (side) {
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters + 2, 1);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, side, b.counters + 3, 1);
-  } else {
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, b.counters + 2, 2);
-  }
+  // the short segments' work counter starts from zero on every call, so one
+  // prepared workspace can be applied more than once; it is cleared on the
+  // stream whose kernel takes work from it
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, side ? side : stream, b.counters + 3, 1);
   if (launch_status() != DLRM_OK) return DLRM_E_HIP;
-  return sgd_segments(tables, d, row_bits, b.seg_key, b.vals[cur], b.seg, b.hot, b.counters, nnz, G, g_ld, g_col0,
-                      lr, stream, side);
+  return sgd_segments(tables, d, row_bits, cur, b, nnz, G, g_ld, g_col0, lr, stream, side);
 }
 
 // ------------------------------------------------------------------ no-allocation form
@@ -1165,8 +1057,9 @@ extern "C" int dlrm_embbag_bwd_sgd_noalloc(float* const* tables, int32_t K, int3
                                            const float* G, int64_t g_ld, int64_t g_col0, float lr,
                                            hipStream_t stream) {
   if (nnz < 0 || nnz > 0x7fffffffLL) return DLRM_E_INVALID;
+  if (d < 0) return DLRM_E_INVALID;
   SparseLayout L;
-  sparse_layout(nnz, &L);
+  sparse_layout(nnz, d, &L);
   if (L.bytes > kNoallocScratchBytes) return DLRM_E_WORKSPACE;
   void* ws = noalloc_scratch();
   if (!ws) return DLRM_E_HIP;
@@ -1192,39 +1085,38 @@ extern "C" int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, c
 
 namespace dlrm {
 namespace {
-int sgd_segments(float* const* tables, int d, int row_bits, const uint32_t* seg_key, const int32_t* vals,
-                 const int32_t* seg, const int32_t* hot, uint32_t* counters, int64_t n, const float* G,
-                 int64_t g_ld, int64_t g_col0, float lr, hipStream_t stream, hipStream_t side) {
-  // short segments: half as many lanes as float4 columns (two float4 per
-  // lane), at most 64
+int sgd_segments(float* const* tables, int d, int row_bits, int cur, const SparseBufs& b, int64_t n,
+                 const float* G, int64_t g_ld, int64_t g_col0, float lr, hipStream_t stream, hipStream_t side) {
+  // lane groups: short segments with half as many lanes as float4 columns
+  // (two float4 per lane), hot blocks and runs with one float4 per lane;
+  // groups of at most 64 lanes
   const int d4 = d / 4;
   int l2 = 0;
   while ((1 << l2) < d4) ++l2;
   const int g_log2 = l2 > 0 ? (l2 - 1 < 6 ? l2 - 1 : 6) : 0;
   const int V = (d4 + (1 << g_log2) - 1) >> g_log2;
-  const dim3 cus((unsigned)device_cu_count()), apply_block(kApplyThreads);
-  if (side) {
-    // long segments on `stream`, short ones on `side` at the same time
-    hipLaunchKernelGGL(hot_sgd_kernel, cus, apply_block, 0, stream, tables, d, row_bits, seg_key, vals, seg,
-                       hot, counters, n, G, g_ld, g_col0, lr, counters + 2);
-    if (launch_status() != DLRM_OK) return DLRM_E_HIP;
-    const dim3 grid(kLightBlocks), block(256);
-#define DLRM_LIGHT(VV)                                                                                            \
-  hipLaunchKernelGGL((light_sgd_kernel<VV>), grid, block, 0, side, tables, d, g_log2, row_bits, seg_key, vals, seg, \
-                     counters, G, g_ld, g_col0, lr, counters + 3)
-    if (V == 1) DLRM_LIGHT(1);
-    else if (V == 2) DLRM_LIGHT(2);
-    else DLRM_LIGHT(4);
+  const int h_log2 = l2 < 6 ? l2 : 6;
+  const dim3 blk(256), hot_grid(kHotBlocks);
+  const int32_t* vals = b.vals[cur];
+  // hot runs on `stream`
+  hipLaunchKernelGGL(hot_scan_kernel, dim3(1), dim3(RT), 0, stream, b.seg, b.hot, b.counters, n, b.hseg, b.hoff);
+  hipLaunchKernelGGL(hot_map_kernel, hot_grid, blk, 0, stream, b.seg, b.seg_key, b.counters, b.hseg, b.hoff,
+                     b.hblocks);
+  hipLaunchKernelGGL((hot_part_kernel<1, 16>), hot_grid, blk, 0, stream, d, h_log2, row_bits, b.hblocks, b.counters,
+                     vals, G, g_ld, g_col0, b.hpart);
+  hipLaunchKernelGGL((hot_final_kernel<1, 16>), hot_grid, blk, 0, stream, tables, d, h_log2, row_bits, b.counters,
+                     b.hseg, b.hoff, b.seg_key, b.hpart, lr);
+  if (launch_status() != DLRM_OK) return DLRM_E_HIP;
+  // short segments beside them on `side`, or after them
+  const dim3 grid(kLightBlocks);
+  hipStream_t ls = side ? side : stream;
+#define DLRM_LIGHT(VV)                                                                                         \
+  hipLaunchKernelGGL((light_sgd_kernel<VV>), grid, blk, 0, ls, tables, d, g_log2, row_bits, b.seg_key, vals, b.seg, \
+                     b.counters, G, g_ld, g_col0, lr, b.counters + 3)
+  if (V == 1) DLRM_LIGHT(1);
+  else if (V == 2) DLRM_LIGHT(2);
+  else DLRM_LIGHT(4);
 #undef DLRM_LIGHT
-    return launch_status();
-  }
-#define DLRM_APPLY(VV)                                                                                          \
-  hipLaunchKernelGGL((sgd_apply_kernel<VV>), cus, apply_block, 0, stream, tables, d, g_log2, row_bits, seg_key, \
-                     vals, seg, hot, counters, n, G, g_ld, g_col0, lr, counters + 2)
-  if (V == 1) DLRM_APPLY(1);
-  else if (V == 2) DLRM_APPLY(2);
-  else DLRM_APPLY(4);
-#undef DLRM_APPLY
   return launch_status();
 }
 }  // namespace

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define DLRM_ABI_VERSION 4
+#define DLRM_ABI_VERSION 5
 
 enum {
   DLRM_OK = 0,
@@ -290,21 +290,27 @@ int dlrm_bce_grad(const float* logit, int64_t logit_ld, const float* y, int64_t 
 /*
  * Sparse embedding backward with row-wise SGD, in place.
  * Sum pooling passes each bag's gradient unchanged to every row it looked
- * up, once per occurrence.  For every row r of table k that the batch
- * touches:
- *     g = sum over r's occurrences p in table k's bags, ascending p, of
- *         G[b(p)*g_ld + g_col0 + k*d + c]          (fp32, from +0.0)
+ * up, once per occurrence ([EXPL] Key Method Details, Embedding tables;
+ * Loss).  For every row r of table k that the batch touches, with x_i =
+ * G[b(p_i)*g_ld + g_col0 + k*d + c] for r's occurrences p_0 < p_1 < ... in
+ * table k's bags:
+ *     S_j = x_{128j} + ... + x_{128j+127} (to the last occurrence), in
+ *           order, fp32 from +0.0
+ *     g   = S_0 + S_1 + ..., in order, fp32 from +0.0
  *     T_k[r][c] <- T_k[r][c] - (lr * g[c])         (two fp32 roundings)
- * computed by a stable radix sort of (table, row) keys, a run-length
- * segmentation and one serial fp32 sum per (row, column).  Untouched rows
- * are not written.  Bit-exact and deterministic.
+ * (the pages fix no order for the sum; up to 129 occurrences this is the
+ * plain left-to-right sum).  Computed by a stable radix sort of (table,
+ * row) keys and a run-length segmentation; the blocks of long rows are
+ * summed in parallel.  Untouched rows are not written.  Bit-exact and
+ * deterministic.
  *
  *   tables   device array of K device pointers, fp32 [m_k][d], updated.
  *   rows     host [K], m_k (bounds the key width: K * max m_k < 2^32).
  *   indices, offsets, B as for dlrm_embbag_fwd; nnz = offsets[K*B] (host).
  *   G        fp32 [B][g_ld]; bag (k, b)'s gradient at G[b*g_ld + g_col0 + k*d].
  *            B * g_ld * 4 < 2^31.
- *   ws       dlrm_embbag_bwd_sgd_workspace_size() bytes (256-byte aligned).
+ *   ws       dlrm_embbag_bwd_sgd_workspace_size() bytes for this d (256-byte
+ *            aligned).
  *   Limits:  d % 4 == 0, 4 <= d <= 1024, nnz < 2^31.
  */
 size_t dlrm_embbag_bwd_sgd_workspace_size(int32_t K, int64_t B, int64_t nnz, int32_t d);
@@ -329,8 +335,7 @@ int dlrm_embbag_bwd_sgd(float* const* tables, int32_t K, int32_t d, const int64_
  *   applying it again updates the same rows again (a second SGD step with
  *   the same indices).
  *   side (nullable): a second stream of the caller.  NULL: everything runs
- *   on `stream` in one launch.  Otherwise the long segments (Zipf heads,
- *   whose serial sums occupy a few CUs for the whole call) run on `stream`
+ *   on `stream`.  Otherwise the long segments (Zipf heads) run on `stream`
  *   and the short ones on `side` at the same time; the two touch disjoint
  *   rows.  The caller orders `side` after everything the call depends on
  *   (e.g. hipStreamWaitEvent(side, e) on an event e recorded on `stream`
@@ -352,8 +357,9 @@ int dlrm_embbag_bwd_sgd_apply(float* const* tables, int32_t K, int32_t d, const 
  * library: each GPU the library runs on holds one until the process ends.
  * The call allocates nothing (no hipMalloc, no hipFree).  Arguments, limits
  * and results as dlrm_embbag_bwd_sgd (bit for bit the same table rows);
- * nnz needing more scratch than the array holds (about 10.7 million lookups)
- * returns DLRM_E_WORKSPACE before anything is enqueued.  Every call on one
+ * nnz needing more scratch than the array holds (about 8.0 million lookups
+ * at d = 128, 10.2 million at d = 16, 3.0 million at d = 1024) returns
+ * DLRM_E_WORKSPACE before anything is enqueued.  Every call on one
  * GPU shares that GPU's array and leaves its contents behind: calls that
  * overlap on one GPU (on different streams, or from different threads
  * without ordering) race and are not allowed.

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_strings(lib):
-    assert C.dlrm_abi_version() == 4
+    assert C.dlrm_abi_version() == 5
     for code in (0, -1, -2, -3, -4):
         assert lib.dlrm_strerror(code)
     assert lib.dlrm_last_hip_error() == 0
