@@ -18,9 +18,10 @@
 //      of at least kHot occurrences ("hot", the Zipf heads with up to 10^5
 //      occurrences) are listed apart;
 //   4. the sums and the update T <- T - lr * g: short runs one lane group
-//      each, in sorted order; hot runs in three steps, their blocks' sums in
-//      parallel (one lane group per block), then per run the block sums in
-//      order and the update.  The blocked order keeps a 10^5-occurrence row
+//      each, in sorted order; hot runs in three steps, their block list
+//      (with the index work of steps 1-3), their blocks' sums in parallel
+//      (one lane group per block), then per run the block sums in order and
+//      the update.  The blocked order keeps a 10^5-occurrence row
 //      from being one serial chain of 10^5 dependent adds.
 #include "common.hpp"
 
@@ -614,20 +615,37 @@ __global__ __launch_bounds__(RT) void hot_scan_kernel(const int32_t* __restrict_
   }
   __syncthreads();
   const uint32_t total = cls_end[kHotClassMin];
+  constexpr int R = 8;  // runs per thread per round, their loads in flight together
   uint32_t carry = 0;
-  for (uint32_t base = 0; base < total; base += RT) {
-    const uint32_t u = base + threadIdx.x;
-    uint32_t nb = 0;
-    if (u < total) {
-      int c = kHotClassMax;
-      while (c > kHotClassMin && u >= cls_end[c]) --c;
-      const int32_t sg = hot[hot_class_base(n, c) + (u - cls_first[c])];
-      hseg[u] = sg;
-      nb = (uint32_t)((seg_start[sg + 1] - seg_start[sg] + kHot - 1) / kHot);
+  for (uint32_t base = 0; base < total; base += RT * R) {
+    const uint32_t u0 = base + threadIdx.x * R;
+    int32_t sg[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t u = u0 + i;
+      sg[i] = 0;
+      if (u < total) {
+        int c = kHotClassMax;
+        while (c > kHotClassMin && u >= cls_end[c]) --c;
+        sg[i] = hot[hot_class_base(n, c) + (u - cls_first[c])];
+      }
+    }
+    uint32_t nb[R], mine = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      nb[i] = u0 + i < total ? (uint32_t)((seg_start[sg[i] + 1] - seg_start[sg[i]] + kHot - 1) / kHot) : 0u;
+      mine += nb[i];
     }
     uint32_t tot;
-    const uint32_t ex = block_exclusive_scan(nb, s_wave, &tot);
-    if (u < total) hoff[u] = (int32_t)(carry + ex);
+    uint32_t at = carry + block_exclusive_scan(mine, s_wave, &tot);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (u0 + i < total) {
+        hseg[u0 + i] = sg[i];
+        hoff[u0 + i] = (int32_t)at;
+      }
+      at += nb[i];
+    }
     carry += tot;
   }
   if (threadIdx.x == 0) {
@@ -696,23 +714,36 @@ __global__ __launch_bounds__(256) void hot_part_kernel(int d, int g_log2, int ro
     const HotBlock hb = blocks[q];
     const int k = (int)(hb.key >> row_bits);
     const float* gbase = G + g_col0 + (int64_t)k * d;
-    float4 acc[V];
+    float4 acc[V], cur[V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int v = 0; v < V; ++v) {
+      acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+      cur[v] = acc[v];
+    }
+    // a long row's occurrences come in runs of one bag (a Zipf head shows
+    // up many times in one bag, and those positions are adjacent): a row
+    // is loaded only where the bag changes (all of a batch's loads go out
+    // first) and added again while it does not
+    int32_t last_bag = -1;
     for (int32_t p0 = hb.beg; p0 < hb.end; p0 += gp.GL) {
       const int m = min(gp.GL, hb.end - p0);
       const int32_t my_bag = gp.gl < m ? bags[p0 + gp.gl] : 0;
       for (int u0 = 0; u0 < m; u0 += U) {
         float4 vv[U][V];
+        bool fresh[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const bool ok = u0 + u < m;
-          const int64_t bag = __shfl(my_bag, ok ? u0 + u : 0, gp.GL);
-          const float4* grow = reinterpret_cast<const float4*>(gbase + bag * g_ld);
+          const int32_t bag = __shfl(my_bag, ok ? u0 + u : 0, gp.GL);
+          fresh[u] = ok && bag != last_bag;
+          if (ok) last_bag = bag;
+          if (fresh[u]) {
+            const float4* grow = reinterpret_cast<const float4*>(gbase + (int64_t)bag * g_ld);
 #pragma unroll
-          for (int v = 0; v < V; ++v) {
-            const int c4 = c40 + gp.gl + v * gp.GL;
-            vv[u][v] = (ok && c4 < d4) ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int v = 0; v < V; ++v) {
+              const int c4 = c40 + gp.gl + v * gp.GL;
+              vv[u][v] = c4 < d4 ? grow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
           }
         }
 #pragma unroll
@@ -720,10 +751,11 @@ __global__ __launch_bounds__(256) void hot_part_kernel(int d, int g_log2, int ro
           if (u0 + u < m) {
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-              acc[v].x = acc[v].x + vv[u][v].x;
-              acc[v].y = acc[v].y + vv[u][v].y;
-              acc[v].z = acc[v].z + vv[u][v].z;
-              acc[v].w = acc[v].w + vv[u][v].w;
+              if (fresh[u]) cur[v] = vv[u][v];
+              acc[v].x = acc[v].x + cur[v].x;
+              acc[v].y = acc[v].y + cur[v].y;
+              acc[v].z = acc[v].z + cur[v].z;
+              acc[v].w = acc[v].w + cur[v].w;
             }
           }
         }
@@ -992,6 +1024,11 @@ extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const
   hipLaunchKernelGGL(heads_scan_kernel, dim3(1), dim3(RT), 0, stream, b.counts, (int)tiles, n, b.seg, b.counters);
   hipLaunchKernelGGL(heads_write_kernel, dim3(tiles), dim3(RT), 0, stream, b.keys[cur], n, b.counts, b.seg,
                      b.seg_key, b.hot, b.counters);
+  // the hot runs' block list (indices only, so it belongs to this step)
+  hipLaunchKernelGGL(hot_scan_kernel, dim3(1), dim3(RT), 0, stream, b.seg, b.hot, b.counters, (int64_t)n, b.hseg,
+                     b.hoff);
+  hipLaunchKernelGGL(hot_map_kernel, dim3(kHotBlocks), dim3(256), 0, stream, b.seg, b.seg_key, b.counters, b.hseg,
+                     b.hoff, b.hblocks);
   return launch_status() != DLRM_OK ? DLRM_E_HIP : DLRM_OK;
 }
 
@@ -1098,13 +1135,10 @@ int sgd_segments(float* const* tables, int d, int row_bits, int cur, const Spars
   const int h_log2 = l2 < 6 ? l2 : 6;
   const dim3 blk(256), hot_grid(kHotBlocks);
   const int32_t* vals = b.vals[cur];
-  // hot runs on `stream`
-  hipLaunchKernelGGL(hot_scan_kernel, dim3(1), dim3(RT), 0, stream, b.seg, b.hot, b.counters, n, b.hseg, b.hoff);
-  hipLaunchKernelGGL(hot_map_kernel, hot_grid, blk, 0, stream, b.seg, b.seg_key, b.counters, b.hseg, b.hoff,
-                     b.hblocks);
+  // hot runs on `stream` (their block list came with the prepare step)
   hipLaunchKernelGGL((hot_part_kernel<1, 16>), hot_grid, blk, 0, stream, d, h_log2, row_bits, b.hblocks, b.counters,
                      vals, G, g_ld, g_col0, b.hpart);
-  hipLaunchKernelGGL((hot_final_kernel<1, 16>), hot_grid, blk, 0, stream, tables, d, h_log2, row_bits, b.counters,
+  hipLaunchKernelGGL((hot_final_kernel<1, 32>), hot_grid, blk, 0, stream, tables, d, h_log2, row_bits, b.counters,
                      b.hseg, b.hoff, b.seg_key, b.hpart, lr);
   if (launch_status() != DLRM_OK) return DLRM_E_HIP;
   // short segments beside them on `side`, or after them
