@@ -586,96 +586,91 @@ __global__ __launch_bounds__(256) void light_sgd_kernel(float* const* __restrict
 }
 
 // Hot runs.  Run number u counts the runs class by class, longest class
-// first, in list order; hot_scan_kernel gives run u its segment (hseg[u])
-// and its first block number (hoff[u], an exclusive scan of the block
-// counts ceil(length / kHot)); hot_map_kernel describes every block
-// (occurrences [beg, end), key); hot_part_kernel sums each block's gradient
-// rows in sorted order from +0 into hpart[block]; hot_final_kernel adds a
-// run's block sums in order from +0 and updates the row.
+// first, in list order.  hot_map_kernel gives run u its segment (hseg[u]),
+// reserves its ceil(length / kHot) blocks (hoff[u], hcnt[u]: an atomic
+// counter hands out the ranges, so where a run's blocks lie varies from
+// call to call, but not their order or their sums) and describes every
+// block (occurrences [beg, end), key); hot_part_kernel sums each block's
+// gradient rows in sorted order from +0 into hpart[block];
+// hot_final_kernel adds a run's block sums in order from +0 and updates the
+// row.
 struct HotBlock {
   int32_t beg, end;
   uint32_t key;
   int32_t pad;
 };
-constexpr int kHotRunsAt = 4, kHotBlocksAt = 5;  // counters[]: hot runs, hot blocks
-
-// one block of RT threads
-__global__ __launch_bounds__(RT) void hot_scan_kernel(const int32_t* __restrict__ seg_start,
-                                                      const int32_t* __restrict__ hot,
-                                                      uint32_t* __restrict__ counters, int64_t n,
-                                                      int32_t* __restrict__ hseg, int32_t* __restrict__ hoff) {
-  __shared__ uint32_t cls_first[kHotClassMax + 1], cls_end[kHotClassMax + 1], s_wave[4];
-  if (threadIdx.x == 0) {
-    uint32_t first = 0;
-    for (int c = kHotClassMax; c >= kHotClassMin; --c) {
-      cls_first[c] = first;
-      first += counters[kHotCountBase + c];
-      cls_end[c] = first;
-    }
-  }
-  __syncthreads();
-  const uint32_t total = cls_end[kHotClassMin];
-  constexpr int R = 8;  // runs per thread per round, their loads in flight together
-  uint32_t carry = 0;
-  for (uint32_t base = 0; base < total; base += RT * R) {
-    const uint32_t u0 = base + threadIdx.x * R;
-    int32_t sg[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const uint32_t u = u0 + i;
-      sg[i] = 0;
-      if (u < total) {
-        int c = kHotClassMax;
-        while (c > kHotClassMin && u >= cls_end[c]) --c;
-        sg[i] = hot[hot_class_base(n, c) + (u - cls_first[c])];
-      }
-    }
-    uint32_t nb[R], mine = 0;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      nb[i] = u0 + i < total ? (uint32_t)((seg_start[sg[i] + 1] - seg_start[sg[i]] + kHot - 1) / kHot) : 0u;
-      mine += nb[i];
-    }
-    uint32_t tot;
-    uint32_t at = carry + block_exclusive_scan(mine, s_wave, &tot);
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      if (u0 + i < total) {
-        hseg[u0 + i] = sg[i];
-        hoff[u0 + i] = (int32_t)at;
-      }
-      at += nb[i];
-    }
-    carry += tot;
-  }
-  if (threadIdx.x == 0) {
-    hoff[total] = (int32_t)carry;
-    counters[kHotRunsAt] = total;
-    counters[kHotBlocksAt] = carry;
-  }
-}
+constexpr int kHotRunsAt = 4, kHotBlocksAt = 5;  // counters[]: hot runs, hot blocks (cleared by the prepare)
 
 // one wave per run (grid-stride), lanes over its blocks
 __global__ __launch_bounds__(256) void hot_map_kernel(const int32_t* __restrict__ seg_start,
                                                       const uint32_t* __restrict__ seg_key,
-                                                      const uint32_t* __restrict__ counters,
-                                                      const int32_t* __restrict__ hseg,
-                                                      const int32_t* __restrict__ hoff,
+                                                      const int32_t* __restrict__ hot, int64_t n,
+                                                      uint32_t* __restrict__ counters, int32_t* __restrict__ hseg,
+                                                      int32_t* __restrict__ hoff, int32_t* __restrict__ hcnt,
                                                       HotBlock* __restrict__ blocks) {
-  const uint32_t total = counters[kHotRunsAt];
+  __shared__ uint32_t cls_first[kHotClassMax + 1], cls_end[kHotClassMax + 1], cls_cnt[kHotClassMax + 1];
+  if (threadIdx.x >= kHotClassMin && threadIdx.x <= kHotClassMax)  // the class counts, loaded side by side
+    cls_cnt[threadIdx.x] = counters[kHotCountBase + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t first = 0;
+    for (int c = kHotClassMax; c >= kHotClassMin; --c) {
+      cls_first[c] = first;
+      first += cls_cnt[c];
+      cls_end[c] = first;
+    }
+    if (blockIdx.x == 0) counters[kHotRunsAt] = first;
+  }
+  __syncthreads();
+  const uint32_t total = cls_end[kHotClassMin];
   const int lane = threadIdx.x & 63;
   const uint32_t waves = gridDim.x * (blockDim.x >> 6);
-  for (uint32_t u = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); u < total; u += waves) {
-    const int32_t sg = hseg[u], q0 = hoff[u], nb = hoff[u + 1] - q0;
-    const int32_t beg = seg_start[sg], end = seg_start[sg + 1];
-    const uint32_t key = seg_key[sg];
-    for (int32_t j = lane; j < nb; j += 64) {
-      HotBlock hb;
-      hb.beg = beg + j * kHot;
-      hb.end = min(end, hb.beg + kHot);
-      hb.key = key;
-      hb.pad = 0;
-      blocks[q0 + j] = hb;
+  // a wave takes 64 runs (one per lane) and reserves their blocks with one
+  // atomic (one counter shared by every wave: an atomic per run would queue)
+  // (runs gi, gi + groups, gi + 2 groups, ...: the classes are longest
+  // first, so each wave gets a share of the long runs' blocks to write)
+  const uint32_t groups = (total + 63) / 64;
+  for (uint32_t gi = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); gi < groups; gi += waves) {
+    const uint32_t u = gi + groups * (uint32_t)lane;
+    int32_t sg = 0, beg = 0, end = 0, nb = 0;
+    uint32_t key = 0;
+    if (u < total) {
+      int c = kHotClassMax;
+      while (c > kHotClassMin && u >= cls_end[c]) --c;
+      sg = hot[hot_class_base(n, c) + (u - cls_first[c])];
+      beg = seg_start[sg];
+      end = seg_start[sg + 1];
+      key = seg_key[sg];
+      nb = (end - beg + kHot - 1) / kHot;
+    }
+    int32_t incl = nb;  // inclusive prefix over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    int32_t base = 0;
+    if (lane == 63) base = (int32_t)atomicAdd(&counters[kHotBlocksAt], (uint32_t)incl);
+    base = __shfl(base, 63, 64);
+    const int32_t q0 = base + incl - nb;
+    if (u < total) {
+      hseg[u] = sg;
+      hoff[u] = q0;
+      hcnt[u] = nb;
+    }
+    for (int r = 0; r < 64; ++r) {  // every lane writes blocks of run r
+      const int32_t nbr = __shfl(nb, r, 64);
+      if (nbr == 0) continue;
+      const int32_t q0r = __shfl(q0, r, 64), begr = __shfl(beg, r, 64), endr = __shfl(end, r, 64);
+      const uint32_t keyr = (uint32_t)__shfl((int)key, r, 64);
+      for (int32_t j = lane; j < nbr; j += 64) {
+        HotBlock hb;
+        hb.beg = begr + j * kHot;
+        hb.end = min(endr, hb.beg + kHot);
+        hb.key = keyr;
+        hb.pad = 0;
+        blocks[q0r + j] = hb;
+      }
     }
   }
 }
@@ -775,6 +770,7 @@ __global__ __launch_bounds__(256) void hot_final_kernel(float* const* __restrict
                                                         int row_bits, const uint32_t* __restrict__ counters,
                                                         const int32_t* __restrict__ hseg,
                                                         const int32_t* __restrict__ hoff,
+                                                        const int32_t* __restrict__ hcnt,
                                                         const uint32_t* __restrict__ seg_key,
                                                         const float* __restrict__ hpart, float lr) {
   const Groups gp(g_log2);
@@ -785,7 +781,7 @@ __global__ __launch_bounds__(256) void hot_final_kernel(float* const* __restrict
   for (uint32_t it = gp.first(); it < items; it += gp.stride()) {
     const uint32_t u = it / (uint32_t)slices;
     const int c40 = (int)(it - u * (uint32_t)slices) * cols4;
-    const int32_t q0 = hoff[u], q1 = hoff[u + 1];
+    const int32_t q0 = hoff[u], q1 = q0 + hcnt[u];
     const uint32_t key = seg_key[hseg[u]];
     const int k = (int)(key >> row_bits);
     const int64_t r = (int64_t)(key & row_mask);
@@ -841,7 +837,7 @@ int bits_for(int64_t x) {  // bits needed to hold 0..x
 }
 
 struct SparseLayout {
-  size_t keys[2], vals[2], counts, sums, offsets, seg, seg_key, counters, hot, hseg, hoff, hblocks, hpart, bytes;
+  size_t keys[2], vals[2], counts, sums, offsets, seg, seg_key, counters, hot, hseg, hoff, hcnt, hblocks, hpart, bytes;
   int64_t tiles;
 };
 
@@ -877,7 +873,8 @@ void sparse_layout(int64_t nnz, int d, SparseLayout* L) {
   L->hot = take(4 * (size_t)hot_class_base(n, kHotClassMax + 1));
   const int64_t max_runs = n / kHot + 1, max_blocks = n / (kHot / 2) + 1;
   L->hseg = take(4 * (size_t)max_runs);
-  L->hoff = take(4 * (size_t)(max_runs + 1));
+  L->hoff = take(4 * (size_t)max_runs);
+  L->hcnt = take(4 * (size_t)max_runs);
   L->hblocks = take(sizeof(HotBlock) * (size_t)max_blocks);
   L->hpart = take(4 * (size_t)max_blocks * (size_t)(d > 0 ? d : 0));
   L->bytes = cv.bytes();
@@ -938,6 +935,7 @@ struct SparseBufs {
   int32_t* hot;
   int32_t* hseg;
   int32_t* hoff;
+  int32_t* hcnt;
   HotBlock* hblocks;
   float* hpart;
 };
@@ -961,6 +959,7 @@ int sparse_bufs(int64_t nnz, int d, void* ws, size_t ws_bytes, SparseLayout* L, 
   b->hot = reinterpret_cast<int32_t*>(w + L->hot);
   b->hseg = reinterpret_cast<int32_t*>(w + L->hseg);
   b->hoff = reinterpret_cast<int32_t*>(w + L->hoff);
+  b->hcnt = reinterpret_cast<int32_t*>(w + L->hcnt);
   b->hblocks = reinterpret_cast<HotBlock*>(w + L->hblocks);
   b->hpart = reinterpret_cast<float*>(w + L->hpart);
   return DLRM_OK;
@@ -1025,10 +1024,8 @@ extern "C" int dlrm_embbag_bwd_sgd_prepare(int32_t K, const int64_t* rows, const
   hipLaunchKernelGGL(heads_write_kernel, dim3(tiles), dim3(RT), 0, stream, b.keys[cur], n, b.counts, b.seg,
                      b.seg_key, b.hot, b.counters);
   // the hot runs' block list (indices only, so it belongs to this step)
-  hipLaunchKernelGGL(hot_scan_kernel, dim3(1), dim3(RT), 0, stream, b.seg, b.hot, b.counters, (int64_t)n, b.hseg,
-                     b.hoff);
-  hipLaunchKernelGGL(hot_map_kernel, dim3(kHotBlocks), dim3(256), 0, stream, b.seg, b.seg_key, b.counters, b.hseg,
-                     b.hoff, b.hblocks);
+  hipLaunchKernelGGL(hot_map_kernel, dim3(kHotBlocks), dim3(256), 0, stream, b.seg, b.seg_key, b.hot, (int64_t)n,
+                     b.counters, b.hseg, b.hoff, b.hcnt, b.hblocks);
   return launch_status() != DLRM_OK ? DLRM_E_HIP : DLRM_OK;
 }
 
@@ -1139,7 +1136,7 @@ int sgd_segments(float* const* tables, int d, int row_bits, int cur, const Spars
   hipLaunchKernelGGL((hot_part_kernel<1, 16>), hot_grid, blk, 0, stream, d, h_log2, row_bits, b.hblocks, b.counters,
                      vals, G, g_ld, g_col0, b.hpart);
   hipLaunchKernelGGL((hot_final_kernel<1, 32>), hot_grid, blk, 0, stream, tables, d, h_log2, row_bits, b.counters,
-                     b.hseg, b.hoff, b.seg_key, b.hpart, lr);
+                     b.hseg, b.hoff, b.hcnt, b.seg_key, b.hpart, lr);
   if (launch_status() != DLRM_OK) return DLRM_E_HIP;
   // short segments beside them on `side`, or after them
   const dim3 grid(kLightBlocks);
