@@ -444,9 +444,10 @@ __global__ __launch_bounds__(RT) void heads_write_kernel(const uint32_t* __restr
 
 // ------------------------------------------------------------------ reduce + SGD
 
-// Short segments (per wave).  A wave takes 64 consecutive segments from a
-// shared counter (waves that start early and late share the work as they
-// come) and loads what every one of them needs first at once, one segment
+// Short segments (per wave).  A wave takes 64 consecutive segments at a
+// time, its first chunk fixed and the others from a shared counter (waves
+// that start early and late share the work as they come), and loads what
+// every one of them needs first at once, one segment
 // per lane: its start, end and key, then the bag of its first occurrence.
 // A group of 2^g_log2 lanes (V float4 of a row each) then takes its share
 // of the 64 segments kLightBatch at a time: the table rows and the first
@@ -472,10 +473,18 @@ __device__ __forceinline__ void light_phase(float* const* __restrict__ tables, i
   const int per_group = 64 / wgroups;  // segments of a chunk per group
   const int d4 = d >> 2;
   const uint32_t nsegs = *nseg;
-  for (;;) {
-    uint32_t c0 = 0;
-    if (lane == 0) c0 = atomicAdd(next, 64u);
-    c0 = (uint32_t)__shfl((int)c0, 0, 64);
+  // a wave's first chunk is fixed (wave w: chunk w), the rest come from the
+  // shared counter after all first chunks: same-address atomics queue at
+  // the cache, one every few nanoseconds, so one per chunk would have set a
+  // floor of its own
+  const uint32_t waves = gridDim.x * (blockDim.x >> 6);
+  uint32_t c0 = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 64u;
+  for (bool first = true;; first = false) {
+    if (!first) {
+      uint32_t c = 0;
+      if (lane == 0) c = atomicAdd(next, 64u);
+      c0 = (uint32_t)__shfl((int)c, 0, 64) + waves * 64u;
+    }
     if (c0 >= nsegs) break;  // whole wave
     // lane i: segment c0 + i
     const uint32_t ms = c0 + (uint32_t)lane;
