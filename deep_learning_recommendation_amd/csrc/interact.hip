@@ -323,13 +323,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
   typedef typename R::T TT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 6);
-  int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-  if (b >= B) return;  // whole wave
+  const int waves = blockDim.x >> 6;
+  const int64_t stride = (int64_t)gridDim.x * waves;
+  int64_t b = (int64_t)blockIdx.x * waves + wave;
   char* rowb = smem + wave * row_bytes;
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t* __restrict__ off = src.off;
   const int64_t* __restrict__ idx = src.idx;
+  constexpr bool kPersist = fused_persistent<NT, DC>();
+  // One sample per wave: the block's bag offsets are loaded together.  For
+  // table k the waves' bags start and end at off[k B + s0 .. s0 + waves],
+  // neighbours in memory, so the block asks for (n - 1) (waves + 1)
+  // consecutive-by-table values instead of every wave asking for its own
+  // 2 (n - 1) scattered ones.
+  const int per = waves + 1;
+  const int64_t* so = reinterpret_cast<const int64_t*>(smem + waves * row_bytes);
+  if constexpr (!kPersist) {
+    const int64_t s0 = (int64_t)blockIdx.x * waves, last = (int64_t)(n - 1) * B;
+    int64_t* sw = reinterpret_cast<int64_t*>(smem + waves * row_bytes);
+    for (int t = threadIdx.x; t < (n - 1) * per; t += blockDim.x) {
+      const int64_t pos = (int64_t)(t / per) * B + s0 + t % per;
+      sw[t] = off[pos < last ? pos : last];
+    }
+    __syncthreads();
+  }
+  if (b >= B) return;  // whole wave
 
   // Every load below is issued unconditionally from a valid address (lanes
   // with nothing to load read the offsets array or the dense row) and masked
@@ -351,9 +369,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
   auto load_offsets = [&](int64_t s, int64_t (&o0)[NT], int64_t (&o1)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int64_t bag = (bagrow[t] && s < B) ? (int64_t)(t * 16 + r16 - 1) * B + s : 0;
-      o0[t] = off[bag];
-      o1[t] = off[bag + 1];
+      if constexpr (kPersist) {
+        const int64_t bag = (bagrow[t] && s < B) ? (int64_t)(t * 16 + r16 - 1) * B + s : 0;
+        o0[t] = off[bag];
+        o1[t] = off[bag + 1];
+      } else {  // this wave's sample, from the block's offsets in LDS
+        const int k = bagrow[t] ? t * 16 + r16 - 1 : 0;
+        o0[t] = so[k * per + wave];
+        o1[t] = so[k * per + wave + 1];
+      }
     }
   };
   int64_t pb[NT], r0[NT];
@@ -408,7 +432,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fused_waves
         }
       }
     }
-    constexpr bool kPersist = fused_persistent<NT, DC>();
     const int64_t bn = kPersist ? b + stride : B;
     int64_t o0n[NT], o1n[NT];
     if constexpr (kPersist) load_offsets(bn, o0n, o1n);
@@ -532,15 +555,18 @@ void launch_mfma(const RowSource& src, int64_t B, int n, int d, OutT* out, int64
     // persistent waves: as many blocks as stay resident, each wave walking
     // the samples with the grid's stride
     typedef typename FRowOf<MODE>::type R;
+    // rows, then (one sample per wave) the block's bag offsets
+    const size_t lds = (size_t)spb * row_bytes +
+                       (fused_persistent<NT, DC>() ? 0 : (size_t)(n - 1) * (size_t)(spb + 1) * sizeof(int64_t));
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
                                                      reinterpret_cast<const void*>(fused_kernel<NT, DC, OutT, R>),
-                                                     64 * spb, (size_t)spb * row_bytes) != hipSuccess || per_cu < 1)
+                                                     64 * spb, lds) != hipSuccess || per_cu < 1)
       per_cu = 1;
     int64_t grid = ceil_div(B, spb);
     if (fused_persistent<NT, DC>() && grid > (int64_t)per_cu * device_cu_count()) grid = (int64_t)per_cu * device_cu_count();
-    hipLaunchKernelGGL((fused_kernel<NT, DC, OutT, R>), dim3((unsigned)grid), dim3(64 * spb), (size_t)spb * row_bytes,
-                       s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
+    hipLaunchKernelGGL((fused_kernel<NT, DC, OutT, R>), dim3((unsigned)grid), dim3(64 * spb), lds, s, src, B, n, d,
+                       out, out_ld, pad_end, row_bytes, wide);
   } else
     hipLaunchKernelGGL((interact_mfma_kernel<NT, DC, OutT>), dim3((unsigned)ceil_div(B, spb)), dim3(64 * spb),
                        (size_t)spb * row_bytes, s, src, B, n, d, out, out_ld, pad_end, row_bytes, wide);
