@@ -426,20 +426,38 @@ def main():
 
     LAYER_REPS = 4
 
+    def fused_pair_at(dims):
+        """Index of the hidden layer that dlrm_mlp_fwd runs together with the
+        single-output layer (at most 256 hidden outputs), or None."""
+        L = len(dims) - 1
+        return L - 2 if L >= 2 and dims[L] == 1 and dims[L - 1] <= 256 else None
+
     def top_layers(m, mark):
         """The forward top MLP one layer at a time (dlrm_linear_fwd: the
-        kernels dlrm_mlp_fwd launches for it), each layer launched LAYER_REPS
-        times back to back between two marks (a layer only reads its input,
-        so every launch does the same work), which spreads the cost of an
-        event record over several launches."""
+        kernels dlrm_mlp_fwd launches for it; the last hidden layer and the
+        single-output layer together through dlrm_mlp_fwd, which runs them as
+        one launch), each launched LAYER_REPS times back to back between two
+        marks (a layer only reads its input, so every launch does the same
+        work), which spreads the cost of an event record over several
+        launches."""
         dims = m.top.dims
+        pair = fused_pair_at(dims)
         if not layer_bufs:
             for l in range(1, len(dims) - 1):
                 ld = (dims[l] + 7) // 8 * 8
                 layer_bufs[l] = (torch.empty((w.B, ld), dtype=torch.bfloat16, device=dev), ld)
+            if pair is not None:
+                sub = dims[pair:]
+                layer_bufs["ws"] = torch.empty((max(256, D.dlrm_mlp_workspace_size(w.B, sub, D.DLRM_BF16, False)),),
+                                               dtype=torch.uint8, device=dev)
         src, ld_src = m.top_in, m.top_ld
         for l in range(len(dims) - 1):
             mark(f"top_l{l}")
+            if l == pair:
+                for _ in range(LAYER_REPS):
+                    D.dlrm_mlp_fwd(src, ld_src, w.B, dims[l:], m.top.Ws[l:], m.top.w_ld[l:], m.top.biases[l:],
+                                   D.DLRM_BF16, D.DLRM_ACT_NONE, m.logit, 1, m.prob, layer_bufs["ws"], False)
+                break
             last = l == len(dims) - 2
             dst, ld_dst = (m.logit, 1) if last else layer_bufs[l + 1]
             for _ in range(LAYER_REPS):
@@ -555,13 +573,18 @@ def main():
         tdims = model.top.dims
         tflops = mlp_layer_flops(w.B, w.top)  # the model's own widths (a padded first layer's zero columns excluded)
         layers = []
+        pair = fused_pair_at(tdims)
         for l in range(len(tdims) - 1):
             if f"top_l{l}" in breakdown:
-                layers.append(dict(frac(tflops[l], breakdown[f"top_l{l}"]), layer=f"{w.top[l]}->{w.top[l + 1]}",
-                                   k_run=tdims[l]))
+                if l == pair:  # the last hidden layer and the logit layer in one launch
+                    layers.append(dict(frac(tflops[l] + tflops[l + 1], breakdown[f"top_l{l}"]),
+                                       layer=f"{w.top[l]}->{w.top[l + 1]}->{w.top[l + 2]}", k_run=tdims[l]))
+                else:
+                    layers.append(dict(frac(tflops[l], breakdown[f"top_l{l}"]), layer=f"{w.top[l]}->{w.top[l + 1]}",
+                                       k_run=tdims[l]))
         if layers:
             mfma["top_layers"] = layers
-            tot = sum(breakdown[f"top_l{l}"] for l in range(len(tdims) - 1))
+            tot = sum(breakdown[k] for k in breakdown if k.startswith("top_l"))
             mfma["top_mlp"] = frac(sum(tflops), tot)
         elif "top_mlp" in breakdown:
             mfma["top_mlp"] = frac(sum(tflops), breakdown["top_mlp"])

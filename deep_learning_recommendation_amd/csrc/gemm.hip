@@ -85,11 +85,11 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ base, i
 constexpr int fast_waves_per_eu(int WM, int WN) { return WM * WN > 128 * 64 ? 1 : 2; }
 
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK, int S, bool PERSIST, int ILV,
-          bool DELTA = false, bool KA = false, bool KW = false>
+          bool DELTA = false, bool KA = false, bool KW = false, bool DOT = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(fast_waves_per_eu(WM, WN)))) void gemm_bf16_fast_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, OutT* __restrict__ C, int64_t ldc, int M, int N, int K, int relu, int tiles_n,
-    int tiles, int k_per_split, int vec_out, DeltaOut dout) {
+    int tiles, int k_per_split, int vec_out, DeltaOut dout, DotOut dot) {
   static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
   constexpr int RB = BK * 2;                      // bytes per tile row
   constexpr int CPR = BK / 8;                     // 16-byte chunks per row
@@ -99,7 +99,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_INS = BM * RB / 1024 / NWAVES, B_INS = BN * RB / 1024 / NWAVES, INS = A_INS + B_INS;
   constexpr int STAGE = (BM + BN) * RB;
-  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+  // DOT: the per-wave row sums of the single-output layer meet past the stages
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE + (DOT ? WAVES_N * BM * 4 : 0)];
   // chunk swizzle: the 16 lanes that one LDS cycle serves read 16 rows of
   // one logical chunk; XOR-ing the chunk with row bits above the rows that
   // share a bank group spreads them over all 64 banks
@@ -451,6 +452,56 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_w
     }
 
     const bool full = m0 + BM <= M && n0 + BN <= N && vec_out;
+    if constexpr (DOT) {
+      // Single-output layer on this tile's rows (the tile spans every column):
+      // each lane sums its columns' bf16 hidden values times w, columns in
+      // (tn, register) order; the two lanes of a row add their sums, then the
+      // waves that split the columns meet in LDS and are added in wave order.
+      static_assert(!PARTIAL && !DELTA && sizeof(OutT) == 2, "DOT: bf16 hidden layer");
+      float* red = reinterpret_cast<float*>(smem + S * STAGE);  // [WAVES_N][BM]
+      float part[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) part[tm] = 0.f;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col0 = colb + tn * 32 + 8 * g;
+          float wv[4];
+          if (col0 + 4 <= N) {
+            const uint2 w4 = *reinterpret_cast<const uint2*>(dot.w + col0);
+            wv[0] = bf16_to_f32((uint16_t)(w4.x & 0xffffu)), wv[1] = bf16_to_f32((uint16_t)(w4.x >> 16));
+            wv[2] = bf16_to_f32((uint16_t)(w4.y & 0xffffu)), wv[3] = bf16_to_f32((uint16_t)(w4.y >> 16));
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wv[q] = col0 + q < N ? bf16_to_f32(dot.w[col0 + q]) : 0.f;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+              float h = acc[tm][tn][4 * g + q];
+              if (relu) h = relu_f(h);
+              part[tm] = __builtin_fmaf(bf16_to_f32(f32_to_bf16(h)), wv[q], part[tm]);
+            }
+        }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        part[tm] = part[tm] + __shfl_xor(part[tm], 32);
+        if (half == 0) red[wn * BM + wm * WM + tm * 32 + r32] = part[tm];
+      }
+      __syncthreads();
+      if (tid < BM && m0 + tid < M) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES_N; ++w) v = v + red[w * BM + tid];
+        if (dot.b) v = v + dot.b[0];
+        if (dot.relu) v = relu_f(v);
+        dot.out[(int64_t)(m0 + tid) * dot.ldo] = v;
+        if (dot.prob) dot.prob[m0 + tid] = 1.f / (1.f + expf(-v));
+      }
+      if (C == nullptr) goto tile_done;
+    }
     if constexpr (DELTA) {
       // Input gradient of a ReLU layer: g = this tile, masked by the layer
       // input y > 0, rounded to bf16 and written row-major to C; the tile then
@@ -650,14 +701,14 @@ int fast_occupancy(Kern kern, int threads) {
 }
 
 template <int BM, int BN, int WM, int WN, typename OutT, bool PARTIAL, int BK = 64, int S = 2, bool PERSIST = false,
-          int ILV = 0, bool DELTA = false, bool KA = false, bool KW = false>
+          int ILV = 0, bool DELTA = false, bool KA = false, bool KW = false, bool DOT = false>
 void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, OutT* C,
                  int64_t ldc, int M, int N, int K, int relu, int splits, int k_per_split, hipStream_t s,
-                 DeltaOut dout = DeltaOut{}) {
+                 DeltaOut dout = DeltaOut{}, DotOut dot = DotOut{}) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int tiles = tm * tn;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S, PERSIST, ILV, DELTA, KA, KW>;
+  auto kern = gemm_bf16_fast_kernel<BM, BN, WM, WN, OutT, PARTIAL, BK, S, PERSIST, ILV, DELTA, KA, KW, DOT>;
   int grid = tiles;
   if constexpr (PERSIST) {
     const int slots = fast_occupancy(kern, threads) * device_cu_count();
@@ -668,7 +719,7 @@ void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw,
   constexpr int VW = 16 / (int)sizeof(OutT);
   const int vec_out = (ldc % VW) == 0 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
   hipLaunchKernelGGL(kern, dim3(grid, 1, splits), dim3(threads), 0, s, A, lda, W, ldw, bias, C, ldc, M, N, K, relu,
-                     tn, tiles, k_per_split, vec_out, dout);
+                     tn, tiles, k_per_split, vec_out, dout, dot);
 }
 
 // Tile choice: the largest block tile that still gives every CU a tile
@@ -1025,6 +1076,26 @@ int gemm_bf16_delta(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t l
       launch_fast<128, 128, 64, 64, uint16_t, false, 64, 2, false, 2, true>(A, lda, W, ldw, nullptr, dlt, ldd, M, N, K,
                                                                            0, 1, kps, s, dout);
   }
+  return launch_status();
+}
+
+int gemm_bf16_dot(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, uint16_t* H,
+                  int64_t ldh, int M, int N, int K, const DotOut& dot, hipStream_t s) {
+  if (M <= 0) return DLRM_OK;
+  if (N < 1 || N > 256 || K < 1 || !dot.w || !dot.out || (reinterpret_cast<uintptr_t>(dot.w) & 7u) ||
+      !fast_operand(A, lda, K) || !fast_operand(W, ldw, K))
+    return DLRM_E_UNSUPPORTED;
+  // 128 x 256 block tiles (every column of a row in one workgroup), eight
+  // waves of 64 x 64; three LDS stages of 64-wide k-tiles (on 512 -> 256 at
+  // batch 32768 the loads of a short k loop wait on HBM: 13.5 us with three
+  // stages, 14.3 with two)
+  const int kps = (int)round_up(K, 64);
+  if ((K % 64) == 0)
+    launch_fast<128, 256, 64, 64, uint16_t, false, 64, 3, false, 2, false, false, false, true>(
+        A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
+  else
+    launch_fast<128, 256, 64, 64, uint16_t, false, 32, 4, false, 1, false, false, false, true>(
+        A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
   return launch_status();
 }
 

@@ -32,6 +32,21 @@ struct DeltaOut {
 };
 int gemm_bf16_delta(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, bool w_kmajor, int M, int N,
                     int K, uint16_t* dlt, int64_t ldd, const DeltaOut& dout, int* tile_rows, hipStream_t s);
+// A hidden ReLU layer followed by a single-output layer, in one launch:
+// h = bf16(relu(A W^T + bias)) with N <= 256 (one block tile holds a row's
+// every column), then out[m] = act(sum_n h[m][n] w[n] + b) in fp32, and
+// prob[m] = 1 / (1 + exp(-out[m])) when prob is set.  h is written to H
+// [M][ldh] only when H is set (the backward pass reads it).
+struct DotOut {
+  const uint16_t* w = nullptr;  // bf16 [N], the single-output layer's weight row
+  const float* b = nullptr;     // its bias (nullable)
+  float* out = nullptr;         // fp32 [M] with pitch ldo
+  int64_t ldo = 1;
+  float* prob = nullptr;  // nullable
+  int relu = 0;           // ReLU on out
+};
+int gemm_bf16_dot(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, uint16_t* H,
+                  int64_t ldh, int M, int N, int K, const DotOut& dot, hipStream_t s);
 int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M, int N,
                      int K, int splits, hipStream_t s);
 // Split-K partials with both operands k-major: part[z][M][N] = the sum over

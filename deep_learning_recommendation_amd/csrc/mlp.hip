@@ -856,6 +856,23 @@ extern "C" int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int
     const int64_t wl = w_ld ? w_ld[l] : fi;
     void* dst = last ? static_cast<void*>(out) : static_cast<void*>(wsb + lay.act_off[l + 1]);
     const int64_t ld_dst = last ? out_ld : lay.act_ld[l + 1];
+    if (l == L - 2 && dims[L] == 1) {
+      // a hidden layer of at most 256 outputs followed by the single-output
+      // layer: one launch computes both (the hidden rows are written only
+      // when the backward pass will read them)
+      DotOut dot;
+      dot.w = static_cast<const uint16_t*>(W[L - 1]);
+      dot.b = bias[L - 1];
+      dot.out = out;
+      dot.ldo = out_ld;
+      dot.prob = prob;
+      dot.relu = last_act == DLRM_ACT_RELU;
+      rc = gemm_bf16_dot(src, ld_src, w, wl, bias[l], save_acts ? static_cast<uint16_t*>(dst) : nullptr, ld_dst, M, fo,
+                         fi, dot, stream);
+      if (rc == DLRM_OK) break;
+      if (rc != DLRM_E_UNSUPPORTED) return rc;
+      rc = DLRM_OK;
+    }
     if (last && fo == 1)
       rc = gemv_bf16(src, ld_src, w, bias[l], out, out_ld, prob, M, fi, relu, stream);
     else

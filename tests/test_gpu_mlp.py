@@ -362,3 +362,48 @@ def test_linear_fwd_against_oracle(M, N, K, out_bf16, relu):
         tol = tol + 2.0 ** -8 * (np.abs(ref) + tol)
     err = np.abs(got[rows].astype(np.float64) - ref)
     assert np.all(err <= tol + 1e-30), float(np.max(err / (tol + 1e-30)))
+
+
+@pytest.mark.parametrize("dims,B,save", [((64, 256, 1), 8192, False), ((64, 256, 1), 1000, True),
+                                         ((40, 200, 1), 1000, False), ((40, 200, 1), 129, True),
+                                         ((512, 256, 1), 333, False), ((96, 64, 1), 1, False),
+                                         ((64, 256, 256, 1), 777, True)])
+def test_mlp_hidden_and_logit_layer_integer_exact(dims, B, save):
+    """A hidden layer of at most 256 outputs followed by the single-output
+    layer runs as one launch (the logit summed in the GEMM's epilogue).  With
+    integer inputs, weights and biases every sum is an exact integer, so the
+    logit, the sigmoid input and (when saved) the hidden rows equal the
+    oracle's bit for bit: ragged batches (1, 129, 333, 777, 1000), hidden
+    widths of 200 and 64 inside the 256-wide tile, and k of 40 and 96 (not a
+    multiple of 64) besides 64, 256 and 512."""
+    import deep_learning_recommendation_amd as D
+
+    banner(f"mlp hidden+logit integer-exact dims={dims} B={B} save={save}")
+    params = _int_params(dims, 31 + B, 0.25)
+    g = np.random.default_rng(B + 3)
+    x = g.integers(-2, 3, size=(B, dims[0])).astype(np.float32)
+    Ws = [p[0] for p in params]
+    bs = [p[2] for p in params]
+    _, _, acts_abs = oracle.mlp_fwd(np.abs(x), [np.abs(w) for w in Ws], [np.abs(b) for b in bs], False, False,
+                                    save_acts=True)
+    # every partial sum an integer below 2^23 in magnitude (the same network
+    # on |x|, |W|, |b| bounds them): exact in fp32 in any order, so both
+    # sides round the same hidden values to bf16 and form the same logit
+    assert max(float(np.max(a)) for a in acts_abs[1:]) < 2.0 ** 23
+    ref_out, ref_p, acts = oracle.mlp_fwd(x, Ws, bs, True, False, save_acts=True)
+    mp = _mlp_dev(dims, params, True)
+    out, prob, ws = _fwd(mp, x, False, save=save)
+    assert np.array_equal(out.cpu().numpy(), ref_out.astype(np.float32))
+    assert np.max(np.abs(prob.cpu().numpy() - ref_p)) <= 1e-6
+    if save:
+        # the hidden rows the backward pass reads: the last hidden layer's
+        # bf16 output in the forward workspace, as the backward locates it
+        dWs = [torch.empty((o, i), dtype=torch.float32, device=DEV) for i, o in zip(dims[:-1], dims[1:])]
+        dbs = [torch.empty((o,), dtype=torch.float32, device=DEV) for o in dims[1:]]
+        ones = torch.ones((B, 1), dtype=torch.float32, device=DEV)
+        wsb = torch.empty((D.dlrm_mlp_bwd_workspace_size(B, dims),), dtype=torch.uint8, device=DEV)
+        D.dlrm_mlp_bwd(B, dims, mp.Ws, mp.w_ld, D.DLRM_ACT_NONE, ws, out, 1, ones, 1, dWs, dbs, None, 0, wsb)
+        torch.cuda.synchronize()
+        # dW of the logit layer with dY = 1 is the column sum of its input rows
+        ref_dw = acts[-2].astype(np.float64).sum(axis=0)
+        assert np.array_equal(dWs[-1].cpu().numpy()[0], ref_dw.astype(np.float32))
