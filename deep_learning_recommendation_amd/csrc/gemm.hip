@@ -1085,17 +1085,29 @@ int gemm_bf16_dot(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw
   if (N < 1 || N > 256 || K < 1 || !dot.w || !dot.out || (reinterpret_cast<uintptr_t>(dot.w) & 7u) ||
       !fast_operand(A, lda, K) || !fast_operand(W, ldw, K))
     return DLRM_E_UNSUPPORTED;
-  // 128 x 256 block tiles (every column of a row in one workgroup), eight
-  // waves of 64 x 64; three LDS stages of 64-wide k-tiles (on 512 -> 256 at
-  // batch 32768 the loads of a short k loop wait on HBM: 13.5 us with three
-  // stages, 14.3 with two)
+  // Block tiles of 256 columns (every column of a row in one workgroup):
+  // 128 rows (eight waves of 64 x 64) where that gives every CU a tile, else
+  // 64 rows (eight waves of 32 x 64); three LDS stages of 64-wide
+  // k-tiles (on 512 -> 256 the loads of a short k loop wait on HBM: at
+  // batch 32768 13.5 us with three stages, 14.3 with two; at batch 8192 the
+  // 64-row tiles take 8.7 us, the 128-row ones 11.4)
   const int kps = (int)round_up(K, 64);
-  if ((K % 64) == 0)
-    launch_fast<128, 256, 64, 64, uint16_t, false, 64, 3, false, 2, false, false, false, true>(
-        A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
-  else
-    launch_fast<128, 256, 64, 64, uint16_t, false, 32, 4, false, 1, false, false, false, true>(
-        A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
+  const bool big = ceil_div(M, 128) >= device_cu_count();
+  if ((K % 64) == 0) {
+    if (big)
+      launch_fast<128, 256, 64, 64, uint16_t, false, 64, 3, false, 2, false, false, false, true>(
+          A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
+    else
+      launch_fast<64, 256, 32, 64, uint16_t, false, 64, 3, false, 2, false, false, false, true>(
+          A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
+  } else {
+    if (big)
+      launch_fast<128, 256, 64, 64, uint16_t, false, 32, 4, false, 1, false, false, false, true>(
+          A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
+    else  // four waves of 64 x 64 (a 32-wide k-tile of 64 rows is half a load per wave of eight)
+      launch_fast<64, 256, 64, 64, uint16_t, false, 32, 4, false, 1, false, false, false, true>(
+          A, lda, W, ldw, bias, H, ldh, M, N, K, 1, 1, kps, s, DeltaOut{}, dot);
+  }
   return launch_status();
 }
 

@@ -364,7 +364,8 @@ def test_linear_fwd_against_oracle(M, N, K, out_bf16, relu):
     assert np.all(err <= tol + 1e-30), float(np.max(err / (tol + 1e-30)))
 
 
-@pytest.mark.parametrize("dims,B,save", [((64, 256, 1), 8192, False), ((64, 256, 1), 1000, True),
+@pytest.mark.parametrize("dims,B,save", [((64, 256, 1), 32768, False), ((40, 200, 1), 32769, True),
+                                         ((64, 256, 1), 8192, False), ((64, 256, 1), 1000, True),
                                          ((40, 200, 1), 1000, False), ((40, 200, 1), 129, True),
                                          ((512, 256, 1), 333, False), ((96, 64, 1), 1, False),
                                          ((64, 256, 256, 1), 777, True)])
@@ -373,9 +374,10 @@ def test_mlp_hidden_and_logit_layer_integer_exact(dims, B, save):
     layer runs as one launch (the logit summed in the GEMM's epilogue).  With
     integer inputs, weights and biases every sum is an exact integer, so the
     logit, the sigmoid input and (when saved) the hidden rows equal the
-    oracle's bit for bit: ragged batches (1, 129, 333, 777, 1000), hidden
-    widths of 200 and 64 inside the 256-wide tile, and k of 40 and 96 (not a
-    multiple of 64) besides 64, 256 and 512."""
+    oracle's bit for bit: 128-row tiles (batches of 32768 and more) and
+    64-row tiles (smaller batches), ragged batches (1, 129, 333, 777, 1000,
+    32769), hidden widths of 200 and 64 inside the 256-wide tile, and k of 40
+    and 96 (not a multiple of 64) besides 64, 256 and 512."""
     import deep_learning_recommendation_amd as D
 
     banner(f"mlp hidden+logit integer-exact dims={dims} B={B} save={save}")
