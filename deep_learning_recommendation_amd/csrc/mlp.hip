@@ -535,48 +535,66 @@ __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__
   }
 }
 
-// One launch finishes a layer's gradients: blocks [0, rblocks) add the
-// split-K partials of dW in split order (eight loads in flight); each other
-// block sums the per-chunk partials of 64 entries of db, wave w taking
-// chunks w, w + 4, ... in order and the four wave sums added in wave order.
-__global__ __launch_bounds__(256) void grad_finalize_kernel(const float* __restrict__ part, int splits, int M,
-                                                            int N, float* __restrict__ dW, int64_t ldw, int rblocks,
-                                                            const float* __restrict__ dbp, int chunks,
-                                                            float* __restrict__ db) {
-  if ((int)blockIdx.x < rblocks) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// One launch finishes the gradients of up to kFinLayers layers, after the
+// whole backward pass (each layer keeps its own partials): per layer, blocks
+// [0, rblocks) add the split-K partials of dW in split order (eight loads
+// in flight); each other block sums the per-chunk partials of 64 entries of
+// db, wave w taking chunks w, w + 4, ... in order and the four wave sums
+// added in wave order.
+constexpr int kFinLayers = 16;
+struct FinLayer {
+  const float* part;
+  float* dW;
+  const float* dbp;
+  float* db;
+  int64_t ldw;
+  int splits, M, N, rblocks, chunks, block0;
+};
+struct FinArgs {
+  FinLayer l[kFinLayers];
+  int count;
+};
+__global__ __launch_bounds__(256) void grad_finalize_kernel(FinArgs args) {
+  int li = 0;
+  while (li + 1 < args.count && (int)blockIdx.x >= args.l[li + 1].block0) ++li;
+  const FinLayer& f = args.l[li];
+  const int blk = (int)blockIdx.x - f.block0;
+  const int M = f.M, N = f.N;
+  if (blk < f.rblocks) {
+    const int64_t t = (int64_t)blk * blockDim.x + threadIdx.x;
     const int64_t MN = (int64_t)M * N;
     if (t >= MN) return;
     const int i = (int)(t / N), j = (int)(t - (int64_t)i * N);
     float v = 0.f;
-    for (int z0 = 0; z0 < splits; z0 += 8) {
+    for (int z0 = 0; z0 < f.splits; z0 += 8) {
       float p[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) p[q] = (z0 + q < splits) ? part[(z0 + q) * MN + t] : 0.f;
+      for (int q = 0; q < 8; ++q) p[q] = (z0 + q < f.splits) ? f.part[(z0 + q) * MN + t] : 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (z0 + q < splits) v = v + p[q];
+        if (z0 + q < f.splits) v = v + p[q];
     }
-    dW[(int64_t)i * ldw + j] = v;
+    f.dW[(int64_t)i * f.ldw + j] = v;
     return;
   }
   __shared__ float red[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int o = ((int)blockIdx.x - rblocks) * 64 + lane;
+  const int o = (blk - f.rblocks) * 64 + lane;
   float s = 0.f;
   if (o < M)
-    for (int c0 = wave; c0 < chunks; c0 += 32) {
+    for (int c0 = wave; c0 < f.chunks; c0 += 32) {
       float v[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = (c0 + 4 * t < chunks) ? dbp[(int64_t)(c0 + 4 * t) * M + o] : 0.f;
+      for (int t = 0; t < 8; ++t) v[t] = (c0 + 4 * t < f.chunks) ? f.dbp[(int64_t)(c0 + 4 * t) * M + o] : 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        if (c0 + 4 * t < chunks) s = s + v[t];
+        if (c0 + 4 * t < f.chunks) s = s + v[t];
     }
   red[wave][lane] = s;
   __syncthreads();
-  if (wave == 0 && o < M) db[o] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  if (wave == 0 && o < M) f.db[o] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
+
 
 // Layers with a single output (the top MLP's logit layer) as two plain
 // kernels instead of degenerate GEMMs.  A block covers kR1Rows rows and 256
@@ -714,22 +732,18 @@ __global__ __launch_bounds__(256) void bce_grad_kernel(const float* __restrict__
 }
 
 struct BwdLayout {
-  size_t dlt[2], wT, part, dbp, bytes;
+  size_t dlt[2], wT, part[64], dbp[64], bytes;
   int64_t ld_dlt;
 };
 
 bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
   if (L < 1 || L > 64 || B < 1) return false;
-  int64_t wmax = 0, wfo = 0, prod = 0;
+  int64_t wmax = 0, wfo = 0;
   for (int l = 0; l <= L; ++l) {
     if (dims[l] < 1) return false;
     wmax = dims[l] > wmax ? dims[l] : wmax;
   }
-  for (int l = 0; l < L; ++l) {
-    wfo = dims[l + 1] > wfo ? dims[l + 1] : wfo;
-    const int64_t p = (int64_t)wgrad_splits(B, dims[l + 1], dims[l]) * dims[l] * dims[l + 1];
-    prod = p > prod ? p : prod;
-  }
+  for (int l = 0; l < L; ++l) wfo = dims[l + 1] > wfo ? dims[l + 1] : wfo;
   Carver cv(nullptr);
   lay->ld_dlt = round_up(wfo, 8);
   auto take = [&](size_t bytes) {
@@ -740,8 +754,14 @@ bool bwd_layout(int64_t B, int32_t L, const int32_t* dims, BwdLayout* lay) {
   };
   for (int i = 0; i < 2; ++i) lay->dlt[i] = take(2 * (size_t)(B * lay->ld_dlt));
   lay->wT = take(2 * (size_t)(wmax * lay->ld_dlt));
-  lay->part = take(4 * (size_t)prod);
-  lay->dbp = take(4 * (size_t)(ceil_div(B, kDRows) * wfo));
+  // every layer keeps its weight-gradient partials and its bias-gradient
+  // chunk partials (at most one chunk per kDRows rows) until the one
+  // finishing launch at the end
+  static_assert(kDRows <= kR1Rows && kDRows <= 128, "chunks of at least kDRows rows");
+  for (int l = 0; l < L; ++l) {
+    lay->part[l] = take(4 * (size_t)wgrad_splits(B, dims[l + 1], dims[l]) * dims[l] * dims[l + 1]);
+    lay->dbp[l] = take(4 * (size_t)(ceil_div(B, kDRows) * dims[l + 1]));
+  }
   lay->bytes = cv.bytes();
   return true;
 }
@@ -927,9 +947,20 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
   char* w = static_cast<char*>(ws);
   uint16_t* dlt[2] = {reinterpret_cast<uint16_t*>(w + bl.dlt[0]), reinterpret_cast<uint16_t*>(w + bl.dlt[1])};
   uint16_t* wT = reinterpret_cast<uint16_t*>(w + bl.wT);
-  float* part = reinterpret_cast<float*>(w + bl.part);
-  float* dbp = reinterpret_cast<float*>(w + bl.dbp);
+  auto part_of = [&](int l) { return reinterpret_cast<float*>(w + bl.part[l]); };
+  auto dbp_of = [&](int l) { return reinterpret_cast<float*>(w + bl.dbp[l]); };
   const int M = (int)B;
+  FinArgs fin;
+  fin.count = 0;
+  int fin_blocks = 0;
+  // the finishing launch for the layers recorded so far
+  auto finish = [&]() -> int {
+    if (fin.count == 0) return DLRM_OK;
+    hipLaunchKernelGGL(grad_finalize_kernel, dim3((unsigned)fin_blocks), dim3(256), 0, stream, fin);
+    fin.count = 0;
+    fin_blocks = 0;
+    return launch_status();
+  };
   const dim3 b1(256);
   int rc = DLRM_OK;
   int db_chunks = 0;  // row chunks of the bias-gradient partials in dbp
@@ -950,7 +981,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     const int vec = al(dY, dy_ld, 4, 16) && al(dlt[0], bl.ld_dlt, 2, 8) && al(y, ldy, 4, 16);
     const int chunks = (int)ceil_div(B, kDRows);
     hipLaunchKernelGGL((delta_db_kernel<float>), dim3((unsigned)ceil_div(fo, kDCols), (unsigned)chunks), b1, 0, stream,
-                       dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, nullptr, 0, dbp, M, fo, vec);
+                       dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, nullptr, 0, dbp_of(L - 1), M, fo, vec);
     db_chunks = chunks;
     rc = launch_status();
   }
@@ -963,18 +994,30 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     const int splits = wgrad_splits(B, fo, fi);
     if (fo == 1) {
       hipLaunchKernelGGL(rank1_wgrad_kernel, dim3((unsigned)ceil_div(fi, 256), (unsigned)splits), b1, 0, stream,
-                         dlt[cur], bl.ld_dlt, x, fl.act_ld[l], M, fi, part);
+                         dlt[cur], bl.ld_dlt, x, fl.act_ld[l], M, fi, part_of(l));
       rc = launch_status();
     } else {
-      rc = gemm_bf16_splitk_kmajor(dlt[cur], bl.ld_dlt, x, fl.act_ld[l], part, fo, fi, M, splits, stream);
+      rc = gemm_bf16_splitk_kmajor(dlt[cur], bl.ld_dlt, x, fl.act_ld[l], part_of(l), fo, fi, M, splits, stream);
     }
     if (rc != DLRM_OK) break;
-    // dW from the partials and db from the partials the layer's delta left
+    // dW from the partials and db from the partials the layer's delta left:
+    // recorded here, computed by one launch after the last layer (nothing
+    // in the pass reads dW or db)
     {
-      const int rblocks = (int)ceil_div((int64_t)fo * fi, 256);
-      hipLaunchKernelGGL(grad_finalize_kernel, dim3((unsigned)(rblocks + ceil_div(fo, 64))), b1, 0, stream, part,
-                         splits, fo, fi, dW[l], (int64_t)fi, rblocks, dbp, db_chunks, db[l]);
-      if ((rc = launch_status()) != DLRM_OK) break;
+      if (fin.count == kFinLayers && (rc = finish()) != DLRM_OK) break;
+      FinLayer& f = fin.l[fin.count++];
+      f.part = part_of(l);
+      f.dW = dW[l];
+      f.dbp = dbp_of(l);
+      f.db = db[l];
+      f.ldw = fi;
+      f.splits = splits;
+      f.M = fo;
+      f.N = fi;
+      f.rblocks = (int)ceil_div((int64_t)fo * fi, 256);
+      f.chunks = db_chunks;
+      f.block0 = fin_blocks;
+      fin_blocks += f.rblocks + (int)ceil_div(fo, 64);
     }
     if (l == 0 && !dX) break;
     // 3. the input gradient delta W  (M = B, N = fi, K = fo): W [fo][fi] is
@@ -983,7 +1026,8 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     const uint16_t* Wl = static_cast<const uint16_t*>(W[l]);
     if (fo == 1 && l > 0) {  // a single-output layer above a ReLU layer
       hipLaunchKernelGGL(rank1_delta_kernel, dim3((unsigned)ceil_div(fi, 256), (unsigned)ceil_div(B, kR1Rows)), b1, 0,
-                         stream, dlt[cur], bl.ld_dlt, Wl, x, fl.act_ld[l], M, fi, dlt[cur ^ 1], bl.ld_dlt, dbp);
+                         stream, dlt[cur], bl.ld_dlt, Wl, x, fl.act_ld[l], M, fi, dlt[cur ^ 1], bl.ld_dlt,
+                         dbp_of(l - 1));
       if ((rc = launch_status()) != DLRM_OK) break;
       db_chunks = (int)ceil_div(B, kR1Rows);
       cur ^= 1;
@@ -1003,7 +1047,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     DeltaOut dout;
     dout.y = x;
     dout.ldy = fl.act_ld[l];
-    dout.dbp = dbp;
+    dout.dbp = dbp_of(l - 1);
     int tile_rows = 128;
     if ((rc = gemm_bf16_delta(dlt[cur], bl.ld_dlt, wop, wop_ld, wk, M, fi, fo, dlt[cur ^ 1], bl.ld_dlt, dout,
                               &tile_rows, stream)) != DLRM_OK)
@@ -1011,6 +1055,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     db_chunks = (int)ceil_div(B, tile_rows);
     cur ^= 1;
   }
+  if (rc == DLRM_OK) rc = finish();
   return rc;
 }
 
