@@ -427,13 +427,13 @@ __device__ __forceinline__ bool positive<uint16_t>(const uint16_t* p) {
 // One pass over the upstream gradient of a layer: delta = g * 1[y > 0] (or
 // g) rounded to bf16 and stored row-major [B][ldd] (for the input gradient)
 // and transposed [N][ldt] (for the weight gradient, K = batch contiguous),
-// plus fp32 column sums of delta per 64-row chunk (for the bias gradient).
-// Block: 64 rows x 256 columns; wave w takes rows w, w+4, ..., lane l the
+// plus fp32 column sums of delta per 32-row chunk (for the bias gradient).
+// Block: 32 rows x 256 columns; wave w takes rows w, w+4, ..., lane l the
 // four consecutive columns 4l .. 4l+3 (16-byte loads of g, 8- or 16-byte
 // loads of y, 8-byte stores of delta when `vec`), eight rows' loads in flight
 // before the first is used.  The column sums add the rows in the same order
 // as a one-row-at-a-time walk.
-constexpr int kDRows = 64, kDCols = 256, kDBatch = 8;
+constexpr int kDRows = 32, kDCols = 256, kDBatch = 8;
 template <typename YT>
 struct YLoad;
 template <>
@@ -533,6 +533,29 @@ __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__
       }
     }
   }
+}
+
+// The same pass for a layer of one output (the logit layer): a lane per
+// row, so the rows' loads go out together; a wave per kDRows-row chunk,
+// whose sum is a fixed tree over its lanes.
+__global__ __launch_bounds__(256) void delta1_kernel(const float* __restrict__ g, int64_t ldg,
+                                                     const float* __restrict__ y, int64_t ldy, int relu,
+                                                     uint16_t* __restrict__ dlt, int64_t ldd,
+                                                     float* __restrict__ part, int B) {
+  static_assert(kDRows <= 64, "a chunk per wave");
+  const int lane = threadIdx.x & 63;
+  const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r = chunk * kDRows + lane;
+  const bool live = lane < kDRows && r < B;
+  float v = 0.f;
+  if (live) {
+    v = g[(int64_t)r * ldg];
+    if (relu && !(y[(int64_t)r * ldy] > 0.f)) v = 0.f;
+    dlt[(int64_t)r * ldd] = f32_to_bf16(v);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o);
+  if (lane == 0 && chunk * kDRows < B) part[chunk] = v;
 }
 
 // One launch finishes the gradients of up to kFinLayers layers, after the
@@ -980,8 +1003,12 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     };
     const int vec = al(dY, dy_ld, 4, 16) && al(dlt[0], bl.ld_dlt, 2, 8) && al(y, ldy, 4, 16);
     const int chunks = (int)ceil_div(B, kDRows);
-    hipLaunchKernelGGL((delta_db_kernel<float>), dim3((unsigned)ceil_div(fo, kDCols), (unsigned)chunks), b1, 0, stream,
-                       dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, nullptr, 0, dbp_of(L - 1), M, fo, vec);
+    if (fo == 1)
+      hipLaunchKernelGGL(delta1_kernel, dim3((unsigned)ceil_div(chunks, 4)), b1, 0, stream, dY, dy_ld, y, ldy, (int)relu,
+                         dlt[0], bl.ld_dlt, dbp_of(L - 1), M);
+    else
+      hipLaunchKernelGGL((delta_db_kernel<float>), dim3((unsigned)ceil_div(fo, kDCols), (unsigned)chunks), b1, 0,
+                         stream, dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, nullptr, 0, dbp_of(L - 1), M, fo, vec);
     db_chunks = chunks;
     rc = launch_status();
   }
