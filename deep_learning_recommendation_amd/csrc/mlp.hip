@@ -651,84 +651,69 @@ __device__ __forceinline__ void r1_group_sum(float (&acc)[8], float (*red)[256])
   }
 }
 
-// Weight gradient: part[z][i] = the fp32 sum over the rows of chunk z of
-// delta[b] x[b][i] (each product of two bf16 values is exact), added up
-// across chunks by grad_finalize_kernel like split-K partials.
-__global__ __launch_bounds__(256) void rank1_wgrad_kernel(const uint16_t* __restrict__ dlt, int64_t ldd,
-                                                          const uint16_t* __restrict__ x, int64_t ldx, int B, int fi,
-                                                          float* __restrict__ part) {
+// A single-output layer's backward in one pass over its input rows x (the
+// saved activations of the ReLU layer below, which are also the mask):
+//   weight gradient: part[z][i] = the fp32 sum over the rows of chunk z of
+//     delta[b] x[b][i] (each product of two bf16 values is exact), added up
+//     across chunks like split-K partials;
+//   with do_delta, the delta of the layer below as the GEMM epilogue forms
+//     it: bf16(+0 + delta[b] w[i]) where x[b][i] > 0, else +0 (columns past
+//     fi written as 0), and per chunk the fp32 column sums of the rounded
+//     values.
+__global__ __launch_bounds__(256) void rank1_kernel(const uint16_t* __restrict__ dlt, int64_t ldd,
+                                                    const uint16_t* __restrict__ x, int64_t ldx, int B, int fi,
+                                                    float* __restrict__ part, int do_delta,
+                                                    const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
+                                                    int64_t ldo, float* __restrict__ dbp) {
   __shared__ float red[8][256];
   const int t = threadIdx.x, rg = t >> 5, z = blockIdx.y;
   const int c = blockIdx.x * 256 + (t & 31) * 8;
-  const int cl = c < fi ? c : 0;  // lanes past the row read its first chunk (results dropped)
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const bool live = c < fi;
+  const int cl = live ? c : 0;  // lanes past the row read its first chunk (results dropped)
   uint4 q[kR1Per];
   float dv[kR1Per];
 #pragma unroll
   for (int r = 0; r < kR1Per; ++r) {
     const int b = z * kR1Rows + rg + 8 * r, bb = b < B ? b : B - 1;
     q[r] = *reinterpret_cast<const uint4*>(x + (int64_t)bb * ldx + cl);
-    dv[r] = b < B ? bf16_to_f32(dlt[(int64_t)bb * ldd]) : 0.f;
+    dv[r] = bf16_to_f32(dlt[(int64_t)bb * ldd]);
   }
+  float wv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) wv[e] = (do_delta && c + e < fi) ? bf16_to_f32(w[c + e]) : 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float accd[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < kR1Per; ++r) {
+    const int b = z * kR1Rows + rg + 8 * r;
     float f[8];
     unpack8(q[r], f);
+    const float d = b < B ? dv[r] : 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + dv[r] * f[e];
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + d * f[e];
+    if (do_delta) {
+      uint32_t h[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t v = (c + e < fi && f[e] > 0.f) ? f32_to_bf16(0.f + dv[r] * wv[e]) : (uint16_t)0;
+        h[e >> 1] |= (uint32_t)v << (16 * (e & 1));
+        if (b < B) accd[e] = accd[e] + bf16_to_f32(v);
+      }
+      if (b < B && live) *reinterpret_cast<uint4*>(out + (int64_t)b * ldo + c) = make_uint4(h[0], h[1], h[2], h[3]);
+    }
   }
   r1_group_sum(acc, red);
   if (rg == 0)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (c + e < fi) part[(int64_t)z * fi + c + e] = acc[e];
-}
-
-// Delta of the ReLU layer below a single-output layer, as the GEMM epilogue
-// forms it: bf16(+0 + delta[b] w[i]) where y[b][i] > 0, else +0 (columns
-// past fi written as 0), and per chunk the fp32 column sums of the rounded
-// values.
-__global__ __launch_bounds__(256) void rank1_delta_kernel(const uint16_t* __restrict__ dlt, int64_t ldd,
-                                                          const uint16_t* __restrict__ w,
-                                                          const uint16_t* __restrict__ y, int64_t ldy, int B, int fi,
-                                                          uint16_t* __restrict__ out, int64_t ldo,
-                                                          float* __restrict__ dbp) {
-  __shared__ float red[8][256];
-  const int t = threadIdx.x, rg = t >> 5, z = blockIdx.y;
-  const int c = blockIdx.x * 256 + (t & 31) * 8;
-  const bool live = c < fi;
-  const int cl = live ? c : 0;
-  float wv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) wv[e] = (c + e < fi) ? bf16_to_f32(w[c + e]) : 0.f;
-  uint4 q[kR1Per];
-  float dv[kR1Per];
-#pragma unroll
-  for (int r = 0; r < kR1Per; ++r) {
-    const int b = z * kR1Rows + rg + 8 * r, bb = b < B ? b : B - 1;
-    q[r] = *reinterpret_cast<const uint4*>(y + (int64_t)bb * ldy + cl);
-    dv[r] = bf16_to_f32(dlt[(int64_t)bb * ldd]);
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int r = 0; r < kR1Per; ++r) {
-    const int b = z * kR1Rows + rg + 8 * r;
-    float f[8];
-    unpack8(q[r], f);
-    uint32_t h[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t v = (c + e < fi && f[e] > 0.f) ? f32_to_bf16(0.f + dv[r] * wv[e]) : (uint16_t)0;
-      h[e >> 1] |= (uint32_t)v << (16 * (e & 1));
-      if (b < B) acc[e] = acc[e] + bf16_to_f32(v);
-    }
-    if (b < B && live) *reinterpret_cast<uint4*>(out + (int64_t)b * ldo + c) = make_uint4(h[0], h[1], h[2], h[3]);
-  }
-  r1_group_sum(acc, red);
+  if (!do_delta) return;
+  __syncthreads();  // group 0 has read red
+  r1_group_sum(accd, red);
   if (rg == 0)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (c + e < fi) dbp[(int64_t)z * fi + c + e] = acc[e];
+      if (c + e < fi) dbp[(int64_t)z * fi + c + e] = accd[e];
 }
 
 // Batch slices of a layer's weight-gradient GEMM: about 256 tiles of 128 x
@@ -1019,9 +1004,12 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     //    delta [B][fo] and x [B][fi] are both read k-major
     const uint16_t* x = reinterpret_cast<const uint16_t*>(fws + fl.act_off[l]);
     const int splits = wgrad_splits(B, fo, fi);
+    const bool rank1_delta = fo == 1 && l > 0;  // a single-output layer above a ReLU layer
     if (fo == 1) {
-      hipLaunchKernelGGL(rank1_wgrad_kernel, dim3((unsigned)ceil_div(fi, 256), (unsigned)splits), b1, 0, stream,
-                         dlt[cur], bl.ld_dlt, x, fl.act_ld[l], M, fi, part_of(l));
+      // its weight gradient and, above a ReLU layer, the delta below in one pass
+      hipLaunchKernelGGL(rank1_kernel, dim3((unsigned)ceil_div(fi, 256), (unsigned)splits), b1, 0, stream, dlt[cur],
+                         bl.ld_dlt, x, fl.act_ld[l], M, fi, part_of(l), (int)rank1_delta,
+                         static_cast<const uint16_t*>(W[l]), dlt[cur ^ 1], bl.ld_dlt, rank1_delta ? dbp_of(l - 1) : nullptr);
       rc = launch_status();
     } else {
       rc = gemm_bf16_splitk_kmajor(dlt[cur], bl.ld_dlt, x, fl.act_ld[l], part_of(l), fo, fi, M, splits, stream);
@@ -1051,11 +1039,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
     //    read k-major where its rows allow, else through a transposed copy
     const int64_t wl = w_ld ? w_ld[l] : fi;
     const uint16_t* Wl = static_cast<const uint16_t*>(W[l]);
-    if (fo == 1 && l > 0) {  // a single-output layer above a ReLU layer
-      hipLaunchKernelGGL(rank1_delta_kernel, dim3((unsigned)ceil_div(fi, 256), (unsigned)ceil_div(B, kR1Rows)), b1, 0,
-                         stream, dlt[cur], bl.ld_dlt, Wl, x, fl.act_ld[l], M, fi, dlt[cur ^ 1], bl.ld_dlt,
-                         dbp_of(l - 1));
-      if ((rc = launch_status()) != DLRM_OK) break;
+    if (rank1_delta) {  // the delta below came out of the weight-gradient pass
       db_chunks = (int)ceil_div(B, kR1Rows);
       cur ^= 1;
       continue;
