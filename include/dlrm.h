@@ -223,6 +223,14 @@ int dlrm_embbag_interact_fwd_lp(const float* x_dense, int64_t xd_ld, const void*
  *   prob     nullable fp32 [B]; when dims[L] == 1 receives 1/(1+exp(-out)).
  *   ws       workspace of dlrm_mlp_workspace_size() bytes (256-byte aligned).
  *   save_acts != 0 keeps every layer's input in ws for dlrm_mlp_bwd.
+ *   bf16 networks ending in a hidden layer of at most 256 outputs and a
+ *   single-output layer run those two layers as one launch: the hidden
+ *   values are rounded to bf16 exactly as when stored, and the logit is
+ *   their fp32 sum of products with the last weight row (a fixed order:
+ *   per lane over its columns, then lane pairs, then four column groups)
+ *   plus the bias; its last bits can differ from dlrm_linear_fwd's
+ *   single-output kernel.  The hidden rows are written to ws only with
+ *   save_acts.
  */
 size_t dlrm_mlp_workspace_size(int64_t B, int32_t L, const int32_t* dims, int32_t w_dtype, int32_t save_acts);
 int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int64_t B, int32_t L, const int32_t* dims,
@@ -232,7 +240,9 @@ int dlrm_mlp_fwd(const void* in, int32_t in_dtype, int64_t in_ld, int64_t B, int
 
 /*
  * One fully connected bf16 layer, the building block of the bf16 MLPs above
- * (dlrm_mlp_fwd runs each of its bf16 layers with the same kernels):
+ * (dlrm_mlp_fwd runs each of its bf16 layers with the same kernels, except
+ * a last hidden layer of at most 256 outputs and the single-output layer
+ * after it, which share one launch):
  *     C = act(A W^T + b)
  * ([EXPL] Key Method Details, "Bottom MLP" / "Top MLP": FC layers with ReLU.)
  *   A        bf16 [M][lda] (lda >= K), the layer input.
