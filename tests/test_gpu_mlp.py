@@ -368,7 +368,8 @@ def test_linear_fwd_against_oracle(M, N, K, out_bf16, relu):
                                          ((64, 256, 1), 8192, False), ((64, 256, 1), 1000, True),
                                          ((40, 200, 1), 1000, False), ((40, 200, 1), 129, True),
                                          ((512, 256, 1), 333, False), ((96, 64, 1), 1, False),
-                                         ((64, 256, 256, 1), 777, True)])
+                                         ((64, 256, 256, 1), 777, True), ((40, 100, 1), 513, True),
+                                         ((136, 37, 1), 300, False)])
 def test_mlp_hidden_and_logit_layer_integer_exact(dims, B, save):
     """A hidden layer of at most 256 outputs followed by the single-output
     layer runs as one launch (the logit summed in the GEMM's epilogue).  With
@@ -376,8 +377,9 @@ def test_mlp_hidden_and_logit_layer_integer_exact(dims, B, save):
     logit, the sigmoid input and (when saved) the hidden rows equal the
     oracle's bit for bit: 128-row tiles (batches of 32768 and more) and
     64-row tiles (smaller batches), ragged batches (1, 129, 333, 777, 1000,
-    32769), hidden widths of 200 and 64 inside the 256-wide tile, and k of 40
-    and 96 (not a multiple of 64) besides 64, 256 and 512."""
+    32769), hidden widths of 200, 100 and 64 inside the 256-wide tile (and
+    37, whose rows have no 16-byte pitch), and k of 40, 96 and 136 (not a
+    multiple of 64) besides 64, 256 and 512."""
     import deep_learning_recommendation_amd as D
 
     banner(f"mlp hidden+logit integer-exact dims={dims} B={B} save={save}")
