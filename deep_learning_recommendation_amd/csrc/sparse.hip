@@ -35,8 +35,15 @@ constexpr int ITEMS = 16;              // keys per thread per tile
 constexpr int TILE = RT * ITEMS;       // 4096 positions per tile
 constexpr int kMaxDigits = 512;        // buckets of a digit of at most 9 bits
 constexpr int kHot = 128;              // occurrences from which a segment is "hot", and its block size
-constexpr int kLightBlocks = 2048;     // persistent blocks of the short-segment kernel
-constexpr int kHotBlocks = 1024;       // persistent blocks of the hot-run kernels
+// Persistent blocks of the short-segment kernel and of the hot-run kernels:
+// four and two per CU.  In a training step the update runs beside the MLP
+// GEMMs, whose workgroups find room only where these leave it; twice as many
+// blocks made each update alone under 1% faster but the training step 1-2%
+// slower (1.245 -> 1.233 ms with the synthetic gradient, 1.297 -> 1.285 ms
+// for the whole chain, 2.72 -> 2.67 ms with uniform indices); fewer (768 /
+// 384) slowed the uniform-index update by 15%.
+constexpr int kLightBlocks = 1024;
+constexpr int kHotBlocks = 512;
 
 // ------------------------------------------------------------------ keys
 
