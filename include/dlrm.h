@@ -279,7 +279,11 @@ int dlrm_linear_fwd(const void* A, int64_t lda, const void* W, int64_t ldw, cons
  *   GEMMs take bf16 operands (delta rounded to bf16) with fp32 sums.
  *   db_l sums delta_l over the batch in fp32: the fp32 delta of the last
  *   layer, the bf16-rounded delta (the GEMM operand) of the others.
- *   ws       dlrm_mlp_bwd_workspace_size() bytes.
+ *   ws       dlrm_mlp_bwd_workspace_size() bytes: the two delta buffers
+ *            and, per layer, its weight-gradient partials (one slice of the
+ *            batch each) and bias-gradient partials, which one launch after
+ *            the last layer adds up in a fixed order (dW and db are written
+ *            only then).
  */
 size_t dlrm_mlp_bwd_workspace_size(int64_t B, int32_t L, const int32_t* dims);
 int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const void* const* W, const int32_t* w_ld,
