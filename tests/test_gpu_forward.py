@@ -41,8 +41,10 @@ def test_forward_tiny_fp32():
     X, top_in, logit, prob = oracle_forward(w, dense, idx, off, bottom, top)
     gX = model.X.cpu().numpy()
     assert np.array_equal(bits(gX[:, 1:]), bits(X[:, 1:]))  # pooled embeddings bit-exact
-    # fp32 network: bottom output and logit within 1e-5 * max(1, |ref|), the
-    # probability within 1e-6 (design notes, reading 27)
+    # fp32 network: bottom output and logit within 1e-5 * max(1, |ref|) (each
+    # layer is one fp32 multiply-add chain, within gamma_65 ~ 3.9e-6 of
+    # sum |w x| + |b|, two layers compounding), the probability within 1e-6
+    # (sigma is 1/4-Lipschitz)
     assert np.all(np.abs(gX[:, 0] - X[:, 0]) <= 1e-5 * np.maximum(1, np.abs(X[:, 0])))
     gl = fused.logit.cpu().numpy()[:, 0]
     assert np.all(np.abs(gl - logit) <= 1e-5 * np.maximum(1.0, np.abs(logit)))
