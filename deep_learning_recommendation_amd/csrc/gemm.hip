@@ -723,8 +723,9 @@ void launch_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw,
 }
 
 // Tile choice: the largest block tile that still gives every CU a tile
-// (256 x 128 only where it gives each CU two; with exactly one, 128 x 128
-// measured as fast or faster).  Deep k (a multiple of 64, at least 512) runs
+// (256 x 128 only where it gives each CU two, or one with a k loop of at
+// least 2048: 5120 -> 512 at batch 16384 84.6 -> 82.1 us; with exactly one
+// and a shorter k loop, 128 x 128 measured as fast or faster).  Deep k (a multiple of 64, at least 512) runs
 // 64-wide k-tiles in two stages, fewer barriers; shallower or ragged k
 // 32-wide k-tiles in four stages.  Every choice interleaves the operand reads with the
 // MFMAs (measured 3-10% faster than reads first on every MLP shape).
@@ -741,7 +742,7 @@ void pick_fast(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, c
   else if (t256x256 >= 256)
     launch_fast<256, 256, 128, 64, OutT, PARTIAL, 32, 4, false, 1>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits,
                                                                    k_per_split, s);
-  else if (t256x128 >= 512)
+  else if (t256x128 >= 512 || (t256x128 >= 256 && deep && k_per_split >= 2048))
     launch_fast<256, 128, 64, 64, OutT, PARTIAL, 64, 2, false, 2>(A, lda, W, ldw, bias, C, ldc, M, N, K, relu, splits,
                                                                   k_per_split, s);
   else
