@@ -987,27 +987,6 @@ __global__ __launch_bounds__(256) void convert_bf16_kernel(const float* __restri
   out[(int64_t)r * ldo + c] = c < C ? f32_to_bf16(in[(int64_t)r * ldi + c]) : (uint16_t)0;
 }
 
-__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int splits, int M, int N,
-                                                            const float* __restrict__ bias, float* __restrict__ C,
-                                                            int64_t ldc, int relu) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t MN = (int64_t)M * N;
-  if (t >= MN) return;
-  const int i = (int)(t / N), j = (int)(t - (int64_t)i * N);
-  float v = 0.f;
-  for (int z0 = 0; z0 < splits; z0 += 8) {  // eight loads in flight, added in split order
-    float p[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) p[q] = (z0 + q < splits) ? part[(z0 + q) * MN + t] : 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (z0 + q < splits) v = v + p[q];
-  }
-  if (bias) v = v + bias[j];
-  if (relu) v = relu_f(v);
-  C[(int64_t)i * ldc + j] = v;
-}
-
 }  // namespace
 
 int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, void* C,
@@ -1112,17 +1091,6 @@ int gemm_bf16_dot(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw
   return launch_status();
 }
 
-int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M, int N,
-                     int K, int splits, hipStream_t s) {
-  if (M <= 0 || N <= 0) return DLRM_OK;
-  const bool fast = aligned16(A) && aligned16(W) && (lda % 8) == 0 && (ldw % 8) == 0 && lda >= K && ldw >= K &&
-                    (int64_t)256 * lda < ((int64_t)1 << 31) && (int64_t)256 * ldw < ((int64_t)1 << 31);
-  const int kps = (int)round_up(ceil_div(K > 0 ? K : 1, splits), 64);
-  if (fast) pick_fast<float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
-  else launch_generic<float, true>(A, lda, W, ldw, nullptr, part, N, M, N, K, 0, splits, kps, s);
-  return launch_status();
-}
-
 int gemm_bf16_splitk_kmajor(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M,
                             int N, int K, int splits, hipStream_t s) {
   if (M <= 0 || N <= 0) return DLRM_OK;
@@ -1130,15 +1098,6 @@ int gemm_bf16_splitk_kmajor(const uint16_t* A, int64_t lda, const uint16_t* W, i
   const int kps = (int)round_up(ceil_div(K > 0 ? K : 1, splits), 64);
   launch_fast<128, 128, 64, 64, float, true, 64, 2, false, 2, false, true, true>(A, lda, W, ldw, nullptr, part, N, M,
                                                                                 N, K, 0, splits, kps, s);
-  return launch_status();
-}
-
-int reduce_splits(const float* part, int splits, int M, int N, const float* bias, float* C, int64_t ldc, bool relu,
-                  hipStream_t s) {
-  const int64_t MN = (int64_t)M * N;
-  if (MN <= 0) return DLRM_OK;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)ceil_div(MN, 256)), dim3(256), 0, s, part, splits, M, N,
-                     bias, C, ldc, (int)relu);
   return launch_status();
 }
 

@@ -7,8 +7,6 @@ namespace dlrm {
 
 // C[M][N] = act(A[M][K] * W[N][K]^T + bias[N]) on bf16 operands with fp32
 // accumulation (MFMA).  A, W: bf16 bits; C: fp32 or bf16 (out_bf16).
-// With splits > 1, each of `splits` K-slices writes fp32 partials to
-// part[z][M][N] (no bias or activation) and reduce_splits() finishes.
 int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, void* C,
               int64_t ldc, bool out_bf16, int M, int N, int K, bool relu, hipStream_t s);
 // As gemm_bf16 without bias or activation, with operands that may be stored
@@ -47,15 +45,11 @@ struct DotOut {
 };
 int gemm_bf16_dot(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, const float* bias, uint16_t* H,
                   int64_t ldh, int M, int N, int K, const DotOut& dot, hipStream_t s);
-int gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M, int N,
-                     int K, int splits, hipStream_t s);
 // Split-K partials with both operands k-major: part[z][M][N] = the sum over
 // slice z of k of A[k][m] W[k][n] (A [K][M], W [K][N]), e.g. a weight
 // gradient delta^T x straight from the row-major delta and activations.
 int gemm_bf16_splitk_kmajor(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, float* part, int M,
                             int N, int K, int splits, hipStream_t s);
-int reduce_splits(const float* part, int splits, int M, int N, const float* bias, float* C, int64_t ldc,
-                  bool relu, hipStream_t s);
 
 // N == 1 layer: out[m] = sum_k A[m][k] w[k] + bias; prob = sigmoid(out).
 int gemv_bf16(const uint16_t* A, int64_t lda, const uint16_t* w, const float* bias, float* out, int64_t ldo,

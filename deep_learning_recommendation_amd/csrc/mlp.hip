@@ -425,9 +425,9 @@ __device__ __forceinline__ bool positive<uint16_t>(const uint16_t* p) {
 }
 
 // One pass over the upstream gradient of a layer: delta = g * 1[y > 0] (or
-// g) rounded to bf16 and stored row-major [B][ldd] (for the input gradient)
-// and transposed [N][ldt] (for the weight gradient, K = batch contiguous),
-// plus fp32 column sums of delta per 32-row chunk (for the bias gradient).
+// g) rounded to bf16 and stored row-major [B][ldd] (the operand of both the
+// input-gradient and the weight-gradient GEMMs), plus fp32 column sums of
+// delta per 32-row chunk (for the bias gradient).
 // Block: 32 rows x 256 columns; wave w takes rows w, w+4, ..., lane l the
 // four consecutive columns 4l .. 4l+3 (16-byte loads of g, 8- or 16-byte
 // loads of y, 8-byte stores of delta when `vec`), eight rows' loads in flight
@@ -455,9 +455,7 @@ template <typename YT>
 __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__ g, int64_t ldg,
                                                        const YT* __restrict__ y, int64_t ldy, int relu,
                                                        uint16_t* __restrict__ dlt, int64_t ldd,
-                                                       uint16_t* __restrict__ dltT, int64_t ldt,
                                                        float* __restrict__ part, int B, int N, int vec) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kDRows][kDCols + 8];
   __shared__ float red[4][kDCols];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = blockIdx.x * kDCols, r0 = blockIdx.y * kDRows;
@@ -498,8 +496,6 @@ __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__
         h[e] = f32_to_bf16(v[e]);
         sum[e] = sum[e] + v[e];
       }
-      *reinterpret_cast<uint2*>(&tile[i][cl]) =
-          make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
       if (r < B) {
         uint16_t* o = dlt + (int64_t)r * ldd + c;
         if (full) {
@@ -519,19 +515,6 @@ __global__ __launch_bounds__(256) void delta_db_kernel(const float* __restrict__
   {
     const int cc = threadIdx.x, col = c0 + cc;
     if (col < N) part[(int64_t)blockIdx.y * N + col] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
-    if (col < N && dltT) {
-      // column cc of the tile is row col of delta^T: 64 rows, 8 per 16-byte store
-      uint16_t* dst = dltT + (int64_t)col * ldt + r0;
-#pragma unroll
-      for (int j = 0; j < kDRows / 8; ++j) {
-        if (r0 + 8 * j >= B) break;
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          w[q] = (uint32_t)tile[8 * j + 2 * q][cc] | ((uint32_t)tile[8 * j + 2 * q + 1][cc] << 16);
-        *reinterpret_cast<uint4*>(dst + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
   }
 }
 
@@ -993,7 +976,7 @@ extern "C" int dlrm_mlp_bwd(int64_t B, int32_t L, const int32_t* dims, const voi
                          dlt[0], bl.ld_dlt, dbp_of(L - 1), M);
     else
       hipLaunchKernelGGL((delta_db_kernel<float>), dim3((unsigned)ceil_div(fo, kDCols), (unsigned)chunks), b1, 0,
-                         stream, dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, nullptr, 0, dbp_of(L - 1), M, fo, vec);
+                         stream, dY, dy_ld, y, ldy, (int)relu, dlt[0], bl.ld_dlt, dbp_of(L - 1), M, fo, vec);
     db_chunks = chunks;
     rc = launch_status();
   }
